@@ -1,0 +1,256 @@
+"""Python binding of the CPU oracle (``rmsnorm_oracle.cpp``) — TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The GPU library does not use it.
+
+Arrays are numpy: bf16 values as ``uint16`` raw bits, fp32 as ``float32``,
+the exact forms as ``float64``. Outputs are freshly allocated and returned.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_LIB_PATH = _HERE / "liboracle_rmsnorm.so"
+_lib = None
+
+R64, A32 = 0, 1
+
+
+def build(force: bool = True, extra_flags: tuple[str, ...] = ()) -> Path:
+    """Compile the oracle with g++ (no fast-math, no FMA contraction)."""
+    if force or not _LIB_PATH.exists():
+        tmp = _LIB_PATH.with_suffix(".so.tmp")
+        subprocess.run(
+            ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math",
+             "-fPIC", "-shared", *extra_flags, str(_HERE / "rmsnorm_oracle.cpp"),
+             "-o", str(tmp)],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        build(force=False)
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    i, i64, f, d, vp = (ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                        ctypes.c_double, ctypes.c_void_p)
+    sigs = {
+        "oracle_bf16_decode": ([vp, i64, vp], None),
+        "oracle_bf16_encode": ([vp, i64, vp], None),
+        "oracle_weights": ([vp, i, i64, vp], i),
+        "oracle_rmsnorm_fwd": ([i, vp, i64, vp, i, f, i64, i64, vp, i64, vp], i),
+        "oracle_rmsnorm_residual_fwd": ([i, vp, i64, vp, i, f, i64, i64, vp, i64,
+                                         vp, i64, vp], i),
+        "oracle_rmsnorm_gated_fwd": ([i, vp, i64, vp, i64, vp, i, f, i64, i64, vp,
+                                      i64, vp], i),
+        "oracle_rmsnorm_bwd_dx": ([i, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64,
+                                   vp, i64], i),
+        "oracle_rmsnorm_dgamma": ([i, vp, i64, vp, i64, vp, i64, i64, vp], i),
+        "oracle_rmsnorm_fwd_f64": ([vp, vp, i, d, i64, i64, vp, vp], i),
+        "oracle_rmsnorm_gated_fwd_f64": ([vp, vp, vp, i, d, i64, i64, vp], i),
+        "oracle_rmsnorm_bwd_f64": ([vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
+        "oracle_set_mutation": ([i], None),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _bf16_2d(a, D=None):
+    a = np.asarray(a)
+    assert a.dtype == np.uint16 and a.ndim == 2, "bf16 [T, ld] uint16"
+    if a.shape[0] <= 1:
+        return np.ascontiguousarray(a)
+    if a.strides[1] != 2 or a.strides[0] % 2 or a.strides[0] < 2 * a.shape[1]:
+        a = np.ascontiguousarray(a)
+    return a
+
+
+def _ld(a):
+    """Row stride in elements (any value >= D for a batch of at most one row)."""
+    return a.strides[0] // 2 if a.shape[0] > 1 else a.shape[1]
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: bad argument (rc={rc})")
+
+
+# ---- bf16 codec ----------------------------------------------------------------
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float32)
+    _load().oracle_bf16_decode(_p(bits), bits.size, _p(out))
+    return out
+
+
+def bf16_encode(vals: np.ndarray) -> np.ndarray:
+    vals = np.ascontiguousarray(vals, dtype=np.float32)
+    out = np.empty(vals.shape, dtype=np.uint16)
+    _load().oracle_bf16_encode(_p(vals), vals.size, _p(out))
+    return out
+
+
+def weights(gamma: np.ndarray, zero_centered: bool) -> np.ndarray:
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    out = np.empty_like(gamma)
+    _check(_load().oracle_weights(_p(gamma), int(zero_centered), gamma.size, _p(out)),
+           "weights")
+    return out
+
+
+# ---- rounded forms (R64 parity reference, A32 report mode) ---------------------
+
+def _shape(x, D):
+    T = x.shape[0]
+    return T, (x.shape[1] if D is None else D)
+
+
+def fwd(x, gamma, zero_centered=False, eps=1e-6, mode=R64, D=None):
+    """(y bf16 [T, D], rstd fp32 [T]). ``D`` < row stride lets x be strided."""
+    x = _bf16_2d(x, D)
+    T, D = _shape(x, D)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    y = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_fwd(mode, _p(x), _ld(x), _p(gamma),
+                                      int(zero_centered), eps, T, D, _p(y), D, _p(rstd)),
+           "fwd")
+    return y, rstd
+
+
+def residual_fwd(x, gamma, zero_centered=False, eps=1e-6, mode=R64, D=None):
+    """(y, residual_out, rstd)."""
+    x = _bf16_2d(x, D)
+    T, D = _shape(x, D)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    y = np.empty((T, D), dtype=np.uint16)
+    res = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_residual_fwd(mode, _p(x), _ld(x), _p(gamma),
+                                               int(zero_centered), eps, T, D, _p(y), D,
+                                               _p(res), D, _p(rstd)),
+           "residual_fwd")
+    return y, res, rstd
+
+
+def gated_fwd(x, z, gamma, zero_centered=False, eps=1e-6, mode=R64, D=None):
+    """(out bf16, rstd)."""
+    x = _bf16_2d(x, D)
+    z = _bf16_2d(z, D)
+    T, D = _shape(x, D)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    out = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_gated_fwd(mode, _p(x), _ld(x), _p(z),
+                                            _ld(z), _p(gamma),
+                                            int(zero_centered), eps, T, D, _p(out), D,
+                                            _p(rstd)),
+           "gated_fwd")
+    return out, rstd
+
+
+def bwd_dx(g, x, rstd, gamma, zero_centered=False, gres=None, mode=R64, D=None):
+    g = _bf16_2d(g, D)
+    x = _bf16_2d(x, D)
+    T, D = _shape(x, D)
+    rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    if gres is not None:
+        gres = _bf16_2d(gres, D)
+    dx = np.empty((T, D), dtype=np.uint16)
+    _check(_load().oracle_rmsnorm_bwd_dx(mode, _p(g), _ld(g), _p(x),
+                                         _ld(x), _p(rstd), _p(gamma),
+                                         int(zero_centered), T, D, _p(gres),
+                                         0 if gres is None else _ld(gres),
+                                         _p(dx), D),
+           "bwd_dx")
+    return dx
+
+
+def dgamma(g, x, rstd, mode=R64, D=None):
+    g = _bf16_2d(g, D)
+    x = _bf16_2d(x, D)
+    T, D = _shape(x, D)
+    rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+    out = np.empty(D, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_dgamma(mode, _p(g), _ld(g), _p(x),
+                                         _ld(x), _p(rstd), T, D, _p(out)),
+           "dgamma")
+    return out
+
+
+def bwd(g, x, rstd, gamma, zero_centered=False, gres=None, mode=R64):
+    """(dx bf16 [T, D], dgamma fp32 [D])."""
+    return (bwd_dx(g, x, rstd, gamma, zero_centered, gres, mode),
+            dgamma(g, x, rstd, mode))
+
+
+# ---- exact double forms --------------------------------------------------------
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def fwd_f64(x, gamma, zero_centered=False, eps=1e-6):
+    x, gamma = _f64(x), _f64(gamma)
+    T, D = x.shape
+    y = np.empty((T, D))
+    rstd = np.empty(T)
+    _check(_load().oracle_rmsnorm_fwd_f64(_p(x), _p(gamma), int(zero_centered), eps,
+                                          T, D, _p(y), _p(rstd)), "fwd_f64")
+    return y, rstd
+
+
+def gated_fwd_f64(x, z, gamma, zero_centered=False, eps=1e-6):
+    x, z, gamma = _f64(x), _f64(z), _f64(gamma)
+    T, D = x.shape
+    out = np.empty((T, D))
+    _check(_load().oracle_rmsnorm_gated_fwd_f64(_p(x), _p(z), _p(gamma),
+                                                int(zero_centered), eps, T, D, _p(out)),
+           "gated_fwd_f64")
+    return out
+
+
+def bwd_f64(g, x, gamma, zero_centered=False, eps=1e-6, gres=None):
+    g, x, gamma = _f64(g), _f64(x), _f64(gamma)
+    gres = None if gres is None else _f64(gres)
+    T, D = x.shape
+    dx = np.empty((T, D))
+    dg = np.empty(D)
+    _check(_load().oracle_rmsnorm_bwd_f64(_p(g), _p(x), _p(gamma), int(zero_centered),
+                                          eps, T, D, _p(gres), _p(dx), _p(dg)),
+           "bwd_f64")
+    return dx, dg
+
+
+@contextlib.contextmanager
+def mutation(m: int):
+    """Plant one of the two defects (1: forward drops the zero-centred offset;
+    2: dx's second term takes the weight twice) for the duration of a block."""
+    lib = _load()
+    lib.oracle_set_mutation(m)
+    try:
+        yield
+    finally:
+        lib.oracle_set_mutation(0)

@@ -1,0 +1,278 @@
+// CPU oracle for batch-invariant RMSNorm — TEST INFRASTRUCTURE ONLY.
+// Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+// load it. Build: g++ -std=c++17 -O2 -ffp-contract=off (no fast-math), so
+// every `float` expression below is exactly one IEEE fp32 operation rounded
+// to nearest-even. Sources and modes are described in rmsnorm_oracle.h.
+#include "rmsnorm_oracle.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace {
+
+int g_mutation = 0;
+
+float bf16_to_f32(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Round to nearest, ties to even: add 0x7FFF plus the lowest kept bit, then
+// drop the low 16 bits. A carry out of the mantissa moves into the exponent,
+// which is also how values past the largest bf16 become infinity.
+uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u)  // NaN: keep sign, force quiet bit
+    return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return static_cast<uint16_t>(u >> 16);
+}
+
+bool bad_2d(const void* p, int64_t ld, int64_t D) { return p == nullptr || ld < D; }
+
+// w_eff = fp32(gamma) (+ 1.0f in fp32 when zero-centred).
+float weight_eff(const float* gamma, int zc, int64_t j) {
+  float w = gamma[j];
+  if (zc) w = w + 1.0f;
+  return w;
+}
+
+// A reduction of fp32 terms in ascending order: in double, rounded once (R64)
+// or in fp32 (A32).
+struct Sum {
+  int mode;
+  double d = 0.0;
+  float f = 0.0f;
+  explicit Sum(int m) : mode(m) {}
+  void add(float t) {
+    if (mode == ORACLE_A32)
+      f = f + t;
+    else
+      d = d + static_cast<double>(t);
+  }
+  float value() const { return mode == ORACLE_A32 ? f : static_cast<float>(d); }
+};
+
+// rsqrt(v) = 1/sqrt(v) in double, rounded to fp32.
+float rsqrt_ref(float v) {
+  return static_cast<float>(1.0 / std::sqrt(static_cast<double>(v)));
+}
+
+// Steps (i)-(v) of the forward for one row: the row's rstd.
+float row_rstd(int mode, const uint16_t* xr, int64_t D, float eps) {
+  Sum ss(mode);
+  for (int64_t j = 0; j < D; ++j) {
+    const float xf = bf16_to_f32(xr[j]);
+    const float sq = xf * xf;
+    ss.add(sq);
+  }
+  const float mean = ss.value() / static_cast<float>(D);
+  const float v = mean + eps;
+  return rsqrt_ref(v);
+}
+
+// n_j = (x_j * r) * w_j, the normalised and weighted value before rounding.
+float row_normed(float xf, float r, float w) {
+  const float xr = xf * r;
+  return xr * w;
+}
+
+bool bad_mode(int mode) { return mode != ORACLE_R64 && mode != ORACLE_A32; }
+
+double silu_d(double z) { return z / (1.0 + std::exp(-z)); }
+
+}  // namespace
+
+extern "C" {
+
+void oracle_set_mutation(int mutation) { g_mutation = mutation; }
+
+void oracle_bf16_decode(const uint16_t* in, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_f32(in[i]);
+}
+
+void oracle_bf16_encode(const float* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16(in[i]);
+}
+
+int oracle_weights(const float* gamma, int zero_centered, int64_t D, float* w_eff) {
+  if (!gamma || !w_eff || D <= 0) return -1;
+  for (int64_t j = 0; j < D; ++j) w_eff[j] = weight_eff(gamma, zero_centered, j);
+  return 0;
+}
+
+static int fwd_common(int mode, const uint16_t* x, int64_t ld_x, const uint16_t* z,
+                      int64_t ld_z, const float* gamma, int zc, float eps, int64_t T,
+                      int64_t D, uint16_t* y, int64_t ld_y, uint16_t* res,
+                      int64_t ld_res, float* rstd) {
+  if (bad_mode(mode) || T < 0 || D <= 0 || !gamma || bad_2d(x, ld_x, D) ||
+      bad_2d(y, ld_y, D))
+    return -1;
+  // Defect 1 of [MEG] (test-only): the forward reads the raw weight.
+  const int zc_fwd = (g_mutation == 1) ? 0 : zc;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + t * ld_x;
+    const float r = row_rstd(mode, xr, D, eps);
+    if (rstd) rstd[t] = r;
+    for (int64_t j = 0; j < D; ++j) {
+      const float n = row_normed(bf16_to_f32(xr[j]), r, weight_eff(gamma, zc_fwd, j));
+      float o = n;
+      if (z) {
+        const float zf = bf16_to_f32(z[t * ld_z + j]);
+        const float sg = static_cast<float>(silu_d(static_cast<double>(zf)));
+        o = n * sg;
+      }
+      y[t * ld_y + j] = f32_to_bf16(o);
+      if (res) res[t * ld_res + j] = xr[j];
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_fwd(int mode, const uint16_t* x, int64_t ld_x, const float* gamma,
+                       int zero_centered, float eps, int64_t T, int64_t D, uint16_t* y,
+                       int64_t ld_y, float* rstd) {
+  return fwd_common(mode, x, ld_x, nullptr, 0, gamma, zero_centered, eps, T, D, y, ld_y,
+                    nullptr, 0, rstd);
+}
+
+int oracle_rmsnorm_residual_fwd(int mode, const uint16_t* x, int64_t ld_x,
+                                const float* gamma, int zero_centered, float eps,
+                                int64_t T, int64_t D, uint16_t* y, int64_t ld_y,
+                                uint16_t* residual_out, int64_t ld_res, float* rstd) {
+  if (bad_2d(residual_out, ld_res, D)) return -1;
+  return fwd_common(mode, x, ld_x, nullptr, 0, gamma, zero_centered, eps, T, D, y, ld_y,
+                    residual_out, ld_res, rstd);
+}
+
+int oracle_rmsnorm_gated_fwd(int mode, const uint16_t* x, int64_t ld_x, const uint16_t* z,
+                             int64_t ld_z, const float* gamma, int zero_centered, float eps,
+                             int64_t T, int64_t D, uint16_t* out, int64_t ld_out,
+                             float* rstd) {
+  if (bad_2d(z, ld_z, D)) return -1;
+  return fwd_common(mode, x, ld_x, z, ld_z, gamma, zero_centered, eps, T, D, out, ld_out,
+                    nullptr, 0, rstd);
+}
+
+int oracle_rmsnorm_bwd_dx(int mode, const uint16_t* g, int64_t ld_g, const uint16_t* x,
+                          int64_t ld_x, const float* rstd, const float* gamma,
+                          int zero_centered, int64_t T, int64_t D, const uint16_t* gres,
+                          int64_t ld_gres, uint16_t* dx, int64_t ld_dx) {
+  if (bad_mode(mode) || T < 0 || D <= 0 || !gamma || !rstd || bad_2d(g, ld_g, D) ||
+      bad_2d(x, ld_x, D) || bad_2d(dx, ld_dx, D) || (gres && ld_gres < D))
+    return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* gr = g + t * ld_g;
+    const uint16_t* xr = x + t * ld_x;
+    const float r = rstd[t];
+    Sum s(mode);
+    for (int64_t i = 0; i < D; ++i) {
+      const float gw = bf16_to_f32(gr[i]) * weight_eff(gamma, zero_centered, i);
+      const float term = gw * bf16_to_f32(xr[i]);
+      s.add(term);
+    }
+    const float r2 = r * r;
+    const float r3 = r2 * r;
+    const float r3s = r3 * s.value();
+    const float c = r3s / static_cast<float>(D);
+    for (int64_t k = 0; k < D; ++k) {
+      const float w = weight_eff(gamma, zero_centered, k);
+      const float xf = bf16_to_f32(xr[k]);
+      const float gw = bf16_to_f32(gr[k]) * w;
+      const float t1 = gw * r;
+      float t2 = xf * c;
+      if (g_mutation == 2) t2 = t2 * w;  // defect 2 of [MEG] (test-only)
+      float d = t1 - t2;
+      if (gres) d = d + bf16_to_f32(gres[t * ld_gres + k]);
+      dx[t * ld_dx + k] = f32_to_bf16(d);
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_dgamma(int mode, const uint16_t* g, int64_t ld_g, const uint16_t* x,
+                          int64_t ld_x, const float* rstd, int64_t T, int64_t ncols,
+                          float* dgamma) {
+  if (bad_mode(mode) || T < 0 || ncols <= 0 || !dgamma || bad_2d(g, ld_g, ncols) ||
+      bad_2d(x, ld_x, ncols) || (T > 0 && !rstd))
+    return -1;
+  for (int64_t j = 0; j < ncols; ++j) {
+    Sum acc(mode);
+    for (int64_t t = 0; t < T; ++t) {
+      const float gx = bf16_to_f32(g[t * ld_g + j]) * bf16_to_f32(x[t * ld_x + j]);
+      const float term = gx * rstd[t];
+      acc.add(term);
+    }
+    dgamma[j] = acc.value();
+  }
+  return 0;
+}
+
+// ---- exact double forms ----------------------------------------------------
+
+static double weight_eff_d(const double* gamma, int zc, int64_t j) {
+  return zc ? gamma[j] + 1.0 : gamma[j];
+}
+
+static double row_rstd_d(const double* xr, int64_t D, double eps) {
+  double ss = 0.0;
+  for (int64_t j = 0; j < D; ++j) ss += xr[j] * xr[j];
+  return 1.0 / std::sqrt(ss / static_cast<double>(D) + eps);
+}
+
+int oracle_rmsnorm_fwd_f64(const double* x, const double* gamma, int zero_centered,
+                           double eps, int64_t T, int64_t D, double* y, double* rstd) {
+  if (!x || !gamma || !y || T < 0 || D <= 0) return -1;
+  const int zc_fwd = (g_mutation == 1) ? 0 : zero_centered;
+  for (int64_t t = 0; t < T; ++t) {
+    const double r = row_rstd_d(x + t * D, D, eps);
+    if (rstd) rstd[t] = r;
+    for (int64_t j = 0; j < D; ++j)
+      y[t * D + j] = x[t * D + j] * r * weight_eff_d(gamma, zc_fwd, j);
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_gated_fwd_f64(const double* x, const double* z, const double* gamma,
+                                 int zero_centered, double eps, int64_t T, int64_t D,
+                                 double* out) {
+  if (!x || !z || !gamma || !out || T < 0 || D <= 0) return -1;
+  const int zc_fwd = (g_mutation == 1) ? 0 : zero_centered;
+  for (int64_t t = 0; t < T; ++t) {
+    const double r = row_rstd_d(x + t * D, D, eps);
+    for (int64_t j = 0; j < D; ++j)
+      out[t * D + j] =
+          x[t * D + j] * r * weight_eff_d(gamma, zc_fwd, j) * silu_d(z[t * D + j]);
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_bwd_f64(const double* g, const double* x, const double* gamma,
+                           int zero_centered, double eps, int64_t T, int64_t D,
+                           const double* gres, double* dx, double* dgamma) {
+  if (!g || !x || !gamma || T < 0 || D <= 0 || (!dx && !dgamma)) return -1;
+  if (dgamma)
+    for (int64_t j = 0; j < D; ++j) dgamma[j] = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    const double* gr = g + t * D;
+    const double* xr = x + t * D;
+    const double r = row_rstd_d(xr, D, eps);
+    // s = sum_i g_i x_i w_i; dr/dx_k = -r^3 x_k / D.
+    double s = 0.0;
+    for (int64_t i = 0; i < D; ++i) s += gr[i] * xr[i] * weight_eff_d(gamma, zero_centered, i);
+    for (int64_t k = 0; k < D; ++k) {
+      const double w = weight_eff_d(gamma, zero_centered, k);
+      double second = r * r * r * xr[k] / static_cast<double>(D) * s;
+      if (g_mutation == 2) second *= w;
+      if (dx) dx[t * D + k] = gr[k] * w * r - second + (gres ? gres[t * D + k] : 0.0);
+      if (dgamma) dgamma[k] += gr[k] * xr[k] * r;
+    }
+  }
+  return 0;
+}
+
+}  // extern "C"

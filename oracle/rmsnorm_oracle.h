@@ -1,0 +1,130 @@
+/*
+ * CPU oracle for batch-invariant RMSNorm — TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct host implementation of what the GPU
+ * library computes, used to check it. Only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg may load or call this library; the
+ * GPU library never links, includes or calls it, and the two share no code.
+ *
+ * Sources (pages by title; section / equation named, no line numbers):
+ *  [MEG]  Megatron-LM PR "Fix the batch-invariant RMSNorm forward and its
+ *         input gradient", section "What does this PR do?": item 1 (the
+ *         zero-centred offset is added after the cast to fp32, in forward and
+ *         backward alike) and item 2 (the input-gradient equation, the weight
+ *         entering once per term; the weight gradient as the plain sum).
+ *  [C1]   RL-Kernel PR "C1: zero-centred RMSNorm references and CUDA kernel":
+ *         the +1 of the zero-centred weight is an fp32 operation; the gated
+ *         norm's SiLU gate with the weight multiply in fp32; the backward
+ *         reuses the forward's saved rstd.
+ *  [RES]  RL-Kernel PR "[DSv4][P1-5] rmsnorm_residual", sections "Summary",
+ *         "Implementation" and the review comment: output is RMSNorm(x) plus
+ *         a byte copy of x; bf16 activations, fp32 gamma, fp32 saved inverse
+ *         RMS, fp32 dgamma; r = rsqrt(mean(x^2) + eps); y = (x * r) * gamma;
+ *         mul and add rounded separately; dx gains the residual branch's
+ *         gradient; dgamma = sum over tokens of dy * x * r.
+ *
+ * Arithmetic modes (argument `mode`):
+ *  ORACLE_R64 (0, the parity reference): every elementwise step is one fp32
+ *     operation rounded to nearest-even, with no FMA contraction (built with
+ *     -ffp-contract=off). The three reductions (sum of squares, the row dot
+ *     product, dgamma over rows) add the fp32 terms in ascending index order
+ *     in double and round the total to fp32 once, so their result does not
+ *     depend on any reduction tree. rsqrt is 1/sqrt taken in double and
+ *     rounded to fp32.
+ *  ORACLE_A32 (1): identical, except the three reductions accumulate in fp32
+ *     in ascending order (the "ascending FP32 reductions" of [RES]). Used only
+ *     to report how far that convention sits from R64.
+ *  The *_f64 entry points take double inputs and compute everything in
+ *     double with no intermediate rounding; they are the exact formulas used
+ *     for finite-difference and invariant checks.
+ *
+ * Layouts: activations are row-major [T, D] with row stride ld >= D
+ * elements; bf16 values travel as raw uint16_t bits. gamma, rstd and dgamma
+ * are fp32. All pointers are host memory owned by the caller. Functions
+ * return 0 on success and -1 on a bad argument (NULL where an array is
+ * needed, T < 0, D <= 0, ld < D), writing nothing in that case.
+ */
+#ifndef RMSNORM_ORACLE_H
+#define RMSNORM_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_R64 = 0, ORACLE_A32 = 1 };
+
+/* bf16 codec: decode is exact (bits << 16); encode rounds to nearest,
+ * ties to even, keeps subnormals, sends overflow to +-inf and maps NaN to a
+ * quiet NaN of the same sign. */
+void oracle_bf16_decode(const uint16_t* in, int64_t n, float* out);
+void oracle_bf16_encode(const float* in, int64_t n, uint16_t* out);
+
+/* w_eff[j] = gamma[j], plus 1.0f in fp32 when zero_centered ([MEG] item 1). */
+int oracle_weights(const float* gamma, int zero_centered, int64_t D, float* w_eff);
+
+/* Forward: rstd[t] = rsqrt(mean_j x^2 + eps); y = bf16((x * r) * w_eff).
+ * rstd may be NULL. */
+int oracle_rmsnorm_fwd(int mode, const uint16_t* x, int64_t ld_x,
+                       const float* gamma, int zero_centered, float eps,
+                       int64_t T, int64_t D, uint16_t* y, int64_t ld_y,
+                       float* rstd);
+
+/* Forward plus residual_out = a byte copy of x ([RES] "Summary"). */
+int oracle_rmsnorm_residual_fwd(int mode, const uint16_t* x, int64_t ld_x,
+                                const float* gamma, int zero_centered,
+                                float eps, int64_t T, int64_t D, uint16_t* y,
+                                int64_t ld_y, uint16_t* residual_out,
+                                int64_t ld_res, float* rstd);
+
+/* SiLU-gated forward ([C1]): n = (x * r) * w_eff in fp32, silu(z) =
+ * z / (1 + exp(-z)) evaluated in double and rounded to fp32,
+ * out = bf16(n * silu(z)). rstd may be NULL. */
+int oracle_rmsnorm_gated_fwd(int mode, const uint16_t* x, int64_t ld_x,
+                             const uint16_t* z, int64_t ld_z,
+                             const float* gamma, int zero_centered, float eps,
+                             int64_t T, int64_t D, uint16_t* out,
+                             int64_t ld_out, float* rstd);
+
+/* Input gradient from the saved rstd ([MEG] item 2, [RES] review):
+ *   gw = g * w_eff; s = sum_j gw_j * x_j; c = ((r*r)*r)*s / D;
+ *   dx = bf16((gw * r - x * c) [+ gres]).
+ * gres may be NULL (ld_gres ignored then). */
+int oracle_rmsnorm_bwd_dx(int mode, const uint16_t* g, int64_t ld_g,
+                          const uint16_t* x, int64_t ld_x, const float* rstd,
+                          const float* gamma, int zero_centered, int64_t T,
+                          int64_t D, const uint16_t* gres, int64_t ld_gres,
+                          uint16_t* dx, int64_t ld_dx);
+
+/* Weight gradient over `ncols` columns: dgamma[j] = sum over t ascending of
+ * (g[t][j] * x[t][j]) * rstd[t]. Independent of the zero-centred flag since
+ * d(w_eff)/d(gamma) = 1. T = 0 gives zeros. */
+int oracle_rmsnorm_dgamma(int mode, const uint16_t* g, int64_t ld_g,
+                          const uint16_t* x, int64_t ld_x, const float* rstd,
+                          int64_t T, int64_t ncols, float* dgamma);
+
+/* Exact (double) forms. w_eff = gamma (+1.0 when zero_centered). */
+int oracle_rmsnorm_fwd_f64(const double* x, const double* gamma,
+                           int zero_centered, double eps, int64_t T, int64_t D,
+                           double* y, double* rstd);
+int oracle_rmsnorm_gated_fwd_f64(const double* x, const double* z,
+                                 const double* gamma, int zero_centered,
+                                 double eps, int64_t T, int64_t D, double* out);
+/* dx (may be NULL) and dgamma (may be NULL) of L = sum g*y, with r recomputed
+ * in double from x. gres (may be NULL) is added to dx. */
+int oracle_rmsnorm_bwd_f64(const double* g, const double* x,
+                           const double* gamma, int zero_centered, double eps,
+                           int64_t T, int64_t D, const double* gres,
+                           double* dx, double* dgamma);
+
+/* Test-only defect planting, so the tests can show that their checks catch
+ * the two defects [MEG] fixes: 0 = none; 1 = the forward ignores the
+ * zero-centred offset (the backward still honours it); 2 = the second term
+ * of dx is multiplied by w_eff[k] a second time. Affects R64/A32 and f64. */
+void oracle_set_mutation(int mutation);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

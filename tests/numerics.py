@@ -1,0 +1,68 @@
+"""Comparison helpers for the tests (numpy / torch library routines only).
+
+Nothing here computes RMSNorm: these functions compare bf16 results with
+exact or reference values, using torch's own bf16 conversions so that the
+comparisons do not rely on the oracle's codec.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+U32 = 2.0 ** -24  # fp32 unit roundoff
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bits (torch's conversion)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    t = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+def f32_to_bf16_torch(v: np.ndarray) -> np.ndarray:
+    """torch's fp32 -> bf16 conversion (round to nearest even), as bits."""
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def ordered(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits -> integers ordered like the values; +0 and -0 both map to 0."""
+    b = bits.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def is_nan_bf16(bits: np.ndarray) -> np.ndarray:
+    return (bits & 0x7FFF) > 0x7F80
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|ordered(a) - ordered(b)|; NaN vs NaN counts 0, NaN vs number a huge value."""
+    d = np.abs(ordered(a) - ordered(b))
+    na, nb = is_nan_bf16(a), is_nan_bf16(b)
+    d = np.where(na & nb, 0, d)
+    return np.where(na ^ nb, 1 << 20, d)
+
+
+def rounding_consistent(res_bits: np.ndarray, exact: np.ndarray,
+                        err_bound: np.ndarray | float) -> np.ndarray:
+    """Mask of elements where a bf16 result is a correct rounding of a value
+    within ``err_bound`` of ``exact``.
+
+    A result equal to bf16_rne(exact) always passes; the other bf16 neighbour
+    passes only when ``exact`` lies within ``err_bound`` of the midpoint
+    between them. Formally: |res - exact| <= |nearest - exact| + 2*err_bound.
+    """
+    res = bf16_to_f64(res_bits)
+    exact = np.asarray(exact, dtype=np.float64)
+    nearest = bf16_to_f64(f32_to_bf16_torch(exact.astype(np.float32)))
+    with np.errstate(invalid="ignore"):
+        ok = np.abs(res - exact) <= np.abs(nearest - exact) + 2.0 * err_bound + 1e-300
+        same_nonfinite = (~np.isfinite(res)) & (~np.isfinite(exact)) & (
+            (np.isnan(res) & np.isnan(exact)) | (res == exact))
+    return ok | same_nonfinite
