@@ -1,0 +1,280 @@
+"""Throughput of batch-invariant RMSNorm forward + backward on one MI355X.
+
+A step is one pass of the whole path over one batch: rmsnorm_fwd (y, rstd),
+then the backward's two kernels, rmsnorm_bwd_rows (dx and the dgamma chunk
+partials) and rmsnorm_bwd_finish (dgamma). Inputs are resident in HBM before
+timing starts. The default workload is the token norm at T=32768, D=4096
+(bf16 activations with 1% outlier rows, fp32 gamma, eps=1e-6); --workload
+selects the other synthetic workloads.
+
+Prints one JSON line. `value` is algorithmic bytes per step / time per step:
+each input element read once, each output written once (formulas in
+ALGO_BYTES). `roofline` reports the dominant kernel (the backward rows
+kernel) against MI355X's 8 TB/s HBM peak, from HIP events recorded around
+that kernel's launches on the stream it runs on. `cpu_baseline` times the CPU
+oracle on the host cores for the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "RMSNorm fwd+bwd GB/s and % HBM peak, T=32768 D=4096 bf16, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = ROOT / "profiles" / "traffic_bwd_rows_T32768_D4096.json"
+BWD_SOURCES = ["bwd.hip", "device_common.hpp", "geometry.hpp", "launch.hpp"]
+
+
+def algo_bytes(kind: str, T: int, D: int) -> int:
+    """Algorithmic bytes (each input read once, each output written once)."""
+    return {
+        "fwd": T * (4 * D + 4) + 4 * D,            # x in, y out, rstd out, gamma in
+        "residual_fwd": T * (6 * D + 4) + 4 * D,   # + residual copy out
+        "gated_fwd": T * 6 * D + 4 * D,            # x, z in, out out, gamma in
+        "bwd_rows": T * (6 * D + 4) + 4 * D,       # g, x in, rstd in, dx out, gamma in
+        "bwd_rows_gres": T * (8 * D + 4) + 4 * D,  # + residual gradient in
+        "bwd_finish": 4 * D,                       # dgamma out
+    }[kind]
+
+
+def bwd_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in BWD_SOURCES:
+        h.update((ROOT / "invariant_rmsnorm_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the rows kernel from committed rocprofv3
+    counter runs, or None if absent or taken on a different kernel source."""
+    try:
+        rec = json.loads(TRAFFIC_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != bwd_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def make_inputs(workload: str, torch, dev):
+    import numpy as np
+    from synth import workloads as wl
+
+    def d_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if workload in ("token", "token_gres"):
+        p = wl.residual(with_gres=(workload == "token_gres"))
+        desc = ("token RMSNorm fwd+bwd with dgamma, T=32768, D=4096, bf16 x ~N(0,1) with 1% "
+                "outlier rows x50, g ~N(0,1), fp32 gamma=1+N(0,0.1), eps=1e-6")
+    elif workload == "large":
+        p = wl.large()
+        desc = ("RMSNorm fwd+bwd with dgamma, T=262144, D=4096, zero-centred gamma, "
+                "g ~0.01 N(0,1), eps=1e-6")
+    elif workload == "gated":
+        p = wl.gated()
+        desc = "SiLU-gated per-head RMSNorm forward, 262144 rows x D=128, x,z ~N(0,1)"
+    else:
+        raise SystemExit(f"unknown workload {workload}")
+    t = {"x": d_bf16(p.x), "gamma": torch.from_numpy(p.gamma).to(dev)}
+    if p.g is not None:
+        t["g"] = d_bf16(p.g)
+    if p.gres is not None:
+        t["gres"] = d_bf16(p.gres)
+    if p.z is not None:
+        t["z"] = d_bf16(p.z)
+    return p, t, desc
+
+
+def cpu_baseline(p, workload: str, reps: int):
+    """The CPU oracle (R64 mode, as it stands) on the same workload, threads
+    over row blocks (forward, dx) and column blocks (dgamma)."""
+    import numpy as np
+    import oracle
+
+    T, D = p.x.shape
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    rows = np.array_split(np.arange(T), nthreads)
+    cols = np.array_split(np.arange(D), nthreads)
+    rstd = np.empty(T, np.float32)
+
+    def fwd_block(ix):
+        a, b = ix[0], ix[-1] + 1
+        if workload == "gated":
+            _, r = oracle.gated_fwd(p.x[a:b], p.z[a:b], p.gamma, p.zero_centered, p.eps)
+        else:
+            _, r = oracle.fwd(p.x[a:b], p.gamma, p.zero_centered, p.eps)
+        rstd[a:b] = r
+
+    def dx_block(ix):
+        a, b = ix[0], ix[-1] + 1
+        oracle.bwd_dx(p.g[a:b], p.x[a:b], rstd[a:b], p.gamma, p.zero_centered,
+                      None if p.gres is None else p.gres[a:b])
+
+    def dg_block(ix):
+        a, b = ix[0], ix[-1] + 1
+        oracle.dgamma(p.g[:, a:b], p.x[:, a:b], rstd)
+
+    nbytes = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nthreads) as ex:
+        for _ in range(reps):
+            list(ex.map(fwd_block, rows))
+            if p.g is not None:
+                list(ex.map(dx_block, rows))
+                list(ex.map(dg_block, cols))
+    dt = time.perf_counter() - t0
+    return dt, nthreads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="token", choices=["token", "token_gres", "large", "gated"])
+    ap.add_argument("--cpu-reps", type=int, default=2, help="oracle passes over the workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(rows shard along T with no communication except one dgamma exchange; "
+              "see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import invariant_rmsnorm_amd as irn
+
+    irn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p, t, desc = make_inputs(args.workload, torch, dev)
+    T, D = p.T, p.D
+    zc, eps = p.zero_centered, p.eps
+    x, gamma = t["x"], t["gamma"]
+    y = torch.empty_like(x)
+    rstd = torch.empty(T, dtype=torch.float32, device=dev)
+    gated = args.workload == "gated"
+    if not gated:
+        g = t["g"]
+        gres = t.get("gres")
+        dx = torch.empty_like(x)
+        dgamma = torch.empty(D, dtype=torch.float32, device=dev)
+        ws, _ = irn.workspace_for(T, D, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        if gated:
+            irn.rmsnorm_gated_fwd(x, t["z"], gamma, zc, eps, out=y, rstd=rstd)
+        else:
+            irn.rmsnorm_fwd(x, gamma, zc, eps, y=y, rstd=rstd)
+        if evs is not None:
+            evs[1].record(stream)
+        if not gated:
+            irn.rmsnorm_bwd_rows(g, x, rstd, gamma, zc, g_residual=gres, dx=dx, workspace=ws)
+            if evs is not None:
+                evs[2].record(stream)
+            irn.rmsnorm_bwd_finish(ws, T, D, dgamma)
+            if evs is not None:
+                evs[3].record(stream)
+
+    # bitwise check before timing (two identical steps)
+    step()
+    ref = [y.clone(), rstd.clone()] + ([] if gated else [dx.clone(), dgamma.clone()])
+    step()
+    torch.cuda.synchronize()
+    now = [y, rstd] + ([] if gated else [dx, dgamma])
+    if not all(torch.equal(a, b) for a, b in zip(ref, now)):
+        raise SystemExit("repeat step is not bitwise identical")
+    del ref
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 27, dtype=torch.int16, device=dev)  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("calibration copy: 5 x 268435456 bytes read + written", file=sys.stderr, flush=True)
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    nev = 2 if gated else 4
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    fwd_kind = "gated_fwd" if gated else "fwd"
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    step_bytes = algo_bytes(fwd_kind, T, D)
+    kernels = {fwd_kind: {"ms": fwd_ms, "GB/s": algo_bytes(fwd_kind, T, D) / fwd_ms / 1e6}}
+    if not gated:
+        rows_kind = "bwd_rows_gres" if gres is not None else "bwd_rows"
+        rows_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+        fin_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+        step_bytes += algo_bytes(rows_kind, T, D) + algo_bytes("bwd_finish", T, D)
+        kernels[rows_kind] = {"ms": rows_ms, "GB/s": algo_bytes(rows_kind, T, D) / rows_ms / 1e6}
+        kernels["bwd_finish"] = {"ms": fin_ms}
+        dom, dom_ms, dom_bytes = "rmsnorm_bwd_rows_kernel", rows_ms, algo_bytes(rows_kind, T, D)
+    else:
+        dom, dom_ms, dom_bytes = "rmsnorm_fwd_kernel (gated)", fwd_ms, step_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic() if args.workload == "token" else None
+
+    cpu = None
+    if not args.no_cpu:
+        dt, nthreads = cpu_baseline(p, args.workload, args.cpu_reps)
+        cpu = {"value": round(step_bytes * args.cpu_reps / dt / 1e9, 3), "unit": "GB/s",
+               "cores": nthreads, "kind": "oracle",
+               "sample": f"the full workload ({T} rows x {D}), {args.cpu_reps} passes of "
+                         f"{'gated forward' if gated else 'forward + dx + dgamma'}, "
+                         f"{dt:.1f} s wall"}
+
+    out = {
+        "metric": METRIC if args.workload == "token" else f"{METRIC} [workload: {args.workload}]",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": desc, "T": T, "D": D, "zero_centered_gamma": zc,
+                   "bytes_per_step": step_bytes, "parallelism": "single GPU"},
+        "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in kernels.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": dom_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * rmsnorm_mi355x — batch-invariant RMSNorm forward and backward for one
+ * MI355X (gfx950), as a C ABI over plain device pointers.
+ *
+ * What is computed (pages by title; the section or equation named):
+ *  - Megatron-LM PR "Fix the batch-invariant RMSNorm forward and its input
+ *    gradient", "What does this PR do?": item 1 (the zero-centred offset,
+ *    added after the cast to fp32, in the forward as in the backward) and
+ *    item 2 (the input gradient dx_k = g_k w_k r - (r^3 x_k / D) sum_i g_i
+ *    x_i w_i, with the weight entering once per term; the weight gradient).
+ *  - RL-Kernel PR "C1: zero-centred RMSNorm references and CUDA kernel":
+ *    the +1 is an fp32 operation; the SiLU-gated norm with the weight
+ *    multiply in fp32; the backward takes the forward's saved rstd.
+ *  - RL-Kernel PR "[DSv4][P1-5] rmsnorm_residual", "Summary" and
+ *    "Implementation": output RMSNorm(x) plus a byte copy of x (not
+ *    RMSNorm(x + residual)); bf16 activations, fp32 gamma, fp32 saved inverse
+ *    RMS, bf16 dx and fp32 dgamma; r = rsqrt(mean(x^2) + eps),
+ *    y = (x * r) * gamma; no atomics, split-K or stream-K; the residual
+ *    branch's gradient is added to dx (review comment).
+ *  - TransformerEngine issue "Expose Batch Invariant Kernels", sections 1-3
+ *    and the checks table: a row's result must not depend on the batch it
+ *    sits in; the reduction layout may depend on the row length only; an
+ *    unsupported input is rejected, never sent silently down another path.
+ *
+ * Precision contract. x, y, dx, g, z and residual tensors are bf16, passed
+ * as raw uint16_t bits. gamma, rstd and dgamma are fp32. Per row:
+ *   ss   = sum_j x_j^2 (fp32, fixed reduction tree chosen by D alone)
+ *   r    = rsqrt(ss / D + eps)                      (fp32; stored in rstd)
+ *   w_j  = gamma_j, or gamma_j + 1.0f when zero_centered_gamma != 0
+ *   y_j  = bf16_rne((x_j * r) * w_j)                (two fp32 products)
+ *   gated: out_j = bf16_rne(((x_j * r) * w_j) * silu(z_j)), silu(z) = z*sigmoid(z)
+ *   bwd: gw_j = g_j * w_j; s = sum_j gw_j * x_j (same tree shape as ss);
+ *        c = ((r * r) * r) * s / D; dx_j = bf16_rne(gw_j * r - x_j * c [+ gres_j])
+ *   dgamma_j = sum over rows of (g_tj * x_tj) * r_t, summed per fixed chunk
+ *        of rows, then the chunk partials in a fixed order (deterministic
+ *        for a given T, no atomics).
+ * Batch invariance: every row's y, rstd and dx are bitwise identical whatever
+ * the batch size T, the row's index, the neighbouring rows, padding rows or
+ * row strides. The kernel variant and every reduction tree are chosen from D
+ * alone.
+ *
+ * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
+ * contiguous. Supported: D a multiple of 8 with 8 <= D <= 8192. Every bf16
+ * base pointer and ld * 2 bytes must be multiples of 16 bytes; gamma,
+ * dgamma and the workspace must be 16-byte aligned; rstd 4-byte aligned.
+ *
+ * Ownership and streams. Every pointer is device memory owned by the caller.
+ * The library never allocates, never synchronises, never changes the
+ * current device and keeps no state between calls except cached
+ * per-kernel occupancy figures. All work is enqueued on `stream` (a
+ * hipStream_t passed as void*; NULL = the null stream) in call order.
+ * Outputs must not overlap inputs or each other; overlapping ranges are
+ * rejected with RMSN_ERR_ALIASING.
+ *
+ * Errors. Arguments are checked on the host before anything is enqueued; on
+ * any error nothing is written and nothing is launched. A launch failure
+ * reports RMSN_ERR_HIP. Faults during kernel execution surface at the
+ * caller's next synchronisation. No C++ exception crosses the ABI. T = 0 is
+ * valid and enqueues nothing, except that a non-NULL dgamma is set to zero
+ * (the empty sum). eps may be 0 (then an all-zero row gives r = +inf).
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMSN_ABI_VERSION 1
+#define RMSN_MAX_D 8192
+
+typedef enum rmsn_status {
+  RMSN_OK = 0,
+  RMSN_ERR_NULL = 1,           /* a required pointer is NULL */
+  RMSN_ERR_SHAPE = 2,          /* T < 0, D <= 0, or ld < D */
+  RMSN_ERR_UNSUPPORTED_D = 3,  /* D not a multiple of 8, or D > RMSN_MAX_D */
+  RMSN_ERR_MISALIGNED = 4,     /* pointer or ld*2 not 16-byte aligned */
+  RMSN_ERR_EPS = 5,            /* eps negative or not finite */
+  RMSN_ERR_ALIASING = 6,       /* an output overlaps an input or another output */
+  RMSN_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than required */
+  RMSN_ERR_HIP = 8             /* the HIP runtime refused a launch */
+} rmsn_status;
+
+/* RMSN_ABI_VERSION of the loaded library. */
+int rmsnorm_abi_version(void);
+
+/* A static, human-readable name for a status code. */
+const char* rmsnorm_status_string(int status);
+
+/*
+ * Forward. y = bf16((x * r) * w_eff); rstd[t] = r (rstd may be NULL).
+ * Megatron-LM PR "Fix the batch-invariant RMSNorm forward ...", item 1;
+ * RL-Kernel "[DSv4][P1-5] rmsnorm_residual", "Implementation".
+ */
+rmsn_status rmsnorm_fwd(const uint16_t* x, int64_t ld_x, const float* gamma,
+                        int zero_centered_gamma, float eps, int64_t T,
+                        int64_t D, uint16_t* y, int64_t ld_y, float* rstd,
+                        void* stream);
+
+/*
+ * Forward plus residual_out = a byte copy of x, written from the same loads
+ * (RL-Kernel "[DSv4][P1-5] rmsnorm_residual", "Summary": not RMSNorm(x+res)).
+ */
+rmsn_status rmsnorm_residual_fwd(const uint16_t* x, int64_t ld_x,
+                                 const float* gamma, int zero_centered_gamma,
+                                 float eps, int64_t T, int64_t D, uint16_t* y,
+                                 int64_t ld_y, uint16_t* residual_out,
+                                 int64_t ld_res, float* rstd, void* stream);
+
+/*
+ * SiLU-gated forward: out = bf16(((x * r) * w_eff) * silu(z)), the weight
+ * multiply in fp32 (RL-Kernel "C1: zero-centred RMSNorm references and CUDA
+ * kernel", the gated-norm conventions). rstd may be NULL.
+ */
+rmsn_status rmsnorm_gated_fwd(const uint16_t* x, int64_t ld_x,
+                              const uint16_t* z, int64_t ld_z,
+                              const float* gamma, int zero_centered_gamma,
+                              float eps, int64_t T, int64_t D, uint16_t* out,
+                              int64_t ld_out, float* rstd, void* stream);
+
+/* Bytes of workspace rmsnorm_bwd / rmsnorm_bwd_rows need for dgamma
+ * (0 when T == 0). Depends on T and D only. */
+size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D);
+
+/* Rows per dgamma chunk used for (T, D): chunk k covers rows
+ * [k*C, min(T, (k+1)*C)). 0 for an unsupported shape. */
+int64_t rmsnorm_bwd_chunk_rows(int64_t T, int64_t D);
+
+/*
+ * Backward. From the upstream gradient g, the input x and the forward's
+ * saved rstd: dx = bf16(gw*r - x*c [+ g_residual]) and the fp32 weight
+ * gradient dgamma (Megatron-LM PR "Fix the batch-invariant RMSNorm forward
+ * and its input gradient", item 2; RL-Kernel "[DSv4][P1-5] rmsnorm_residual",
+ * review comment). g_residual (may be NULL) is the gradient reaching the
+ * residual copy; it is added in fp32 before dx's one rounding. dx may be
+ * NULL (weight gradient only) and dgamma may be NULL (input gradient only),
+ * not both. When dgamma is non-NULL the caller passes a workspace of at
+ * least rmsnorm_bwd_workspace_bytes(T, D) bytes, 16-byte aligned; its
+ * contents on return are the per-chunk partials. Two kernels on `stream`.
+ */
+rmsn_status rmsnorm_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x,
+                        int64_t ld_x, const float* rstd, const float* gamma,
+                        int zero_centered_gamma, int64_t T, int64_t D,
+                        const uint16_t* g_residual, int64_t ld_gres,
+                        uint16_t* dx, int64_t ld_dx, float* dgamma,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of rmsnorm_bwd, for callers that schedule them apart.
+ * rmsnorm_bwd_rows writes dx (if non-NULL) and, if workspace is non-NULL,
+ * the dgamma partials: workspace[k][j] (fp32, [K][D], K = ceil(T / C)) is
+ * the sum over chunk k's rows in a fixed order. rmsnorm_bwd_finish sums the
+ * K partials of each column in a fixed order into dgamma[D].
+ * rmsnorm_bwd(...) == rmsnorm_bwd_rows(...) then rmsnorm_bwd_finish(...).
+ */
+rmsn_status rmsnorm_bwd_rows(const uint16_t* g, int64_t ld_g,
+                             const uint16_t* x, int64_t ld_x,
+                             const float* rstd, const float* gamma,
+                             int zero_centered_gamma, int64_t T, int64_t D,
+                             const uint16_t* g_residual, int64_t ld_gres,
+                             uint16_t* dx, int64_t ld_dx, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+rmsn_status rmsnorm_bwd_finish(const void* workspace, size_t workspace_bytes,
+                               int64_t T, int64_t D, float* dgamma,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RMSNORM_MI355X_H */

@@ -1,0 +1,260 @@
+// C-ABI entry points of librmsnorm_mi355x.so: argument checks on the host,
+// then the gfx950 kernels (fwd.hip, bwd.hip). The declarations and their
+// contract live in include/rmsnorm_mi355x.h.
+//
+// Every check runs before anything is enqueued, so a rejected call writes
+// nothing. Unsupported input is reported, never routed to another code path
+// (TransformerEngine issue "Expose Batch Invariant Kernels", checks table:
+// unsupported combinations are rejected rather than silently falling back).
+#include "rmsnorm_mi355x.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "geometry.hpp"
+#include "launch.hpp"
+
+namespace {
+
+using rmsn::kMaxD;
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Range mat_range(const void* p, int64_t T, int64_t ld, int64_t D, int64_t elem) {
+  if (p == nullptr || T <= 0) return {};
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + static_cast<uintptr_t>(((T - 1) * ld + D) * elem)};
+}
+
+Range vec_range(const void* p, int64_t n, int64_t elem) {
+  if (p == nullptr || n <= 0) return {};
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + static_cast<uintptr_t>(n * elem)};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Each output must be disjoint from every input and every other output.
+template <size_t NO, size_t NI>
+bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
+  for (size_t i = 0; i < NO; ++i) {
+    for (size_t j = 0; j < NI; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (size_t j = i + 1; j < NO; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+rmsn_status check_D(int64_t D) {
+  if (D <= 0) return RMSN_ERR_SHAPE;
+  if (D % 8 != 0 || D > kMaxD) return RMSN_ERR_UNSUPPORTED_D;
+  return RMSN_OK;
+}
+
+// A bf16 [T, D] operand with row stride ld: shape, then (when T > 0) the
+// pointer and its 16-byte alignment. (T*ld is bounded so byte offsets fit.)
+rmsn_status check_mat(const uint16_t* p, int64_t ld, int64_t T, int64_t D, bool required) {
+  if (!required && p == nullptr) return RMSN_OK;
+  if (ld < D) return RMSN_ERR_SHAPE;
+  if (T > 0 && ld > (int64_t{1} << 62) / T) return RMSN_ERR_SHAPE;
+  if (T == 0) return RMSN_OK;
+  if (p == nullptr) return RMSN_ERR_NULL;
+  if (!aligned(p, 16) || (ld % 8) != 0) return RMSN_ERR_MISALIGNED;
+  return RMSN_OK;
+}
+
+rmsn_status check_f32(const float* p, uintptr_t align, bool required) {
+  if (p == nullptr) return required ? RMSN_ERR_NULL : RMSN_OK;
+  return aligned(p, align) ? RMSN_OK : RMSN_ERR_MISALIGNED;
+}
+
+#define RMSN_TRY(expr)                   \
+  do {                                   \
+    const rmsn_status s_ = (expr);       \
+    if (s_ != RMSN_OK) return s_;        \
+  } while (0)
+
+rmsn_status hip_status(int rc) { return rc == 0 ? RMSN_OK : RMSN_ERR_HIP; }
+
+rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
+                       bool gated, const float* gamma, int zc, float eps, int64_t T, int64_t D,
+                       uint16_t* y, int64_t ld_y, uint16_t* res, int64_t ld_res, bool residual,
+                       float* rstd, void* stream) {
+  if (T < 0) return RMSN_ERR_SHAPE;
+  RMSN_TRY(check_D(D));
+  RMSN_TRY(check_mat(x, ld_x, T, D, true));
+  if (gated) RMSN_TRY(check_mat(z, ld_z, T, D, true));
+  RMSN_TRY(check_mat(y, ld_y, T, D, true));
+  if (residual) RMSN_TRY(check_mat(res, ld_res, T, D, true));
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return RMSN_ERR_EPS;
+  if (T == 0) return RMSN_OK;
+  RMSN_TRY(check_f32(gamma, 16, true));
+  RMSN_TRY(check_f32(rstd, 4, false));
+  const Range outs[] = {mat_range(y, T, ld_y, D, 2), mat_range(res, T, ld_res, D, 2),
+                        vec_range(rstd, T, 4)};
+  const Range ins[] = {mat_range(x, T, ld_x, D, 2), mat_range(z, T, ld_z, D, 2),
+                       vec_range(gamma, D, 4)};
+  if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
+
+  rmsn::FwdArgs a{x, ld_x, gated ? z : nullptr, ld_z, gamma, zc != 0, eps, T, static_cast<int>(D),
+                  y, ld_y, residual ? res : nullptr, ld_res, rstd};
+  return hip_status(rmsn::launch_fwd(a, stream));
+}
+
+size_t workspace_bytes(int64_t T, int64_t D) {
+  if (T <= 0 || check_D(D) != RMSN_OK) return 0;
+  const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
+  return static_cast<size_t>(p.chunks) * static_cast<size_t>(D) * sizeof(float);
+}
+
+// Checks shared by rmsnorm_bwd and rmsnorm_bwd_rows; `dgamma` is only
+// checked for aliasing here (rmsnorm_bwd_rows passes nullptr).
+rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                      const float* rstd, const float* gamma, int64_t T, int64_t D,
+                      const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
+                      bool want_part, const float* dgamma, void* ws, size_t ws_bytes) {
+  if (T < 0) return RMSN_ERR_SHAPE;
+  RMSN_TRY(check_D(D));
+  RMSN_TRY(check_mat(g, ld_g, T, D, true));
+  RMSN_TRY(check_mat(x, ld_x, T, D, true));
+  RMSN_TRY(check_mat(gres, ld_gres, T, D, false));
+  RMSN_TRY(check_mat(dx, ld_dx, T, D, false));
+  if (T == 0) return RMSN_OK;
+  RMSN_TRY(check_f32(rstd, 4, true));
+  RMSN_TRY(check_f32(gamma, 16, dx != nullptr));
+  if (want_part) {
+    if (ws == nullptr || ws_bytes < workspace_bytes(T, D)) return RMSN_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return RMSN_ERR_MISALIGNED;
+  }
+  const Range outs[] = {mat_range(dx, T, ld_dx, D, 2),
+                        want_part ? vec_range(ws, static_cast<int64_t>(workspace_bytes(T, D)), 1)
+                                  : Range{},
+                        vec_range(dgamma, D, 4)};
+  const Range ins[] = {mat_range(g, T, ld_g, D, 2), mat_range(x, T, ld_x, D, 2),
+                       vec_range(rstd, T, 4), vec_range(dx ? gamma : nullptr, D, 4),
+                       mat_range(gres, T, ld_gres, D, 2)};
+  if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
+  return RMSN_OK;
+}
+
+rmsn::BwdArgs bwd_args(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                       const float* rstd, const float* gamma, int zc, int64_t T, int64_t D,
+                       const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
+                       void* ws) {
+  const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
+  return rmsn::BwdArgs{g, ld_g, x, ld_x, rstd, gamma, zc != 0, T, static_cast<int>(D),
+                       dx ? gres : nullptr, ld_gres, dx, ld_dx, static_cast<float*>(ws),
+                       p.chunk_rows, p.chunks};
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmsnorm_abi_version(void) { return RMSN_ABI_VERSION; }
+
+const char* rmsnorm_status_string(int status) {
+  switch (status) {
+    case RMSN_OK: return "RMSN_OK";
+    case RMSN_ERR_NULL: return "RMSN_ERR_NULL: a required pointer is NULL";
+    case RMSN_ERR_SHAPE: return "RMSN_ERR_SHAPE: T < 0, D <= 0 or ld < D";
+    case RMSN_ERR_UNSUPPORTED_D: return "RMSN_ERR_UNSUPPORTED_D: D must be a multiple of 8 in [8, 8192]";
+    case RMSN_ERR_MISALIGNED: return "RMSN_ERR_MISALIGNED: pointers and row strides must be 16-byte aligned";
+    case RMSN_ERR_EPS: return "RMSN_ERR_EPS: eps must be finite and >= 0";
+    case RMSN_ERR_ALIASING: return "RMSN_ERR_ALIASING: an output overlaps an input or another output";
+    case RMSN_ERR_WORKSPACE: return "RMSN_ERR_WORKSPACE: workspace missing or too small";
+    case RMSN_ERR_HIP: return "RMSN_ERR_HIP: the HIP runtime refused a kernel launch";
+    default: return "unknown rmsn_status";
+  }
+}
+
+rmsn_status rmsnorm_fwd(const uint16_t* x, int64_t ld_x, const float* gamma, int zero_centered_gamma,
+                        float eps, int64_t T, int64_t D, uint16_t* y, int64_t ld_y, float* rstd,
+                        void* stream) {
+  return fwd_common(x, ld_x, nullptr, 0, false, gamma, zero_centered_gamma, eps, T, D, y, ld_y,
+                    nullptr, 0, false, rstd, stream);
+}
+
+rmsn_status rmsnorm_residual_fwd(const uint16_t* x, int64_t ld_x, const float* gamma,
+                                 int zero_centered_gamma, float eps, int64_t T, int64_t D,
+                                 uint16_t* y, int64_t ld_y, uint16_t* residual_out, int64_t ld_res,
+                                 float* rstd, void* stream) {
+  return fwd_common(x, ld_x, nullptr, 0, false, gamma, zero_centered_gamma, eps, T, D, y, ld_y,
+                    residual_out, ld_res, true, rstd, stream);
+}
+
+rmsn_status rmsnorm_gated_fwd(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
+                              const float* gamma, int zero_centered_gamma, float eps, int64_t T,
+                              int64_t D, uint16_t* out, int64_t ld_out, float* rstd, void* stream) {
+  return fwd_common(x, ld_x, z, ld_z, true, gamma, zero_centered_gamma, eps, T, D, out, ld_out,
+                    nullptr, 0, false, rstd, stream);
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D) { return workspace_bytes(T, D); }
+
+int64_t rmsnorm_bwd_chunk_rows(int64_t T, int64_t D) {
+  if (T < 0 || check_D(D) != RMSN_OK) return 0;
+  return rmsn::bwd_plan(T, D).chunk_rows;
+}
+
+rmsn_status rmsnorm_bwd_rows(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                             const float* rstd, const float* gamma, int zero_centered_gamma,
+                             int64_t T, int64_t D, const uint16_t* g_residual, int64_t ld_gres,
+                             uint16_t* dx, int64_t ld_dx, void* workspace, size_t workspace_bytes_,
+                             void* stream) {
+  if (dx == nullptr && workspace == nullptr) return RMSN_ERR_NULL;
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, g_residual, ld_gres, dx, ld_dx,
+                     workspace != nullptr, nullptr, workspace, workspace_bytes_));
+  if (T == 0) return RMSN_OK;
+  const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
+                                   g_residual, ld_gres, dx, ld_dx, workspace);
+  return hip_status(rmsn::launch_bwd_rows(a, stream));
+}
+
+rmsn_status rmsnorm_bwd_finish(const void* workspace, size_t workspace_bytes_, int64_t T, int64_t D,
+                               float* dgamma, void* stream) {
+  if (T < 0) return RMSN_ERR_SHAPE;
+  RMSN_TRY(check_D(D));
+  RMSN_TRY(check_f32(dgamma, 16, true));
+  const size_t need = workspace_bytes(T, D);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes_ < need) return RMSN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return RMSN_ERR_MISALIGNED;
+    const Range outs[] = {vec_range(dgamma, D, 4)};
+    const Range ins[] = {vec_range(workspace, static_cast<int64_t>(need), 1)};
+    if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
+  }
+  const int64_t chunks = T > 0 ? rmsn::bwd_plan(T, D).chunks : 0;
+  return hip_status(rmsn::launch_bwd_finish(static_cast<const float*>(workspace), chunks,
+                                            static_cast<int>(D), dgamma, stream));
+}
+
+rmsn_status rmsnorm_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                        const float* rstd, const float* gamma, int zero_centered_gamma, int64_t T,
+                        int64_t D, const uint16_t* g_residual, int64_t ld_gres, uint16_t* dx,
+                        int64_t ld_dx, float* dgamma, void* workspace, size_t workspace_bytes_,
+                        void* stream) {
+  if (dx == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
+  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, g_residual, ld_gres, dx, ld_dx,
+                     dgamma != nullptr, dgamma, workspace, workspace_bytes_));
+  if (T > 0) {
+    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
+                                     g_residual, ld_gres, dx, ld_dx,
+                                     dgamma != nullptr ? workspace : nullptr);
+    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
+  }
+  if (dgamma == nullptr) return RMSN_OK;
+  const int64_t chunks = T > 0 ? rmsn::bwd_plan(T, D).chunks : 0;
+  return hip_status(rmsn::launch_bwd_finish(static_cast<const float*>(workspace), chunks,
+                                            static_cast<int>(D), dgamma, stream));
+}
+
+}  // extern "C"

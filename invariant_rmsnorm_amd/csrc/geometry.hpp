@@ -1,0 +1,74 @@
+// Row geometry of the gfx950 kernels, shared by the host launchers and the
+// kernels. Everything here is a function of D alone: the batch size, a row's
+// index and the row strides never enter, which is what makes each row's
+// arithmetic identical in every batch (TransformerEngine issue "Expose Batch
+// Invariant Kernels", sections 2-3: the reduction layout must come from the
+// problem's fixed dimensions, never from the batch dimension).
+//
+// A row of D bf16 values is NV = D/8 vectors of 16 bytes. LPR lanes of a
+// 64-lane wavefront share one row: LPR = 64 when NV >= 64 (each lane then
+// holds VPL = ceil(NV/64) vectors), otherwise the smallest power of two
+// >= NV (VPL = 1, and a wave carries 64/LPR rows side by side). Lane l of a
+// row owns the vectors c = v*LPR + l, v = 0..VPL-1; MASKED marks geometries
+// where the last of those vectors is missing on some lanes.
+#pragma once
+
+#include <stdint.h>
+
+namespace rmsn {
+
+constexpr int kWaves = 4;            // wavefronts per workgroup
+constexpr int kBlock = 64 * kWaves;  // threads per workgroup
+constexpr int kMaxD = 8192;
+constexpr int kMaxVpl = kMaxD / 512;
+// The backward splits the batch into at most this many chunks of rows; one
+// workgroup per chunk (2 per compute unit on a 256-CU part).
+constexpr int64_t kTargetChunks = 512;
+
+struct RowGeom {
+  int lpr;     // lanes per row (1, 2, 4, ..., 64)
+  int vpl;     // 16-byte vectors per lane (1..16)
+  bool masked; // some lanes lack their last vector
+};
+
+inline RowGeom row_geom(int64_t D) {
+  const int64_t nv = D / 8;
+  if (nv >= 64) return {64, static_cast<int>((nv + 63) / 64), (nv % 64) != 0};
+  int lpr = 1;
+  while (lpr < nv) lpr <<= 1;
+  return {lpr, 1, lpr != nv};
+}
+
+// Rows a wave keeps in flight per step: enough that each lane has about
+// 128 bytes of one input stream outstanding.
+constexpr int fwd_unroll(int lpr, int vpl) {
+  return lpr < 64 ? 8 : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
+}
+constexpr int bwd_unroll(int lpr, int vpl) {
+  return lpr < 64 ? 4 : (vpl == 1 ? 4 : vpl == 2 ? 2 : 1);
+}
+
+inline int64_t bwd_rows_per_step(int64_t D) {
+  const RowGeom g = row_geom(D);
+  return static_cast<int64_t>(kWaves) * bwd_unroll(g.lpr, g.vpl) * (64 / g.lpr);
+}
+
+// dgamma chunking for a batch of T rows: chunk k = rows [k*C, min(T,(k+1)*C)).
+// C is a multiple of the rows one workgroup step covers, and the number of
+// chunks is at most kTargetChunks. (dgamma sums over the whole batch, so its
+// grouping may depend on T; the per-row outputs never do.)
+struct BwdPlan {
+  int64_t chunk_rows;
+  int64_t chunks;
+};
+
+inline BwdPlan bwd_plan(int64_t T, int64_t D) {
+  const int64_t R = bwd_rows_per_step(D);
+  if (T <= 0) return {R, 0};
+  const int64_t steps = (T + R - 1) / R;
+  const int64_t per = (steps + kTargetChunks - 1) / kTargetChunks;
+  const int64_t C = per * R;
+  return {C, (T + C - 1) / C};
+}
+
+}  // namespace rmsn

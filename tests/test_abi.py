@@ -1,0 +1,164 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/rmsnorm_mi355x.h declares, and rejects every malformed call on the
+host before anything is launched (fake, never-dereferenced pointers).
+
+Rejection rules follow TransformerEngine issue "Expose Batch Invariant
+Kernels", checks table (unsupported combinations are rejected, not silently
+sent elsewhere) and RL-Kernel PR "[DSv4][P1-5] rmsnorm_residual",
+"Correctness / Tests" (invalid inputs)."""
+from __future__ import annotations
+
+import re
+from pathlib import Path
+
+import pytest
+
+import invariant_rmsnorm_amd as irn
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "rmsnorm_mi355x.h"
+
+A = 0x7F0000000000          # aligned fake device addresses, far apart
+B = A + (1 << 36)
+C = A + (2 << 36)
+E = A + (3 << 36)
+W = A + (4 << 36)
+GAM = A + (5 << 36)
+RS = A + (6 << 36)
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(rmsnorm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = irn.load()
+    names = declared_functions()
+    assert set(names) == set(irn.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert irn.rmsnorm_abi_version() == 1
+
+
+def test_status_strings():
+    for code in range(9):
+        assert irn.status_string(code).startswith("RMSN_")
+    assert "unknown" in irn.status_string(99)
+
+
+def fwd(**kw):
+    a = dict(x=A, ld_x=4096, gamma=GAM, zc=0, eps=1e-6, T=8, D=4096, y=B, ld_y=4096, rstd=RS)
+    a.update(kw)
+    return irn.load().rmsnorm_fwd(a["x"], a["ld_x"], a["gamma"], a["zc"], a["eps"], a["T"], a["D"],
+                                  a["y"], a["ld_y"], a["rstd"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), irn.RMSN_ERR_NULL),
+    (dict(y=None), irn.RMSN_ERR_NULL),
+    (dict(gamma=None), irn.RMSN_ERR_NULL),
+    (dict(T=-1), irn.RMSN_ERR_SHAPE),
+    (dict(D=0), irn.RMSN_ERR_SHAPE),
+    (dict(D=-8), irn.RMSN_ERR_SHAPE),
+    (dict(D=100, ld_x=100, ld_y=104), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=8200, ld_x=8200, ld_y=8200), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(ld_x=4000), irn.RMSN_ERR_SHAPE),
+    (dict(ld_y=4088), irn.RMSN_ERR_SHAPE),
+    (dict(x=A + 2), irn.RMSN_ERR_MISALIGNED),
+    (dict(y=B + 8), irn.RMSN_ERR_MISALIGNED),
+    (dict(ld_x=4100), irn.RMSN_ERR_MISALIGNED),
+    (dict(gamma=GAM + 4), irn.RMSN_ERR_MISALIGNED),
+    (dict(rstd=RS + 2), irn.RMSN_ERR_MISALIGNED),
+    (dict(eps=-1e-6), irn.RMSN_ERR_EPS),
+    (dict(eps=float("nan")), irn.RMSN_ERR_EPS),
+    (dict(eps=float("inf")), irn.RMSN_ERR_EPS),
+    (dict(y=A), irn.RMSN_ERR_ALIASING),                       # in place
+    (dict(y=A + 2 * 4096 * 4), irn.RMSN_ERR_ALIASING),         # y starts inside x
+    (dict(rstd=A + 64), irn.RMSN_ERR_ALIASING),                # rstd inside x
+    (dict(rstd=B + 16), irn.RMSN_ERR_ALIASING),                # rstd inside y
+    (dict(gamma=B + 32), irn.RMSN_ERR_ALIASING),               # y over gamma
+    (dict(T=1 << 61), irn.RMSN_ERR_SHAPE),                     # byte offsets overflow
+])
+def test_forward_rejections(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_forward_empty_batch_is_a_noop():
+    assert fwd(T=0, x=None, y=None, rstd=None, gamma=None) == irn.RMSN_OK
+
+
+def test_residual_and_gated_rejections():
+    lib = irn.load()
+    ok = (A, 4096, GAM, 0, 1e-6, 8, 4096, B)
+    assert lib.rmsnorm_residual_fwd(*ok, 4096, None, 4096, RS, None) == irn.RMSN_ERR_NULL
+    assert lib.rmsnorm_residual_fwd(*ok, 4096, A, 4096, RS, None) == irn.RMSN_ERR_ALIASING
+    assert lib.rmsnorm_residual_fwd(*ok, 4096, B, 4096, RS, None) == irn.RMSN_ERR_ALIASING
+    assert lib.rmsnorm_residual_fwd(*ok, 4096, C + 2, 4096, RS, None) == irn.RMSN_ERR_MISALIGNED
+    # gated: z required, may not alias the output
+    assert lib.rmsnorm_gated_fwd(A, 4096, None, 4096, GAM, 0, 1e-6, 8, 4096, B, 4096, None,
+                                 None) == irn.RMSN_ERR_NULL
+    assert lib.rmsnorm_gated_fwd(A, 4096, B, 4096, GAM, 0, 1e-6, 8, 4096, B, 4096, None,
+                                 None) == irn.RMSN_ERR_ALIASING
+    assert lib.rmsnorm_gated_fwd(A, 4096, C, 4000, GAM, 0, 1e-6, 8, 4096, B, 4096, None,
+                                 None) == irn.RMSN_ERR_SHAPE
+
+
+def bwd(**kw):
+    a = dict(g=A, ld_g=4096, x=B, ld_x=4096, rstd=RS, gamma=GAM, zc=0, T=1000, D=4096, gres=None,
+             ld_gres=0, dx=C, ld_dx=4096, dgamma=E, ws=W, ws_bytes=1 << 30)
+    a.update(kw)
+    return irn.load().rmsnorm_bwd(a["g"], a["ld_g"], a["x"], a["ld_x"], a["rstd"], a["gamma"],
+                                  a["zc"], a["T"], a["D"], a["gres"], a["ld_gres"], a["dx"],
+                                  a["ld_dx"], a["dgamma"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dx=None, dgamma=None), irn.RMSN_ERR_NULL),
+    (dict(g=None), irn.RMSN_ERR_NULL),
+    (dict(x=None), irn.RMSN_ERR_NULL),
+    (dict(rstd=None), irn.RMSN_ERR_NULL),
+    (dict(gamma=None), irn.RMSN_ERR_NULL),                  # dx needs the weights
+    (dict(ws=None), irn.RMSN_ERR_WORKSPACE),
+    (dict(ws_bytes=16), irn.RMSN_ERR_WORKSPACE),
+    (dict(ws=W + 4), irn.RMSN_ERR_MISALIGNED),
+    (dict(dgamma=E + 4), irn.RMSN_ERR_MISALIGNED),
+    (dict(dx=A), irn.RMSN_ERR_ALIASING),
+    (dict(dx=B), irn.RMSN_ERR_ALIASING),
+    (dict(dgamma=RS), irn.RMSN_ERR_ALIASING),
+    (dict(ws=C), irn.RMSN_ERR_ALIASING),
+    (dict(gres=C, ld_gres=4096), irn.RMSN_ERR_ALIASING),
+    (dict(gres=E + (1 << 30), ld_gres=100), irn.RMSN_ERR_SHAPE),
+    (dict(D=4100, ld_g=4104, ld_x=4104, ld_dx=4104), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(T=-5), irn.RMSN_ERR_SHAPE),
+])
+def test_backward_rejections(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_workspace_and_chunking_contract():
+    assert irn.rmsnorm_bwd_workspace_bytes(0, 4096) == 0
+    assert irn.rmsnorm_bwd_workspace_bytes(10, 100) == 0
+    for T, D in ((1, 128), (16, 128), (32768, 4096), (262144, 4096), (262144, 128), (1000, 2048),
+                 (7, 8), (12345, 8192)):
+        C = irn.rmsnorm_bwd_chunk_rows(T, D)
+        K = -(-T // C)
+        assert C > 0 and K <= 512
+        assert irn.rmsnorm_bwd_workspace_bytes(T, D) == K * D * 4
+    # the chunk grouping is fixed per (T, D): the same plan on every call
+    assert irn.rmsnorm_bwd_chunk_rows(32768, 4096) == irn.rmsnorm_bwd_chunk_rows(32768, 4096)
+
+
+def test_finish_rejections():
+    lib = irn.load()
+    assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 4096, None, None) == irn.RMSN_ERR_NULL
+    assert lib.rmsnorm_bwd_finish(None, 0, 1000, 4096, E, None) == irn.RMSN_ERR_WORKSPACE
+    assert lib.rmsnorm_bwd_finish(W, 64, 1000, 4096, E, None) == irn.RMSN_ERR_WORKSPACE
+    assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 4096, W + 64, None) == irn.RMSN_ERR_ALIASING
+    assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 12, E, None) == irn.RMSN_ERR_UNSUPPORTED_D
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(irn, "_lib", None)
+    monkeypatch.setattr(irn, "LIB_PATH", tmp_path / "missing.so")
+    with pytest.raises(ImportError):
+        irn.load()

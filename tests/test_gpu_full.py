@@ -1,0 +1,99 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (the same entry points, on the same shapes).
+
+* token norm with outlier rows, T=32768, D=4096: every element of y, rstd,
+  dx (with and without the residual gradient) and dgamma against the oracle;
+* SiLU-gated per-head norm, 262144 x 128: every output element;
+* T=262144, D=4096, zero-centred: dgamma over all rows against the oracle,
+  y/rstd/dx on sampled rows, and ten runs bitwise identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_rmsnorm_amd as irn
+import oracle
+from gpu_util import dev_bf16, dev_f32, host_bits
+from numerics import dgamma_rel_err, dx_check, max_ulp, rstd_rel_err
+from synth import workloads as wl
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def test_residual_token_norm_full(gpu):
+    p = wl.residual()
+    _log(f"residual workload {p.T}x{p.D}: generated")
+    x, g, gr, gamma = dev_bf16(p.x), dev_bf16(p.g), dev_bf16(p.gres), dev_f32(p.gamma)
+    y, res, rstd = irn.rmsnorm_residual_fwd(x, gamma, False, p.eps)
+    dx, dg = irn.rmsnorm_bwd(g, x, rstd, gamma, False)
+    dxr, dgr = irn.rmsnorm_bwd(g, x, rstd, gamma, False, g_residual=gr)
+    torch.cuda.synchronize()
+    assert torch.equal(res, x)
+    assert torch.equal(dg, dgr)
+
+    ry, rr = oracle.fwd(p.x, p.gamma, False, p.eps)
+    _log("oracle forward done")
+    assert max_ulp(host_bits(y), ry) <= 1
+    assert rstd_rel_err(rstd.cpu().numpy(), rr) <= 1e-6
+    w = oracle.weights(p.gamma, False)
+    for gpu_dx, gres in ((dx, None), (dxr, p.gres)):
+        rdx = oracle.bwd_dx(p.g, p.x, rr, p.gamma, False, gres)
+        n_over, n_canc, n_fail = dx_check(host_bits(gpu_dx), rdx, p.g, p.x, w, rr, gres)
+        _log(f"dx (gres={gres is not None}): >1ulp cancellations {n_canc}, failures {n_fail}")
+        assert n_fail == 0
+    rdg = oracle.dgamma(p.g, p.x, rr)
+    err = dgamma_rel_err(dg.cpu().numpy(), rdg)
+    _log(f"dgamma rel err {err:.3e}")
+    assert err <= 1e-5
+
+
+def test_gated_per_head_full(gpu):
+    p = wl.gated()
+    out, rstd = irn.rmsnorm_gated_fwd(dev_bf16(p.x), dev_bf16(p.z), dev_f32(p.gamma), False,
+                                      p.eps, want_rstd=True)
+    ro, rr = oracle.gated_fwd(p.x, p.z, p.gamma, False, p.eps)
+    got = host_bits(out)
+    assert max_ulp(got, ro) <= 1
+    _log(f"gated: {(got != ro).sum()} of {got.size} elements 1 ulp apart")
+    assert rstd_rel_err(rstd.cpu().numpy(), rr) <= 1e-6
+
+
+def test_large_zero_centered_full(gpu):
+    p = wl.large()
+    _log(f"large workload {p.T}x{p.D}: generated")
+    x, g, gamma = dev_bf16(p.x), dev_bf16(p.g), dev_f32(p.gamma)
+    y, rstd = irn.rmsnorm_fwd(x, gamma, True, p.eps)
+    ws, _ = irn.workspace_for(p.T, p.D, "cuda")
+    dx, dg = irn.rmsnorm_bwd(g, x, rstd, gamma, True, workspace=ws)
+    torch.cuda.synchronize()
+
+    _, rr = oracle.fwd(p.x, p.gamma, True, p.eps)
+    _log("oracle forward done")
+    assert rstd_rel_err(rstd.cpu().numpy(), rr) <= 1e-6
+    rdg = oracle.dgamma(p.g, p.x, rr)
+    err = dgamma_rel_err(dg.cpu().numpy(), rdg)
+    _log(f"dgamma over {p.T} rows: rel err {err:.3e}")
+    assert err <= 1e-5
+
+    rows = np.unique(np.concatenate([[0, 1, p.T // 2, p.T - 1],
+                                     np.random.default_rng(4004).integers(0, p.T, 2000)]))
+    idx = torch.from_numpy(rows).cuda()
+    ys, dxs = host_bits(y[idx]), host_bits(dx[idx])
+    sy, sr = oracle.fwd(p.x[rows], p.gamma, True, p.eps)
+    sdx = oracle.bwd_dx(p.g[rows], p.x[rows], sr, p.gamma, True)
+    assert max_ulp(ys, sy) <= 1
+    assert dx_check(dxs, sdx, p.g[rows], p.x[rows], oracle.weights(p.gamma, True), sr)[2] == 0
+
+    # ten runs: every output bitwise identical
+    for i in range(10):
+        y2, r2 = irn.rmsnorm_fwd(x, gamma, True, p.eps)
+        dx2, dg2 = irn.rmsnorm_bwd(g, x, r2, gamma, True, workspace=ws)
+        assert torch.equal(y, y2) and torch.equal(rstd, r2)
+        assert torch.equal(dx, dx2) and torch.equal(dg.view(torch.int32), dg2.view(torch.int32))
+    _log("ten repeat runs bitwise identical")
