@@ -40,7 +40,8 @@
  * alone.
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
- * contiguous. Supported: D a multiple of 8 with 8 <= D <= 8192. Every bf16
+ * contiguous. Supported: D a multiple of 8 with 8 <= D <= 8192, and
+ * D <= ld <= 2^24 (RMSN_MAX_LD). Every bf16
  * base pointer and ld * 2 bytes must be multiples of 16 bytes; gamma,
  * dgamma and the workspace must be 16-byte aligned; rstd 4-byte aligned.
  *
@@ -71,11 +72,12 @@ extern "C" {
 
 #define RMSN_ABI_VERSION 1
 #define RMSN_MAX_D 8192
+#define RMSN_MAX_LD (1 << 24)
 
 typedef enum rmsn_status {
   RMSN_OK = 0,
   RMSN_ERR_NULL = 1,           /* a required pointer is NULL */
-  RMSN_ERR_SHAPE = 2,          /* T < 0, D <= 0, or ld < D */
+  RMSN_ERR_SHAPE = 2,          /* T < 0, D <= 0, ld < D or ld > RMSN_MAX_LD */
   RMSN_ERR_UNSUPPORTED_D = 3,  /* D not a multiple of 8, or D > RMSN_MAX_D */
   RMSN_ERR_MISALIGNED = 4,     /* pointer or ld*2 not 16-byte aligned */
   RMSN_ERR_EPS = 5,            /* eps negative or not finite */

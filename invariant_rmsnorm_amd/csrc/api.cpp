@@ -17,6 +17,9 @@
 namespace {
 
 using rmsn::kMaxD;
+// Row strides up to 2^24 elements keep every per-lane byte offset of a
+// 64-row group below 2^31 (the kernels address rows through 32-bit offsets).
+constexpr int64_t kMaxLd = int64_t{1} << 24;
 
 struct Range {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -62,7 +65,7 @@ rmsn_status check_D(int64_t D) {
 // pointer and its 16-byte alignment. (T*ld is bounded so byte offsets fit.)
 rmsn_status check_mat(const uint16_t* p, int64_t ld, int64_t T, int64_t D, bool required) {
   if (!required && p == nullptr) return RMSN_OK;
-  if (ld < D) return RMSN_ERR_SHAPE;
+  if (ld < D || ld > kMaxLd) return RMSN_ERR_SHAPE;
   if (T > 0 && ld > (int64_t{1} << 62) / T) return RMSN_ERR_SHAPE;
   if (T == 0) return RMSN_OK;
   if (p == nullptr) return RMSN_ERR_NULL;
@@ -164,7 +167,7 @@ const char* rmsnorm_status_string(int status) {
   switch (status) {
     case RMSN_OK: return "RMSN_OK";
     case RMSN_ERR_NULL: return "RMSN_ERR_NULL: a required pointer is NULL";
-    case RMSN_ERR_SHAPE: return "RMSN_ERR_SHAPE: T < 0, D <= 0 or ld < D";
+    case RMSN_ERR_SHAPE: return "RMSN_ERR_SHAPE: T < 0, D <= 0, ld < D or ld > 2^24";
     case RMSN_ERR_UNSUPPORTED_D: return "RMSN_ERR_UNSUPPORTED_D: D must be a multiple of 8 in [8, 8192]";
     case RMSN_ERR_MISALIGNED: return "RMSN_ERR_MISALIGNED: pointers and row strides must be 16-byte aligned";
     case RMSN_ERR_EPS: return "RMSN_ERR_EPS: eps must be finite and >= 0";

@@ -21,8 +21,9 @@
 // added by a butterfly, the 4 waves as ((w0 + w2) + (w1 + w3)) through LDS,
 // and the chunk's partial row is written to workspace[k][:].
 // Kernel 2 (finish): dgamma[j] = a fixed tree over 32 slices, each slice an
-// ascending sum over k of the partials. The grouping depends on T (dgamma is
-// a sum over the whole batch) but never on timing: the bits repeat run to run.
+// ascending sum over a contiguous range of the chunk partials. The grouping
+// depends on T (dgamma is a sum over the whole batch) but never on timing:
+// the bits repeat run to run.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -30,25 +31,88 @@
 
 namespace rmsn {
 
-template <int LPR, int VPL, bool MASKED>
-__global__ __launch_bounds__(kBlock) void rmsnorm_bwd_rows_kernel(BwdArgs a) {
+// Tuning switches (fixed at build time; they change speed, not results):
+// weights held in LDS instead of registers, and loading the next step's rows
+// before computing the current one.
+#ifndef RMSN_BWD_WEIGHTS_IN_LDS
+#define RMSN_BWD_WEIGHTS_IN_LDS 1
+#endif
+#ifndef RMSN_BWD_PREFETCH
+#define RMSN_BWD_PREFETCH 0
+#endif
+// Optional scheduling fence after each vector, so the scheduler does not
+// unpack a whole row at once for instruction-level parallelism.
+#ifndef RMSN_BWD_FENCE
+#define RMSN_BWD_FENCE 1
+#endif
+#if RMSN_BWD_FENCE
+#define RMSN_BWD_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define RMSN_BWD_SCHED_FENCE() ((void)0)
+#endif
+// Minimum waves per SIMD the register allocator must allow for a geometry
+// (more waves = more rows in flight; too many forces spills).
+#ifndef RMSN_BWD_WAVES_WIDE
+#define RMSN_BWD_WAVES_WIDE 2
+#endif
+constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 12 ? 1 : vpl >= 5 ? RMSN_BWD_WAVES_WIDE : 2; }
+
+// LDS floats the rows kernel needs: the weights (one float4 pair per vector
+// slot, laid out so that consecutive lanes read consecutive 16 bytes) and,
+// after the rows are done, two rows of D floats for the wave merge (which
+// reuse the same space).
+inline size_t bwd_rows_lds_floats(int D, bool want_part) {
+  const RowGeom g = row_geom(D);
+  const size_t w = RMSN_BWD_WEIGHTS_IN_LDS ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
+  const size_t m = want_part ? 2 * static_cast<size_t>(D) : 0;
+  return w > m ? w : m;
+}
+
+template <int LPR, int VPL, bool MASKED, bool GRES>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL)))) void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr int RPW = 64 / LPR;
   constexpr int U = bwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
-  extern __shared__ float lds[];  // [2][D] when dgamma partials are wanted
+  constexpr bool WLDS = RMSN_BWD_WEIGHTS_IN_LDS;
+  extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int slot = lane / LPR;
   const int l = lane % LPR;
   const int nv = a.D >> 3;
   const float Df = static_cast<float>(a.D);
-  const bool want_dx = a.dx != nullptr;
   const bool want_part = a.part != nullptr;
 
-  float w[VPL][8];
-  load_weights<LPR, VPL, MASKED>(a.gamma, a.zc, nv, l, w);
+  // Weights w_eff = gamma (+1 in fp32 when zero-centred).
+  float wreg[WLDS ? 1 : VPL][8];
+  float4* const wl4 = reinterpret_cast<float4*>(lds);
+  if constexpr (WLDS) {
+    // float4 h (0/1) of vector c = v*LPR + l goes to slot (2v + h)*LPR + l
+    for (int j = threadIdx.x; j < 2 * nv; j += kBlock) {
+      const int c = j >> 1, h = j & 1;
+      float4 q = reinterpret_cast<const float4*>(a.gamma)[j];
+      if (a.zc) { q.x = q.x + 1.0f; q.y = q.y + 1.0f; q.z = q.z + 1.0f; q.w = q.w + 1.0f; }
+      wl4[((c / LPR) * 2 + h) * LPR + (c % LPR)] = q;
+    }
+    __syncthreads();
+  } else {
+    load_weights<LPR, (WLDS ? 1 : VPL), MASKED>(a.gamma, a.zc, nv, l, wreg);
+  }
+  // `base` is an opaque zero (see below) so that the reads stay inside the
+  // row loop instead of being hoisted into registers for the whole chunk.
+  auto weights = [&](int base, int v, float (&w8)[8]) {
+    if constexpr (WLDS) {
+      const float4 p0 = wl4[base + (2 * v) * LPR + l];
+      const float4 p1 = wl4[base + (2 * v + 1) * LPR + l];
+      w8[0] = p0.x; w8[1] = p0.y; w8[2] = p0.z; w8[3] = p0.w;
+      w8[4] = p1.x; w8[5] = p1.y; w8[6] = p1.z; w8[7] = p1.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w8[k] = wreg[WLDS ? 0 : v][k];
+    }
+  };
 
   float acc[VPL][8];
 #pragma unroll
@@ -59,87 +123,122 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   const int64_t begin = static_cast<int64_t>(blockIdx.x) * a.chunk_rows;
   const int64_t end = begin + a.chunk_rows < a.T ? begin + a.chunk_rows : a.T;
 
-  for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
-    const int64_t row0 = step + wave * ROWS_WAVE + slot;
-    uint4 gv[U][VPL], xv[U][VPL];
-    float r[U];
+  // Byte offset of this lane's vector v within its row group, per tensor;
+  // vectors past D get an offset no resource reaches. Rows past the chunk's
+  // end read as zero (and then contribute nothing) and their stores drop.
+  auto voff = [&](int v, int64_t ld) -> uint32_t {
+    const int c = v * LPR + l;
+    if (MASKED && c >= nv) return kOutOfRange;
+    return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
+  };
+  auto group_first = [&](int64_t step, int u) { return step + wave * ROWS_WAVE + u * RPW; };
+
+  auto load_step = [&](int64_t step, u32x4 (&gq)[U][VPL], u32x4 (&xq)[U][VPL], float (&rq)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = row0 + u * RPW;
-      const bool valid = row < end;
-      r[u] = valid ? a.rstd[row] : 0.0f;
+      const int64_t first = group_first(step, u);
+      rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
+      const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
+      const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int c = v * LPR + l;
-        const bool ok = valid && (!MASKED || c < nv);
-        gv[u][v] = ok ? load16(a.g + row * a.ld_g + 8 * c) : uint4{0, 0, 0, 0};
-        xv[u][v] = ok ? load16(a.x + row * a.ld_x + 8 * c) : uint4{0, 0, 0, 0};
+        gq[u][v] = buf_load16(rg, voff(v, a.ld_g));
+        xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
       }
     }
+  };
 
+  auto process = [&](int64_t step, u32x4 (&gq)[U][VPL], u32x4 (&xq)[U][VPL], const float (&rq)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = row0 + u * RPW;
-      const bool valid = row < end;
-
-      if (want_dx) {
-        // s = sum_i (g_i * w_i) * x_i: lane partial in (vector, element)
-        // order, then the row's fixed butterfly.
-        float s = 0.0f;
+      const int64_t first = group_first(step, u);
+      const float r = rq[u];
+      int wbase = 0;
+      asm("" : "+v"(wbase));
+      // Pass 1: the lane partial of s = sum_i (g_i * w_i) * x_i in (vector,
+      // element) order, and this row's (g*x)*r added to the dgamma
+      // accumulators ((g*x) is exact in fp32 for bf16 inputs; rows past the
+      // chunk read as zeros with r = 0 and add +0).
+      acc_t sa = 0;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          float gf[8], xf[8];
-          unpack8(gv[u][v], gf);
-          unpack8(xv[u][v], xf);
+      for (int v = 0; v < VPL; ++v) {
+        if (MASKED && v * LPR + l >= nv) continue;  // no such vector (weights unset)
+        float gf[8], xf[8], w8[8];
+        unpack8(gq[u][v], gf);
+        unpack8(xq[u][v], xf);
+        weights(wbase, v, w8);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float gw = gf[k] * w[v][k];
-            s = __builtin_fmaf(gw, xf[k], s);
-          }
+        for (int k = 0; k < 8; ++k) {
+          const float gw = gf[k] * w8[k];
+          const float t = gw * xf[k];
+          sa = acc_add(sa, t);
+          acc[v][k] = __builtin_fmaf(gf[k] * xf[k], r, acc[v][k]);
         }
-        s = row_sum<LPR>(s);
-        const float rr = r[u] * r[u];
-        const float r3 = rr * r[u];
-        const float r3s = r3 * s;
-        const float c = r3s / Df;
-
-        if (valid) {
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) {
-            const int cv = v * LPR + l;
-            if (MASKED && cv >= nv) continue;
-            float gf[8], xf[8], o[8];
-            unpack8(gv[u][v], gf);
-            unpack8(xv[u][v], xf);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const float gw = gf[k] * w[v][k];
-              const float t1 = gw * r[u];
-              const float t2 = xf[k] * c;
-              o[k] = t1 - t2;
-            }
-            if (a.gres != nullptr) {
-              float rf[8];
-              unpack8(load16(a.gres + row * a.ld_gres + 8 * cv), rf);
-#pragma unroll
-              for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
-            }
-            store16_stream(a.dx + row * a.ld_dx + 8 * cv, pack8(o));
-          }
-        }
+        RMSN_BWD_SCHED_FENCE();
       }
-
-      if (want_part) {
-        // (g*x) is exact in fp32 for bf16 inputs; one rounding per row.
+      const float s = static_cast<float>(row_sum<LPR>(sa));
+      const float rr = r * r;
+      const float r3 = rr * r;
+      const float r3s = r3 * s;
+      const float c = r3s / Df;
+      // Pass 2: dx = gw*r - x*c (+ gres), one rounding to bf16.
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          float gf[8], xf[8];
-          unpack8(gv[u][v], gf);
-          unpack8(xv[u][v], xf);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) acc[v][k] = __builtin_fmaf(gf[k] * xf[k], r[u], acc[v][k]);
-        }
+      for (int v = 0; v < VPL; ++v) {
+        opaque(gq[u][v]);
+        opaque(xq[u][v]);
       }
+      asm("" : "+v"(wbase));
+      // Without dx (weight gradient only) the resource is empty and the
+      // stores drop; computing dx anyway keeps this loop free of branches.
+      const auto rdx = rows_rsrc(a.dx, first, a.dx != nullptr ? end : first, RPW, a.ld_dx, a.D);
+      const auto rgr = rows_rsrc(GRES ? a.gres : a.g, first, GRES ? end : first, RPW,
+                                 GRES ? a.ld_gres : a.ld_g, a.D);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        if (MASKED && v * LPR + l >= nv) continue;
+        float gf[8], xf[8], w8[8], o[8];
+        unpack8(gq[u][v], gf);
+        unpack8(xq[u][v], xf);
+        weights(wbase, v, w8);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float gw = gf[k] * w8[k];
+          const float t1 = gw * r;
+          const float t2 = xf[k] * c;
+          o[k] = t1 - t2;
+        }
+        if constexpr (GRES) {
+          float rf[8];
+          unpack8(buf_load16(rgr, voff(v, a.ld_gres)), rf);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
+        }
+        buf_store16_nt(pack8(o), rdx, voff(v, a.ld_dx));
+        RMSN_BWD_SCHED_FENCE();
+      }
+    }
+  };
+
+  u32x4 gv[U][VPL], xv[U][VPL];
+  float rv[U];
+  if constexpr (RMSN_BWD_PREFETCH) {
+    load_step(begin, gv, xv, rv);
+    for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
+      u32x4 gn[U][VPL], xn[U][VPL];
+      float rn[U];
+      load_step(step + ROWS_BLOCK, gn, xn, rn);
+      process(step, gv, xv, rv);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        rv[u] = rn[u];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) { gv[u][v] = gn[u][v]; xv[u][v] = xn[u][v]; }
+      }
+    }
+  } else {
+    for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
+      load_step(step, gv, xv, rv);
+      process(step, gv, xv, rv);
     }
   }
 
@@ -154,7 +253,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[v][k] = acc[v][k] + __shfl_xor(acc[v][k], m);
 
-  // Waves: ((w0 + w2) + (w1 + w3)) through two LDS rows of D floats.
+  // Waves: ((w0 + w2) + (w1 + w3)) through two LDS rows of D floats (the
+  // weights' space is reused, hence the barrier first).
+  __syncthreads();
   const bool writer = slot == 0;
   auto lds_row = [&](int b) { return lds + b * a.D; };
   if (wave >= 2 && writer) {
@@ -205,11 +306,15 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 }
 
 // dgamma from the chunk partials. A workgroup covers 32 columns (8 float4
-// groups) with 32 k-slices; slice s sums k = s, s+32, s+64, ... in ascending
-// order, then the 32 slice sums meet in a fixed halving tree in LDS.
-// chunks == 0 writes zeros (the empty sum).
+// groups) with 32 slices; slice s sums its contiguous range of chunks in
+// ascending order (loads issued 8 at a time), then the 32 slice sums meet in
+// a fixed halving tree in LDS. chunks == 0 writes zeros (the empty sum).
 constexpr int kFinishSlices = 32;
 constexpr int kFinishQuads = kBlock / kFinishSlices;  // float4 groups per block
+#ifndef RMSN_FINISH_BATCH
+#define RMSN_FINISH_BATCH 8
+#endif
+constexpr int kFinishBatch = RMSN_FINISH_BATCH;
 
 __global__ __launch_bounds__(kBlock) void rmsnorm_bwd_finish_kernel(const float* __restrict__ part,
                                                                     int64_t chunks, int D,
@@ -220,12 +325,24 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_bwd_finish_kernel(const float*
   const int col4 = blockIdx.x * kFinishQuads + q;
   const int d4 = D >> 2;
   const bool ok = col4 < d4;
+  const int64_t per = (chunks + kFinishSlices - 1) / kFinishSlices;
+  const int64_t k0 = s * per;
+  const int64_t k1 = k0 + per < chunks ? k0 + per : chunks;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (ok) {
     const float4* p = reinterpret_cast<const float4*>(part) + col4;
-    for (int64_t k = s; k < chunks; k += kFinishSlices) {
-      const float4 t = p[k * d4];
-      acc.x = acc.x + t.x; acc.y = acc.y + t.y; acc.z = acc.z + t.z; acc.w = acc.w + t.w;
+    for (int64_t kb = k0; kb < k1; kb += kFinishBatch) {
+      float4 t[kFinishBatch];
+#pragma unroll
+      for (int j = 0; j < kFinishBatch; ++j)
+        t[j] = kb + j < k1 ? p[(kb + j) * d4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int j = 0; j < kFinishBatch; ++j) {
+        if (kb + j < k1) {
+          acc.x = acc.x + t[j].x; acc.y = acc.y + t[j].y;
+          acc.z = acc.z + t[j].z; acc.w = acc.w + t[j].w;
+        }
+      }
     }
   }
   red[s][q] = acc;
@@ -245,35 +362,41 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_bwd_finish_kernel(const float*
 
 namespace {
 
-template <int LPR, int VPL, bool MASKED>
+template <int LPR, int VPL, bool MASKED, bool GRES>
 int launch_rows_inst(const BwdArgs& a, void* stream) {
-  const size_t lds = a.part != nullptr ? 2 * sizeof(float) * static_cast<size_t>(a.D) : 0;
-  hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED>), dim3(static_cast<unsigned>(a.chunks)),
-                     dim3(kBlock), lds, static_cast<hipStream_t>(stream), a);
+  const size_t lds = sizeof(float) * bwd_rows_lds_floats(a.D, a.part != nullptr);
+  hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, GRES>),
+                     dim3(static_cast<unsigned>(a.chunks)), dim3(kBlock), lds,
+                     static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
 
 using RowsLaunch = int (*)(const BwdArgs&, void*);
 
+template <int LPR, int VPL, bool MASKED>
+RowsLaunch pick_gres(bool gres) {
+  return gres ? &launch_rows_inst<LPR, VPL, MASKED, true> : &launch_rows_inst<LPR, VPL, MASKED, false>;
+}
+
 template <int VPL = 1>
-RowsLaunch pick_wide(int vpl, bool masked) {
+RowsLaunch pick_wide(int vpl, bool masked, bool gres) {
   if constexpr (VPL > kMaxVpl) {
     return nullptr;
   } else {
-    if (vpl == VPL) return masked ? &launch_rows_inst<64, VPL, true> : &launch_rows_inst<64, VPL, false>;
-    return pick_wide<VPL + 1>(vpl, masked);
+    if (vpl == VPL) return masked ? pick_gres<64, VPL, true>(gres) : pick_gres<64, VPL, false>(gres);
+    return pick_wide<VPL + 1>(vpl, masked, gres);
   }
 }
 
-RowsLaunch pick(const RowGeom& g) {
+RowsLaunch pick(const RowGeom& g, bool gres) {
   switch (g.lpr) {
-    case 64: return pick_wide(g.vpl, g.masked);
-    case 32: return g.masked ? &launch_rows_inst<32, 1, true> : &launch_rows_inst<32, 1, false>;
-    case 16: return g.masked ? &launch_rows_inst<16, 1, true> : &launch_rows_inst<16, 1, false>;
-    case 8: return g.masked ? &launch_rows_inst<8, 1, true> : &launch_rows_inst<8, 1, false>;
-    case 4: return g.masked ? &launch_rows_inst<4, 1, true> : &launch_rows_inst<4, 1, false>;
-    case 2: return &launch_rows_inst<2, 1, false>;
-    case 1: return &launch_rows_inst<1, 1, false>;
+    case 64: return pick_wide(g.vpl, g.masked, gres);
+    case 32: return g.masked ? pick_gres<32, 1, true>(gres) : pick_gres<32, 1, false>(gres);
+    case 16: return g.masked ? pick_gres<16, 1, true>(gres) : pick_gres<16, 1, false>(gres);
+    case 8: return g.masked ? pick_gres<8, 1, true>(gres) : pick_gres<8, 1, false>(gres);
+    case 4: return g.masked ? pick_gres<4, 1, true>(gres) : pick_gres<4, 1, false>(gres);
+    case 2: return pick_gres<2, 1, false>(gres);
+    case 1: return pick_gres<1, 1, false>(gres);
     default: return nullptr;
   }
 }
@@ -282,7 +405,7 @@ RowsLaunch pick(const RowGeom& g) {
 
 int launch_bwd_rows(const BwdArgs& a, void* stream) {
   if (a.T == 0 || a.chunks == 0) return 0;
-  const RowsLaunch f = pick(row_geom(a.D));
+  const RowsLaunch f = pick(row_geom(a.D), a.gres != nullptr);
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);
   return f(a, stream);
 }

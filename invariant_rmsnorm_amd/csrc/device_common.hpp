@@ -18,7 +18,7 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Unpack the 8 bf16 values of a 16-byte vector, in memory order.
-__device__ __forceinline__ void unpack8(const uint4& q, float (&f)[8]) {
+__device__ __forceinline__ void unpack8(const u32x4& q, float (&f)[8]) {
   f[0] = bf16_lo(q.x); f[1] = bf16_hi(q.x);
   f[2] = bf16_lo(q.y); f[3] = bf16_hi(q.y);
   f[4] = bf16_lo(q.z); f[5] = bf16_hi(q.z);
@@ -33,17 +33,66 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
-  return uint4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  return u32x4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
 }
 
-__device__ __forceinline__ uint4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
+// ---- buffer access -----------------------------------------------------------
+// Rows are read and written through buffer resources: a wave-uniform base
+// address and byte count in scalar registers plus a 32-bit per-lane offset.
+// The hardware returns zeros for loads at or past the byte count and drops
+// such stores, so rows past the end of the batch (or of a chunk) and vectors
+// past D need no branches: they are given offsets beyond the count.
+// Word 3 of the descriptor selects 32-bit raw access on gfx9-family parts.
+constexpr uint32_t kBufWord3 = 0x00020000u;
+// An offset no resource built below reaches (all counts stay under 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Resource over the rows [first, min(first + cap, limit)) (empty when
+// first >= limit), each row D bf16 values at a stride of ld elements. With
+// cap <= 64 and ld <= 2^24 (checked by the host) the byte count stays below
+// 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t first,
+                                                            int64_t limit, int cap, int64_t ld,
+                                                            int D) {
+  const int64_t left = limit - first;
+  const int64_t count = left < cap ? left : cap;
+  const char* p = static_cast<const char*>(base) + first * ld * 2;
+  const uint32_t n = count > 0 ? static_cast<uint32_t>(((count - 1) * ld + D) * 2) : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), 0, static_cast<int>(n), kBufWord3);
 }
-__device__ __forceinline__ void store16_stream(uint16_t* p, const uint4& v) {
-  const u32x4 q = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
+
+// Resource over the fp32 values [first, min(first + cap, limit)).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_rsrc(const float* base, int64_t first,
+                                                           int64_t limit, int cap) {
+  const int64_t left = limit - first;
+  const int64_t count = left < cap ? left : cap;
+  const uint32_t n = count > 0 ? static_cast<uint32_t>(count * 4) : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base + first), 0, static_cast<int>(n),
+                                           kBufWord3);
 }
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+// Streaming store (non-temporal: the line is not kept in the caches).
+__device__ __forceinline__ void buf_store16_nt(const u32x4& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 2);
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+
+// The wave's index within the workgroup, known to the compiler as uniform.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
+
+// Makes the compiler treat a register vector as rewritten here, so values it
+// derived from the vector earlier (unpacked floats, products) are recomputed
+// afterwards instead of being kept alive. Re-deriving them costs one VALU op
+// each; keeping them would cost a row's worth of extra registers.
+__device__ __forceinline__ void opaque(u32x4& q) { asm("" : "+v"(q)); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -72,6 +121,74 @@ __device__ __forceinline__ float row_sum(float v) {
     v = lo + hi;
   }
   return v;
+}
+
+// The same butterfly on fp64 partials (each 64-bit value moves as two 32-bit
+// halves through the same DPP / swizzle / readlane patterns).
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(b)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(b >> 32)), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ double swizzle_xor16_64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_ds_swizzle(static_cast<int>(static_cast<uint32_t>(b)), 0x401F));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_ds_swizzle(static_cast<int>(static_cast<uint32_t>(b >> 32)), 0x401F));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ double readlane64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), lane));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), lane));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int LPR>
+__device__ __forceinline__ double row_sum(double v) {
+  if constexpr (LPR >= 2) v = v + dpp64<0xB1>(v);
+  if constexpr (LPR >= 4) v = v + dpp64<0x4E>(v);
+  if constexpr (LPR >= 8) v = v + dpp64<0x141>(v);
+  if constexpr (LPR >= 16) v = v + dpp64<0x140>(v);
+  if constexpr (LPR >= 32) v = v + swizzle_xor16_64(v);
+  if constexpr (LPR >= 64) v = readlane64(v, 0) + readlane64(v, 32);
+  return v;
+}
+
+// Row reductions accumulate fp32 terms (squares of bf16 values, which are
+// exact, and the fp32 products gw*x) in fp64 along the fixed tree above, and
+// round the total to fp32 once. The fp64 sum of such terms is exact, or
+// within a few fp64 ulp of exact, whatever the order, so the fp32 result is
+// the same as an ordered sum's except when the exact value lies within those
+// few fp64 ulp of an fp32 rounding boundary.
+#ifndef RMSN_ACC_F64
+#define RMSN_ACC_F64 1
+#endif
+#if RMSN_ACC_F64
+typedef double acc_t;
+#else
+typedef float acc_t;
+#endif
+__device__ __forceinline__ acc_t acc_add(acc_t a, float t) { return a + static_cast<acc_t>(t); }
+
+// r = rsqrt(ss / D + eps): the mean is an fp32 division and the sum with eps
+// an fp32 addition; the reciprocal square root is 1/sqrt taken in fp64 (both
+// operations correctly rounded) and rounded to fp32 once.
+__device__ __forceinline__ float rstd_of(float ss, float Df, float eps) {
+  const float mean = ss / Df;
+  const float var = mean + eps;
+#if RMSN_ACC_F64
+  return static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(var)));
+#else
+  return rsqrtf(var);
+#endif
 }
 
 // Loads this lane's weights w_eff = gamma (+1.0f in fp32 when zero-centred)

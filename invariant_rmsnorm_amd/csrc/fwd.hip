@@ -38,86 +38,135 @@ __device__ __forceinline__ float silu(float z) {
   return z * sg;
 }
 
+// Tuning switch (fixed at build time; changes speed, not results): load the
+// next step's rows before computing the current one.
+#ifndef RMSN_FWD_PREFETCH
+#define RMSN_FWD_PREFETCH 0
+#endif
+
 template <int LPR, int VPL, bool MASKED, bool GATED>
 __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   constexpr int RPW = 64 / LPR;
   constexpr int U = fwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
+  constexpr int ZU = GATED ? U : 1;
+  constexpr int ZV = GATED ? VPL : 1;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int slot = lane / LPR;
   const int l = lane % LPR;
   const int nv = a.D >> 3;
   const float Df = static_cast<float>(a.D);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS_BLOCK;
 
   float w[VPL][8];
   load_weights<LPR, VPL, MASKED>(a.gamma, a.zc, nv, l, w);
 
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * ROWS_BLOCK; base < a.T;
-       base += static_cast<int64_t>(gridDim.x) * ROWS_BLOCK) {
-    const int64_t row0 = base + wave * ROWS_WAVE + slot;
+  // Byte offset of this lane's vector v within its row group, per tensor;
+  // vectors past D get an offset no resource reaches.
+  auto voff = [&](int v, int64_t ld) -> uint32_t {
+    const int c = v * LPR + l;
+    if (MASKED && c >= nv) return kOutOfRange;
+    return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
+  };
+  // Rows first .. first+RPW-1 form row group u of the wave; `first` is
+  // wave-uniform.
+  auto group_first = [&](int64_t base, int u) { return base + wave * ROWS_WAVE + u * RPW; };
 
-    uint4 xv[U][VPL];
-    uint4 zv[GATED ? U : 1][GATED ? VPL : 1];
+  auto load_step = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = row0 + u * RPW;
-      const bool valid = row < a.T;
+      const int64_t first = group_first(base, u);
+      const auto rx = rows_rsrc(a.x, first, a.T, RPW, a.ld_x, a.D);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int c = v * LPR + l;
-        const bool ok = valid && (!MASKED || c < nv);
-        xv[u][v] = ok ? load16(a.x + row * a.ld_x + 8 * c) : uint4{0, 0, 0, 0};
-        if constexpr (GATED)
-          zv[u][v] = ok ? load16(a.z + row * a.ld_z + 8 * c) : uint4{0, 0, 0, 0};
+      for (int v = 0; v < VPL; ++v) xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
+      if constexpr (GATED) {
+        const auto rz = rows_rsrc(a.z, first, a.T, RPW, a.ld_z, a.D);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16(rz, voff(v, a.ld_z));
       }
     }
+  };
 
+  auto process = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t row = row0 + u * RPW;
-      const bool valid = row < a.T;
+      const int64_t first = group_first(base, u);
+      const int64_t row = first + slot;
 
       // sum of squares: this lane's elements in (vector, element) order, then
       // the row's fixed butterfly. Squares of bf16 values are exact in fp32.
-      float ss = 0.0f;
+      acc_t ssa = 0;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         float f[8];
-        unpack8(xv[u][v], f);
+        unpack8(xq[u][v], f);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ss = __builtin_fmaf(f[k], f[k], ss);
-      }
-      ss = row_sum<LPR>(ss);
-      const float mean = ss / Df;
-      const float var = mean + a.eps;
-      const float r = rsqrtf(var);
-
-      if (valid) {
-        if (a.rstd != nullptr && l == 0) a.rstd[row] = r;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          const int c = v * LPR + l;
-          if (MASKED && c >= nv) continue;
-          float f[8], o[8];
-          unpack8(xv[u][v], f);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float xr = f[k] * r;
-            o[k] = xr * w[v][k];
-          }
-          if constexpr (GATED) {
-            float zf[8];
-            unpack8(zv[u][v], zf);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) o[k] = o[k] * silu(zf[k]);
-          }
-          store16_stream(a.y + row * a.ld_y + 8 * c, pack8(o));
-          if (a.res != nullptr) store16_stream(a.res + row * a.ld_res + 8 * c, xv[u][v]);
+        for (int k = 0; k < 8; ++k) {
+          const float sq = f[k] * f[k];
+          ssa = acc_add(ssa, sq);
         }
       }
+      const float ss = static_cast<float>(row_sum<LPR>(ssa));
+      const float r = rstd_of(ss, Df, a.eps);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) opaque(xq[u][v]);
+
+      if (a.rstd != nullptr && l == 0 && row < a.T) a.rstd[row] = r;
+      // rows past T: the resources below are empty and drop the stores
+      const auto ry = rows_rsrc(a.y, first, a.T, RPW, a.ld_y, a.D);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        float f[8], o[8];
+        unpack8(xq[u][v], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float xr = f[k] * r;
+          o[k] = xr * w[v][k];
+        }
+        if constexpr (GATED) {
+          float zf[8];
+          unpack8(zq[u][v], zf);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = o[k] * silu(zf[k]);
+        }
+        buf_store16_nt(pack8(o), ry, voff(v, a.ld_y));
+      }
+      if (a.res != nullptr) {
+        const auto rr = rows_rsrc(a.res, first, a.T, RPW, a.ld_res, a.D);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) buf_store16_nt(xq[u][v], rr, voff(v, a.ld_res));
+      }
+    }
+  };
+
+  u32x4 xv[U][VPL];
+  u32x4 zv[ZU][ZV];
+  int64_t base = static_cast<int64_t>(blockIdx.x) * ROWS_BLOCK;
+  if constexpr (RMSN_FWD_PREFETCH) {
+    load_step(base, xv, zv);
+    for (; base < a.T; base += stride) {
+      u32x4 xn[U][VPL];
+      u32x4 zn[ZU][ZV];
+      load_step(base + stride, xn, zn);
+      process(base, xv, zv);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) xv[u][v] = xn[u][v];
+      if constexpr (GATED) {
+#pragma unroll
+        for (int u = 0; u < ZU; ++u)
+#pragma unroll
+          for (int v = 0; v < ZV; ++v) zv[u][v] = zn[u][v];
+      }
+    }
+  } else {
+    for (; base < a.T; base += stride) {
+      load_step(base, xv, zv);
+      process(base, xv, zv);
     }
   }
 }

@@ -22,8 +22,12 @@ constexpr int kBlock = 64 * kWaves;  // threads per workgroup
 constexpr int kMaxD = 8192;
 constexpr int kMaxVpl = kMaxD / 512;
 // The backward splits the batch into at most this many chunks of rows; one
-// workgroup per chunk (2 per compute unit on a 256-CU part).
-constexpr int64_t kTargetChunks = 512;
+// workgroup per chunk, one per compute unit on a 256-CU part (measured
+// faster than two: fewer concurrent row streams per HBM channel).
+#ifndef RMSN_TARGET_CHUNKS
+#define RMSN_TARGET_CHUNKS 256
+#endif
+constexpr int64_t kTargetChunks = RMSN_TARGET_CHUNKS;
 
 struct RowGeom {
   int lpr;     // lanes per row (1, 2, 4, ..., 64)

@@ -69,11 +69,9 @@ def rounding_consistent(res_bits: np.ndarray, exact: np.ndarray,
 
 
 # ---- GPU-vs-oracle tolerances ------------------------------------------------
-# y, gated out: <= 1 bf16 ulp. rstd: <= 1e-6 relative. dgamma: infinity-norm
-# relative <= 1e-5. dx: <= 1 bf16 ulp, except where the oracle's value comes
-# from catastrophic cancellation, |d| < 2^-10 * (|t1| + |t2| + |gres|): there
-# the GPU's differently ordered (but equally accurate) row sum s moves t2 by a
-# few fp32 ulp, so |dx - ref| <= ulp(ref) + 2^-20 * (|t1| + |t2| + |gres|).
+# y, gated out and dx: <= 1 bf16 ulp (ordered-integer distance, +0 == -0, NaN
+# matches NaN). rstd: <= 1e-6 relative. dgamma: infinity-norm relative
+# <= 1e-5, i.e. max|gpu - ref| <= 1e-5 * max|ref|.
 
 def max_ulp(a_bits: np.ndarray, b_bits: np.ndarray) -> int:
     if a_bits.size == 0:
@@ -98,43 +96,3 @@ def dgamma_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     if scale == 0:
         return float(np.abs(gpu).max())
     return float(np.abs(gpu.astype(np.float64) - ref).max() / scale)
-
-
-def dx_check(gpu_bits, ref_bits, g_bits, x_bits, w_eff, rstd_ref, gres_bits=None):
-    """(n_over_1ulp_outside_cancellation, n_cancellation_exceptions,
-    n_failing) for dx against the oracle (see the rule above)."""
-    d = ulp_distance(gpu_bits, ref_bits)
-    over = d > 1
-    if not over.any():
-        return 0, 0, 0
-    rows, cols = np.nonzero(over)
-    g = bf16_to_f64(g_bits[rows, cols])
-    x = bf16_to_f64(x_bits[rows, cols])
-    r = rstd_ref[rows].astype(np.float64)
-    w = np.asarray(w_eff, np.float64)[cols]
-    D = x_bits.shape[1]
-    # |t2| = |x * r^3 * s / D| needs the row's s: recompute per affected row
-    s_rows = {}
-    for t in np.unique(rows):
-        gr = bf16_to_f64(g_bits[t])
-        xr = bf16_to_f64(x_bits[t])
-        s_rows[t] = float((gr * np.asarray(w_eff, np.float64) * xr).sum())
-    s = np.array([s_rows[t] for t in rows])
-    t1 = np.abs(g * w * r)
-    t2 = np.abs(x * r ** 3 * s / D)
-    gr_abs = 0.0 if gres_bits is None else np.abs(bf16_to_f64(gres_bits[rows, cols]))
-    mag = t1 + t2 + gr_abs
-    ref = bf16_to_f64(ref_bits[rows, cols])
-    gpu = bf16_to_f64(gpu_bits[rows, cols])
-    cancelled = np.abs(ref) < 2.0 ** -10 * mag
-    ulp_ref = _bf16_ulp(ref)
-    ok = cancelled & (np.abs(gpu - ref) <= ulp_ref + 2.0 ** -20 * mag)
-    return int((~cancelled).sum()), int(cancelled.sum()), int((~ok).sum())
-
-
-def _bf16_ulp(v: np.ndarray) -> np.ndarray:
-    """Spacing of bf16 numbers at |v| (subnormal spacing near zero)."""
-    a = np.abs(v)
-    e = np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0))), -126.0)
-    e = np.maximum(e, -126)
-    return 2.0 ** (e - 7)

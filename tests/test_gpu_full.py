@@ -16,7 +16,7 @@ import torch
 import invariant_rmsnorm_amd as irn
 import oracle
 from gpu_util import dev_bf16, dev_f32, host_bits
-from numerics import dgamma_rel_err, dx_check, max_ulp, rstd_rel_err
+from numerics import dgamma_rel_err, max_ulp, rstd_rel_err
 from synth import workloads as wl
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -39,14 +39,17 @@ def test_residual_token_norm_full(gpu):
 
     ry, rr = oracle.fwd(p.x, p.gamma, False, p.eps)
     _log("oracle forward done")
-    assert max_ulp(host_bits(y), ry) <= 1
-    assert rstd_rel_err(rstd.cpu().numpy(), rr) <= 1e-6
-    w = oracle.weights(p.gamma, False)
+    gy, gr_ = host_bits(y), rstd.cpu().numpy()
+    _log(f"y: {(gy != ry).sum()} of {gy.size} differ from the oracle; "
+         f"rstd: {(gr_ != rr).sum()} of {rr.size}")
+    assert max_ulp(gy, ry) <= 1
+    assert rstd_rel_err(gr_, rr) <= 1e-6
     for gpu_dx, gres in ((dx, None), (dxr, p.gres)):
         rdx = oracle.bwd_dx(p.g, p.x, rr, p.gamma, False, gres)
-        n_over, n_canc, n_fail = dx_check(host_bits(gpu_dx), rdx, p.g, p.x, w, rr, gres)
-        _log(f"dx (gres={gres is not None}): >1ulp cancellations {n_canc}, failures {n_fail}")
-        assert n_fail == 0
+        gdx = host_bits(gpu_dx)
+        _log(f"dx (gres={gres is not None}): {(gdx != rdx).sum()} of {gdx.size} differ, "
+             f"max ulp {max_ulp(gdx, rdx)}")
+        assert max_ulp(gdx, rdx) <= 1
     rdg = oracle.dgamma(p.g, p.x, rr)
     err = dgamma_rel_err(dg.cpu().numpy(), rdg)
     _log(f"dgamma rel err {err:.3e}")
@@ -88,7 +91,8 @@ def test_large_zero_centered_full(gpu):
     sy, sr = oracle.fwd(p.x[rows], p.gamma, True, p.eps)
     sdx = oracle.bwd_dx(p.g[rows], p.x[rows], sr, p.gamma, True)
     assert max_ulp(ys, sy) <= 1
-    assert dx_check(dxs, sdx, p.g[rows], p.x[rows], oracle.weights(p.gamma, True), sr)[2] == 0
+    assert max_ulp(dxs, sdx) <= 1
+    _log(f"sampled rows: y {(ys != sy).sum()}, dx {(dxs != sdx).sum()} elements differ")
 
     # ten runs: every output bitwise identical
     for i in range(10):

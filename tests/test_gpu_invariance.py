@@ -23,7 +23,7 @@ import invariant_rmsnorm_amd as irn
 import oracle
 import synth
 from gpu_util import dev_bf16, dev_f32, host_bits
-from numerics import dx_check, max_ulp, rstd_rel_err
+from numerics import max_ulp, rstd_rel_err
 from synth import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_anchor_rows_across_batches(gpu, k):
     oy, orr = oracle.fwd(ax[None], gamma_np)
     odx = oracle.bwd_dx(ag[None], ax[None], orr, gamma_np)
     assert max_ulp(host_bits(y1), oy) <= 1 and rstd_rel_err(r1.cpu().numpy(), orr) <= 1e-6
-    assert dx_check(host_bits(dx1), odx, ag[None], ax[None], gamma_np, orr)[2] == 0
+    assert max_ulp(host_bits(dx1), odx) <= 1
     n = 0
     for M in wl.SWEEP_M:
         for pos in wl.SWEEP_POSITIONS:

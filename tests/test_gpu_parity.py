@@ -15,8 +15,7 @@ import invariant_rmsnorm_amd as irn
 import oracle
 import synth
 from gpu_util import dev_bf16, dev_f32, host_bits, run_fwd_bwd
-from numerics import (bf16_to_f64, dgamma_rel_err, dx_check, f32_to_bf16_torch, max_ulp,
-                      rstd_rel_err)
+from numerics import bf16_to_f64, dgamma_rel_err, f32_to_bf16_torch, max_ulp, rstd_rel_err
 from synth import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -35,10 +34,7 @@ def assert_parity(p, got, ref, gres=False, label=""):
     assert max_ulp(got["y"], ref["y"]) <= 1, label
     assert rstd_rel_err(got["rstd"], ref["rstd"]) <= 1e-6, label
     if "dx" in ref:
-        n_over, n_canc, n_fail = dx_check(got["dx"], ref["dx"], p.g, p.x,
-                                          oracle.weights(p.gamma, p.zero_centered), ref["rstd"],
-                                          p.gres if gres else None)
-        assert n_fail == 0, (label, n_over, n_canc, n_fail)
+        assert max_ulp(got["dx"], ref["dx"]) <= 1, label
         assert dgamma_rel_err(got["dgamma"], ref["dgamma"]) <= 1e-5, label
 
 
@@ -147,10 +143,8 @@ def test_edge_values(gpu, D, eps):
     got, ref = run_fwd_bwd(p), oracle_all(p)
     assert max_ulp(got["y"], ref["y"]) <= 1
     assert rstd_rel_err(got["rstd"], ref["rstd"]) <= 1e-6
-    # dx: rows with finite, non-degenerate data follow the usual rule;
-    # NaN/inf positions must agree exactly
-    n_over, n_canc, n_fail = dx_check(got["dx"], ref["dx"], g, x, gamma, ref["rstd"])
-    assert n_fail == 0, (n_over, n_canc)
+    # dx within 1 ulp; NaN/inf positions must agree exactly
+    assert max_ulp(got["dx"], ref["dx"]) <= 1
     nan_g = np.isnan(bf16_to_f64(got["dx"]))
     nan_r = np.isnan(bf16_to_f64(ref["dx"]))
     assert np.array_equal(nan_g, nan_r)
