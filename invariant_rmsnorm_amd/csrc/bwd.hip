@@ -20,7 +20,7 @@
 // row in chunk order. At the end of the chunk the row slots of a wave are
 // added by a butterfly, the 4 waves as ((w0 + w2) + (w1 + w3)) through LDS,
 // and the chunk's partial row is written to workspace[k][:].
-// Kernel 2 (finish): dgamma[j] = a fixed tree over 32 slices, each slice an
+// Kernel 2 (finish): dgamma[j] = a fixed tree over 16 slices, each slice an
 // ascending sum over a contiguous range of the chunk partials. The grouping
 // depends on T (dgamma is a sum over the whole batch) but never on timing:
 // the bits repeat run to run.
@@ -31,50 +31,34 @@
 
 namespace rmsn {
 
-// Tuning switches (fixed at build time; they change speed, not results):
-// weights held in LDS instead of registers, and loading the next step's rows
-// before computing the current one.
-#ifndef RMSN_BWD_WEIGHTS_IN_LDS
-#define RMSN_BWD_WEIGHTS_IN_LDS 1
-#endif
-#ifndef RMSN_BWD_PREFETCH
-#define RMSN_BWD_PREFETCH 0
-#endif
-// Optional scheduling fence after each vector, so the scheduler does not
-// unpack a whole row at once for instruction-level parallelism.
-#ifndef RMSN_BWD_FENCE
-#define RMSN_BWD_FENCE 1
-#endif
-#if RMSN_BWD_FENCE
-#define RMSN_BWD_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define RMSN_BWD_SCHED_FENCE() ((void)0)
-#endif
-// Minimum waves per SIMD the register allocator must allow for a geometry
-// (more waves = more rows in flight; too many forces spills).
-#ifndef RMSN_BWD_WAVES_WIDE
-#define RMSN_BWD_WAVES_WIDE 2
-#endif
-constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 12 ? 1 : vpl >= 5 ? RMSN_BWD_WAVES_WIDE : 2; }
+// Register plan by geometry (chosen by measurement at D=4096; results do not
+// depend on it). The kernel runs one 4-wave workgroup per compute unit, so
+// each wave may use the whole register file. Up to 12 vectors per lane the
+// weights stay in registers and the values unpacked in the first pass are
+// reused by the second. Beyond that the registers would spill, so the
+// weights move to LDS and the second pass unpacks the raw vectors again.
+constexpr bool bwd_lean(int vpl) { return vpl >= 13; }
+constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 5 ? 1 : 2; }
 
-// LDS floats the rows kernel needs: the weights (one float4 pair per vector
-// slot, laid out so that consecutive lanes read consecutive 16 bytes) and,
-// after the rows are done, two rows of D floats for the wave merge (which
-// reuse the same space).
+// LDS floats the rows kernel needs: the weights when held in LDS (one float4
+// pair per vector slot, laid out so that consecutive lanes read consecutive
+// 16 bytes) and, after the rows are done, two rows of D floats for the wave
+// merge (which reuse the same space).
 inline size_t bwd_rows_lds_floats(int D, bool want_part) {
   const RowGeom g = row_geom(D);
-  const size_t w = RMSN_BWD_WEIGHTS_IN_LDS ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
+  const size_t w = bwd_lean(g.vpl) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
   const size_t m = want_part ? 2 * static_cast<size_t>(D) : 0;
   return w > m ? w : m;
 }
 
 template <int LPR, int VPL, bool MASKED, bool GRES>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL)))) void rmsnorm_bwd_rows_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL))))
+void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr int RPW = 64 / LPR;
   constexpr int U = bwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
-  constexpr bool WLDS = RMSN_BWD_WEIGHTS_IN_LDS;
+  constexpr bool LEAN = bwd_lean(VPL);
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
@@ -86,9 +70,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
   const bool want_part = a.part != nullptr;
 
   // Weights w_eff = gamma (+1 in fp32 when zero-centred).
-  float wreg[WLDS ? 1 : VPL][8];
+  float wreg[LEAN ? 1 : VPL][8];
   float4* const wl4 = reinterpret_cast<float4*>(lds);
-  if constexpr (WLDS) {
+  if constexpr (LEAN) {
     // float4 h (0/1) of vector c = v*LPR + l goes to slot (2v + h)*LPR + l
     for (int j = threadIdx.x; j < 2 * nv; j += kBlock) {
       const int c = j >> 1, h = j & 1;
@@ -98,19 +82,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
     }
     __syncthreads();
   } else {
-    load_weights<LPR, (WLDS ? 1 : VPL), MASKED>(a.gamma, a.zc, nv, l, wreg);
+    load_weights<LPR, (LEAN ? 1 : VPL), MASKED>(a.gamma, a.zc, nv, l, wreg);
   }
-  // `base` is an opaque zero (see below) so that the reads stay inside the
-  // row loop instead of being hoisted into registers for the whole chunk.
+  // In the lean plan `base` is an opaque zero, so that the LDS reads stay
+  // inside the row loop instead of being hoisted into registers.
   auto weights = [&](int base, int v, float (&w8)[8]) {
-    if constexpr (WLDS) {
+    if constexpr (LEAN) {
       const float4 p0 = wl4[base + (2 * v) * LPR + l];
       const float4 p1 = wl4[base + (2 * v + 1) * LPR + l];
       w8[0] = p0.x; w8[1] = p0.y; w8[2] = p0.z; w8[3] = p0.w;
       w8[4] = p1.x; w8[5] = p1.y; w8[6] = p1.z; w8[7] = p1.w;
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w8[k] = wreg[WLDS ? 0 : v][k];
+      for (int k = 0; k < 8; ++k) w8[k] = wreg[LEAN ? 0 : v][k];
     }
   };
 
@@ -131,12 +115,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
     if (MASKED && c >= nv) return kOutOfRange;
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
-  auto group_first = [&](int64_t step, int u) { return step + wave * ROWS_WAVE + u * RPW; };
 
-  auto load_step = [&](int64_t step, u32x4 (&gq)[U][VPL], u32x4 (&xq)[U][VPL], float (&rq)[U]) {
+  for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
+    u32x4 gq[U][VPL], xq[U][VPL];
+    u32x4 rq_res[GRES ? U : 1][GRES ? VPL : 1];  // residual-branch gradient
+    float rq[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t first = group_first(step, u);
+      const int64_t first = step + wave * ROWS_WAVE + u * RPW;
       rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
       const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
       const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
@@ -145,16 +131,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
         gq[u][v] = buf_load16(rg, voff(v, a.ld_g));
         xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
       }
+      if constexpr (GRES) {
+        const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) rq_res[u][v] = buf_load16(rgr, voff(v, a.ld_gres));
+      }
     }
-  };
 
-  auto process = [&](int64_t step, u32x4 (&gq)[U][VPL], u32x4 (&xq)[U][VPL], const float (&rq)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t first = group_first(step, u);
+      const int64_t first = step + wave * ROWS_WAVE + u * RPW;
       const float r = rq[u];
       int wbase = 0;
-      asm("" : "+v"(wbase));
+      if constexpr (LEAN) asm("" : "+v"(wbase));
       // Pass 1: the lane partial of s = sum_i (g_i * w_i) * x_i in (vector,
       // element) order, and this row's (g*x)*r added to the dgamma
       // accumulators ((g*x) is exact in fp32 for bf16 inputs; rows past the
@@ -174,7 +163,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
           sa = acc_add(sa, t);
           acc[v][k] = __builtin_fmaf(gf[k] * xf[k], r, acc[v][k]);
         }
-        RMSN_BWD_SCHED_FENCE();
+        // one vector at a time: without this fence the scheduler unpacks the
+        // whole row up front and the kernel runs ~10% slower (measured)
+        __builtin_amdgcn_sched_barrier(0);
       }
       const float s = static_cast<float>(row_sum<LPR>(sa));
       const float rr = r * r;
@@ -182,17 +173,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
       const float r3s = r3 * s;
       const float c = r3s / Df;
       // Pass 2: dx = gw*r - x*c (+ gres), one rounding to bf16.
+      if constexpr (LEAN) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        opaque(gq[u][v]);
-        opaque(xq[u][v]);
+        for (int v = 0; v < VPL; ++v) {
+          opaque(gq[u][v]);
+          opaque(xq[u][v]);
+        }
+        asm("" : "+v"(wbase));
       }
-      asm("" : "+v"(wbase));
       // Without dx (weight gradient only) the resource is empty and the
       // stores drop; computing dx anyway keeps this loop free of branches.
       const auto rdx = rows_rsrc(a.dx, first, a.dx != nullptr ? end : first, RPW, a.ld_dx, a.D);
-      const auto rgr = rows_rsrc(GRES ? a.gres : a.g, first, GRES ? end : first, RPW,
-                                 GRES ? a.ld_gres : a.ld_g, a.D);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         if (MASKED && v * LPR + l >= nv) continue;
@@ -209,36 +200,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
         }
         if constexpr (GRES) {
           float rf[8];
-          unpack8(buf_load16(rgr, voff(v, a.ld_gres)), rf);
+          unpack8(rq_res[u][v], rf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
         }
         buf_store16_nt(pack8(o), rdx, voff(v, a.ld_dx));
-        RMSN_BWD_SCHED_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-  };
-
-  u32x4 gv[U][VPL], xv[U][VPL];
-  float rv[U];
-  if constexpr (RMSN_BWD_PREFETCH) {
-    load_step(begin, gv, xv, rv);
-    for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
-      u32x4 gn[U][VPL], xn[U][VPL];
-      float rn[U];
-      load_step(step + ROWS_BLOCK, gn, xn, rn);
-      process(step, gv, xv, rv);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        rv[u] = rn[u];
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) { gv[u][v] = gn[u][v]; xv[u][v] = xn[u][v]; }
-      }
-    }
-  } else {
-    for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
-      load_step(step, gv, xv, rv);
-      process(step, gv, xv, rv);
     }
   }
 
@@ -305,59 +273,54 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_wave
   }
 }
 
-// dgamma from the chunk partials. A workgroup covers 32 columns (8 float4
-// groups) with 32 slices; slice s sums its contiguous range of chunks in
-// ascending order (loads issued 8 at a time), then the 32 slice sums meet in
-// a fixed halving tree in LDS. chunks == 0 writes zeros (the empty sum).
-constexpr int kFinishSlices = 32;
-constexpr int kFinishQuads = kBlock / kFinishSlices;  // float4 groups per block
-#ifndef RMSN_FINISH_BATCH
-#define RMSN_FINISH_BATCH 8
-#endif
-constexpr int kFinishBatch = RMSN_FINISH_BATCH;
+// dgamma from the chunk partials. A workgroup is two waves covering 32
+// columns (one 128-byte line of each partial row, so no line is fetched by
+// two workgroups); in wave w, lane = 16*q + s, where q picks one of the
+// wave's 4 float4 groups and s one of 16 slices. Slice s sums its contiguous
+// range of chunks in ascending order (its loads issued together), then the
+// 16 slice sums meet in the fixed DPP butterfly over the 16 lanes that share
+// q. chunks == 0 writes zeros (the empty sum).
+constexpr int kFinishSlices = 16;
+constexpr int kFinishQuads = 64 / kFinishSlices;  // float4 groups per wave
+constexpr int kFinishWaves = 2;
+constexpr int kFinishLoads = 16;                  // loads in flight per lane
 
-__global__ __launch_bounds__(kBlock) void rmsnorm_bwd_finish_kernel(const float* __restrict__ part,
-                                                                    int64_t chunks, int D,
-                                                                    float* __restrict__ dgamma) {
-  __shared__ float4 red[kFinishSlices][kFinishQuads];
-  const int q = threadIdx.x % kFinishQuads;
-  const int s = threadIdx.x / kFinishQuads;
-  const int col4 = blockIdx.x * kFinishQuads + q;
+__global__ __launch_bounds__(64 * kFinishWaves) void rmsnorm_bwd_finish_kernel(
+    const float* __restrict__ part, int64_t chunks, int D, float* __restrict__ dgamma) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane / kFinishSlices;
+  const int s = lane % kFinishSlices;
+  const int col4 = (blockIdx.x * kFinishWaves + wave_id()) * kFinishQuads + q;
   const int d4 = D >> 2;
-  const bool ok = col4 < d4;
   const int64_t per = (chunks + kFinishSlices - 1) / kFinishSlices;
   const int64_t k0 = s * per;
   const int64_t k1 = k0 + per < chunks ? k0 + per : chunks;
+  // One resource over all partials (at most 256 x 8192 floats = 8 MiB);
+  // lanes past D and chunks past the slice's range get an offset beyond it
+  // and read zeros, so the loads need no branches.
+  const bool ok = col4 < d4;
+  const auto rp = f32_rsrc(part, 0, chunks * D, 0x7FFFFFFF / 4);
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (ok) {
-    const float4* p = reinterpret_cast<const float4*>(part) + col4;
-    for (int64_t kb = k0; kb < k1; kb += kFinishBatch) {
-      float4 t[kFinishBatch];
+  for (int64_t kb = k0; kb < k1; kb += kFinishLoads) {
+    u32x4 t[kFinishLoads];
 #pragma unroll
-      for (int j = 0; j < kFinishBatch; ++j)
-        t[j] = kb + j < k1 ? p[(kb + j) * d4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int j = 0; j < kFinishLoads; ++j) {
+      const bool in = ok && kb + j < k1;
+      t[j] = buf_load16(rp, in ? static_cast<uint32_t>(((kb + j) * d4 + col4) * 16) : kOutOfRange);
+    }
 #pragma unroll
-      for (int j = 0; j < kFinishBatch; ++j) {
-        if (kb + j < k1) {
-          acc.x = acc.x + t[j].x; acc.y = acc.y + t[j].y;
-          acc.z = acc.z + t[j].z; acc.w = acc.w + t[j].w;
-        }
+    for (int j = 0; j < kFinishLoads; ++j) {
+      if (kb + j < k1) {
+        acc.x = acc.x + __uint_as_float(t[j].x); acc.y = acc.y + __uint_as_float(t[j].y);
+        acc.z = acc.z + __uint_as_float(t[j].z); acc.w = acc.w + __uint_as_float(t[j].w);
       }
     }
   }
-  red[s][q] = acc;
-  __syncthreads();
-#pragma unroll
-  for (int h = kFinishSlices / 2; h >= 1; h >>= 1) {
-    if (s < h) {
-      const float4 o = red[s + h][q];
-      float4 m = red[s][q];
-      m.x = m.x + o.x; m.y = m.y + o.y; m.z = m.z + o.z; m.w = m.w + o.w;
-      red[s][q] = m;
-    }
-    __syncthreads();
-  }
-  if (s == 0 && ok) reinterpret_cast<float4*>(dgamma)[col4] = red[0][q];
+  acc.x = row_sum<kFinishSlices>(acc.x);
+  acc.y = row_sum<kFinishSlices>(acc.y);
+  acc.z = row_sum<kFinishSlices>(acc.z);
+  acc.w = row_sum<kFinishSlices>(acc.w);
+  if (s == 0 && ok) reinterpret_cast<float4*>(dgamma)[col4] = acc;
 }
 
 namespace {
@@ -411,9 +374,9 @@ int launch_bwd_rows(const BwdArgs& a, void* stream) {
 }
 
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream) {
-  const int cols_per_block = 4 * kFinishQuads;
+  const int cols_per_block = 4 * kFinishQuads * kFinishWaves;
   const int grid = (D + cols_per_block - 1) / cols_per_block;
-  hipLaunchKernelGGL(rmsnorm_bwd_finish_kernel, dim3(grid), dim3(kBlock), 0,
+  hipLaunchKernelGGL(rmsnorm_bwd_finish_kernel, dim3(grid), dim3(64 * kFinishWaves), 0,
                      static_cast<hipStream_t>(stream), part, chunks, D, dgamma);
   return static_cast<int>(hipGetLastError());
 }

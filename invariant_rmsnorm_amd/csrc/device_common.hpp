@@ -168,14 +168,7 @@ __device__ __forceinline__ double row_sum(double v) {
 // within a few fp64 ulp of exact, whatever the order, so the fp32 result is
 // the same as an ordered sum's except when the exact value lies within those
 // few fp64 ulp of an fp32 rounding boundary.
-#ifndef RMSN_ACC_F64
-#define RMSN_ACC_F64 1
-#endif
-#if RMSN_ACC_F64
 typedef double acc_t;
-#else
-typedef float acc_t;
-#endif
 __device__ __forceinline__ acc_t acc_add(acc_t a, float t) { return a + static_cast<acc_t>(t); }
 
 // r = rsqrt(ss / D + eps): the mean is an fp32 division and the sum with eps
@@ -184,11 +177,7 @@ __device__ __forceinline__ acc_t acc_add(acc_t a, float t) { return a + static_c
 __device__ __forceinline__ float rstd_of(float ss, float Df, float eps) {
   const float mean = ss / Df;
   const float var = mean + eps;
-#if RMSN_ACC_F64
   return static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(var)));
-#else
-  return rsqrtf(var);
-#endif
 }
 
 // Loads this lane's weights w_eff = gamma (+1.0f in fp32 when zero-centred)

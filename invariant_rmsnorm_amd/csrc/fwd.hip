@@ -38,10 +38,9 @@ __device__ __forceinline__ float silu(float z) {
   return z * sg;
 }
 
-// Tuning switch (fixed at build time; changes speed, not results): load the
-// next step's rows before computing the current one.
-#ifndef RMSN_FWD_PREFETCH
-#define RMSN_FWD_PREFETCH 0
+// Workgroups per compute unit in the persistent grid (0 = as many as fit).
+#ifndef RMSN_FWD_BLOCKS_PER_CU
+#define RMSN_FWD_BLOCKS_PER_CU 0
 #endif
 
 template <int LPR, int VPL, bool MASKED, bool GATED>
@@ -142,32 +141,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
     }
   };
 
-  u32x4 xv[U][VPL];
-  u32x4 zv[ZU][ZV];
-  int64_t base = static_cast<int64_t>(blockIdx.x) * ROWS_BLOCK;
-  if constexpr (RMSN_FWD_PREFETCH) {
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * ROWS_BLOCK; base < a.T; base += stride) {
+    u32x4 xv[U][VPL];
+    u32x4 zv[ZU][ZV];
     load_step(base, xv, zv);
-    for (; base < a.T; base += stride) {
-      u32x4 xn[U][VPL];
-      u32x4 zn[ZU][ZV];
-      load_step(base + stride, xn, zn);
-      process(base, xv, zv);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) xv[u][v] = xn[u][v];
-      if constexpr (GATED) {
-#pragma unroll
-        for (int u = 0; u < ZU; ++u)
-#pragma unroll
-          for (int v = 0; v < ZV; ++v) zv[u][v] = zn[u][v];
-      }
-    }
-  } else {
-    for (; base < a.T; base += stride) {
-      load_step(base, xv, zv);
-      process(base, xv, zv);
-    }
+    process(base, xv, zv);
   }
 }
 
@@ -197,7 +175,8 @@ int launch_fwd_inst(const FwdArgs& a, void* stream) {
     return b;
   }();
   const int64_t blocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu;
+  const int64_t cap = static_cast<int64_t>(cu_count()) *
+                      (RMSN_FWD_BLOCKS_PER_CU > 0 ? std::min(per_cu, RMSN_FWD_BLOCKS_PER_CU) : per_cu);
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min(blocks, cap)));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
