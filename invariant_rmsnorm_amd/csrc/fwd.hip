@@ -38,10 +38,6 @@ __device__ __forceinline__ float silu(float z) {
   return z * sg;
 }
 
-// Workgroups per compute unit in the persistent grid (0 = as many as fit).
-#ifndef RMSN_FWD_BLOCKS_PER_CU
-#define RMSN_FWD_BLOCKS_PER_CU 0
-#endif
 
 template <int LPR, int VPL, bool MASKED, bool GATED>
 __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
@@ -174,10 +170,13 @@ int launch_fwd_inst(const FwdArgs& a, void* stream) {
       b = 1;
     return b;
   }();
+  // Persistent grid: at most as many workgroups as fit on the device, and
+  // every workgroup given the same number of steps (a grid of `cap` over
+  // 1.6 * cap steps would leave half the device idle for the last step).
   const int64_t blocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
-  const int64_t cap = static_cast<int64_t>(cu_count()) *
-                      (RMSN_FWD_BLOCKS_PER_CU > 0 ? std::min(per_cu, RMSN_FWD_BLOCKS_PER_CU) : per_cu);
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min(blocks, cap)));
+  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu;
+  const int64_t steps = (blocks + cap - 1) / cap;
+  const int grid = static_cast<int>(std::max<int64_t>(1, (blocks + steps - 1) / steps));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }

@@ -45,8 +45,11 @@ inline RowGeom row_geom(int64_t D) {
 
 // Rows a wave keeps in flight per step: enough that each lane has about
 // 128 bytes of one input stream outstanding.
+#ifndef RMSN_FWD_UNROLL_NARROW
+#define RMSN_FWD_UNROLL_NARROW 2
+#endif
 constexpr int fwd_unroll(int lpr, int vpl) {
-  return lpr < 64 ? 8 : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
+  return lpr < 64 ? RMSN_FWD_UNROLL_NARROW : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
 }
 constexpr int bwd_unroll(int lpr, int vpl) {
   return lpr < 64 ? 4 : (vpl == 1 ? 4 : vpl == 2 ? 2 : 1);
