@@ -21,6 +21,8 @@ _LIB_PATH = _HERE / "liboracle_rmsnorm.so"
 _lib = None
 
 R64, A32 = 0, 1
+SILU, SIGMOID = 0, 1          # gate activations
+FP32_WEIGHT, CAST_INPUT = 0, 1  # gated-norm rounding conventions
 
 
 def build(force: bool = True, extra_flags: tuple[str, ...] = ()) -> Path:
@@ -62,6 +64,14 @@ def _load():
         "oracle_rmsnorm_gated_fwd_f64": ([vp, vp, vp, i, d, i64, i64, vp], i),
         "oracle_rmsnorm_bwd_f64": ([vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
         "oracle_set_mutation": ([i], None),
+        "oracle_rmsnorm_gated_fwd_ex": ([i, i, i, vp, i64, vp, i64, vp, i, f, i64, i64, vp, i64,
+                                         vp], i),
+        "oracle_rmsnorm_gated_fwd_f32io": ([i, i, vp, vp, vp, i, f, i64, i64, vp], i),
+        "oracle_rmsnorm_gated_bwd": ([i, i, vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, vp,
+                                      i64, vp, i64], i),
+        "oracle_rmsnorm_gated_dgamma": ([i, i, vp, i64, vp, i64, vp, i64, vp, i64, i64, vp], i),
+        "oracle_rmsnorm_gated_fwd_ex_f64": ([i, vp, vp, vp, i, d, i64, i64, vp], i),
+        "oracle_rmsnorm_gated_bwd_f64": ([i, vp, vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -254,3 +264,76 @@ def mutation(m: int):
         yield
     finally:
         lib.oracle_set_mutation(0)
+
+
+# ---- gated-norm variants -------------------------------------------------------
+
+def gated_fwd_ex(x, z, gamma, zero_centered=False, eps=1e-6, activation=SILU,
+                 convention=FP32_WEIGHT, mode=R64):
+    """(out bf16, rstd) for either gate activation and rounding convention."""
+    x = _bf16_2d(x)
+    z = _bf16_2d(z)
+    T, D = x.shape
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    out = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_gated_fwd_ex(mode, activation, convention, _p(x), _ld(x),
+                                               _p(z), _ld(z), _p(gamma), int(zero_centered),
+                                               eps, T, D, _p(out), D, _p(rstd)),
+           "gated_fwd_ex")
+    return out, rstd
+
+
+def gated_fwd_f32io(x, z, gamma, zero_centered=False, eps=1e-6, activation=SILU,
+                    convention=FP32_WEIGHT):
+    """The gated forward on fp32 inputs and outputs."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    T, D = x.shape
+    out = np.empty((T, D), dtype=np.float32)
+    _check(_load().oracle_rmsnorm_gated_fwd_f32io(activation, convention, _p(x), _p(z),
+                                                  _p(gamma), int(zero_centered), eps, T, D,
+                                                  _p(out)),
+           "gated_fwd_f32io")
+    return out
+
+
+def gated_bwd(g, x, z, rstd, gamma, zero_centered=False, activation=SILU, mode=R64):
+    """(dx bf16, dz bf16, dgamma fp32) of the gated norm (fp32 convention)."""
+    g, x, z = _bf16_2d(g), _bf16_2d(x), _bf16_2d(z)
+    T, D = x.shape
+    rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    dx = np.empty((T, D), dtype=np.uint16)
+    dz = np.empty((T, D), dtype=np.uint16)
+    dg = np.empty(D, dtype=np.float32)
+    lib = _load()
+    _check(lib.oracle_rmsnorm_gated_bwd(mode, activation, _p(g), _ld(g), _p(x), _ld(x), _p(z),
+                                        _ld(z), _p(rstd), _p(gamma), int(zero_centered), T, D,
+                                        _p(dx), D, _p(dz), D), "gated_bwd")
+    _check(lib.oracle_rmsnorm_gated_dgamma(mode, activation, _p(g), _ld(g), _p(x), _ld(x), _p(z),
+                                           _ld(z), _p(rstd), T, D, _p(dg)), "gated_dgamma")
+    return dx, dz, dg
+
+
+def gated_fwd_ex_f64(x, z, gamma, zero_centered=False, eps=1e-6, activation=SILU):
+    x, z, gamma = _f64(x), _f64(z), _f64(gamma)
+    T, D = x.shape
+    out = np.empty((T, D))
+    _check(_load().oracle_rmsnorm_gated_fwd_ex_f64(activation, _p(x), _p(z), _p(gamma),
+                                                   int(zero_centered), eps, T, D, _p(out)),
+           "gated_fwd_ex_f64")
+    return out
+
+
+def gated_bwd_f64(g, x, z, gamma, zero_centered=False, eps=1e-6, activation=SILU):
+    """(dx, dz, dgamma) in double."""
+    g, x, z, gamma = _f64(g), _f64(x), _f64(z), _f64(gamma)
+    T, D = x.shape
+    dx, dz, dg = np.empty((T, D)), np.empty((T, D)), np.empty(D)
+    _check(_load().oracle_rmsnorm_gated_bwd_f64(activation, _p(g), _p(x), _p(z), _p(gamma),
+                                                int(zero_centered), eps, T, D, _p(dx), _p(dz),
+                                                _p(dg)),
+           "gated_bwd_f64")
+    return dx, dz, dg

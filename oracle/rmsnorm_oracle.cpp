@@ -85,6 +85,20 @@ bool bad_mode(int mode) { return mode != ORACLE_R64 && mode != ORACLE_A32; }
 
 double silu_d(double z) { return z / (1.0 + std::exp(-z)); }
 
+double sigmoid_d(double z) { return 1.0 / (1.0 + std::exp(-z)); }
+
+// The gate a(z) and its derivative, in double.
+double gate_d(int act, double z) { return act == ORACLE_GATE_SIGMOID ? sigmoid_d(z) : silu_d(z); }
+double gate_grad_d(int act, double z) {
+  const double s = sigmoid_d(z);
+  return act == ORACLE_GATE_SIGMOID ? s * (1.0 - s) : s * (1.0 + z * (1.0 - s));
+}
+bool bad_act(int act) { return act != ORACLE_GATE_SILU && act != ORACLE_GATE_SIGMOID; }
+
+// bf16 rounding of an fp32 value, returned as fp32 (the cast to the input
+// dtype in the cast convention).
+float round_bf16(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+
 }  // namespace
 
 extern "C" {
@@ -212,6 +226,133 @@ int oracle_rmsnorm_dgamma(int mode, const uint16_t* g, int64_t ld_g, const uint1
   return 0;
 }
 
+// ---- gated-norm variants -----------------------------------------------------
+
+int oracle_rmsnorm_gated_fwd_ex(int mode, int activation, int convention, const uint16_t* x,
+                                int64_t ld_x, const uint16_t* z, int64_t ld_z, const float* gamma,
+                                int zero_centered, float eps, int64_t T, int64_t D, uint16_t* out,
+                                int64_t ld_out, float* rstd) {
+  if (bad_mode(mode) || bad_act(activation) ||
+      (convention != ORACLE_GATED_FP32 && convention != ORACLE_GATED_CAST) || T < 0 || D <= 0 ||
+      !gamma || bad_2d(x, ld_x, D) || bad_2d(z, ld_z, D) || bad_2d(out, ld_out, D))
+    return -1;
+  const int zc_fwd = (g_mutation == 1) ? 0 : zero_centered;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + t * ld_x;
+    const float r = row_rstd(mode, xr, D, eps);
+    if (rstd) rstd[t] = r;
+    for (int64_t j = 0; j < D; ++j) {
+      const float w = weight_eff(gamma, zc_fwd, j);
+      const float a = static_cast<float>(gate_d(activation, bf16_to_f32(z[t * ld_z + j])));
+      float n = bf16_to_f32(xr[j]) * r;
+      if (convention == ORACLE_GATED_CAST) n = round_bf16(n);
+      float nw = n * w;
+      if (convention == ORACLE_GATED_CAST) nw = round_bf16(nw);
+      const float o = nw * a;
+      out[t * ld_out + j] = f32_to_bf16(o);
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_gated_fwd_f32io(int activation, int convention, const float* x, const float* z,
+                                   const float* gamma, int zero_centered, float eps, int64_t T,
+                                   int64_t D, float* out) {
+  if (bad_act(activation) || (convention != ORACLE_GATED_FP32 && convention != ORACLE_GATED_CAST) ||
+      !x || !z || !gamma || !out || T < 0 || D <= 0)
+    return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const float* xr = x + t * D;
+    double ss = 0.0;
+    for (int64_t j = 0; j < D; ++j) {
+      const float sq = xr[j] * xr[j];
+      ss += static_cast<double>(sq);
+    }
+    const float mean = static_cast<float>(ss) / static_cast<float>(D);
+    const float r = rsqrt_ref(mean + eps);
+    for (int64_t j = 0; j < D; ++j) {
+      const float w = weight_eff(gamma, zero_centered, j);
+      const float a = static_cast<float>(gate_d(activation, static_cast<double>(z[t * D + j])));
+      // the casts to the input dtype are the identity for fp32 inputs
+      const float n = xr[j] * r;
+      const float nw = n * w;
+      out[t * D + j] = nw * a;
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_gated_bwd(int mode, int activation, const uint16_t* g, int64_t ld_g,
+                             const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
+                             const float* rstd, const float* gamma, int zero_centered, int64_t T,
+                             int64_t D, uint16_t* dx, int64_t ld_dx, uint16_t* dz, int64_t ld_dz) {
+  if (bad_mode(mode) || bad_act(activation) || T < 0 || D <= 0 || !gamma || !rstd ||
+      bad_2d(g, ld_g, D) || bad_2d(x, ld_x, D) || bad_2d(z, ld_z, D) || (!dx && !dz) ||
+      (dx && ld_dx < D) || (dz && ld_dz < D))
+    return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* gr = g + t * ld_g;
+    const uint16_t* xr = x + t * ld_x;
+    const uint16_t* zr = z + t * ld_z;
+    const float r = rstd[t];
+    Sum s(mode);
+    for (int64_t i = 0; i < D; ++i) {
+      const float a = static_cast<float>(gate_d(activation, bf16_to_f32(zr[i])));
+      const float gn = bf16_to_f32(gr[i]) * a;
+      const float gw = gn * weight_eff(gamma, zero_centered, i);
+      const float term = gw * bf16_to_f32(xr[i]);
+      s.add(term);
+    }
+    const float r2 = r * r;
+    const float r3 = r2 * r;
+    const float r3s = r3 * s.value();
+    const float c = r3s / static_cast<float>(D);
+    for (int64_t k = 0; k < D; ++k) {
+      const float w = weight_eff(gamma, zero_centered, k);
+      const float xf = bf16_to_f32(xr[k]);
+      const float gf = bf16_to_f32(gr[k]);
+      const double zd = bf16_to_f32(zr[k]);
+      const float a = static_cast<float>(gate_d(activation, zd));
+      const float da = static_cast<float>(gate_grad_d(activation, zd));
+      if (dz) {
+        const float n = xf * r;
+        const float nw = n * w;
+        const float gnw = gf * nw;
+        dz[t * ld_dz + k] = f32_to_bf16(gnw * da);
+      }
+      if (dx) {
+        const float gn = gf * a;
+        const float gw = gn * w;
+        const float t1 = gw * r;
+        const float t2 = xf * c;
+        dx[t * ld_dx + k] = f32_to_bf16(t1 - t2);
+      }
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_gated_dgamma(int mode, int activation, const uint16_t* g, int64_t ld_g,
+                                const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
+                                const float* rstd, int64_t T, int64_t ncols, float* dgamma) {
+  if (bad_mode(mode) || bad_act(activation) || T < 0 || ncols <= 0 || !dgamma ||
+      bad_2d(g, ld_g, ncols) || bad_2d(x, ld_x, ncols) || bad_2d(z, ld_z, ncols) ||
+      (T > 0 && !rstd))
+    return -1;
+  for (int64_t j = 0; j < ncols; ++j) {
+    Sum acc(mode);
+    for (int64_t t = 0; t < T; ++t) {
+      const float a = static_cast<float>(gate_d(activation, bf16_to_f32(z[t * ld_z + j])));
+      const float gn = bf16_to_f32(g[t * ld_g + j]) * a;
+      const float gx = gn * bf16_to_f32(x[t * ld_x + j]);
+      const float term = gx * rstd[t];
+      acc.add(term);
+    }
+    dgamma[j] = acc.value();
+  }
+  return 0;
+}
+
 // ---- exact double forms ----------------------------------------------------
 
 static double weight_eff_d(const double* gamma, int zc, int64_t j) {
@@ -249,6 +390,44 @@ int oracle_rmsnorm_gated_fwd_f64(const double* x, const double* z, const double*
           x[t * D + j] * r * weight_eff_d(gamma, zc_fwd, j) * silu_d(z[t * D + j]);
   }
   return 0;
+}
+
+int oracle_rmsnorm_gated_fwd_ex_f64(int activation, const double* x, const double* z,
+                                    const double* gamma, int zero_centered, double eps, int64_t T,
+                                    int64_t D, double* out) {
+  if (bad_act(activation) || !x || !z || !gamma || !out || T < 0 || D <= 0) return -1;
+  const int zc_fwd = (g_mutation == 1) ? 0 : zero_centered;
+  for (int64_t t = 0; t < T; ++t) {
+    const double r = row_rstd_d(x + t * D, D, eps);
+    for (int64_t j = 0; j < D; ++j)
+      out[t * D + j] =
+          x[t * D + j] * r * weight_eff_d(gamma, zc_fwd, j) * gate_d(activation, z[t * D + j]);
+  }
+  return 0;
+}
+
+// L = sum g * out with out = (x r w) a(z): dz = g x r w a'(z); the norm sees
+// the upstream gradient gn = g a(z), and dx, dgamma follow from the plain
+// backward with gn in place of g.
+int oracle_rmsnorm_gated_bwd_f64(int activation, const double* g, const double* x, const double* z,
+                                 const double* gamma, int zero_centered, double eps, int64_t T,
+                                 int64_t D, double* dx, double* dz, double* dgamma) {
+  if (bad_act(activation) || !g || !x || !z || !gamma || T < 0 || D <= 0) return -1;
+  double* gn = new double[static_cast<size_t>(T * D)];
+  for (int64_t i = 0; i < T * D; ++i) gn[i] = g[i] * gate_d(activation, z[i]);
+  if (dz) {
+    for (int64_t t = 0; t < T; ++t) {
+      const double r = row_rstd_d(x + t * D, D, eps);
+      for (int64_t k = 0; k < D; ++k)
+        dz[t * D + k] = g[t * D + k] * x[t * D + k] * r * weight_eff_d(gamma, zero_centered, k) *
+                        gate_grad_d(activation, z[t * D + k]);
+    }
+  }
+  int rc = 0;
+  if (dx || dgamma)
+    rc = oracle_rmsnorm_bwd_f64(gn, x, gamma, zero_centered, eps, T, D, nullptr, dx, dgamma);
+  delete[] gn;
+  return rc;
 }
 
 int oracle_rmsnorm_bwd_f64(const double* g, const double* x, const double* gamma,

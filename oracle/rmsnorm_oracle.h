@@ -118,6 +118,69 @@ int oracle_rmsnorm_bwd_f64(const double* g, const double* x,
                            int64_t T, int64_t D, const double* gres,
                            double* dx, double* dgamma);
 
+/* ---- Gated-norm variants -------------------------------------------------
+ * activation: ORACLE_GATE_SILU a(z) = z*sigmoid(z), ORACLE_GATE_SIGMOID
+ * a(z) = sigmoid(z) (the two gate activations [C1] names).
+ * convention: ORACLE_GATED_FP32 (the weight multiply in fp32, one rounding
+ * at the end: out = bf16(fp32(fp32(x*r)*w) * a(z))) or ORACLE_GATED_CAST
+ * (the other upstream's convention as read here: the normalised value and
+ * the weighted value are each cast to the input dtype before the next
+ * multiply, out = bf16(fp32(bf16(fp32(bf16(x*r)*w)) * a(z))). With fp32
+ * inputs those casts are no-ops and the two conventions agree bitwise.)
+ * a(z) is evaluated in double and rounded to fp32.
+ */
+enum { ORACLE_GATE_SILU = 0, ORACLE_GATE_SIGMOID = 1 };
+enum { ORACLE_GATED_FP32 = 0, ORACLE_GATED_CAST = 1 };
+
+int oracle_rmsnorm_gated_fwd_ex(int mode, int activation, int convention,
+                                const uint16_t* x, int64_t ld_x,
+                                const uint16_t* z, int64_t ld_z,
+                                const float* gamma, int zero_centered,
+                                float eps, int64_t T, int64_t D,
+                                uint16_t* out, int64_t ld_out, float* rstd);
+
+/* The same forward on fp32 inputs and outputs (contiguous [T, D]): every
+ * cast to the input dtype is then the identity. */
+int oracle_rmsnorm_gated_fwd_f32io(int activation, int convention,
+                                   const float* x, const float* z,
+                                   const float* gamma, int zero_centered,
+                                   float eps, int64_t T, int64_t D, float* out);
+
+/* Gated backward (the fp32 convention), from the saved rstd. With
+ * n = fp32(x*r), nw = fp32(n*w), a = fp32(a(z)), a' = fp32(a'(z)) (double,
+ * rounded), and g the gradient of out:
+ *   dz = bf16(fp32(fp32(g*nw) * a'))
+ *   gn = fp32(g*a)                      (gradient reaching nw)
+ *   dx = the plain input gradient with gn in place of g:
+ *        gw = fp32(gn*w); s = sum gw*x; c = ((r*r)*r)*s/D;
+ *        dx = bf16(fp32(gw*r) - fp32(x*c))
+ * dx or dz may be NULL. */
+int oracle_rmsnorm_gated_bwd(int mode, int activation, const uint16_t* g,
+                             int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                             const uint16_t* z, int64_t ld_z, const float* rstd,
+                             const float* gamma, int zero_centered, int64_t T,
+                             int64_t D, uint16_t* dx, int64_t ld_dx,
+                             uint16_t* dz, int64_t ld_dz);
+
+/* dgamma[j] = sum over t ascending of fp32(fp32(gn[t][j]*x[t][j]) * r[t]),
+ * gn = fp32(g*a(z)), over `ncols` columns. */
+int oracle_rmsnorm_gated_dgamma(int mode, int activation, const uint16_t* g,
+                                int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                                const uint16_t* z, int64_t ld_z,
+                                const float* rstd, int64_t T, int64_t ncols,
+                                float* dgamma);
+
+/* Exact forms of the gated forward and backward (contiguous [T, D]). */
+int oracle_rmsnorm_gated_fwd_ex_f64(int activation, const double* x,
+                                    const double* z, const double* gamma,
+                                    int zero_centered, double eps, int64_t T,
+                                    int64_t D, double* out);
+int oracle_rmsnorm_gated_bwd_f64(int activation, const double* g,
+                                 const double* x, const double* z,
+                                 const double* gamma, int zero_centered,
+                                 double eps, int64_t T, int64_t D, double* dx,
+                                 double* dz, double* dgamma);
+
 /* Test-only defect planting, so the tests can show that their checks catch
  * the two defects [MEG] fixes: 0 = none; 1 = the forward ignores the
  * zero-centred offset (the backward still honours it); 2 = the second term
