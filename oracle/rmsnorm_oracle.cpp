@@ -87,11 +87,24 @@ double silu_d(double z) { return z / (1.0 + std::exp(-z)); }
 
 double sigmoid_d(double z) { return 1.0 / (1.0 + std::exp(-z)); }
 
-// The gate a(z) and its derivative, in double.
+// sigmoid(z) and 1 - sigmoid(z) in double, both from e = exp(-|z|):
+// 1/(1+e) and e/(1+e), assigned by the sign of z. Neither comes from a
+// subtraction 1 - s, which would lose the relative precision of the small
+// one (for z = 30, 1 - s is about 1e-13).
+void sigmoid_pair_d(double z, double& s, double& sc) {
+  const double e = std::exp(-std::fabs(z));
+  const double inv = 1.0 / (1.0 + e);
+  s = z >= 0.0 ? inv : e * inv;
+  sc = z >= 0.0 ? e * inv : inv;
+}
+
+// The gate a(z) and its derivative, in double: silu' = s (1 + z (1 - s)),
+// sigmoid' = s (1 - s).
 double gate_d(int act, double z) { return act == ORACLE_GATE_SIGMOID ? sigmoid_d(z) : silu_d(z); }
 double gate_grad_d(int act, double z) {
-  const double s = sigmoid_d(z);
-  return act == ORACLE_GATE_SIGMOID ? s * (1.0 - s) : s * (1.0 + z * (1.0 - s));
+  double s, sc;
+  sigmoid_pair_d(z, s, sc);
+  return act == ORACLE_GATE_SIGMOID ? s * sc : s * (1.0 + z * sc);
 }
 bool bad_act(int act) { return act != ORACLE_GATE_SILU && act != ORACLE_GATE_SIGMOID; }
 

@@ -113,6 +113,11 @@ def test_gate_derivatives_match_finite_differences(act):
     _, dz, _ = oracle.gated_bwd_f64(np.ones((1, D)), bf16_to_f64(x), zb, np.ones(D), eps=0.0,
                                     activation=act)
     np.testing.assert_allclose(dz[0], fd, rtol=1e-6, atol=1e-9)
+    # relative precision in the tails: with 1 - sigmoid(z) = sigmoid(-z),
+    # sigmoid' = expit(z) expit(-z) and silu' = expit(z) (1 + z expit(-z))
+    s, sc = scipy.special.expit(z), scipy.special.expit(-z)
+    exact = s * sc if act == oracle.SIGMOID else s * (1 + z * sc)
+    np.testing.assert_allclose(dz[0], exact, rtol=1e-13, atol=0)
 
 
 def _gated_fd(g, x, z, gamma, zc, act, eps, h=1e-5):
