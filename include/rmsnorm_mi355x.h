@@ -22,15 +22,18 @@
  *    sits in; the reduction layout may depend on the row length only; an
  *    unsupported input is rejected, never sent silently down another path.
  *
- * Precision contract. x, y, dx, g, z and residual tensors are bf16, passed
- * as raw uint16_t bits. gamma, rstd and dgamma are fp32. Per row:
- *   ss   = sum_j x_j^2 (fp32, fixed reduction tree chosen by D alone)
- *   r    = rsqrt(ss / D + eps)                      (fp32; stored in rstd)
+ * Precision contract. x, y, dx, g, z, dz and residual tensors are bf16,
+ * passed as raw uint16_t bits. gamma, rstd and dgamma are fp32. Per row:
+ *   ss   = sum_j x_j^2: fp32 squares added in fp64 along a fixed reduction
+ *          tree chosen by D alone, rounded to fp32 once
+ *   r    = 1/sqrt(ss / D + eps): fp32 division and addition, the reciprocal
+ *          square root in fp64 and rounded to fp32 once; stored in rstd
  *   w_j  = gamma_j, or gamma_j + 1.0f when zero_centered_gamma != 0
  *   y_j  = bf16_rne((x_j * r) * w_j)                (two fp32 products)
- *   gated: out_j = bf16_rne(((x_j * r) * w_j) * silu(z_j)), silu(z) = z*sigmoid(z)
- *   bwd: gw_j = g_j * w_j; s = sum_j gw_j * x_j (same tree shape as ss);
- *        c = ((r * r) * r) * s / D; dx_j = bf16_rne(gw_j * r - x_j * c [+ gres_j])
+ *   gated: out_j = bf16_rne(((x_j * r) * w_j) * a(z_j)), a = silu or sigmoid
+ *   bwd: gw_j = g_j * w_j; s = sum_j gw_j * x_j (fp32 products, fp64 sum,
+ *        same tree shape as ss); c = ((r * r) * r) * s / D;
+ *        dx_j = bf16_rne(gw_j * r - x_j * c [+ gres_j])
  *   dgamma_j = sum over rows of (g_tj * x_tj) * r_t, summed per fixed chunk
  *        of rows, then the chunk partials in a fixed order (deterministic
  *        for a given T, no atomics).
@@ -70,7 +73,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 1
+#define RMSN_ABI_VERSION 2
 #define RMSN_MAX_D 8192
 #define RMSN_MAX_LD (1 << 24)
 
@@ -83,8 +86,24 @@ typedef enum rmsn_status {
   RMSN_ERR_EPS = 5,            /* eps negative or not finite */
   RMSN_ERR_ALIASING = 6,       /* an output overlaps an input or another output */
   RMSN_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than required */
-  RMSN_ERR_HIP = 8             /* the HIP runtime refused a launch */
+  RMSN_ERR_HIP = 8,            /* the HIP runtime refused a launch */
+  RMSN_ERR_MODE = 9            /* unknown gate activation or rounding convention */
 } rmsn_status;
+
+/* Gate activations of the gated norm (RL-Kernel PR "C1: zero-centred RMSNorm
+ * references and CUDA kernel" names both; silu is its default). */
+#define RMSN_GATE_SILU 0     /* a(z) = z * sigmoid(z) */
+#define RMSN_GATE_SIGMOID 1  /* a(z) = sigmoid(z) */
+
+/* Rounding conventions of the gated forward (the same page: its two upstream
+ * implementations round at different points; in bf16 their outputs differ by
+ * more than 1e-3, with fp32 inputs they agree bitwise).
+ * FP32:  out = bf16(((x * r) * w) * a(z)), every product in fp32.
+ * CAST:  n = bf16(x * r), nw = bf16(n * w), out = bf16(nw * a(z)): the
+ *        normalised and the weighted value are cast to the input dtype
+ *        before the next multiply. */
+#define RMSN_GATED_ROUND_FP32 0
+#define RMSN_GATED_ROUND_CAST 1
 
 /* RMSN_ABI_VERSION of the loaded library. */
 int rmsnorm_abi_version(void);
@@ -123,7 +142,21 @@ rmsn_status rmsnorm_gated_fwd(const uint16_t* x, int64_t ld_x,
                               float eps, int64_t T, int64_t D, uint16_t* out,
                               int64_t ld_out, float* rstd, void* stream);
 
-/* Bytes of workspace rmsnorm_bwd / rmsnorm_bwd_rows need for dgamma
+/*
+ * Gated forward with a choice of activation (RMSN_GATE_*) and rounding
+ * convention (RMSN_GATED_ROUND_*); rmsnorm_gated_fwd is the SILU / FP32
+ * case. a(z) is evaluated in fp32 to within a few ulp of the exact value
+ * (the result is within 1 bf16 ulp of the correctly rounded one). rstd may
+ * be NULL. An unknown activation or rounding value returns RMSN_ERR_MODE.
+ */
+rmsn_status rmsnorm_gated_fwd_ex(const uint16_t* x, int64_t ld_x,
+                                 const uint16_t* z, int64_t ld_z,
+                                 const float* gamma, int zero_centered_gamma,
+                                 float eps, int64_t T, int64_t D,
+                                 int activation, int rounding, uint16_t* out,
+                                 int64_t ld_out, float* rstd, void* stream);
+
+/* Bytes of workspace the backward entry points need for dgamma
  * (0 when T == 0). Depends on T and D only. */
 size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D);
 
@@ -139,7 +172,8 @@ int64_t rmsnorm_bwd_chunk_rows(int64_t T, int64_t D);
  * review comment). g_residual (may be NULL) is the gradient reaching the
  * residual copy; it is added in fp32 before dx's one rounding. dx may be
  * NULL (weight gradient only) and dgamma may be NULL (input gradient only),
- * not both. When dgamma is non-NULL the caller passes a workspace of at
+ * not both; gamma is required either way. When dgamma is non-NULL the
+ * caller passes a workspace of at
  * least rmsnorm_bwd_workspace_bytes(T, D) bytes, 16-byte aligned; its
  * contents on return are the per-chunk partials. Two kernels on `stream`.
  */
@@ -169,6 +203,30 @@ rmsn_status rmsnorm_bwd_rows(const uint16_t* g, int64_t ld_g,
 rmsn_status rmsnorm_bwd_finish(const void* workspace, size_t workspace_bytes,
                                int64_t T, int64_t D, float* dgamma,
                                void* stream);
+
+/*
+ * Backward of the gated forward in the FP32 rounding convention (the pages
+ * give the forward only; this is its chain rule). With n = x * r,
+ * nw = n * w and a, a' the gate and its derivative at z (fp32):
+ *   dz = bf16((g * nw) * a'(z))
+ *   gn = g * a(z), the gradient reaching nw; then dx and dgamma are those of
+ *   rmsnorm_bwd with gn in place of g:
+ *   dx = bf16(gw * r - x * c), gw = gn * w, c = ((r * r) * r) * sum(gw * x) / D
+ *   dgamma_j = sum over rows of (gn_tj * x_tj) * r_t (same chunked order).
+ * rstd is the forward's saved inverse RMS. dx, dz and dgamma may each be
+ * NULL, not all three; gamma is required. The workspace rule is
+ * rmsnorm_bwd's (rmsnorm_bwd_workspace_bytes). An unknown activation
+ * returns RMSN_ERR_MODE. Two kernels on `stream`.
+ */
+rmsn_status rmsnorm_gated_bwd(const uint16_t* g, int64_t ld_g,
+                              const uint16_t* x, int64_t ld_x,
+                              const uint16_t* z, int64_t ld_z,
+                              const float* rstd, const float* gamma,
+                              int zero_centered_gamma, int64_t T, int64_t D,
+                              int activation, uint16_t* dx, int64_t ld_dx,
+                              uint16_t* dz, int64_t ld_dz, float* dgamma,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 #ifdef __cplusplus
 }

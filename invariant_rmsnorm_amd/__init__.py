@@ -28,11 +28,18 @@ RMSN_ERR_EPS = 5
 RMSN_ERR_ALIASING = 6
 RMSN_ERR_WORKSPACE = 7
 RMSN_ERR_HIP = 8
+RMSN_ERR_MODE = 9
+
+RMSN_GATE_SILU = 0
+RMSN_GATE_SIGMOID = 1
+RMSN_GATED_ROUND_FP32 = 0
+RMSN_GATED_ROUND_CAST = 1
 
 EXPORTED = (
     "rmsnorm_abi_version", "rmsnorm_status_string", "rmsnorm_fwd", "rmsnorm_residual_fwd",
-    "rmsnorm_gated_fwd", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd_chunk_rows",
-    "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
+    "rmsnorm_gated_fwd", "rmsnorm_gated_fwd_ex", "rmsnorm_bwd_workspace_bytes",
+    "rmsnorm_bwd_chunk_rows", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
+    "rmsnorm_gated_bwd",
 )
 
 
@@ -58,11 +65,14 @@ def load():
         "rmsnorm_fwd": ([vp, i64, vp, i, f, i64, i64, vp, i64, vp, vp], i),
         "rmsnorm_residual_fwd": ([vp, i64, vp, i, f, i64, i64, vp, i64, vp, i64, vp, vp], i),
         "rmsnorm_gated_fwd": ([vp, i64, vp, i64, vp, i, f, i64, i64, vp, i64, vp, vp], i),
+        "rmsnorm_gated_fwd_ex": ([vp, i64, vp, i64, vp, i, f, i64, i64, i, i, vp, i64, vp, vp], i),
         "rmsnorm_bwd_workspace_bytes": ([i64, i64], sz),
         "rmsnorm_bwd_chunk_rows": ([i64, i64], i64),
         "rmsnorm_bwd": ([vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, vp, sz, vp], i),
         "rmsnorm_bwd_rows": ([vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, sz, vp], i),
         "rmsnorm_bwd_finish": ([vp, sz, i64, i64, vp, vp], i),
+        "rmsnorm_gated_bwd": ([vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, i, vp, i64, vp, i64,
+                               vp, vp, sz, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -166,6 +176,23 @@ def rmsnorm_gated_fwd(x, z, gamma, zero_centered_gamma=False, eps=1e-6, *, out=N
     return out, rstd
 
 
+def rmsnorm_gated_fwd_ex(x, z, gamma, zero_centered_gamma=False, eps=1e-6, *,
+                         activation=RMSN_GATE_SILU, rounding=RMSN_GATED_ROUND_FP32, out=None,
+                         rstd=None, want_rstd=False, stream=None):
+    """(out, rstd or None): the gated forward with a choice of activation
+    (RMSN_GATE_*) and rounding convention (RMSN_GATED_ROUND_*)."""
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(z, torch.bfloat16, "z")
+    T, D = x.shape
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device) if out is None else out
+    if rstd is None and want_rstd:
+        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check("rmsnorm_gated_fwd_ex", load().rmsnorm_gated_fwd_ex(
+        _ptr(x), _ld(x), _ptr(z), _ld(z), _ptr(gamma), int(zero_centered_gamma), eps, T, D,
+        int(activation), int(rounding), _ptr(out), _ld(out), _ptr(rstd), _stream(x, stream)))
+    return out, rstd
+
+
 def workspace_for(T, D, device):
     n = rmsnorm_bwd_workspace_bytes(T, D)
     return torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=device), n
@@ -212,3 +239,30 @@ def rmsnorm_bwd_finish(workspace, T, D, dgamma, stream=None):
     _check("rmsnorm_bwd_finish", load().rmsnorm_bwd_finish(
         _ptr(workspace), nbytes, T, D, _ptr(dgamma), _stream(dgamma, stream)))
     return dgamma
+
+
+def rmsnorm_gated_bwd(g, x, z, rstd, gamma, zero_centered_gamma=False, *,
+                      activation=RMSN_GATE_SILU, dx=None, dz=None, dgamma=None, want_dx=True,
+                      want_dz=True, want_dgamma=True, workspace=None, stream=None):
+    """(dx or None, dz or None, dgamma or None): the backward of the gated
+    forward (fp32 rounding convention) from the saved rstd."""
+    _dtype(g, torch.bfloat16, "g")
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(z, torch.bfloat16, "z")
+    T, D = x.shape
+    if dx is None and want_dx:
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    if dz is None and want_dz:
+        dz = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty(D, dtype=torch.float32, device=x.device)
+    ws, nbytes = (None, 0)
+    if dgamma is not None:
+        if workspace is None:
+            workspace, _ = workspace_for(T, D, x.device)
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    _check("rmsnorm_gated_bwd", load().rmsnorm_gated_bwd(
+        _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(z), _ld(z), _ptr(rstd), _ptr(gamma),
+        int(zero_centered_gamma), T, D, int(activation), _ptr(dx), _ld(dx), _ptr(dz), _ld(dz),
+        _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
+    return dx, dz, dgamma

@@ -86,10 +86,15 @@ rmsn_status check_f32(const float* p, uintptr_t align, bool required) {
 
 rmsn_status hip_status(int rc) { return rc == 0 ? RMSN_OK : RMSN_ERR_HIP; }
 
+bool bad_activation(int act) { return act != RMSN_GATE_SILU && act != RMSN_GATE_SIGMOID; }
+
 rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
-                       bool gated, const float* gamma, int zc, float eps, int64_t T, int64_t D,
-                       uint16_t* y, int64_t ld_y, uint16_t* res, int64_t ld_res, bool residual,
-                       float* rstd, void* stream) {
+                       bool gated, int act, int rounding, const float* gamma, int zc, float eps,
+                       int64_t T, int64_t D, uint16_t* y, int64_t ld_y, uint16_t* res,
+                       int64_t ld_res, bool residual, float* rstd, void* stream) {
+  if (gated && (bad_activation(act) ||
+                (rounding != RMSN_GATED_ROUND_FP32 && rounding != RMSN_GATED_ROUND_CAST)))
+    return RMSN_ERR_MODE;
   if (T < 0) return RMSN_ERR_SHAPE;
   RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
@@ -106,8 +111,9 @@ rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64
                        vec_range(gamma, D, 4)};
   if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
 
-  rmsn::FwdArgs a{x, ld_x, gated ? z : nullptr, ld_z, gamma, zc != 0, eps, T, static_cast<int>(D),
-                  y, ld_y, residual ? res : nullptr, ld_res, rstd};
+  rmsn::FwdArgs a{x, ld_x, gated ? z : nullptr, ld_z, act, rounding == RMSN_GATED_ROUND_CAST,
+                  gamma, zc != 0, eps, T, static_cast<int>(D), y, ld_y,
+                  residual ? res : nullptr, ld_res, rstd};
   return hip_status(rmsn::launch_fwd(a, stream));
 }
 
@@ -117,21 +123,36 @@ size_t workspace_bytes(int64_t T, int64_t D) {
   return static_cast<size_t>(p.chunks) * static_cast<size_t>(D) * sizeof(float);
 }
 
-// Checks shared by rmsnorm_bwd and rmsnorm_bwd_rows; `dgamma` is only
-// checked for aliasing here (rmsnorm_bwd_rows passes nullptr).
+// The gate operands of the gated backward (absent for the other forms).
+struct GateIO {
+  const uint16_t* z = nullptr;
+  int64_t ld_z = 0;
+  uint16_t* dz = nullptr;
+  int64_t ld_dz = 0;
+};
+
+// Checks shared by the backward entry points; `dgamma` is only checked for
+// aliasing here (rmsnorm_bwd_rows passes nullptr).
 rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
                       const float* rstd, const float* gamma, int64_t T, int64_t D,
                       const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
-                      bool want_part, const float* dgamma, void* ws, size_t ws_bytes) {
+                      bool want_part, const float* dgamma, void* ws, size_t ws_bytes,
+                      bool gated = false, const GateIO& gate = GateIO{}) {
   if (T < 0) return RMSN_ERR_SHAPE;
   RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(g, ld_g, T, D, true));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
   RMSN_TRY(check_mat(gres, ld_gres, T, D, false));
   RMSN_TRY(check_mat(dx, ld_dx, T, D, false));
+  if (gated) {
+    RMSN_TRY(check_mat(gate.z, gate.ld_z, T, D, true));
+    RMSN_TRY(check_mat(gate.dz, gate.ld_dz, T, D, false));
+  }
   if (T == 0) return RMSN_OK;
   RMSN_TRY(check_f32(rstd, 4, true));
-  RMSN_TRY(check_f32(gamma, 16, dx != nullptr));
+  // The rows kernel loads the weights whatever it writes, so gamma is
+  // required even for a weight-gradient-only call.
+  RMSN_TRY(check_f32(gamma, 16, true));
   if (want_part) {
     if (ws == nullptr || ws_bytes < workspace_bytes(T, D)) return RMSN_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return RMSN_ERR_MISALIGNED;
@@ -139,10 +160,10 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
   const Range outs[] = {mat_range(dx, T, ld_dx, D, 2),
                         want_part ? vec_range(ws, static_cast<int64_t>(workspace_bytes(T, D)), 1)
                                   : Range{},
-                        vec_range(dgamma, D, 4)};
+                        vec_range(dgamma, D, 4), mat_range(gate.dz, T, gate.ld_dz, D, 2)};
   const Range ins[] = {mat_range(g, T, ld_g, D, 2), mat_range(x, T, ld_x, D, 2),
-                       vec_range(rstd, T, 4), vec_range(dx ? gamma : nullptr, D, 4),
-                       mat_range(gres, T, ld_gres, D, 2)};
+                       vec_range(rstd, T, 4), vec_range(gamma, D, 4),
+                       mat_range(gres, T, ld_gres, D, 2), mat_range(gate.z, T, gate.ld_z, D, 2)};
   if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
   return RMSN_OK;
 }
@@ -150,11 +171,18 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
 rmsn::BwdArgs bwd_args(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
                        const float* rstd, const float* gamma, int zc, int64_t T, int64_t D,
                        const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
-                       void* ws) {
+                       void* ws, const GateIO& gate = GateIO{}, int act = 0) {
   const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
   return rmsn::BwdArgs{g, ld_g, x, ld_x, rstd, gamma, zc != 0, T, static_cast<int>(D),
                        dx ? gres : nullptr, ld_gres, dx, ld_dx, static_cast<float*>(ws),
-                       p.chunk_rows, p.chunks};
+                       p.chunk_rows, p.chunks, gate.z, gate.ld_z, act, gate.dz, gate.ld_dz};
+}
+
+// dgamma from the workspace partials (zeros when T == 0).
+rmsn_status finish_dgamma(void* workspace, int64_t T, int64_t D, float* dgamma, void* stream) {
+  const int64_t chunks = T > 0 ? rmsn::bwd_plan(T, D).chunks : 0;
+  return hip_status(rmsn::launch_bwd_finish(static_cast<const float*>(workspace), chunks,
+                                            static_cast<int>(D), dgamma, stream));
 }
 
 }  // namespace
@@ -174,6 +202,7 @@ const char* rmsnorm_status_string(int status) {
     case RMSN_ERR_ALIASING: return "RMSN_ERR_ALIASING: an output overlaps an input or another output";
     case RMSN_ERR_WORKSPACE: return "RMSN_ERR_WORKSPACE: workspace missing or too small";
     case RMSN_ERR_HIP: return "RMSN_ERR_HIP: the HIP runtime refused a kernel launch";
+    case RMSN_ERR_MODE: return "RMSN_ERR_MODE: unknown gate activation or rounding convention";
     default: return "unknown rmsn_status";
   }
 }
@@ -181,23 +210,31 @@ const char* rmsnorm_status_string(int status) {
 rmsn_status rmsnorm_fwd(const uint16_t* x, int64_t ld_x, const float* gamma, int zero_centered_gamma,
                         float eps, int64_t T, int64_t D, uint16_t* y, int64_t ld_y, float* rstd,
                         void* stream) {
-  return fwd_common(x, ld_x, nullptr, 0, false, gamma, zero_centered_gamma, eps, T, D, y, ld_y,
-                    nullptr, 0, false, rstd, stream);
+  return fwd_common(x, ld_x, nullptr, 0, false, 0, 0, gamma, zero_centered_gamma, eps, T, D, y,
+                    ld_y, nullptr, 0, false, rstd, stream);
 }
 
 rmsn_status rmsnorm_residual_fwd(const uint16_t* x, int64_t ld_x, const float* gamma,
                                  int zero_centered_gamma, float eps, int64_t T, int64_t D,
                                  uint16_t* y, int64_t ld_y, uint16_t* residual_out, int64_t ld_res,
                                  float* rstd, void* stream) {
-  return fwd_common(x, ld_x, nullptr, 0, false, gamma, zero_centered_gamma, eps, T, D, y, ld_y,
-                    residual_out, ld_res, true, rstd, stream);
+  return fwd_common(x, ld_x, nullptr, 0, false, 0, 0, gamma, zero_centered_gamma, eps, T, D, y,
+                    ld_y, residual_out, ld_res, true, rstd, stream);
 }
 
 rmsn_status rmsnorm_gated_fwd(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
                               const float* gamma, int zero_centered_gamma, float eps, int64_t T,
                               int64_t D, uint16_t* out, int64_t ld_out, float* rstd, void* stream) {
-  return fwd_common(x, ld_x, z, ld_z, true, gamma, zero_centered_gamma, eps, T, D, out, ld_out,
-                    nullptr, 0, false, rstd, stream);
+  return fwd_common(x, ld_x, z, ld_z, true, RMSN_GATE_SILU, RMSN_GATED_ROUND_FP32, gamma,
+                    zero_centered_gamma, eps, T, D, out, ld_out, nullptr, 0, false, rstd, stream);
+}
+
+rmsn_status rmsnorm_gated_fwd_ex(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
+                                 const float* gamma, int zero_centered_gamma, float eps, int64_t T,
+                                 int64_t D, int activation, int rounding, uint16_t* out,
+                                 int64_t ld_out, float* rstd, void* stream) {
+  return fwd_common(x, ld_x, z, ld_z, true, activation, rounding, gamma, zero_centered_gamma, eps,
+                    T, D, out, ld_out, nullptr, 0, false, rstd, stream);
 }
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D) { return workspace_bytes(T, D); }
@@ -234,9 +271,7 @@ rmsn_status rmsnorm_bwd_finish(const void* workspace, size_t workspace_bytes_, i
     const Range ins[] = {vec_range(workspace, static_cast<int64_t>(need), 1)};
     if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
   }
-  const int64_t chunks = T > 0 ? rmsn::bwd_plan(T, D).chunks : 0;
-  return hip_status(rmsn::launch_bwd_finish(static_cast<const float*>(workspace), chunks,
-                                            static_cast<int>(D), dgamma, stream));
+  return finish_dgamma(const_cast<void*>(workspace), T, D, dgamma, stream);
 }
 
 rmsn_status rmsnorm_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
@@ -255,9 +290,29 @@ rmsn_status rmsnorm_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int6
     RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
   }
   if (dgamma == nullptr) return RMSN_OK;
-  const int64_t chunks = T > 0 ? rmsn::bwd_plan(T, D).chunks : 0;
-  return hip_status(rmsn::launch_bwd_finish(static_cast<const float*>(workspace), chunks,
-                                            static_cast<int>(D), dgamma, stream));
+  return finish_dgamma(workspace, T, D, dgamma, stream);
+}
+
+rmsn_status rmsnorm_gated_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                              const uint16_t* z, int64_t ld_z, const float* rstd,
+                              const float* gamma, int zero_centered_gamma, int64_t T, int64_t D,
+                              int activation, uint16_t* dx, int64_t ld_dx, uint16_t* dz,
+                              int64_t ld_dz, float* dgamma, void* workspace,
+                              size_t workspace_bytes_, void* stream) {
+  if (bad_activation(activation)) return RMSN_ERR_MODE;
+  if (dx == nullptr && dz == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
+  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
+  const GateIO gate{z, ld_z, dz, ld_dz};
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, nullptr, 0, dx, ld_dx,
+                     dgamma != nullptr, dgamma, workspace, workspace_bytes_, true, gate));
+  if (T > 0) {
+    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
+                                     nullptr, 0, dx, ld_dx,
+                                     dgamma != nullptr ? workspace : nullptr, gate, activation);
+    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
+  }
+  if (dgamma == nullptr) return RMSN_OK;
+  return finish_dgamma(workspace, T, D, dgamma, stream);
 }
 
 }  // extern "C"

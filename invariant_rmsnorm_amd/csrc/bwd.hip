@@ -1,277 +1,14 @@
-// Backward kernels for gfx950: the input gradient dx and the deterministic
-// weight gradient dgamma.
+// Backward launchers: the plain and residual-gradient rows kernels (the
+// template is in bwd_kernel.hpp; the gated forms are in bwd_gated.hip) and
+// the dgamma finish kernel.
 //
-// Formulas: Megatron-LM PR "Fix the batch-invariant RMSNorm forward and its
-// input gradient", item 2 — with dr/dx_k = -r^3 x_k / D,
-//     dx_k = g_k w_k r - (r^3 x_k / D) * sum_i g_i x_i w_i,
-// the weight entering once in each term; RL-Kernel PR "[DSv4][P1-5]
-// rmsnorm_residual", review comment — dx also receives the residual copy's
-// gradient, and dgamma_j = sum over tokens of dy * x * r. The rstd used is
-// the one the forward saved (RL-Kernel PR "C1: zero-centred RMSNorm
-// references and CUDA kernel", parameter-VJP paragraph). No atomics, split-K
-// or stream-K ("Implementation" of the rmsnorm_residual PR).
-//
-// Kernel 1 (rows): workgroup k owns the fixed chunk of rows
-// [k*C, min(T,(k+1)*C)). Its waves walk the chunk in steps; per row a wave
-// forms gw = g*w, the lane partial of s = sum gw*x, the fixed butterfly
-// (same shape as the forward's), c = ((r*r)*r)*s/D and dx = gw*r - x*c
-// (+ gres), stored with 16-byte non-temporal stores. For dgamma each lane
-// keeps fp32 accumulators for the columns it owns, adding (g*x)*r row after
-// row in chunk order. At the end of the chunk the row slots of a wave are
-// added by a butterfly, the 4 waves as ((w0 + w2) + (w1 + w3)) through LDS,
-// and the chunk's partial row is written to workspace[k][:].
-// Kernel 2 (finish): dgamma[j] = a fixed tree over 16 slices, each slice an
-// ascending sum over a contiguous range of the chunk partials. The grouping
-// depends on T (dgamma is a sum over the whole batch) but never on timing:
-// the bits repeat run to run.
-#include <hip/hip_runtime.h>
-
-#include "device_common.hpp"
-#include "launch.hpp"
+// Finish: dgamma[j] = a fixed tree over 16 slices, each slice an ascending
+// sum over a contiguous range of the chunk partials. The grouping depends on
+// T (dgamma is a sum over the whole batch) but never on timing: the bits
+// repeat run to run.
+#include "bwd_kernel.hpp"
 
 namespace rmsn {
-
-// Register plan by geometry (chosen by measurement at D=4096; results do not
-// depend on it). The kernel runs one 4-wave workgroup per compute unit, so
-// each wave may use the whole register file. Up to 12 vectors per lane the
-// weights stay in registers and the values unpacked in the first pass are
-// reused by the second. Beyond that the registers would spill, so the
-// weights move to LDS and the second pass unpacks the raw vectors again.
-constexpr bool bwd_lean(int vpl) { return vpl >= 13; }
-constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 5 ? 1 : 2; }
-
-// LDS floats the rows kernel needs: the weights when held in LDS (one float4
-// pair per vector slot, laid out so that consecutive lanes read consecutive
-// 16 bytes) and, after the rows are done, two rows of D floats for the wave
-// merge (which reuse the same space).
-inline size_t bwd_rows_lds_floats(int D, bool want_part) {
-  const RowGeom g = row_geom(D);
-  const size_t w = bwd_lean(g.vpl) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
-  const size_t m = want_part ? 2 * static_cast<size_t>(D) : 0;
-  return w > m ? w : m;
-}
-
-template <int LPR, int VPL, bool MASKED, bool GRES>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL))))
-void rmsnorm_bwd_rows_kernel(BwdArgs a) {
-  constexpr int RPW = 64 / LPR;
-  constexpr int U = bwd_unroll(LPR, VPL);
-  constexpr int ROWS_WAVE = U * RPW;
-  constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
-  constexpr bool LEAN = bwd_lean(VPL);
-  extern __shared__ float lds[];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int slot = lane / LPR;
-  const int l = lane % LPR;
-  const int nv = a.D >> 3;
-  const float Df = static_cast<float>(a.D);
-  const bool want_part = a.part != nullptr;
-
-  // Weights w_eff = gamma (+1 in fp32 when zero-centred).
-  float wreg[LEAN ? 1 : VPL][8];
-  float4* const wl4 = reinterpret_cast<float4*>(lds);
-  if constexpr (LEAN) {
-    // float4 h (0/1) of vector c = v*LPR + l goes to slot (2v + h)*LPR + l
-    for (int j = threadIdx.x; j < 2 * nv; j += kBlock) {
-      const int c = j >> 1, h = j & 1;
-      float4 q = reinterpret_cast<const float4*>(a.gamma)[j];
-      if (a.zc) { q.x = q.x + 1.0f; q.y = q.y + 1.0f; q.z = q.z + 1.0f; q.w = q.w + 1.0f; }
-      wl4[((c / LPR) * 2 + h) * LPR + (c % LPR)] = q;
-    }
-    __syncthreads();
-  } else {
-    load_weights<LPR, (LEAN ? 1 : VPL), MASKED>(a.gamma, a.zc, nv, l, wreg);
-  }
-  // In the lean plan `base` is an opaque zero, so that the LDS reads stay
-  // inside the row loop instead of being hoisted into registers.
-  auto weights = [&](int base, int v, float (&w8)[8]) {
-    if constexpr (LEAN) {
-      const float4 p0 = wl4[base + (2 * v) * LPR + l];
-      const float4 p1 = wl4[base + (2 * v + 1) * LPR + l];
-      w8[0] = p0.x; w8[1] = p0.y; w8[2] = p0.z; w8[3] = p0.w;
-      w8[4] = p1.x; w8[5] = p1.y; w8[6] = p1.z; w8[7] = p1.w;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) w8[k] = wreg[LEAN ? 0 : v][k];
-    }
-  };
-
-  float acc[VPL][8];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[v][k] = 0.0f;
-
-  const int64_t begin = static_cast<int64_t>(blockIdx.x) * a.chunk_rows;
-  const int64_t end = begin + a.chunk_rows < a.T ? begin + a.chunk_rows : a.T;
-
-  // Byte offset of this lane's vector v within its row group, per tensor;
-  // vectors past D get an offset no resource reaches. Rows past the chunk's
-  // end read as zero (and then contribute nothing) and their stores drop.
-  auto voff = [&](int v, int64_t ld) -> uint32_t {
-    const int c = v * LPR + l;
-    if (MASKED && c >= nv) return kOutOfRange;
-    return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
-  };
-
-  for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
-    u32x4 gq[U][VPL], xq[U][VPL];
-    u32x4 rq_res[GRES ? U : 1][GRES ? VPL : 1];  // residual-branch gradient
-    float rq[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t first = step + wave * ROWS_WAVE + u * RPW;
-      rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
-      const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
-      const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        gq[u][v] = buf_load16(rg, voff(v, a.ld_g));
-        xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
-      }
-      if constexpr (GRES) {
-        const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) rq_res[u][v] = buf_load16(rgr, voff(v, a.ld_gres));
-      }
-    }
-
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t first = step + wave * ROWS_WAVE + u * RPW;
-      const float r = rq[u];
-      int wbase = 0;
-      if constexpr (LEAN) asm("" : "+v"(wbase));
-      // Pass 1: the lane partial of s = sum_i (g_i * w_i) * x_i in (vector,
-      // element) order, and this row's (g*x)*r added to the dgamma
-      // accumulators ((g*x) is exact in fp32 for bf16 inputs; rows past the
-      // chunk read as zeros with r = 0 and add +0).
-      acc_t sa = 0;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        if (MASKED && v * LPR + l >= nv) continue;  // no such vector (weights unset)
-        float gf[8], xf[8], w8[8];
-        unpack8(gq[u][v], gf);
-        unpack8(xq[u][v], xf);
-        weights(wbase, v, w8);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float gw = gf[k] * w8[k];
-          const float t = gw * xf[k];
-          sa = acc_add(sa, t);
-          acc[v][k] = __builtin_fmaf(gf[k] * xf[k], r, acc[v][k]);
-        }
-        // one vector at a time: without this fence the scheduler unpacks the
-        // whole row up front and the kernel runs ~10% slower (measured)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const float s = static_cast<float>(row_sum<LPR>(sa));
-      const float rr = r * r;
-      const float r3 = rr * r;
-      const float r3s = r3 * s;
-      const float c = r3s / Df;
-      // Pass 2: dx = gw*r - x*c (+ gres), one rounding to bf16.
-      if constexpr (LEAN) {
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          opaque(gq[u][v]);
-          opaque(xq[u][v]);
-        }
-        asm("" : "+v"(wbase));
-      }
-      // Without dx (weight gradient only) the resource is empty and the
-      // stores drop; computing dx anyway keeps this loop free of branches.
-      const auto rdx = rows_rsrc(a.dx, first, a.dx != nullptr ? end : first, RPW, a.ld_dx, a.D);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        if (MASKED && v * LPR + l >= nv) continue;
-        float gf[8], xf[8], w8[8], o[8];
-        unpack8(gq[u][v], gf);
-        unpack8(xq[u][v], xf);
-        weights(wbase, v, w8);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float gw = gf[k] * w8[k];
-          const float t1 = gw * r;
-          const float t2 = xf[k] * c;
-          o[k] = t1 - t2;
-        }
-        if constexpr (GRES) {
-          float rf[8];
-          unpack8(rq_res[u][v], rf);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
-        }
-        buf_store16_nt(pack8(o), rdx, voff(v, a.ld_dx));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-
-  if (!want_part) return;
-
-  // Row slots of one wave hold different rows of the same columns: add them
-  // with a butterfly over the slot bits (every slot ends with equal bits).
-#pragma unroll
-  for (int m = LPR; m < 64; m <<= 1)
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[v][k] = acc[v][k] + __shfl_xor(acc[v][k], m);
-
-  // Waves: ((w0 + w2) + (w1 + w3)) through two LDS rows of D floats (the
-  // weights' space is reused, hence the barrier first).
-  __syncthreads();
-  const bool writer = slot == 0;
-  auto lds_row = [&](int b) { return lds + b * a.D; };
-  if (wave >= 2 && writer) {
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int c = v * LPR + l;
-      if (MASKED && c >= nv) continue;
-      float* d = lds_row(wave - 2) + 8 * c;
-      *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-      *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
-    }
-  }
-  __syncthreads();
-  if (wave < 2 && writer) {
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int c = v * LPR + l;
-      if (MASKED && c >= nv) continue;
-      float* d = lds_row(wave) + 8 * c;
-      const float4 p0 = *reinterpret_cast<const float4*>(d);
-      const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
-      acc[v][0] = acc[v][0] + p0.x; acc[v][1] = acc[v][1] + p0.y;
-      acc[v][2] = acc[v][2] + p0.z; acc[v][3] = acc[v][3] + p0.w;
-      acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
-      acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
-      if (wave == 1) {  // the same wave read this row just above
-        *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-        *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
-      }
-    }
-  }
-  __syncthreads();
-  if (wave == 0 && writer) {
-    float* out = a.part + static_cast<int64_t>(blockIdx.x) * a.D;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int c = v * LPR + l;
-      if (MASKED && c >= nv) continue;
-      const float* d = lds_row(1) + 8 * c;
-      const float4 p0 = *reinterpret_cast<const float4*>(d);
-      const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
-      const float4 o0 = make_float4(acc[v][0] + p0.x, acc[v][1] + p0.y, acc[v][2] + p0.z, acc[v][3] + p0.w);
-      const float4 o1 = make_float4(acc[v][4] + p1.x, acc[v][5] + p1.y, acc[v][6] + p1.z, acc[v][7] + p1.w);
-      *reinterpret_cast<float4*>(out + 8 * c) = o0;
-      *reinterpret_cast<float4*>(out + 8 * c + 4) = o1;
-    }
-  }
-}
 
 // dgamma from the chunk partials. A workgroup is two waves covering 32
 // columns (one 128-byte line of each partial row, so no line is fetched by
@@ -323,52 +60,12 @@ __global__ __launch_bounds__(64 * kFinishWaves) void rmsnorm_bwd_finish_kernel(
   if (s == 0 && ok) reinterpret_cast<float4*>(dgamma)[col4] = acc;
 }
 
-namespace {
-
-template <int LPR, int VPL, bool MASKED, bool GRES>
-int launch_rows_inst(const BwdArgs& a, void* stream) {
-  const size_t lds = sizeof(float) * bwd_rows_lds_floats(a.D, a.part != nullptr);
-  hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, GRES>),
-                     dim3(static_cast<unsigned>(a.chunks)), dim3(kBlock), lds,
-                     static_cast<hipStream_t>(stream), a);
-  return static_cast<int>(hipGetLastError());
-}
-
-using RowsLaunch = int (*)(const BwdArgs&, void*);
-
-template <int LPR, int VPL, bool MASKED>
-RowsLaunch pick_gres(bool gres) {
-  return gres ? &launch_rows_inst<LPR, VPL, MASKED, true> : &launch_rows_inst<LPR, VPL, MASKED, false>;
-}
-
-template <int VPL = 1>
-RowsLaunch pick_wide(int vpl, bool masked, bool gres) {
-  if constexpr (VPL > kMaxVpl) {
-    return nullptr;
-  } else {
-    if (vpl == VPL) return masked ? pick_gres<64, VPL, true>(gres) : pick_gres<64, VPL, false>(gres);
-    return pick_wide<VPL + 1>(vpl, masked, gres);
-  }
-}
-
-RowsLaunch pick(const RowGeom& g, bool gres) {
-  switch (g.lpr) {
-    case 64: return pick_wide(g.vpl, g.masked, gres);
-    case 32: return g.masked ? pick_gres<32, 1, true>(gres) : pick_gres<32, 1, false>(gres);
-    case 16: return g.masked ? pick_gres<16, 1, true>(gres) : pick_gres<16, 1, false>(gres);
-    case 8: return g.masked ? pick_gres<8, 1, true>(gres) : pick_gres<8, 1, false>(gres);
-    case 4: return g.masked ? pick_gres<4, 1, true>(gres) : pick_gres<4, 1, false>(gres);
-    case 2: return pick_gres<2, 1, false>(gres);
-    case 1: return pick_gres<1, 1, false>(gres);
-    default: return nullptr;
-  }
-}
-
-}  // namespace
-
 int launch_bwd_rows(const BwdArgs& a, void* stream) {
   if (a.T == 0 || a.chunks == 0) return 0;
-  const RowsLaunch f = pick(row_geom(a.D), a.gres != nullptr);
+  if (a.z != nullptr) return launch_bwd_rows_gated(a, stream);
+  const RowGeom g = row_geom(a.D);
+  const bwd_detail::RowsLaunch f =
+      a.gres != nullptr ? bwd_detail::pick<kBwdGres>(g) : bwd_detail::pick<kBwdPlain>(g);
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);
   return f(a, stream);
 }

@@ -180,6 +180,63 @@ __device__ __forceinline__ float rstd_of(float ss, float Df, float eps) {
   return static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(var)));
 }
 
+// ---- gate activations of the gated norm -----------------------------------
+enum : int { kGateSilu = 0, kGateSigmoid = 1 };
+
+// sigmoid(z) and 1 - sigmoid(z), each within a few fp32 ulp, from
+// e = exp(-|z|): for z >= 0 they are 1/(1+e) and e/(1+e), for z < 0 the other
+// way round, so neither is a cancelling subtraction and nothing overflows.
+// exp(-|z|) = 2^y with y = -|z| log2(e) carried in two parts (argument
+// splitting after Cody and Waite): y_hi = fp32(-|z| * L) and y_lo = the
+// rounding error of that product (an fma) plus -|z| * (log2(e) - L);
+// then e = 2^y_hi * (1 + y_lo ln 2). |z| is clamped to 128, far past the
+// point where e underflows, so infinities give e = 0; NaN passes through.
+// The reciprocal is v_rcp_f32 refined by one Newton step.
+__device__ __forceinline__ void sigmoid_pair(float z, float& s, float& sc) {
+  constexpr float kL = 1.44269504088896340736f;
+  constexpr float kLlo = static_cast<float>(1.44269504088896340736 - static_cast<double>(kL));
+  constexpr float kLn2 = 0.69314718055994530942f;
+  float m = -__builtin_fabsf(z);
+  m = m < -128.0f ? -128.0f : m;
+  const float yh = m * kL;
+  const float yl = __builtin_fmaf(m, kL, -yh) + m * kLlo;
+  const float eh = __builtin_exp2f(yh);  // subnormal results kept
+  const float e = __builtin_fmaf(eh, yl * kLn2, eh);
+  const float d = 1.0f + e;
+  float inv = __builtin_amdgcn_rcpf(d);
+  inv = __builtin_fmaf(__builtin_fmaf(-d, inv, 1.0f), inv, inv);
+  const float ei = e * inv;
+  const bool pos = z >= 0.0f;
+  s = pos ? inv : ei;
+  sc = pos ? ei : inv;
+}
+
+// The gate a(z): silu(z) = z * sigmoid(z), or sigmoid(z).
+template <int ACT>
+__device__ __forceinline__ float gate(float z) {
+  float s, sc;
+  sigmoid_pair(z, s, sc);
+  return ACT == kGateSigmoid ? s : z * s;
+}
+
+// a(z) and a'(z): silu' = s (1 + z (1 - s)), sigmoid' = s (1 - s).
+template <int ACT>
+__device__ __forceinline__ void gate_and_grad(float z, float& a, float& da) {
+  float s, sc;
+  sigmoid_pair(z, s, sc);
+  if constexpr (ACT == kGateSigmoid) {
+    a = s;
+    da = s * sc;
+  } else {
+    a = z * s;
+    const float zsc = z * sc;
+    da = s * (1.0f + zsc);
+  }
+}
+
+// Rounds 8 fp32 values to bf16 and back (round to nearest even).
+__device__ __forceinline__ void round8_bf16(float (&f)[8]) { unpack8(pack8(f), f); }
+
 // Loads this lane's weights w_eff = gamma (+1.0f in fp32 when zero-centred)
 // for its vectors c = v*LPR + l; columns past D read as zero.
 template <int LPR, int VPL, bool MASKED>

@@ -1,219 +1,13 @@
-// Forward kernels: plain, residual-copy and SiLU-gated RMSNorm over the last
-// axis of a [T, D] bf16 tensor, for gfx950.
-//
-// What a row computes follows Megatron-LM PR "Fix the batch-invariant RMSNorm
-// forward and its input gradient" (item 1: w_eff = fp32(gamma) + 1 when
-// zero-centred), RL-Kernel PR "[DSv4][P1-5] rmsnorm_residual"
-// ("Implementation": r = rsqrt(mean(x^2) + eps), y = (x * r) * gamma, mul and
-// add rounded separately; "Summary": the residual output is a byte copy of x)
-// and RL-Kernel PR "C1: zero-centred RMSNorm references and CUDA kernel" (the
-// gated norm multiplies by the weight in fp32, then by silu(z)).
-//
-// Work split. A 256-thread workgroup is 4 waves; each wave processes U*RPW
-// rows per step (RPW = 64/LPR rows side by side, U steps unrolled so each
-// lane has ~128 bytes of loads in flight), and workgroups stride over the
-// batch. Per row: 16-byte loads of x, the fp32 sum of squares of the lane's
-// own elements in a fixed order, the fixed DPP butterfly over the row's
-// lanes (row_sum), r, then y written with 16-byte non-temporal stores. None
-// of these steps looks at T, the row index or the strides except to address
-// memory, so each row's bits are the same in any batch.
-#include <hip/hip_runtime.h>
-
-#include <algorithm>
-#include <atomic>
-
-#include "device_common.hpp"
-#include "launch.hpp"
+// Forward launchers: the plain and residual-copy forms here, the gated forms
+// in fwd_gated.hip. The kernel itself is in fwd_kernel.hpp.
+#include "fwd_kernel.hpp"
 
 namespace rmsn {
 
-// sigmoid-weighted gate silu(z) = z * sigmoid(z), from e = exp(-|z|) so that
-// nothing overflows: sigmoid = 1/(1+e) for z >= 0 and e/(1+e) for z < 0.
-// exp and the reciprocal are the hardware v_exp_f32 / v_rcp_f32 (about 1 ulp
-// each); the result is within a few fp32 ulp of silu(z).
-__device__ __forceinline__ float silu(float z) {
-  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(z) * 1.44269504088896340736f);
-  const float inv = __builtin_amdgcn_rcpf(1.0f + e);
-  const float sg = z >= 0.0f ? inv : e * inv;
-  return z * sg;
-}
-
-
-template <int LPR, int VPL, bool MASKED, bool GATED>
-__global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
-  constexpr int RPW = 64 / LPR;
-  constexpr int U = fwd_unroll(LPR, VPL);
-  constexpr int ROWS_WAVE = U * RPW;
-  constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
-  constexpr int ZU = GATED ? U : 1;
-  constexpr int ZV = GATED ? VPL : 1;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int slot = lane / LPR;
-  const int l = lane % LPR;
-  const int nv = a.D >> 3;
-  const float Df = static_cast<float>(a.D);
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS_BLOCK;
-
-  float w[VPL][8];
-  load_weights<LPR, VPL, MASKED>(a.gamma, a.zc, nv, l, w);
-
-  // Byte offset of this lane's vector v within its row group, per tensor;
-  // vectors past D get an offset no resource reaches.
-  auto voff = [&](int v, int64_t ld) -> uint32_t {
-    const int c = v * LPR + l;
-    if (MASKED && c >= nv) return kOutOfRange;
-    return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
-  };
-  // Rows first .. first+RPW-1 form row group u of the wave; `first` is
-  // wave-uniform.
-  auto group_first = [&](int64_t base, int u) { return base + wave * ROWS_WAVE + u * RPW; };
-
-  auto load_step = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t first = group_first(base, u);
-      const auto rx = rows_rsrc(a.x, first, a.T, RPW, a.ld_x, a.D);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
-      if constexpr (GATED) {
-        const auto rz = rows_rsrc(a.z, first, a.T, RPW, a.ld_z, a.D);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16(rz, voff(v, a.ld_z));
-      }
-    }
-  };
-
-  auto process = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t first = group_first(base, u);
-      const int64_t row = first + slot;
-
-      // sum of squares: this lane's elements in (vector, element) order, then
-      // the row's fixed butterfly. Squares of bf16 values are exact in fp32.
-      acc_t ssa = 0;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        float f[8];
-        unpack8(xq[u][v], f);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float sq = f[k] * f[k];
-          ssa = acc_add(ssa, sq);
-        }
-      }
-      const float ss = static_cast<float>(row_sum<LPR>(ssa));
-      const float r = rstd_of(ss, Df, a.eps);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) opaque(xq[u][v]);
-
-      if (a.rstd != nullptr && l == 0 && row < a.T) a.rstd[row] = r;
-      // rows past T: the resources below are empty and drop the stores
-      const auto ry = rows_rsrc(a.y, first, a.T, RPW, a.ld_y, a.D);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        float f[8], o[8];
-        unpack8(xq[u][v], f);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float xr = f[k] * r;
-          o[k] = xr * w[v][k];
-        }
-        if constexpr (GATED) {
-          float zf[8];
-          unpack8(zq[u][v], zf);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) o[k] = o[k] * silu(zf[k]);
-        }
-        buf_store16_nt(pack8(o), ry, voff(v, a.ld_y));
-      }
-      if (a.res != nullptr) {
-        const auto rr = rows_rsrc(a.res, first, a.T, RPW, a.ld_res, a.D);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) buf_store16_nt(xq[u][v], rr, voff(v, a.ld_res));
-      }
-    }
-  };
-
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * ROWS_BLOCK; base < a.T; base += stride) {
-    u32x4 xv[U][VPL];
-    u32x4 zv[ZU][ZV];
-    load_step(base, xv, zv);
-    process(base, xv, zv);
-  }
-}
-
-namespace {
-
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-template <int LPR, int VPL, bool MASKED, bool GATED>
-int launch_fwd_inst(const FwdArgs& a, void* stream) {
-  constexpr int ROWS_BLOCK = kWaves * fwd_unroll(LPR, VPL) * (64 / LPR);
-  auto kern = rmsnorm_fwd_kernel<LPR, VPL, MASKED, GATED>;
-  static const int per_cu = [&] {
-    int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, kBlock, 0) != hipSuccess || b < 1)
-      b = 1;
-    return b;
-  }();
-  // Persistent grid: at most as many workgroups as fit on the device, and
-  // every workgroup given the same number of steps (a grid of `cap` over
-  // 1.6 * cap steps would leave half the device idle for the last step).
-  const int64_t blocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu;
-  const int64_t steps = (blocks + cap - 1) / cap;
-  const int grid = static_cast<int>(std::max<int64_t>(1, (blocks + steps - 1) / steps));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
-  return static_cast<int>(hipGetLastError());
-}
-
-using FwdLaunch = int (*)(const FwdArgs&, void*);
-
-template <bool GATED, int VPL = 1>
-FwdLaunch pick_wide(int vpl, bool masked) {
-  if constexpr (VPL > kMaxVpl) {
-    return nullptr;
-  } else {
-    if (vpl == VPL)
-      return masked ? &launch_fwd_inst<64, VPL, true, GATED> : &launch_fwd_inst<64, VPL, false, GATED>;
-    return pick_wide<GATED, VPL + 1>(vpl, masked);
-  }
-}
-
-template <bool GATED>
-FwdLaunch pick(const RowGeom& g) {
-  switch (g.lpr) {
-    case 64: return pick_wide<GATED>(g.vpl, g.masked);
-    case 32: return g.masked ? &launch_fwd_inst<32, 1, true, GATED> : &launch_fwd_inst<32, 1, false, GATED>;
-    case 16: return g.masked ? &launch_fwd_inst<16, 1, true, GATED> : &launch_fwd_inst<16, 1, false, GATED>;
-    case 8: return g.masked ? &launch_fwd_inst<8, 1, true, GATED> : &launch_fwd_inst<8, 1, false, GATED>;
-    case 4: return g.masked ? &launch_fwd_inst<4, 1, true, GATED> : &launch_fwd_inst<4, 1, false, GATED>;
-    case 2: return &launch_fwd_inst<2, 1, false, GATED>;
-    case 1: return &launch_fwd_inst<1, 1, false, GATED>;
-    default: return nullptr;
-  }
-}
-
-}  // namespace
-
 int launch_fwd(const FwdArgs& a, void* stream) {
   if (a.T == 0) return 0;
-  const RowGeom g = row_geom(a.D);
-  const FwdLaunch f = a.z != nullptr ? pick<true>(g) : pick<false>(g);
+  if (a.z != nullptr) return launch_fwd_gated(a, stream);
+  const fwd_detail::FwdLaunch f = fwd_detail::pick<0>(row_geom(a.D));
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);
   return f(a, stream);
 }

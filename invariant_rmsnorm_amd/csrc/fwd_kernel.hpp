@@ -1,0 +1,213 @@
+// Forward kernel template: plain, residual-copy and gated RMSNorm over the
+// last axis of a [T, D] bf16 tensor, for gfx950. fwd.hip instantiates the
+// ungated forms, fwd_gated.hip the gated ones (built apart, in parallel).
+//
+// What a row computes follows Megatron-LM PR "Fix the batch-invariant RMSNorm
+// forward and its input gradient" (item 1: w_eff = fp32(gamma) + 1 when
+// zero-centred), RL-Kernel PR "[DSv4][P1-5] rmsnorm_residual"
+// ("Implementation": r = rsqrt(mean(x^2) + eps), y = (x * r) * gamma, mul and
+// add rounded separately; "Summary": the residual output is a byte copy of x)
+// and RL-Kernel PR "C1: zero-centred RMSNorm references and CUDA kernel" (the
+// gated norm: out = norm * a(z), a = silu or sigmoid; one upstream does the
+// weight multiply in fp32, the other casts to the input dtype first).
+//
+// Work split. A 256-thread workgroup is 4 waves; each wave processes U*RPW
+// rows per step (RPW = 64/LPR rows side by side, U steps unrolled so each
+// lane has ~128 bytes of loads in flight), and workgroups stride over the
+// batch. Per row: 16-byte loads of x, the sum of squares of the lane's own
+// elements in a fixed order, the fixed DPP butterfly over the row's lanes
+// (row_sum), r, then y written with 16-byte non-temporal stores. None of
+// these steps looks at T, the row index or the strides except to address
+// memory, so each row's bits are the same in any batch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace rmsn {
+
+// GATE: 0 = no gate; otherwise 1 + activation + 2 * cast, where cast selects
+// the convention that rounds the normalised and the weighted value to bf16
+// before the next multiply.
+constexpr int fwd_gate_code(bool gated, int act, bool cast) { return gated ? 1 + act + 2 * cast : 0; }
+
+template <int LPR, int VPL, bool MASKED, int GATE>
+__global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
+  constexpr bool GATED = GATE != 0;
+  constexpr int ACT = GATED ? (GATE - 1) & 1 : 0;
+  constexpr bool CAST = GATED && (GATE - 1) >= 2;
+  constexpr int RPW = 64 / LPR;
+  constexpr int U = fwd_unroll(LPR, VPL);
+  constexpr int ROWS_WAVE = U * RPW;
+  constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
+  constexpr int ZU = GATED ? U : 1;
+  constexpr int ZV = GATED ? VPL : 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int slot = lane / LPR;
+  const int l = lane % LPR;
+  const int nv = a.D >> 3;
+  const float Df = static_cast<float>(a.D);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS_BLOCK;
+
+  float w[VPL][8];
+  load_weights<LPR, VPL, MASKED>(a.gamma, a.zc, nv, l, w);
+
+  // Byte offset of this lane's vector v within its row group, per tensor;
+  // vectors past D get an offset no resource reaches.
+  auto voff = [&](int v, int64_t ld) -> uint32_t {
+    const int c = v * LPR + l;
+    if (MASKED && c >= nv) return kOutOfRange;
+    return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
+  };
+  // Rows first .. first+RPW-1 form row group u of the wave; `first` is
+  // wave-uniform.
+  auto group_first = [&](int64_t base, int u) { return base + wave * ROWS_WAVE + u * RPW; };
+
+  auto load_step = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t first = group_first(base, u);
+      const auto rx = rows_rsrc(a.x, first, a.T, RPW, a.ld_x, a.D);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
+      if constexpr (GATED) {
+        const auto rz = rows_rsrc(a.z, first, a.T, RPW, a.ld_z, a.D);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16(rz, voff(v, a.ld_z));
+      }
+    }
+  };
+
+  auto process = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t first = group_first(base, u);
+      const int64_t row = first + slot;
+
+      // sum of squares: this lane's elements in (vector, element) order, then
+      // the row's fixed butterfly. Squares of bf16 values are exact in fp32.
+      acc_t ssa = 0;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        float f[8];
+        unpack8(xq[u][v], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float sq = f[k] * f[k];
+          ssa = acc_add(ssa, sq);
+        }
+      }
+      const float ss = static_cast<float>(row_sum<LPR>(ssa));
+      const float r = rstd_of(ss, Df, a.eps);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) opaque(xq[u][v]);
+
+      if (a.rstd != nullptr && l == 0 && row < a.T) a.rstd[row] = r;
+      // rows past T: the resources below are empty and drop the stores
+      const auto ry = rows_rsrc(a.y, first, a.T, RPW, a.ld_y, a.D);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        float f[8], o[8];
+        unpack8(xq[u][v], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = f[k] * r;
+        if constexpr (CAST) round8_bf16(o);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = o[k] * w[v][k];
+        if constexpr (GATED) {
+          if constexpr (CAST) round8_bf16(o);
+          float zf[8];
+          unpack8(zq[u][v], zf);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[k] = o[k] * gate<ACT>(zf[k]);
+        }
+        buf_store16_nt(pack8(o), ry, voff(v, a.ld_y));
+      }
+      if (a.res != nullptr) {
+        const auto rr = rows_rsrc(a.res, first, a.T, RPW, a.ld_res, a.D);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) buf_store16_nt(xq[u][v], rr, voff(v, a.ld_res));
+      }
+    }
+  };
+
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * ROWS_BLOCK; base < a.T; base += stride) {
+    u32x4 xv[U][VPL];
+    u32x4 zv[ZU][ZV];
+    load_step(base, xv, zv);
+    process(base, xv, zv);
+  }
+}
+
+namespace fwd_detail {
+
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int LPR, int VPL, bool MASKED, int GATE>
+int launch_inst(const FwdArgs& a, void* stream) {
+  constexpr int ROWS_BLOCK = kWaves * fwd_unroll(LPR, VPL) * (64 / LPR);
+  auto kern = rmsnorm_fwd_kernel<LPR, VPL, MASKED, GATE>;
+  static const int per_cu = [&] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, kBlock, 0) != hipSuccess || b < 1)
+      b = 1;
+    return b;
+  }();
+  // Persistent grid: at most as many workgroups as fit on the device, and
+  // every workgroup given the same number of steps (a grid of `cap` over
+  // 1.6 * cap steps would leave half the device idle for the last step).
+  const int64_t blocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
+  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu;
+  const int64_t steps = (blocks + cap - 1) / cap;
+  const int grid = static_cast<int>(std::max<int64_t>(1, (blocks + steps - 1) / steps));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+using FwdLaunch = int (*)(const FwdArgs&, void*);
+
+template <int GATE, int VPL = 1>
+FwdLaunch pick_wide(int vpl, bool masked) {
+  if constexpr (VPL > kMaxVpl) {
+    return nullptr;
+  } else {
+    if (vpl == VPL)
+      return masked ? &launch_inst<64, VPL, true, GATE> : &launch_inst<64, VPL, false, GATE>;
+    return pick_wide<GATE, VPL + 1>(vpl, masked);
+  }
+}
+
+template <int GATE>
+FwdLaunch pick(const RowGeom& g) {
+  switch (g.lpr) {
+    case 64: return pick_wide<GATE>(g.vpl, g.masked);
+    case 32: return g.masked ? &launch_inst<32, 1, true, GATE> : &launch_inst<32, 1, false, GATE>;
+    case 16: return g.masked ? &launch_inst<16, 1, true, GATE> : &launch_inst<16, 1, false, GATE>;
+    case 8: return g.masked ? &launch_inst<8, 1, true, GATE> : &launch_inst<8, 1, false, GATE>;
+    case 4: return g.masked ? &launch_inst<4, 1, true, GATE> : &launch_inst<4, 1, false, GATE>;
+    case 2: return &launch_inst<2, 1, false, GATE>;
+    case 1: return &launch_inst<1, 1, false, GATE>;
+    default: return nullptr;
+  }
+}
+
+}  // namespace fwd_detail
+}  // namespace rmsn

@@ -1,6 +1,7 @@
 // Host-side interface between the C-ABI entry points (api.cpp) and the
-// kernel launchers (fwd.hip, bwd.hip). Plain types only: api.cpp does not
-// include any HIP header. Arguments arrive already validated.
+// kernel launchers (fwd.hip, fwd_gated.hip, bwd.hip, bwd_gated.hip). Plain
+// types only: api.cpp does not include any HIP header. Arguments arrive
+// already validated.
 #pragma once
 
 #include <stdint.h>
@@ -10,8 +11,10 @@ namespace rmsn {
 struct FwdArgs {
   const uint16_t* x;
   int64_t ld_x;
-  const uint16_t* z;  // gate, or nullptr
+  const uint16_t* z;  // gate input, or nullptr (no gate)
   int64_t ld_z;
+  int act;   // gate activation: 0 silu, 1 sigmoid
+  int cast;  // gated rounding convention: 0 weight multiply in fp32, 1 casts
   const float* gamma;
   int zc;
   float eps;
@@ -41,11 +44,19 @@ struct BwdArgs {
   float* part;  // [chunks][D] dgamma partials, or nullptr
   int64_t chunk_rows;
   int64_t chunks;
+  // gated backward only (z == nullptr otherwise)
+  const uint16_t* z;
+  int64_t ld_z;
+  int act;       // 0 silu, 1 sigmoid
+  uint16_t* dz;  // or nullptr
+  int64_t ld_dz;
 };
 
 // Each returns 0 on success or the HIP error code of a refused launch.
 int launch_fwd(const FwdArgs& a, void* stream);
+int launch_fwd_gated(const FwdArgs& a, void* stream);  // a.z != nullptr
 int launch_bwd_rows(const BwdArgs& a, void* stream);
+int launch_bwd_rows_gated(const BwdArgs& a, void* stream);  // a.z != nullptr
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
 
 }  // namespace rmsn

@@ -85,12 +85,14 @@ def residual(T: int = 32768, D: int = 4096, seed: int = 2002,
 
 
 def gated(T: int = 262144, D: int = 128, seed: int = 3003,
-          rows: np.ndarray | None = None) -> Problem:
-    """SiLU-gated per-head norm: x, z ~ N(0,1); gamma = 1 + N(0,0.1)."""
+          rows: np.ndarray | None = None, with_grad: bool = False) -> Problem:
+    """Gated per-head norm: x, z ~ N(0,1); gamma = 1 + N(0,0.1); with
+    ``with_grad`` also an upstream gradient g ~ N(0,1) for the backward."""
     idx = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
     return Problem(name=f"gated_T{T}_D{D}", T=T, D=D, eps=1e-6, zero_centered=False,
                    gamma=gamma_for(seed, D, False),
                    x=_rows_of(seed, S_X, idx, D, 1.0),
+                   g=_rows_of(seed, S_G, idx, D, 1.0) if with_grad else None,
                    z=_rows_of(seed, S_Z, idx, D, 1.0))
 
 

@@ -96,3 +96,41 @@ def dgamma_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     if scale == 0:
         return float(np.abs(gpu).max())
     return float(np.abs(gpu.astype(np.float64) - ref).max() / scale)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (8 significant bits; subnormal spacing
+    2^-133 below 2^-126)."""
+    _, e = np.frexp(np.abs(np.asarray(v, dtype=np.float64)))
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def ulp_or_cancelled(got_bits: np.ndarray, ref_bits: np.ndarray, terms: np.ndarray,
+                     k: float = 2.0 ** -20) -> np.ndarray:
+    """Mask: within 1 bf16 ulp of the reference or, for a result that is a
+    difference of terms whose magnitudes add to ``terms``, within
+    ulp(ref) + k * terms. The second branch covers inputs that carry a few
+    fp32 ulps of approximation error (the gate a(z)): relative to the terms
+    such an error is tiny, but a cancelling difference magnifies it relative
+    to the result."""
+    d = ulp_distance(got_bits, ref_bits)
+    got, ref = bf16_to_f64(got_bits), bf16_to_f64(ref_bits)
+    with np.errstate(invalid="ignore"):
+        near = np.abs(got - ref) <= bf16_ulp(ref) + k * np.abs(terms)
+    return (d <= 1) | near
+
+
+def gated_dx_terms(g_bits, x_bits, z_bits, gamma, zero_centered, rstd, sigmoid):
+    """Magnitude of the two terms of the gated dx, per element, in double:
+    |gn w r| + |x| r^3 sum_i |gn_i w_i x_i| / D, with gn = g a(z) and a the
+    sigmoid (``sigmoid``) or silu gate (scipy's expit)."""
+    import scipy.special
+    g, x, z = bf16_to_f64(g_bits), bf16_to_f64(x_bits), bf16_to_f64(z_bits)
+    w = np.asarray(gamma, np.float64) + (1.0 if zero_centered else 0.0)
+    s = scipy.special.expit(z)
+    with np.errstate(invalid="ignore", over="ignore"):
+        a = s if sigmoid else z * s
+        gw = g * a * w
+        r = np.asarray(rstd, np.float64)[:, None]
+        D = x.shape[1]
+        return np.abs(gw * r) + np.abs(x) * r ** 3 * np.abs(gw * x).sum(1, keepdims=True) / D

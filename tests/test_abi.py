@@ -37,11 +37,11 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 1
+    assert irn.rmsnorm_abi_version() == 2
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         assert irn.status_string(code).startswith("RMSN_")
     assert "unknown" in irn.status_string(99)
 
@@ -119,6 +119,7 @@ def bwd(**kw):
     (dict(x=None), irn.RMSN_ERR_NULL),
     (dict(rstd=None), irn.RMSN_ERR_NULL),
     (dict(gamma=None), irn.RMSN_ERR_NULL),                  # dx needs the weights
+    (dict(gamma=None, dx=None), irn.RMSN_ERR_NULL),         # the kernel loads them anyway
     (dict(ws=None), irn.RMSN_ERR_WORKSPACE),
     (dict(ws_bytes=16), irn.RMSN_ERR_WORKSPACE),
     (dict(ws=W + 4), irn.RMSN_ERR_MISALIGNED),
@@ -156,6 +157,83 @@ def test_finish_rejections():
     assert lib.rmsnorm_bwd_finish(W, 64, 1000, 4096, E, None) == irn.RMSN_ERR_WORKSPACE
     assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 4096, W + 64, None) == irn.RMSN_ERR_ALIASING
     assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 12, E, None) == irn.RMSN_ERR_UNSUPPORTED_D
+
+
+Z = A + (7 << 36)
+DZ = A + (8 << 36)
+
+
+def gated_fwd_ex(**kw):
+    a = dict(x=A, ld_x=4096, z=Z, ld_z=4096, gamma=GAM, zc=0, eps=1e-6, T=8, D=4096,
+             act=irn.RMSN_GATE_SIGMOID, rounding=irn.RMSN_GATED_ROUND_CAST, out=B, ld_out=4096,
+             rstd=RS)
+    a.update(kw)
+    return irn.load().rmsnorm_gated_fwd_ex(a["x"], a["ld_x"], a["z"], a["ld_z"], a["gamma"],
+                                           a["zc"], a["eps"], a["T"], a["D"], a["act"],
+                                           a["rounding"], a["out"], a["ld_out"], a["rstd"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(act=2), irn.RMSN_ERR_MODE),
+    (dict(act=-1), irn.RMSN_ERR_MODE),
+    (dict(rounding=2), irn.RMSN_ERR_MODE),
+    (dict(act=7, T=0), irn.RMSN_ERR_MODE),                  # checked even for an empty batch
+    (dict(z=None), irn.RMSN_ERR_NULL),
+    (dict(z=Z + 2), irn.RMSN_ERR_MISALIGNED),
+    (dict(ld_z=100), irn.RMSN_ERR_SHAPE),
+    (dict(out=Z), irn.RMSN_ERR_ALIASING),
+    (dict(rstd=Z + 64), irn.RMSN_ERR_ALIASING),
+    (dict(D=12, ld_x=16, ld_z=16, ld_out=16), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(eps=-1.0), irn.RMSN_ERR_EPS),
+])
+def test_gated_forward_ex_rejections(kw, code):
+    assert gated_fwd_ex(**kw) == code
+
+
+def test_gated_forward_ex_empty_batch_is_a_no_op():
+    assert gated_fwd_ex(T=0, x=None, z=None, out=None, gamma=None, rstd=None) == irn.RMSN_OK
+
+
+def gated_bwd(**kw):
+    a = dict(g=A, ld_g=4096, x=B, ld_x=4096, z=Z, ld_z=4096, rstd=RS, gamma=GAM, zc=0, T=1000,
+             D=4096, act=irn.RMSN_GATE_SILU, dx=C, ld_dx=4096, dz=DZ, ld_dz=4096, dgamma=E, ws=W,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return irn.load().rmsnorm_gated_bwd(a["g"], a["ld_g"], a["x"], a["ld_x"], a["z"], a["ld_z"],
+                                        a["rstd"], a["gamma"], a["zc"], a["T"], a["D"], a["act"],
+                                        a["dx"], a["ld_dx"], a["dz"], a["ld_dz"], a["dgamma"],
+                                        a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(act=2), irn.RMSN_ERR_MODE),
+    (dict(dx=None, dz=None, dgamma=None), irn.RMSN_ERR_NULL),
+    (dict(z=None), irn.RMSN_ERR_NULL),
+    (dict(gamma=None), irn.RMSN_ERR_NULL),
+    (dict(gamma=None, dx=None, dz=None), irn.RMSN_ERR_NULL),
+    (dict(rstd=None), irn.RMSN_ERR_NULL),
+    (dict(z=Z + 8), irn.RMSN_ERR_MISALIGNED),
+    (dict(dz=DZ + 8), irn.RMSN_ERR_MISALIGNED),
+    (dict(ld_dz=4000), irn.RMSN_ERR_SHAPE),
+    (dict(ld_z=4000), irn.RMSN_ERR_SHAPE),
+    (dict(dz=Z), irn.RMSN_ERR_ALIASING),                    # dz over the gate input
+    (dict(dz=C), irn.RMSN_ERR_ALIASING),                    # dz over dx
+    (dict(dx=Z + 4096), irn.RMSN_ERR_ALIASING),             # partial overlap with z
+    (dict(ws=DZ), irn.RMSN_ERR_ALIASING),
+    (dict(ws=None), irn.RMSN_ERR_WORKSPACE),
+    (dict(D=4100, ld_g=4104, ld_x=4104, ld_z=4104, ld_dx=4104, ld_dz=4104),
+     irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(T=-1), irn.RMSN_ERR_SHAPE),
+])
+def test_gated_backward_rejections(kw, code):
+    assert gated_bwd(**kw) == code
+
+
+def test_gated_backward_accepts_dx_or_dz_alone():
+    # validation only, at T = 0 (nothing launches; a non-NULL dgamma would
+    # launch its zero fill, which the GPU empty-batch test covers)
+    for kw in (dict(dz=None, dgamma=None), dict(dx=None, dgamma=None)):
+        assert gated_bwd(T=0, **kw) == irn.RMSN_OK
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

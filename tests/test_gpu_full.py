@@ -3,7 +3,9 @@ benchmark times (the same entry points, on the same shapes).
 
 * token norm with outlier rows, T=32768, D=4096: every element of y, rstd,
   dx (with and without the residual gradient) and dgamma against the oracle;
-* SiLU-gated per-head norm, 262144 x 128: every output element;
+* gated per-head norm, 262144 x 128: every output element of the forward
+  (both gates, both rounding conventions) and of the backward (dx, dz,
+  dgamma; both gates);
 * T=262144, D=4096, zero-centred: dgamma over all rows against the oracle,
   y/rstd/dx on sampled rows, and ten runs bitwise identical.
 """
@@ -16,7 +18,8 @@ import torch
 import invariant_rmsnorm_amd as irn
 import oracle
 from gpu_util import dev_bf16, dev_f32, host_bits
-from numerics import dgamma_rel_err, max_ulp, rstd_rel_err
+from numerics import (dgamma_rel_err, gated_dx_terms, max_ulp, rstd_rel_err, ulp_distance,
+                      ulp_or_cancelled)
 from synth import workloads as wl
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -65,6 +68,38 @@ def test_gated_per_head_full(gpu):
     assert max_ulp(got, ro) <= 1
     _log(f"gated: {(got != ro).sum()} of {got.size} elements 1 ulp apart")
     assert rstd_rel_err(rstd.cpu().numpy(), rr) <= 1e-6
+
+
+@pytest.mark.parametrize("act,act_o", [(irn.RMSN_GATE_SILU, oracle.SILU),
+                                       (irn.RMSN_GATE_SIGMOID, oracle.SIGMOID)])
+def test_gated_variants_full(gpu, act, act_o):
+    p = wl.gated(with_grad=True)
+    x, z, gamma = dev_bf16(p.x), dev_bf16(p.z), dev_f32(p.gamma)
+    for rounding, conv in ((irn.RMSN_GATED_ROUND_FP32, oracle.FP32_WEIGHT),
+                           (irn.RMSN_GATED_ROUND_CAST, oracle.CAST_INPUT)):
+        out, _ = irn.rmsnorm_gated_fwd_ex(x, z, gamma, False, p.eps, activation=act,
+                                          rounding=rounding)
+        ro, _ = oracle.gated_fwd_ex(p.x, p.z, p.gamma, False, p.eps, activation=act_o,
+                                    convention=conv)
+        got = host_bits(out)
+        _log(f"gated fwd act={act} rounding={rounding}: {(got != ro).sum()} of {got.size} "
+             f"elements 1 ulp apart")
+        assert max_ulp(got, ro) <= 1
+
+    g = p.g
+    _, rstd = irn.rmsnorm_fwd(x, gamma, False, p.eps)
+    dx, dz, dg = irn.rmsnorm_gated_bwd(dev_bf16(g), x, z, rstd, gamma, False, activation=act)
+    _, rr = oracle.fwd(p.x, p.gamma, False, p.eps)
+    rdx, rdz, rdg = oracle.gated_bwd(g, p.x, p.z, rr, p.gamma, False, activation=act_o)
+    gdx, gdz = host_bits(dx), host_bits(dz)
+    udx, udz = ulp_distance(gdx, rdx), ulp_distance(gdz, rdz)
+    err = dgamma_rel_err(dg.cpu().numpy(), rdg)
+    _log(f"gated bwd act={act}: dx {(udx > 0).sum()} differ (max {udx.max()} ulp), "
+         f"dz {(udz > 0).sum()} differ (max {udz.max()} ulp), dgamma rel err {err:.3e}")
+    terms = gated_dx_terms(g, p.x, p.z, p.gamma, False, rr, act_o == oracle.SIGMOID)
+    assert ulp_or_cancelled(gdx, rdx, terms).all()
+    assert udz.max() <= 1
+    assert err <= 1e-5
 
 
 def test_large_zero_centered_full(gpu):
