@@ -7,12 +7,16 @@ timing starts. The default workload is the token norm at T=32768, D=4096
 (bf16 activations with 1% outlier rows, fp32 gamma, eps=1e-6); --workload
 selects the other synthetic workloads.
 
-Prints one JSON line. `value` is algorithmic bytes per step / time per step:
-each input element read once, each output written once (formulas in
-ALGO_BYTES). `roofline` reports the dominant kernel (the backward rows
-kernel) against MI355X's 8 TB/s HBM peak, from HIP events recorded around
-that kernel's launches on the stream it runs on. `cpu_baseline` times the CPU
-oracle on the host cores for the same workload.
+Prints one JSON line. `value` is algorithmic bytes per step / wall time per
+step over the K timed steps: each input element read once, each output
+written once (formulas in algo_bytes). `roofline` reports the dominant kernel
+(the backward rows kernel; the gated kernel for the gated workload) against
+MI355X's 8 TB/s HBM peak, from HIP events recorded around that kernel on
+every tenth timed step, on the stream it runs on. `kernels` and `cold_cache`
+are per-kernel times from separate passes whose steps bracket every kernel
+with events (events make the GPU drain the stream, so those passes run a few
+microseconds per event slower than the timed steps). `cpu_baseline` times the
+CPU oracle on the host cores for the same workload.
 """
 from __future__ import annotations
 
@@ -67,7 +71,7 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def make_inputs(workload: str, torch, dev):
+def make_inputs(workload: str, torch, dev, rows: int = 0):
     import numpy as np
     from synth import workloads as wl
 
@@ -75,8 +79,8 @@ def make_inputs(workload: str, torch, dev):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     if workload in ("token", "token_gres"):
-        p = wl.residual(with_gres=(workload == "token_gres"))
-        desc = ("token RMSNorm fwd+bwd with dgamma, T=32768, D=4096, bf16 x ~N(0,1) with 1% "
+        p = wl.residual(T=rows or 32768, with_gres=(workload == "token_gres"))
+        desc = (f"token RMSNorm fwd+bwd with dgamma, T={p.T}, D=4096, bf16 x ~N(0,1) with 1% "
                 "outlier rows x50, g ~N(0,1), fp32 gamma=1+N(0,0.1), eps=1e-6")
     elif workload == "large":
         p = wl.large()
@@ -147,12 +151,17 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="token", choices=["token", "token_gres", "large", "gated"])
+    ap.add_argument("--rows", type=int, default=0,
+                    help="token workloads: batch rows T (default 32768, the metric's size)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time of the CPU-oracle baseline (whole passes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="cold-cache pass: MiB read between steps to evict the Infinity "
                          "Cache before each step (0 = skip)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="bracket the dominant kernel with timing events on every N-th "
+                         "timed step (the roofline figure)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -169,7 +178,7 @@ def main():
     irn.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    p, t, desc = make_inputs(args.workload, torch, dev)
+    p, t, desc = make_inputs(args.workload, torch, dev, args.rows)
     T, D = p.T, p.D
     zc, eps = p.zero_centered, p.eps
     x, gamma = t["x"], t["gamma"]
@@ -184,17 +193,27 @@ def main():
         ws, _ = irn.workspace_for(T, D, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(evs=None):
+    def step(evs=None, dom=None):
+        """One pass of the path. `evs` brackets every kernel (the breakdown
+        and cold passes); `dom` brackets only the dominant kernel."""
         if evs is not None:
             evs[0].record(stream)
         if gated:
+            if dom is not None:
+                dom[0].record(stream)
             irn.rmsnorm_gated_fwd(x, t["z"], gamma, zc, eps, out=y)
+            if dom is not None:
+                dom[1].record(stream)
         else:
             irn.rmsnorm_fwd(x, gamma, zc, eps, y=y, rstd=rstd)
         if evs is not None:
             evs[1].record(stream)
         if not gated:
+            if dom is not None:
+                dom[0].record(stream)
             irn.rmsnorm_bwd_rows(g, x, rstd, gamma, zc, g_residual=gres, dx=dx, workspace=ws)
+            if dom is not None:
+                dom[1].record(stream)
             if evs is not None:
                 evs[2].record(stream)
             irn.rmsnorm_bwd_finish(ws, T, D, dgamma)
@@ -222,61 +241,72 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    nev = 2 if gated else 4
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+
+    # Timed region: K steps back to back. A timing event costs the GPU a few
+    # microseconds (it waits for the stream to drain), so only every
+    # `event_every`-th step brackets its dominant kernel with a pair of events;
+    # the other steps run exactly as a caller would run them.
+    every = max(1, args.event_every)
+    sampled = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for i in range(0, args.steps, every)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(dom=sampled.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    dom_ms = sum(a.elapsed_time(b) for a, b in sampled.values()) / len(sampled)
 
-    ms_step = wall * 1e3 / args.steps
     fwd_kind = "gated_fwd" if gated else "fwd"
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    rows_kind = None if gated else ("bwd_rows_gres" if gres is not None else "bwd_rows")
     step_bytes = algo_bytes(fwd_kind, T, D)
-    kernels = {fwd_kind: {"ms": fwd_ms, "GB/s": algo_bytes(fwd_kind, T, D) / fwd_ms / 1e6}}
     if not gated:
-        rows_kind = "bwd_rows_gres" if gres is not None else "bwd_rows"
-        rows_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-        fin_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
         step_bytes += algo_bytes(rows_kind, T, D) + algo_bytes("bwd_finish", T, D)
-        kernels[rows_kind] = {"ms": rows_ms, "GB/s": algo_bytes(rows_kind, T, D) / rows_ms / 1e6}
-        kernels["bwd_finish"] = {"ms": fin_ms}
-        dom, dom_ms, dom_bytes = "rmsnorm_bwd_rows_kernel", rows_ms, algo_bytes(rows_kind, T, D)
+        dom, dom_bytes = "rmsnorm_bwd_rows_kernel", algo_bytes(rows_kind, T, D)
     else:
-        dom, dom_ms, dom_bytes = "rmsnorm_fwd_kernel (gated)", fwd_ms, step_bytes
+        dom, dom_bytes = "rmsnorm_fwd_kernel (gated)", step_bytes
+    ms_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic() if args.workload == "token" else None
+    traffic = measured_traffic() if (args.workload == "token" and T == 32768) else None
 
-    # Cold-cache pass: the same steps, each preceded (outside its events) by a
-    # read-only pass over a buffer larger than the 256 MB Infinity Cache, so
-    # the kernels' times reflect HBM rather than cache hits (a read leaves no
-    # dirty lines to be written back during the next kernel). Reported beside
-    # the contract figures above, which time back-to-back steps.
+    nev = 2 if gated else 4
+
+    def breakdown(flush=None):
+        """Per-kernel times from a separate pass whose steps bracket every
+        kernel with events (each optionally preceded, outside its events, by
+        a read of `flush`)."""
+        n = max(10, min(args.steps, 250))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
+        for i in range(n):
+            if flush is not None:
+                flush.sum()
+            step(evs[i])
+        torch.cuda.synchronize()
+        f = sum(e[0].elapsed_time(e[1]) for e in evs) / n
+        out = {fwd_kind: {"ms": round(f, 5), "GB/s": round(algo_bytes(fwd_kind, T, D) / f / 1e6, 2)}}
+        tot = f
+        if not gated:
+            r = sum(e[1].elapsed_time(e[2]) for e in evs) / n
+            fin = sum(e[2].elapsed_time(e[3]) for e in evs) / n
+            out[rows_kind] = {"ms": round(r, 5), "GB/s": round(algo_bytes(rows_kind, T, D) / r / 1e6, 2)}
+            out["bwd_finish"] = {"ms": round(fin, 5)}
+            tot += r + fin
+        out["steps"] = n
+        out["step_GB/s_from_kernel_events"] = round(step_bytes / tot / 1e6, 2)
+        return out
+
+    kernels = breakdown()
+
+    # Cold-cache pass: each step preceded (outside its events) by a read-only
+    # pass over a buffer larger than the 256 MB Infinity Cache, so the
+    # kernels' times reflect HBM rather than cache hits left by the previous
+    # step (a read leaves no dirty lines to be written back during the next
+    # kernel). Reported beside the contract figures above.
     cold = None
     if args.flush_mib > 0:
         fsrc = torch.zeros(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
-        nc = max(10, args.steps // 4)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(nc)]
-        for i in range(nc):
-            fsrc.sum()
-            step(cev[i])
-        torch.cuda.synchronize()
-        c_fwd = sum(e[0].elapsed_time(e[1]) for e in cev) / nc
-        cold = {"flush_MiB": args.flush_mib, "steps": nc,
-                fwd_kind: {"ms": round(c_fwd, 5),
-                           "GB/s": round(algo_bytes(fwd_kind, T, D) / c_fwd / 1e6, 2)}}
-        kern_ms = c_fwd
-        if not gated:
-            c_rows = sum(e[1].elapsed_time(e[2]) for e in cev) / nc
-            c_fin = sum(e[2].elapsed_time(e[3]) for e in cev) / nc
-            cold[rows_kind] = {"ms": round(c_rows, 5),
-                               "GB/s": round(algo_bytes(rows_kind, T, D) / c_rows / 1e6, 2)}
-            cold["bwd_finish"] = {"ms": round(c_fin, 5)}
-            kern_ms += c_rows + c_fin
-        cold["step_GB/s_from_kernel_events"] = round(step_bytes / kern_ms / 1e6, 2)
+        cold = {"flush_MiB": args.flush_mib, **breakdown(fsrc)}
         del fsrc
 
     cpu = None
@@ -289,7 +319,8 @@ def main():
                          f"{dt:.1f} s wall"}
 
     out = {
-        "metric": METRIC if args.workload == "token" else f"{METRIC} [workload: {args.workload}]",
+        "metric": (METRIC if args.workload == "token" and T == 32768
+                   else f"{METRIC} [workload: {args.workload}, T={T}]"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -305,10 +336,11 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "config": {"workload": desc, "T": T, "D": D, "zero_centered_gamma": zc,
                    "bytes_per_step": step_bytes, "parallelism": "single GPU"},
-        "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in kernels.items()},
+        "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": dom_bytes},
+                     "traffic": traffic, "bytes_per_launch": dom_bytes,
+                     "launch_ms": round(dom_ms, 5), "launches_timed": len(sampled)},
         "cpu_baseline": cpu,
         "cold_cache": cold,
     }

@@ -35,8 +35,8 @@
  *        same tree shape as ss); c = ((r * r) * r) * s / D;
  *        dx_j = bf16_rne(gw_j * r - x_j * c [+ gres_j])
  *   dgamma_j = sum over rows of (g_tj * x_tj) * r_t, summed per fixed chunk
- *        of rows, then the chunk partials in a fixed order (deterministic
- *        for a given T, no atomics).
+ *        of rows (rmsnorm_bwd_partials_layout), then the chunk partials in a
+ *        fixed order (deterministic for a given T, no atomics).
  * Batch invariance: every row's y, rstd and dx are bitwise identical whatever
  * the batch size T, the row's index, the neighbouring rows, padding rows or
  * row strides. The kernel variant and every reduction tree are chosen from D
@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 2
+#define RMSN_ABI_VERSION 3
 #define RMSN_MAX_D 8192
 #define RMSN_MAX_LD (1 << 24)
 
@@ -145,9 +145,10 @@ rmsn_status rmsnorm_gated_fwd(const uint16_t* x, int64_t ld_x,
 /*
  * Gated forward with a choice of activation (RMSN_GATE_*) and rounding
  * convention (RMSN_GATED_ROUND_*); rmsnorm_gated_fwd is the SILU / FP32
- * case. a(z) is evaluated in fp32 to within a few ulp of the exact value
- * (the result is within 1 bf16 ulp of the correctly rounded one). rstd may
- * be NULL. An unknown activation or rounding value returns RMSN_ERR_MODE.
+ * case. a(z) is evaluated in fp32 to about 2^-16 relative (where a(z) is a
+ * normal number), so the bf16 result is within 1 ulp of the correctly
+ * rounded one. rstd may be NULL. An unknown activation or rounding value
+ * returns RMSN_ERR_MODE.
  */
 rmsn_status rmsnorm_gated_fwd_ex(const uint16_t* x, int64_t ld_x,
                                  const uint16_t* z, int64_t ld_z,
@@ -160,9 +161,18 @@ rmsn_status rmsnorm_gated_fwd_ex(const uint16_t* x, int64_t ld_x,
  * (0 when T == 0). Depends on T and D only. */
 size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D);
 
-/* Rows per dgamma chunk used for (T, D): chunk k covers rows
- * [k*C, min(T, (k+1)*C)). 0 for an unsupported shape. */
-int64_t rmsnorm_bwd_chunk_rows(int64_t T, int64_t D);
+/*
+ * Layout of the dgamma partials for (T, D). The batch is cut into blocks of
+ * R rows (block b = rows [b*R, min(T, (b+1)*R))), the blocks into groups of
+ * S consecutive blocks (group q = blocks [q*S, (q+1)*S)), and chunk k of the
+ * K chunks holds the groups k, k+K, k+2K, ... Partial row k of the
+ * workspace is the sum over chunk k's rows (a fixed order: from the highest
+ * row block down). R depends on D only; S and K on (T, D). Writes R, S and
+ * K (each pointer may be NULL) and returns RMSN_OK, or RMSN_ERR_SHAPE /
+ * RMSN_ERR_UNSUPPORTED_D without writing. K = 0 when T = 0.
+ */
+rmsn_status rmsnorm_bwd_partials_layout(int64_t T, int64_t D, int64_t* block_rows,
+                                        int64_t* group_blocks, int64_t* chunks);
 
 /*
  * Backward. From the upstream gradient g, the input x and the forward's

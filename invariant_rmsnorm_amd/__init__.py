@@ -38,7 +38,7 @@ RMSN_GATED_ROUND_CAST = 1
 EXPORTED = (
     "rmsnorm_abi_version", "rmsnorm_status_string", "rmsnorm_fwd", "rmsnorm_residual_fwd",
     "rmsnorm_gated_fwd", "rmsnorm_gated_fwd_ex", "rmsnorm_bwd_workspace_bytes",
-    "rmsnorm_bwd_chunk_rows", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
+    "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
     "rmsnorm_gated_bwd",
 )
 
@@ -67,7 +67,7 @@ def load():
         "rmsnorm_gated_fwd": ([vp, i64, vp, i64, vp, i, f, i64, i64, vp, i64, vp, vp], i),
         "rmsnorm_gated_fwd_ex": ([vp, i64, vp, i64, vp, i, f, i64, i64, i, i, vp, i64, vp, vp], i),
         "rmsnorm_bwd_workspace_bytes": ([i64, i64], sz),
-        "rmsnorm_bwd_chunk_rows": ([i64, i64], i64),
+        "rmsnorm_bwd_partials_layout": ([i64, i64, vp, vp, vp], i),
         "rmsnorm_bwd": ([vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, vp, sz, vp], i),
         "rmsnorm_bwd_rows": ([vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, sz, vp], i),
         "rmsnorm_bwd_finish": ([vp, sz, i64, i64, vp, vp], i),
@@ -94,8 +94,24 @@ def rmsnorm_bwd_workspace_bytes(T: int, D: int) -> int:
     return load().rmsnorm_bwd_workspace_bytes(T, D)
 
 
-def rmsnorm_bwd_chunk_rows(T: int, D: int) -> int:
-    return load().rmsnorm_bwd_chunk_rows(T, D)
+def rmsnorm_bwd_partials_layout(T: int, D: int):
+    """(R, S, K): rows per block, blocks per group, chunks. Chunk k holds the
+    groups k, k+K, k+2K, ... of S consecutive R-row blocks."""
+    out = [ctypes.c_int64(0) for _ in range(3)]
+    _check("rmsnorm_bwd_partials_layout", load().rmsnorm_bwd_partials_layout(
+        T, D, *(ctypes.byref(v) for v in out)))
+    return tuple(v.value for v in out)
+
+
+def chunk_rows(k: int, T: int, D: int):
+    """Row indices of dgamma chunk k, in the order the backward adds them."""
+    R, S, K = rmsnorm_bwd_partials_layout(T, D)
+    nblocks = -(-T // R)
+    rows = []
+    for q in range(k, -(-nblocks // S), K):
+        for b in range(q * S, min(nblocks, (q + 1) * S)):
+            rows.extend(range(b * R, min(T, (b + 1) * R)))
+    return rows[::-1]
 
 
 # ---- marshalling helpers -------------------------------------------------------

@@ -175,7 +175,8 @@ rmsn::BwdArgs bwd_args(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64
   const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
   return rmsn::BwdArgs{g, ld_g, x, ld_x, rstd, gamma, zc != 0, T, static_cast<int>(D),
                        dx ? gres : nullptr, ld_gres, dx, ld_dx, static_cast<float*>(ws),
-                       p.chunk_rows, p.chunks, gate.z, gate.ld_z, act, gate.dz, gate.ld_dz};
+                       p.chunks, p.group_blocks, gate.z, gate.ld_z, act, gate.dz, gate.ld_dz,
+                       T * D * 2 > rmsn::kCacheBytes};
 }
 
 // dgamma from the workspace partials (zeros when T == 0).
@@ -239,9 +240,15 @@ rmsn_status rmsnorm_gated_fwd_ex(const uint16_t* x, int64_t ld_x, const uint16_t
 
 size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D) { return workspace_bytes(T, D); }
 
-int64_t rmsnorm_bwd_chunk_rows(int64_t T, int64_t D) {
-  if (T < 0 || check_D(D) != RMSN_OK) return 0;
-  return rmsn::bwd_plan(T, D).chunk_rows;
+rmsn_status rmsnorm_bwd_partials_layout(int64_t T, int64_t D, int64_t* block_rows,
+                                        int64_t* group_blocks, int64_t* chunks) {
+  if (T < 0) return RMSN_ERR_SHAPE;
+  RMSN_TRY(check_D(D));
+  const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
+  if (block_rows) *block_rows = p.block_rows;
+  if (group_blocks) *group_blocks = p.group_blocks;
+  if (chunks) *chunks = p.chunks;
+  return RMSN_OK;
 }
 
 rmsn_status rmsnorm_bwd_rows(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,

@@ -19,8 +19,9 @@
 // formulas above (dx and dgamma); the gate's own gradient is
 // dz = (g * (n * w)) * a'(z).
 //
-// Work split: workgroup k owns the fixed chunk of rows [k*C, min(T,(k+1)*C)).
-// Its waves walk the chunk in steps; per row a wave forms gw = g*w, the lane
+// Work split: workgroup k owns dgamma chunk k, a fixed set of row blocks
+// spread over the batch (bwd_plan in geometry.hpp). Its waves walk the
+// chunk's blocks in steps; per row a wave forms gw = g*w, the lane
 // partial of s = sum gw*x, the fixed butterfly (same shape as the forward's),
 // c = ((r*r)*r)*s/D and dx = gw*r - x*c (+ gres), stored with 16-byte
 // non-temporal stores. For dgamma each lane keeps fp32 accumulators for the
@@ -117,8 +118,23 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[v][k] = 0.0f;
 
-  const int64_t begin = static_cast<int64_t>(blockIdx.x) * a.chunk_rows;
-  const int64_t end = begin + a.chunk_rows < a.T ? begin + a.chunk_rows : a.T;
+  // Chunk k = the groups of S consecutive row blocks (block b = rows
+  // [b*ROWS_BLOCK, (b+1)*ROWS_BLOCK)) numbered k, k + K, k + 2K, ...
+  // (K = gridDim.x chunks, S = a.group_blocks), taken from the highest block
+  // down. With small S all workgroups sweep one narrow front of the batch
+  // together, starting at its end, where the rows the forward read last
+  // may still sit in the Infinity Cache.
+  const int64_t end = a.T;
+  const int64_t nblocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
+  const int64_t S = a.group_blocks;
+  const int64_t ngroups = (nblocks + S - 1) / S;
+  const int64_t k = blockIdx.x;
+  const int64_t K = gridDim.x;
+  const int64_t mine_groups = ngroups > k ? (ngroups - 1 - k) / K + 1 : 0;
+  // blocks of this chunk: all S blocks of each group except, possibly, the
+  // last group of the batch
+  const int64_t last_group = k + (mine_groups - 1) * K;
+  const int64_t mine = mine_groups == 0 ? 0 : (mine_groups - 1) * S + (nblocks - last_group * S < S ? nblocks - last_group * S : S);
 
   // Byte offset of this lane's vector v within its row group, per tensor;
   // vectors past D get an offset no resource reaches. Rows past the chunk's
@@ -129,7 +145,11 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
 
-  for (int64_t step = begin; step < end; step += ROWS_BLOCK) {
+  for (int64_t j = 0; j < mine; ++j) {
+    // j-th block of the chunk from the top: group (mine-1-j)/S from the
+    // chunk's first, block S-1-(j%S) within it (the last group may be short)
+    const int64_t jj = mine - 1 - j;
+    const int64_t step = ((k + (jj / S) * K) * S + jj % S) * ROWS_BLOCK;
     u32x4 gq[U][VPL], xq[U][VPL];
     u32x4 rq_res[GRES ? U : 1][GRES ? VPL : 1];  // residual-branch gradient
     u32x4 zq[GATED ? U : 1][GATED ? VPL : 1];     // gate input
@@ -140,20 +160,30 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
       const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
       const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
+      // g (and gres, z) are read once: streaming hint. x takes it only when
+      // it does not fit in the Infinity Cache (a wave-uniform branch).
+      if (a.x_stream) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        gq[u][v] = buf_load16(rg, voff(v, a.ld_g));
-        xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
+        for (int v = 0; v < VPL; ++v) {
+          gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
+          xq[u][v] = buf_load16<kLoadStream>(rx, voff(v, a.ld_x));
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
+          xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
+        }
       }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) rq_res[u][v] = buf_load16(rgr, voff(v, a.ld_gres));
+        for (int v = 0; v < VPL; ++v) rq_res[u][v] = buf_load16<kLoadStream>(rgr, voff(v, a.ld_gres));
       }
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, end, RPW, a.ld_z, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16(rz, voff(v, a.ld_z));
+        for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16<kLoadStream>(rz, voff(v, a.ld_z));
       }
     }
 

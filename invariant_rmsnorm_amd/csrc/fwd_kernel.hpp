@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
           float zf[8];
           unpack8(zq[u][v], zf);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) o[k] = o[k] * gate<ACT>(zf[k]);
+          for (int k = 0; k < 8; ++k) o[k] = o[k] * gate_fast<ACT>(zf[k]);
         }
         buf_store16_nt(pack8(o), ry, voff(v, a.ld_y));
       }

@@ -48,6 +48,13 @@ inline RowGeom row_geom(int64_t D) {
 #ifndef RMSN_FWD_UNROLL_NARROW
 #define RMSN_FWD_UNROLL_NARROW 2
 #endif
+// Infinity Cache (MALL) capacity of an MI355X. The backward reads x with the
+// non-temporal hint only when x is larger than this: a tensor that fits may
+// be served from the cache when it is read again (the forward just read it;
+// a repeated call reads it next), while a larger one would only evict other
+// lines. The hint changes no result.
+constexpr int64_t kCacheBytes = int64_t{256} << 20;
+
 constexpr int fwd_unroll(int lpr, int vpl) {
   return lpr < 64 ? RMSN_FWD_UNROLL_NARROW : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
 }
@@ -60,22 +67,33 @@ inline int64_t bwd_rows_per_step(int64_t D) {
   return static_cast<int64_t>(kWaves) * bwd_unroll(g.lpr, g.vpl) * (64 / g.lpr);
 }
 
-// dgamma chunking for a batch of T rows: chunk k = rows [k*C, min(T,(k+1)*C)).
-// C is a multiple of the rows one workgroup step covers, and the number of
-// chunks is at most kTargetChunks. (dgamma sums over the whole batch, so its
+// Row blocks per group of the backward's traversal (0: one contiguous group
+// per chunk). Groups of 4 blocks keep the workgroups on a front of
+// 256 x 4 blocks (at D = 4096, 32 MiB of each input), measured faster at
+// 1-2 GiB per tensor than 1, 16 or one contiguous group per chunk; all are
+// equal at 256 MiB.
+#ifndef RMSN_BWD_GROUP
+#define RMSN_BWD_GROUP 4
+#endif
+
+// dgamma chunking for a batch of T rows. The batch is cut into blocks of
+// R = bwd_rows_per_step(D) rows (block b = rows [b*R, min(T, (b+1)*R))) and
+// the blocks into groups of S consecutive blocks; chunk k of K holds the
+// groups k, k+K, k+2K, ... (dgamma sums over the whole batch, so its
 // grouping may depend on T; the per-row outputs never do.)
 struct BwdPlan {
-  int64_t chunk_rows;
-  int64_t chunks;
+  int64_t block_rows;    // R
+  int64_t chunks;        // K <= kTargetChunks
+  int64_t group_blocks;  // S
 };
 
 inline BwdPlan bwd_plan(int64_t T, int64_t D) {
   const int64_t R = bwd_rows_per_step(D);
-  if (T <= 0) return {R, 0};
-  const int64_t steps = (T + R - 1) / R;
-  const int64_t per = (steps + kTargetChunks - 1) / kTargetChunks;
-  const int64_t C = per * R;
-  return {C, (T + C - 1) / C};
+  if (T <= 0) return {R, 0, 1};
+  const int64_t blocks = (T + R - 1) / R;
+  const int64_t S = RMSN_BWD_GROUP > 0 ? RMSN_BWD_GROUP : (blocks + kTargetChunks - 1) / kTargetChunks;
+  const int64_t groups = (blocks + S - 1) / S;
+  return {R, groups < kTargetChunks ? groups : kTargetChunks, S};
 }
 
 }  // namespace rmsn

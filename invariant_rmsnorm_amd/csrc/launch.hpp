@@ -42,14 +42,15 @@ struct BwdArgs {
   uint16_t* dx;  // or nullptr
   int64_t ld_dx;
   float* part;  // [chunks][D] dgamma partials, or nullptr
-  int64_t chunk_rows;
   int64_t chunks;
+  int64_t group_blocks;  // row blocks per group of the chunk traversal
   // gated backward only (z == nullptr otherwise)
   const uint16_t* z;
   int64_t ld_z;
   int act;       // 0 silu, 1 sigmoid
   uint16_t* dz;  // or nullptr
   int64_t ld_dz;
+  int x_stream;  // read x with the non-temporal hint (set by the launcher)
 };
 
 // Each returns 0 on success or the HIP error code of a refused launch.

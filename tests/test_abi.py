@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 2
+    assert irn.rmsnorm_abi_version() == 3
 
 
 def test_status_strings():
@@ -142,12 +142,25 @@ def test_workspace_and_chunking_contract():
     assert irn.rmsnorm_bwd_workspace_bytes(10, 100) == 0
     for T, D in ((1, 128), (16, 128), (32768, 4096), (262144, 4096), (262144, 128), (1000, 2048),
                  (7, 8), (12345, 8192)):
-        C = irn.rmsnorm_bwd_chunk_rows(T, D)
-        K = -(-T // C)
-        assert C > 0 and K <= 256
+        R, S, K = irn.rmsnorm_bwd_partials_layout(T, D)
+        assert R > 0 and S > 0 and 0 < K <= 256
         assert irn.rmsnorm_bwd_workspace_bytes(T, D) == K * D * 4
+        # R depends on D alone
+        assert irn.rmsnorm_bwd_partials_layout(1, D)[0] == R
+        # every row belongs to exactly one chunk
+        if T <= 20000:
+            rows = [r for k in range(K) for r in irn.chunk_rows(k, T, D)]
+            assert sorted(rows) == list(range(T))
     # the chunk grouping is fixed per (T, D): the same plan on every call
-    assert irn.rmsnorm_bwd_chunk_rows(32768, 4096) == irn.rmsnorm_bwd_chunk_rows(32768, 4096)
+    assert irn.rmsnorm_bwd_partials_layout(32768, 4096) == irn.rmsnorm_bwd_partials_layout(32768, 4096)
+    assert irn.rmsnorm_bwd_partials_layout(0, 4096)[2] == 0
+
+
+def test_partials_layout_rejections():
+    lib = irn.load()
+    assert lib.rmsnorm_bwd_partials_layout(-1, 4096, None, None, None) == irn.RMSN_ERR_SHAPE
+    assert lib.rmsnorm_bwd_partials_layout(16, 100, None, None, None) == irn.RMSN_ERR_UNSUPPORTED_D
+    assert lib.rmsnorm_bwd_partials_layout(16, 0, None, None, None) == irn.RMSN_ERR_SHAPE
 
 
 def test_finish_rejections():

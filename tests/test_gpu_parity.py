@@ -213,15 +213,14 @@ def test_backward_stages_and_partials(gpu, D):
     dg2 = torch.empty_like(dg)
     irn.rmsnorm_bwd_finish(ws, p.T, D, dg2)
     assert torch.equal(dx, dx2) and torch.equal(dg, dg2)
-    C = irn.rmsnorm_bwd_chunk_rows(p.T, D)
-    K = -(-p.T // C)
+    _, _, K = irn.rmsnorm_bwd_partials_layout(p.T, D)
     part = ws[: K * D].view(K, D).double().cpu().numpy()
     ref_dg = oracle.dgamma(p.g, p.x, oracle.fwd(p.x, p.gamma)[1])
     assert dgamma_rel_err(part.sum(axis=0), ref_dg) <= 1e-5
     # chunk k's partial is the oracle's dgamma over chunk k's rows
     _, r_ref = oracle.fwd(p.x, p.gamma)
-    for k in (0, K - 1):
-        rows = slice(k * C, min(p.T, (k + 1) * C))
+    for k in (0, K // 2, K - 1):
+        rows = np.array(irn.chunk_rows(k, p.T, D))
         want = oracle.dgamma(p.g[rows], p.x[rows], r_ref[rows])
         assert dgamma_rel_err(part[k], want) <= 1e-5
     # T = 1
