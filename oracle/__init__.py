@@ -72,6 +72,12 @@ def _load():
         "oracle_rmsnorm_gated_dgamma": ([i, i, vp, i64, vp, i64, vp, i64, vp, i64, i64, vp], i),
         "oracle_rmsnorm_gated_fwd_ex_f64": ([i, vp, vp, vp, i, d, i64, i64, vp], i),
         "oracle_rmsnorm_gated_bwd_f64": ([i, vp, vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
+        "oracle_rmsnorm_add_fwd": ([i, vp, i64, vp, i64, vp, i, f, i64, i64, vp, i64, vp, i64,
+                                    vp], i),
+        "oracle_rmsnorm_add_bwd": ([i, vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64,
+                                    vp, i64, vp], i),
+        "oracle_rmsnorm_add_fwd_f64": ([vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
+        "oracle_rmsnorm_add_bwd_f64": ([vp, vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -337,3 +343,60 @@ def gated_bwd_f64(g, x, z, gamma, zero_centered=False, eps=1e-6, activation=SILU
                                                 _p(dg)),
            "gated_bwd_f64")
     return dx, dz, dg
+
+
+# ---- fused add-RMSNorm ---------------------------------------------------------
+
+def add_fwd(x, residual, gamma, zero_centered=False, eps=1e-6, mode=R64):
+    """(y bf16, residual_out bf16, rstd fp32): the norm of h = x + residual
+    (fp32 sum), residual_out = bf16(h)."""
+    x, residual = _bf16_2d(x), _bf16_2d(residual)
+    T, D = x.shape
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    y = np.empty((T, D), dtype=np.uint16)
+    rout = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_add_fwd(mode, _p(x), _ld(x), _p(residual), _ld(residual),
+                                          _p(gamma), int(zero_centered), eps, T, D, _p(y), D,
+                                          _p(rout), D, _p(rstd)), "add_fwd")
+    return y, rout, rstd
+
+
+def add_bwd(g, x, residual, rstd, gamma, zero_centered=False, g_rout=None, mode=R64):
+    """(dh bf16, dgamma fp32): dh is the gradient of x and of residual."""
+    g, x, residual = _bf16_2d(g), _bf16_2d(x), _bf16_2d(residual)
+    T, D = x.shape
+    rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    if g_rout is not None:
+        g_rout = _bf16_2d(g_rout)
+    dh = np.empty((T, D), dtype=np.uint16)
+    dg = np.empty(D, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_add_bwd(mode, _p(g), _ld(g), _p(x), _ld(x), _p(residual),
+                                          _ld(residual), _p(rstd), _p(gamma),
+                                          int(zero_centered), T, D, _p(g_rout),
+                                          0 if g_rout is None else _ld(g_rout), _p(dh), D,
+                                          _p(dg)), "add_bwd")
+    return dh, dg
+
+
+def add_fwd_f64(x, residual, gamma, zero_centered=False, eps=1e-6):
+    """(y, h, rstd) in double, h = x + residual."""
+    x, residual, gamma = _f64(x), _f64(residual), _f64(gamma)
+    T, D = x.shape
+    y, h, rstd = np.empty((T, D)), np.empty((T, D)), np.empty(T)
+    _check(_load().oracle_rmsnorm_add_fwd_f64(_p(x), _p(residual), _p(gamma), int(zero_centered),
+                                              eps, T, D, _p(y), _p(h), _p(rstd)), "add_fwd_f64")
+    return y, h, rstd
+
+
+def add_bwd_f64(g, x, residual, gamma, zero_centered=False, eps=1e-6, g_rout=None):
+    """(dh, dgamma) in double for L = sum g*y + sum g_rout*h."""
+    g, x, residual, gamma = _f64(g), _f64(x), _f64(residual), _f64(gamma)
+    g_rout = None if g_rout is None else _f64(g_rout)
+    T, D = x.shape
+    dh, dg = np.empty((T, D)), np.empty(D)
+    _check(_load().oracle_rmsnorm_add_bwd_f64(_p(g), _p(x), _p(residual), _p(gamma),
+                                              int(zero_centered), eps, T, D, _p(g_rout), _p(dh),
+                                              _p(dg)), "add_bwd_f64")
+    return dh, dg

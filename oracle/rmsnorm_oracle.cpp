@@ -366,6 +366,101 @@ int oracle_rmsnorm_gated_dgamma(int mode, int activation, const uint16_t* g, int
   return 0;
 }
 
+// ---- fused add-RMSNorm ------------------------------------------------------
+// The decoder-norm residual path of [C1] ("fused_add_rms_norm, which
+// normalises the fp32 sum"): h = fp32(x) + fp32(residual), rounded once to
+// fp32; the norm of h; the updated residual stored as bf16(h).
+
+// One row of h = x + residual in fp32.
+static void row_sum_inputs(const uint16_t* xr, const uint16_t* rr, int64_t D, float* h) {
+  for (int64_t j = 0; j < D; ++j) h[j] = bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]);
+}
+
+// rstd of an fp32 row: ss = ascending sum of the fp32 squares fp32(h*h).
+static float row_rstd_f32(int mode, const float* h, int64_t D, float eps) {
+  Sum ss(mode);
+  for (int64_t j = 0; j < D; ++j) {
+    const float sq = h[j] * h[j];
+    ss.add(sq);
+  }
+  const float mean = ss.value() / static_cast<float>(D);
+  const float v = mean + eps;
+  return rsqrt_ref(v);
+}
+
+int oracle_rmsnorm_add_fwd(int mode, const uint16_t* x, int64_t ld_x, const uint16_t* residual,
+                           int64_t ld_res, const float* gamma, int zero_centered, float eps,
+                           int64_t T, int64_t D, uint16_t* y, int64_t ld_y,
+                           uint16_t* residual_out, int64_t ld_rout, float* rstd) {
+  if (bad_mode(mode) || T < 0 || D <= 0 || !gamma || bad_2d(x, ld_x, D) ||
+      bad_2d(residual, ld_res, D) || bad_2d(y, ld_y, D) || bad_2d(residual_out, ld_rout, D))
+    return -1;
+  float* h = new float[static_cast<size_t>(D)];
+  for (int64_t t = 0; t < T; ++t) {
+    row_sum_inputs(x + t * ld_x, residual + t * ld_res, D, h);
+    const float r = row_rstd_f32(mode, h, D, eps);
+    if (rstd) rstd[t] = r;
+    for (int64_t j = 0; j < D; ++j) {
+      const float n = row_normed(h[j], r, weight_eff(gamma, zero_centered, j));
+      y[t * ld_y + j] = f32_to_bf16(n);
+      residual_out[t * ld_rout + j] = f32_to_bf16(h[j]);
+    }
+  }
+  delete[] h;
+  return 0;
+}
+
+int oracle_rmsnorm_add_bwd(int mode, const uint16_t* g, int64_t ld_g, const uint16_t* x,
+                           int64_t ld_x, const uint16_t* residual, int64_t ld_res,
+                           const float* rstd, const float* gamma, int zero_centered, int64_t T,
+                           int64_t D, const uint16_t* g_rout, int64_t ld_gro, uint16_t* dh,
+                           int64_t ld_dh, float* dgamma) {
+  if (bad_mode(mode) || T < 0 || D <= 0 || !gamma || (T > 0 && !rstd) || bad_2d(g, ld_g, D) ||
+      bad_2d(x, ld_x, D) || bad_2d(residual, ld_res, D) || (!dh && !dgamma) ||
+      (dh && ld_dh < D) || (g_rout && ld_gro < D))
+    return -1;
+  float* h = new float[static_cast<size_t>(D)];
+  if (dh) {
+    for (int64_t t = 0; t < T; ++t) {
+      const uint16_t* gr = g + t * ld_g;
+      row_sum_inputs(x + t * ld_x, residual + t * ld_res, D, h);
+      const float r = rstd[t];
+      Sum s(mode);
+      for (int64_t i = 0; i < D; ++i) {
+        const float gw = bf16_to_f32(gr[i]) * weight_eff(gamma, zero_centered, i);
+        const float term = gw * h[i];
+        s.add(term);
+      }
+      const float r2 = r * r;
+      const float r3 = r2 * r;
+      const float r3s = r3 * s.value();
+      const float c = r3s / static_cast<float>(D);
+      for (int64_t k = 0; k < D; ++k) {
+        const float gw = bf16_to_f32(gr[k]) * weight_eff(gamma, zero_centered, k);
+        const float t1 = gw * r;
+        const float t2 = h[k] * c;
+        float d = t1 - t2;
+        if (g_rout) d = d + bf16_to_f32(g_rout[t * ld_gro + k]);
+        dh[t * ld_dh + k] = f32_to_bf16(d);
+      }
+    }
+  }
+  if (dgamma) {
+    for (int64_t j = 0; j < D; ++j) {
+      Sum acc(mode);
+      for (int64_t t = 0; t < T; ++t) {
+        const float hj = bf16_to_f32(x[t * ld_x + j]) + bf16_to_f32(residual[t * ld_res + j]);
+        const float gh = bf16_to_f32(g[t * ld_g + j]) * hj;
+        const float term = gh * rstd[t];
+        acc.add(term);
+      }
+      dgamma[j] = acc.value();
+    }
+  }
+  delete[] h;
+  return 0;
+}
+
 // ---- exact double forms ----------------------------------------------------
 
 static double weight_eff_d(const double* gamma, int zc, int64_t j) {
@@ -465,6 +560,34 @@ int oracle_rmsnorm_bwd_f64(const double* g, const double* x, const double* gamma
     }
   }
   return 0;
+}
+
+// Fused add-RMSNorm in double: h = x + residual exactly, y = h r w; the
+// residual output is h. For L = sum g * y + sum g_rout * h, the gradient
+// with respect to h (and so to x and to residual alike) is the plain
+// backward at h plus g_rout.
+int oracle_rmsnorm_add_fwd_f64(const double* x, const double* residual, const double* gamma,
+                               int zero_centered, double eps, int64_t T, int64_t D, double* y,
+                               double* h_out, double* rstd) {
+  if (!x || !residual || !gamma || !y || T < 0 || D <= 0) return -1;
+  double* h = new double[static_cast<size_t>(T * D)];
+  for (int64_t i = 0; i < T * D; ++i) h[i] = x[i] + residual[i];
+  const int rc = oracle_rmsnorm_fwd_f64(h, gamma, zero_centered, eps, T, D, y, rstd);
+  if (h_out)
+    for (int64_t i = 0; i < T * D; ++i) h_out[i] = h[i];
+  delete[] h;
+  return rc;
+}
+
+int oracle_rmsnorm_add_bwd_f64(const double* g, const double* x, const double* residual,
+                               const double* gamma, int zero_centered, double eps, int64_t T,
+                               int64_t D, const double* g_rout, double* dh, double* dgamma) {
+  if (!g || !x || !residual || !gamma || T < 0 || D <= 0 || (!dh && !dgamma)) return -1;
+  double* h = new double[static_cast<size_t>(T * D)];
+  for (int64_t i = 0; i < T * D; ++i) h[i] = x[i] + residual[i];
+  const int rc = oracle_rmsnorm_bwd_f64(g, h, gamma, zero_centered, eps, T, D, g_rout, dh, dgamma);
+  delete[] h;
+  return rc;
 }
 
 }  // extern "C"

@@ -181,6 +181,45 @@ int oracle_rmsnorm_gated_bwd_f64(int activation, const double* g,
                                  double eps, int64_t T, int64_t D, double* dx,
                                  double* dz, double* dgamma);
 
+/* ---- Fused add-RMSNorm -------------------------------------------------
+ * The residual form of the decoder norm ([C1]: fused_add_rms_norm
+ * "normalises the fp32 sum"; the page has no reference arithmetic for it,
+ * so this is the plainest reading):
+ *   h = fp32(x) + fp32(residual)          (one fp32 rounding)
+ *   ss = sum_j fp32(h_j * h_j)            (ascending; double in R64)
+ *   r = rsqrt(fp32(ss / D) + eps); y = bf16((h * r) * w_eff);
+ *   residual_out = bf16(h); rstd[t] = r (rstd may be NULL).
+ * Backward, h recomputed from x and residual exactly as above:
+ *   gw = g * w_eff; s = sum gw * h; c = ((r*r)*r)*s / D;
+ *   dh = bf16((gw * r - h * c) [+ g_rout])
+ * dh is the gradient of both x and residual; g_rout (may be NULL) is the
+ * gradient arriving at residual_out. dgamma[j] = sum over t ascending of
+ * fp32(fp32(g*h) * r). dh or dgamma may be NULL, not both. */
+int oracle_rmsnorm_add_fwd(int mode, const uint16_t* x, int64_t ld_x,
+                           const uint16_t* residual, int64_t ld_res,
+                           const float* gamma, int zero_centered, float eps,
+                           int64_t T, int64_t D, uint16_t* y, int64_t ld_y,
+                           uint16_t* residual_out, int64_t ld_rout, float* rstd);
+int oracle_rmsnorm_add_bwd(int mode, const uint16_t* g, int64_t ld_g,
+                           const uint16_t* x, int64_t ld_x,
+                           const uint16_t* residual, int64_t ld_res,
+                           const float* rstd, const float* gamma,
+                           int zero_centered, int64_t T, int64_t D,
+                           const uint16_t* g_rout, int64_t ld_gro, uint16_t* dh,
+                           int64_t ld_dh, float* dgamma);
+/* Exact forms (contiguous [T, D]): h = x + residual in double; h_out and
+ * rstd may be NULL; dh is the gradient of L = sum g*y + sum g_rout*h with
+ * respect to h (g_rout may be NULL). */
+int oracle_rmsnorm_add_fwd_f64(const double* x, const double* residual,
+                               const double* gamma, int zero_centered, double eps,
+                               int64_t T, int64_t D, double* y, double* h_out,
+                               double* rstd);
+int oracle_rmsnorm_add_bwd_f64(const double* g, const double* x,
+                               const double* residual, const double* gamma,
+                               int zero_centered, double eps, int64_t T,
+                               int64_t D, const double* g_rout, double* dh,
+                               double* dgamma);
+
 /* Test-only defect planting, so the tests can show that their checks catch
  * the two defects [MEG] fixes: 0 = none; 1 = the forward ignores the
  * zero-centred offset (the backward still honours it); 2 = the second term

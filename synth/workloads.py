@@ -3,7 +3,8 @@
 Every tensor is drawn from ``synth`` with a fixed (seed, stream) pair, so the
 same bytes are produced on any machine and for any thread count. Streams:
 1 = x, 2 = upstream gradient g, 3 = gamma, 4 = residual gradient,
-5 = gate z, 9 = outlier-row choice, 10 = outlier-row values.
+5 = gate z, 6 = residual input of the fused add, 9 = outlier-row choice,
+10 = outlier-row values.
 
 The workloads follow the pages' synthetic recipes: rows of ``randn``
 activations and gradients, fp32 weights drawn as ``1 + N(0, 0.1)`` (or
@@ -19,7 +20,7 @@ import numpy as np
 
 from . import normal_bf16, normal_f32, permutation, pick_rows
 
-S_X, S_G, S_GAMMA, S_GRES, S_Z, S_OUTLIER_PICK, S_OUTLIER_VAL = 1, 2, 3, 4, 5, 9, 10
+S_X, S_G, S_GAMMA, S_GRES, S_Z, S_RES_IN, S_OUTLIER_PICK, S_OUTLIER_VAL = 1, 2, 3, 4, 5, 6, 9, 10
 
 
 @dataclass
@@ -34,6 +35,7 @@ class Problem:
     g: np.ndarray | None = None          # bf16 bits [T, D]
     gres: np.ndarray | None = None       # bf16 bits [T, D]
     z: np.ndarray | None = None          # bf16 bits [T, D]
+    residual: np.ndarray | None = None   # bf16 bits [T, D] (fused add input)
     meta: dict = field(default_factory=dict)
 
 
@@ -43,7 +45,8 @@ def gamma_for(seed: int, D: int, zero_centered: bool) -> np.ndarray:
 
 
 def tiny(zero_centered: bool, T: int = 16, D: int = 128, seed: int = 1001,
-         with_gres: bool = False, with_gate: bool = False) -> Problem:
+         with_gres: bool = False, with_gate: bool = False,
+         with_residual: bool = False) -> Problem:
     """Small fixture: x, g ~ N(0,1); non-unit weights; eps = 1e-6."""
     p = Problem(
         name=f"tiny_T{T}_D{D}_zc{int(zero_centered)}", T=T, D=D, eps=1e-6,
@@ -53,6 +56,8 @@ def tiny(zero_centered: bool, T: int = 16, D: int = 128, seed: int = 1001,
         p.gres = normal_bf16(seed, S_GRES, T, D)
     if with_gate:
         p.z = normal_bf16(seed, S_Z, T, D)
+    if with_residual:
+        p.residual = normal_bf16(seed, S_RES_IN, T, D)
     return p
 
 
@@ -94,6 +99,21 @@ def gated(T: int = 262144, D: int = 128, seed: int = 3003,
                    x=_rows_of(seed, S_X, idx, D, 1.0),
                    g=_rows_of(seed, S_G, idx, D, 1.0) if with_grad else None,
                    z=_rows_of(seed, S_Z, idx, D, 1.0))
+
+
+def fused_add(T: int = 32768, D: int = 4096, seed: int = 6006,
+              rows: np.ndarray | None = None, with_gres: bool = True) -> Problem:
+    """Fused add-norm of a decoder layer: x (the sublayer output) and the
+    residual stream ~ N(0,1); g ~ N(0,1); the gradient arriving at the
+    updated residual (``gres``) ~ N(0,1); gamma = 1 + N(0,0.1); eps = 1e-6."""
+    idx = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    p = Problem(name=f"fused_add_T{T}_D{D}", T=T, D=D, eps=1e-6, zero_centered=False,
+                gamma=gamma_for(seed, D, False), x=_rows_of(seed, S_X, idx, D, 1.0),
+                g=_rows_of(seed, S_G, idx, D, 1.0),
+                residual=_rows_of(seed, S_RES_IN, idx, D, 1.0))
+    if with_gres:
+        p.gres = _rows_of(seed, S_GRES, idx, D, 1.0)
+    return p
 
 
 def large(T: int = 262144, D: int = 4096, seed: int = 4004,
