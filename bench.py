@@ -49,6 +49,9 @@ def algo_bytes(kind: str, T: int, D: int) -> int:
         "bwd_rows": T * (6 * D + 4) + 4 * D,       # g, x in, rstd in, dx out, gamma in
         "bwd_rows_gres": T * (8 * D + 4) + 4 * D,  # + residual gradient in
         "bwd_finish": 4 * D,                       # dgamma out
+        "add_fwd": T * (8 * D + 4) + 4 * D,        # x, residual in; y, residual_out, rstd out
+        "add_bwd_rows": T * (8 * D + 4) + 4 * D,   # g, x, residual, rstd in; dh out
+        "add_bwd_rows_gres": T * (10 * D + 4) + 4 * D,  # + gradient of residual_out in
     }[kind]
 
 
@@ -86,6 +89,11 @@ def make_inputs(workload: str, torch, dev, rows: int = 0):
         p = wl.large()
         desc = ("RMSNorm fwd+bwd with dgamma, T=262144, D=4096, zero-centred gamma, "
                 "g ~0.01 N(0,1), eps=1e-6")
+    elif workload == "add":
+        p = wl.fused_add(T=rows or 32768)
+        desc = (f"fused add-RMSNorm fwd+bwd with dgamma, T={p.T}, D=4096: h = x + residual "
+                "(fp32), bf16 x, residual, g, residual-output gradient ~N(0,1), fp32 "
+                "gamma=1+N(0,0.1), eps=1e-6")
     elif workload == "gated":
         p = wl.gated()
         desc = "SiLU-gated per-head RMSNorm forward, 262144 rows x D=128, x,z ~N(0,1)"
@@ -98,6 +106,8 @@ def make_inputs(workload: str, torch, dev, rows: int = 0):
         t["gres"] = d_bf16(p.gres)
     if p.z is not None:
         t["z"] = d_bf16(p.z)
+    if p.residual is not None:
+        t["residual"] = d_bf16(p.residual)
     return p, t, desc
 
 
@@ -119,17 +129,28 @@ def cpu_baseline(p, workload: str, seconds: float):
         a, b = ix[0], ix[-1] + 1
         if workload == "gated":
             _, r = oracle.gated_fwd(p.x[a:b], p.z[a:b], p.gamma, p.zero_centered, p.eps)
+        elif workload == "add":
+            _, _, r = oracle.add_fwd(p.x[a:b], p.residual[a:b], p.gamma, p.zero_centered, p.eps)
         else:
             _, r = oracle.fwd(p.x[a:b], p.gamma, p.zero_centered, p.eps)
         rstd[a:b] = r
 
     def dx_block(ix):
         a, b = ix[0], ix[-1] + 1
+        if workload == "add":
+            oracle.add_bwd(p.g[a:b], p.x[a:b], p.residual[a:b], rstd[a:b], p.gamma,
+                           p.zero_centered, None if p.gres is None else p.gres[a:b],
+                           want_dgamma=False)
+            return
         oracle.bwd_dx(p.g[a:b], p.x[a:b], rstd[a:b], p.gamma, p.zero_centered,
                       None if p.gres is None else p.gres[a:b])
 
     def dg_block(ix):
         a, b = ix[0], ix[-1] + 1
+        if workload == "add":
+            oracle.add_bwd(p.g[:, a:b], p.x[:, a:b], p.residual[:, a:b], rstd,
+                           p.gamma[a:b], p.zero_centered, want_dh=False)
+            return
         oracle.dgamma(p.g[:, a:b], p.x[:, a:b], rstd)
 
     passes = 0
@@ -150,7 +171,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="token", choices=["token", "token_gres", "large", "gated"])
+    ap.add_argument("--workload", default="token",
+                    choices=["token", "token_gres", "large", "gated", "add"])
     ap.add_argument("--rows", type=int, default=0,
                     help="token workloads: batch rows T (default 32768, the metric's size)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -185,6 +207,8 @@ def main():
     y = torch.empty_like(x)
     rstd = torch.empty(T, dtype=torch.float32, device=dev)
     gated = args.workload == "gated"
+    add = args.workload == "add"
+    rout = torch.empty_like(x) if add else None
     if not gated:
         g = t["g"]
         gres = t.get("gres")
@@ -204,6 +228,8 @@ def main():
             irn.rmsnorm_gated_fwd(x, t["z"], gamma, zc, eps, out=y)
             if dom is not None:
                 dom[1].record(stream)
+        elif add:
+            irn.rmsnorm_add_fwd(x, t["residual"], gamma, zc, eps, y=y, residual_out=rout, rstd=rstd)
         else:
             irn.rmsnorm_fwd(x, gamma, zc, eps, y=y, rstd=rstd)
         if evs is not None:
@@ -211,7 +237,11 @@ def main():
         if not gated:
             if dom is not None:
                 dom[0].record(stream)
-            irn.rmsnorm_bwd_rows(g, x, rstd, gamma, zc, g_residual=gres, dx=dx, workspace=ws)
+            if add:
+                irn.rmsnorm_add_bwd_rows(g, x, t["residual"], rstd, gamma, zc,
+                                         g_residual_out=gres, dh=dx, workspace=ws)
+            else:
+                irn.rmsnorm_bwd_rows(g, x, rstd, gamma, zc, g_residual=gres, dx=dx, workspace=ws)
             if dom is not None:
                 dom[1].record(stream)
             if evs is not None:
@@ -222,11 +252,11 @@ def main():
 
     # bitwise check before timing (two identical steps)
     step()
-    ref = [y.clone()] + ([] if gated else [rstd.clone(), dx.clone(), dgamma.clone()])
+    outs = [y] + ([] if gated else [rstd, dx, dgamma]) + ([rout] if add else [])
+    ref = [o.clone() for o in outs]
     step()
     torch.cuda.synchronize()
-    now = [y] + ([] if gated else [rstd, dx, dgamma])
-    if not all(torch.equal(a, b) for a, b in zip(ref, now)):
+    if not all(torch.equal(a, b) for a, b in zip(ref, outs)):
         raise SystemExit("repeat step is not bitwise identical")
     del ref
 
@@ -257,12 +287,14 @@ def main():
     wall = time.perf_counter() - t0
     dom_ms = sum(a.elapsed_time(b) for a, b in sampled.values()) / len(sampled)
 
-    fwd_kind = "gated_fwd" if gated else "fwd"
-    rows_kind = None if gated else ("bwd_rows_gres" if gres is not None else "bwd_rows")
+    fwd_kind = "gated_fwd" if gated else "add_fwd" if add else "fwd"
+    rows_kind = None if gated else (("add_" if add else "") +
+                                    ("bwd_rows_gres" if gres is not None else "bwd_rows"))
     step_bytes = algo_bytes(fwd_kind, T, D)
     if not gated:
         step_bytes += algo_bytes(rows_kind, T, D) + algo_bytes("bwd_finish", T, D)
-        dom, dom_bytes = "rmsnorm_bwd_rows_kernel", algo_bytes(rows_kind, T, D)
+        dom, dom_bytes = ("rmsnorm_bwd_rows_kernel" + (" (fused add)" if add else ""),
+                          algo_bytes(rows_kind, T, D))
     else:
         dom, dom_bytes = "rmsnorm_fwd_kernel (gated)", step_bytes
     ms_step = wall * 1e3 / args.steps

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 3
+#define RMSN_ABI_VERSION 4
 #define RMSN_MAX_D 8192
 #define RMSN_MAX_LD (1 << 24)
 
@@ -237,6 +237,60 @@ rmsn_status rmsnorm_gated_bwd(const uint16_t* g, int64_t ld_g,
                               uint16_t* dz, int64_t ld_dz, float* dgamma,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * Fused add-norm forward (RL-Kernel PR "C1: zero-centred RMSNorm references
+ * and CUDA kernel", decoder-norm note: all decoder norms but the first take a
+ * residual, through a fused add that normalises the fp32 sum; the page has
+ * no reference arithmetic, this is its plainest reading):
+ *   h = fp32(x) + fp32(residual)         (one fp32 rounding)
+ *   ss = sum_j fp32(h_j * h_j)           (fp64 sum along the fixed tree)
+ *   r = 1/sqrt(ss / D + eps) as in rmsnorm_fwd; rstd[t] = r (may be NULL)
+ *   y = bf16((h * r) * w_eff); residual_out = bf16(h), the updated residual.
+ * In place: y may be x itself and residual_out may be residual itself (the
+ * same pointer and row stride); any other overlap returns
+ * RMSN_ERR_ALIASING. Other errors as rmsnorm_fwd.
+ */
+rmsn_status rmsnorm_add_fwd(const uint16_t* x, int64_t ld_x,
+                            const uint16_t* residual, int64_t ld_res,
+                            const float* gamma, int zero_centered_gamma,
+                            float eps, int64_t T, int64_t D, uint16_t* y,
+                            int64_t ld_y, uint16_t* residual_out,
+                            int64_t ld_rout, float* rstd, void* stream);
+
+/*
+ * Backward of rmsnorm_add_fwd from the forward's saved rstd. h = x + residual
+ * is recomputed exactly as in the forward; with gw = g * w_eff,
+ * s = sum_j gw_j * h_j (fp32 products, fp64 sum), c = ((r*r)*r) * s / D:
+ *   dh = bf16(gw * r - h * c [+ g_residual_out])
+ * dh is the gradient of both x and residual (d h / d x = d h / d residual =
+ * 1); g_residual_out (may be NULL) is the gradient arriving at residual_out,
+ * added in fp32 before the one rounding. dgamma_j = sum over rows of
+ * (g_tj * h_tj) * r_t, chunked as rmsnorm_bwd's. dh or dgamma may be NULL,
+ * not both; gamma is required; the workspace rule is rmsnorm_bwd's. No
+ * output may overlap an input. Two kernels on `stream`.
+ */
+rmsn_status rmsnorm_add_bwd(const uint16_t* g, int64_t ld_g,
+                            const uint16_t* x, int64_t ld_x,
+                            const uint16_t* residual, int64_t ld_res,
+                            const float* rstd, const float* gamma,
+                            int zero_centered_gamma, int64_t T, int64_t D,
+                            const uint16_t* g_residual_out, int64_t ld_gro,
+                            uint16_t* dh, int64_t ld_dh, float* dgamma,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* The first stage of rmsnorm_add_bwd alone: dh (if non-NULL) and, if
+ * workspace is non-NULL, the dgamma partials that rmsnorm_bwd_finish turns
+ * into dgamma. */
+rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g,
+                                 const uint16_t* x, int64_t ld_x,
+                                 const uint16_t* residual, int64_t ld_res,
+                                 const float* rstd, const float* gamma,
+                                 int zero_centered_gamma, int64_t T, int64_t D,
+                                 const uint16_t* g_residual_out, int64_t ld_gro,
+                                 uint16_t* dh, int64_t ld_dh, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

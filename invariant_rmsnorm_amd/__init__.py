@@ -39,7 +39,7 @@ EXPORTED = (
     "rmsnorm_abi_version", "rmsnorm_status_string", "rmsnorm_fwd", "rmsnorm_residual_fwd",
     "rmsnorm_gated_fwd", "rmsnorm_gated_fwd_ex", "rmsnorm_bwd_workspace_bytes",
     "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
-    "rmsnorm_gated_bwd",
+    "rmsnorm_gated_bwd", "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_rows",
 )
 
 
@@ -73,6 +73,11 @@ def load():
         "rmsnorm_bwd_finish": ([vp, sz, i64, i64, vp, vp], i),
         "rmsnorm_gated_bwd": ([vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, i, vp, i64, vp, i64,
                                vp, vp, sz, vp], i),
+        "rmsnorm_add_fwd": ([vp, i64, vp, i64, vp, i, f, i64, i64, vp, i64, vp, i64, vp, vp], i),
+        "rmsnorm_add_bwd": ([vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp,
+                             vp, sz, vp], i),
+        "rmsnorm_add_bwd_rows": ([vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp,
+                                  i64, vp, sz, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -282,3 +287,60 @@ def rmsnorm_gated_bwd(g, x, z, rstd, gamma, zero_centered_gamma=False, *,
         int(zero_centered_gamma), T, D, int(activation), _ptr(dx), _ld(dx), _ptr(dz), _ld(dz),
         _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
     return dx, dz, dgamma
+
+
+def rmsnorm_add_fwd(x, residual, gamma, zero_centered_gamma=False, eps=1e-6, *, y=None,
+                    residual_out=None, rstd=None, want_rstd=True, stream=None):
+    """(y, residual_out, rstd or None): the norm of h = x + residual (fp32
+    sum) and the updated residual bf16(h). ``y=x`` and ``residual_out=residual``
+    run in place."""
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(residual, torch.bfloat16, "residual")
+    T, D = x.shape
+    y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device) if y is None else y
+    if residual_out is None:
+        residual_out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    if rstd is None and want_rstd:
+        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check("rmsnorm_add_fwd", load().rmsnorm_add_fwd(
+        _ptr(x), _ld(x), _ptr(residual), _ld(residual), _ptr(gamma), int(zero_centered_gamma),
+        eps, T, D, _ptr(y), _ld(y), _ptr(residual_out), _ld(residual_out), _ptr(rstd),
+        _stream(x, stream)))
+    return y, residual_out, rstd
+
+
+def rmsnorm_add_bwd(g, x, residual, rstd, gamma, zero_centered_gamma=False, *,
+                    g_residual_out=None, dh=None, dgamma=None, want_dh=True, want_dgamma=True,
+                    workspace=None, stream=None):
+    """(dh or None, dgamma or None): dh is the gradient of x and of residual."""
+    _dtype(g, torch.bfloat16, "g")
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(residual, torch.bfloat16, "residual")
+    T, D = x.shape
+    if dh is None and want_dh:
+        dh = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty(D, dtype=torch.float32, device=x.device)
+    ws, nbytes = (None, 0)
+    if dgamma is not None:
+        if workspace is None:
+            workspace, _ = workspace_for(T, D, x.device)
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    _check("rmsnorm_add_bwd", load().rmsnorm_add_bwd(
+        _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(residual), _ld(residual), _ptr(rstd), _ptr(gamma),
+        int(zero_centered_gamma), T, D, _ptr(g_residual_out), _ld(g_residual_out), _ptr(dh),
+        _ld(dh), _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
+    return dh, dgamma
+
+
+def rmsnorm_add_bwd_rows(g, x, residual, rstd, gamma, zero_centered_gamma=False, *,
+                         g_residual_out=None, dh=None, workspace=None, stream=None):
+    """Stage 1 of the fused add backward: dh (if given) and the dgamma
+    partials into ``workspace`` (if given); rmsnorm_bwd_finish completes it."""
+    T, D = x.shape
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("rmsnorm_add_bwd_rows", load().rmsnorm_add_bwd_rows(
+        _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(residual), _ld(residual), _ptr(rstd), _ptr(gamma),
+        int(zero_centered_gamma), T, D, _ptr(g_residual_out), _ld(g_residual_out), _ptr(dh),
+        _ld(dh), _ptr(workspace), nbytes, _stream(x, stream)))
+    return dh, workspace

@@ -22,7 +22,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "bwd.hip", "bwd_gated.hip"]
+HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "fwd_add.hip", "bwd.hip", "bwd_gated.hip", "bwd_add.hip"]
 CXX_SOURCES = ["api.cpp"]
 
 

@@ -113,8 +113,26 @@ rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64
 
   rmsn::FwdArgs a{x, ld_x, gated ? z : nullptr, ld_z, act, rounding == RMSN_GATED_ROUND_CAST,
                   gamma, zc != 0, eps, T, static_cast<int>(D), y, ld_y,
-                  residual ? res : nullptr, ld_res, rstd};
+                  residual ? res : nullptr, ld_res, rstd, nullptr, 0};
   return hip_status(rmsn::launch_fwd(a, stream));
+}
+
+// Aliasing of the fused add forward: y may be x itself and residual_out the
+// residual input itself (the same memory and row stride: each lane stores
+// only values it computed from elements it has already loaded at those
+// addresses, and rows do not overlap); any other overlap is rejected.
+bool add_fwd_alias(const uint16_t* x, int64_t ld_x, const uint16_t* rin, int64_t ld_rin,
+                   const float* gamma, int64_t T, int64_t D, const uint16_t* y, int64_t ld_y,
+                   const uint16_t* rout, int64_t ld_rout, const float* rstd) {
+  const Range X = mat_range(x, T, ld_x, D, 2), RI = mat_range(rin, T, ld_rin, D, 2),
+              G = vec_range(gamma, D, 4), Y = mat_range(y, T, ld_y, D, 2),
+              RO = mat_range(rout, T, ld_rout, D, 2), RS = vec_range(rstd, T, 4);
+  const bool y_in_place = y == x && ld_y == ld_x;
+  const bool r_in_place = rout == rin && ld_rout == ld_rin;
+  if ((!y_in_place && overlap(Y, X)) || overlap(Y, RI) || overlap(Y, G)) return true;
+  if ((!r_in_place && overlap(RO, RI)) || overlap(RO, X) || overlap(RO, G)) return true;
+  if (overlap(RS, X) || overlap(RS, RI) || overlap(RS, G)) return true;
+  return overlap(Y, RO) || overlap(Y, RS) || overlap(RO, RS);
 }
 
 size_t workspace_bytes(int64_t T, int64_t D) {
@@ -137,11 +155,13 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
                       const float* rstd, const float* gamma, int64_t T, int64_t D,
                       const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
                       bool want_part, const float* dgamma, void* ws, size_t ws_bytes,
-                      bool gated = false, const GateIO& gate = GateIO{}) {
+                      bool gated = false, const GateIO& gate = GateIO{},
+                      const uint16_t* rin = nullptr, int64_t ld_rin = 0, bool add = false) {
   if (T < 0) return RMSN_ERR_SHAPE;
   RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(g, ld_g, T, D, true));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
+  if (add) RMSN_TRY(check_mat(rin, ld_rin, T, D, true));
   RMSN_TRY(check_mat(gres, ld_gres, T, D, false));
   RMSN_TRY(check_mat(dx, ld_dx, T, D, false));
   if (gated) {
@@ -163,7 +183,8 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
                         vec_range(dgamma, D, 4), mat_range(gate.dz, T, gate.ld_dz, D, 2)};
   const Range ins[] = {mat_range(g, T, ld_g, D, 2), mat_range(x, T, ld_x, D, 2),
                        vec_range(rstd, T, 4), vec_range(gamma, D, 4),
-                       mat_range(gres, T, ld_gres, D, 2), mat_range(gate.z, T, gate.ld_z, D, 2)};
+                       mat_range(gres, T, ld_gres, D, 2), mat_range(gate.z, T, gate.ld_z, D, 2),
+                       mat_range(add ? rin : nullptr, T, ld_rin, D, 2)};
   if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
   return RMSN_OK;
 }
@@ -171,12 +192,13 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
 rmsn::BwdArgs bwd_args(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
                        const float* rstd, const float* gamma, int zc, int64_t T, int64_t D,
                        const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
-                       void* ws, const GateIO& gate = GateIO{}, int act = 0) {
+                       void* ws, const GateIO& gate = GateIO{}, int act = 0,
+                       const uint16_t* rin = nullptr, int64_t ld_rin = 0) {
   const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
   return rmsn::BwdArgs{g, ld_g, x, ld_x, rstd, gamma, zc != 0, T, static_cast<int>(D),
                        dx ? gres : nullptr, ld_gres, dx, ld_dx, static_cast<float*>(ws),
                        p.chunks, p.group_blocks, gate.z, gate.ld_z, act, gate.dz, gate.ld_dz,
-                       T * D * 2 > rmsn::kCacheBytes};
+                       T * D * 2 > rmsn::kCacheBytes, rin, ld_rin};
 }
 
 // dgamma from the workspace partials (zeros when T == 0).
@@ -316,6 +338,67 @@ rmsn_status rmsnorm_gated_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x
     const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
                                      nullptr, 0, dx, ld_dx,
                                      dgamma != nullptr ? workspace : nullptr, gate, activation);
+    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
+  }
+  if (dgamma == nullptr) return RMSN_OK;
+  return finish_dgamma(workspace, T, D, dgamma, stream);
+}
+
+rmsn_status rmsnorm_add_fwd(const uint16_t* x, int64_t ld_x, const uint16_t* residual,
+                            int64_t ld_res, const float* gamma, int zero_centered_gamma, float eps,
+                            int64_t T, int64_t D, uint16_t* y, int64_t ld_y, uint16_t* residual_out,
+                            int64_t ld_rout, float* rstd, void* stream) {
+  if (T < 0) return RMSN_ERR_SHAPE;
+  RMSN_TRY(check_D(D));
+  RMSN_TRY(check_mat(x, ld_x, T, D, true));
+  RMSN_TRY(check_mat(residual, ld_res, T, D, true));
+  RMSN_TRY(check_mat(y, ld_y, T, D, true));
+  RMSN_TRY(check_mat(residual_out, ld_rout, T, D, true));
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return RMSN_ERR_EPS;
+  if (T == 0) return RMSN_OK;
+  RMSN_TRY(check_f32(gamma, 16, true));
+  RMSN_TRY(check_f32(rstd, 4, false));
+  if (add_fwd_alias(x, ld_x, residual, ld_res, gamma, T, D, y, ld_y, residual_out, ld_rout, rstd))
+    return RMSN_ERR_ALIASING;
+  const rmsn::FwdArgs a{x, ld_x, nullptr, 0, 0, 0, gamma, zero_centered_gamma != 0, eps, T,
+                        static_cast<int>(D), y, ld_y, residual_out, ld_rout, rstd, residual,
+                        ld_res};
+  return hip_status(rmsn::launch_fwd(a, stream));
+}
+
+rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                                 const uint16_t* residual, int64_t ld_res, const float* rstd,
+                                 const float* gamma, int zero_centered_gamma, int64_t T, int64_t D,
+                                 const uint16_t* g_residual_out, int64_t ld_gro, uint16_t* dh,
+                                 int64_t ld_dh, void* workspace, size_t workspace_bytes_,
+                                 void* stream) {
+  if (dh == nullptr && workspace == nullptr) return RMSN_ERR_NULL;
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, g_residual_out, ld_gro, dh, ld_dh,
+                     workspace != nullptr, nullptr, workspace, workspace_bytes_, false, GateIO{},
+                     residual, ld_res, true));
+  if (T == 0) return RMSN_OK;
+  const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
+                                   g_residual_out, ld_gro, dh, ld_dh, workspace, GateIO{}, 0,
+                                   residual, ld_res);
+  return hip_status(rmsn::launch_bwd_rows(a, stream));
+}
+
+rmsn_status rmsnorm_add_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                            const uint16_t* residual, int64_t ld_res, const float* rstd,
+                            const float* gamma, int zero_centered_gamma, int64_t T, int64_t D,
+                            const uint16_t* g_residual_out, int64_t ld_gro, uint16_t* dh,
+                            int64_t ld_dh, float* dgamma, void* workspace, size_t workspace_bytes_,
+                            void* stream) {
+  if (dh == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
+  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, g_residual_out, ld_gro, dh, ld_dh,
+                     dgamma != nullptr, dgamma, workspace, workspace_bytes_, false, GateIO{},
+                     residual, ld_res, true));
+  if (T > 0) {
+    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
+                                     g_residual_out, ld_gro, dh, ld_dh,
+                                     dgamma != nullptr ? workspace : nullptr, GateIO{}, 0,
+                                     residual, ld_res);
     RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
   }
   if (dgamma == nullptr) return RMSN_OK;

@@ -1,6 +1,6 @@
 // Backward launchers: the plain and residual-gradient rows kernels (the
-// template is in bwd_kernel.hpp; the gated forms are in bwd_gated.hip) and
-// the dgamma finish kernel.
+// template is in bwd_kernel.hpp; the gated forms are in bwd_gated.hip, the
+// fused add-norm forms in bwd_add.hip) and the dgamma finish kernel.
 //
 // Finish: dgamma[j] = a fixed tree over 16 slices, each slice an ascending
 // sum over a contiguous range of the chunk partials. The grouping depends on
@@ -63,6 +63,7 @@ __global__ __launch_bounds__(64 * kFinishWaves) void rmsnorm_bwd_finish_kernel(
 int launch_bwd_rows(const BwdArgs& a, void* stream) {
   if (a.T == 0 || a.chunks == 0) return 0;
   if (a.z != nullptr) return launch_bwd_rows_gated(a, stream);
+  if (a.rin != nullptr) return launch_bwd_rows_add(a, stream);
   const RowGeom g = row_geom(a.D);
   const bwd_detail::RowsLaunch f =
       a.gres != nullptr ? bwd_detail::pick<kBwdGres>(g) : bwd_detail::pick<kBwdPlain>(g);

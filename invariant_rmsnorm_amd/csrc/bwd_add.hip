@@ -1,0 +1,18 @@
+// Fused add-norm backward launchers: dh (the gradient of both x and the
+// residual input, plus the gradient arriving at the updated residual) and
+// the dgamma partials, with h = x + residual recomputed in fp32 (RL-Kernel PR
+// "C1: zero-centred RMSNorm references and CUDA kernel", decoder-norm note).
+// The kernel template is in bwd_kernel.hpp.
+#include "bwd_kernel.hpp"
+
+namespace rmsn {
+
+int launch_bwd_rows_add(const BwdArgs& a, void* stream) {
+  const RowGeom g = row_geom(a.D);
+  const bwd_detail::RowsLaunch f =
+      a.gres != nullptr ? bwd_detail::pick<kBwdAddGres>(g) : bwd_detail::pick<kBwdAdd>(g);
+  if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);
+  return f(a, stream);
+}
+
+}  // namespace rmsn

@@ -38,8 +38,14 @@
 
 namespace rmsn {
 
-// What the rows kernel computes besides plain dx / dgamma.
-enum : int { kBwdPlain = 0, kBwdGres = 1, kBwdGatedSilu = 2, kBwdGatedSigmoid = 3 };
+// What the rows kernel computes besides plain dx / dgamma. The fused add
+// modes take h = x + rin (fp32) in place of x and write the one gradient dh
+// of both inputs; kBwdAddGres adds the gradient arriving at the updated
+// residual (in the gres slot).
+enum : int {
+  kBwdPlain = 0, kBwdGres = 1, kBwdGatedSilu = 2, kBwdGatedSigmoid = 3,
+  kBwdAdd = 4, kBwdAddGres = 5
+};
 
 // Register plan by geometry (chosen by measurement at D=4096; results do not
 // depend on it). The kernel runs one 4-wave workgroup per compute unit, so
@@ -48,16 +54,16 @@ enum : int { kBwdPlain = 0, kBwdGres = 1, kBwdGatedSilu = 2, kBwdGatedSigmoid = 
 // reused by the second. Beyond that the registers would spill, so the
 // weights move to LDS and the second pass unpacks the raw vectors again.
 // The gated form holds a third input row (z), so it goes lean from 11.
-constexpr bool bwd_lean(int vpl, bool gated) { return vpl >= (gated ? 11 : 13); }
+constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_inputs ? 11 : 13); }
 constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 5 ? 1 : 2; }
 
 // LDS floats the rows kernel needs: the weights when held in LDS (one float4
 // pair per vector slot, laid out so that consecutive lanes read consecutive
 // 16 bytes) and, after the rows are done, two rows of D floats for the wave
 // merge (which reuse the same space).
-inline size_t bwd_rows_lds_floats(int D, bool want_part, bool gated) {
+inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
   const RowGeom g = row_geom(D);
-  const size_t w = bwd_lean(g.vpl, gated) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
+  const size_t w = bwd_lean(g.vpl, three_inputs) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
   const size_t m = want_part ? 2 * static_cast<size_t>(D) : 0;
   return w > m ? w : m;
 }
@@ -65,14 +71,15 @@ inline size_t bwd_rows_lds_floats(int D, bool want_part, bool gated) {
 template <int LPR, int VPL, bool MASKED, int MODE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL))))
 void rmsnorm_bwd_rows_kernel(BwdArgs a) {
-  constexpr bool GRES = MODE == kBwdGres;
+  constexpr bool ADD = MODE == kBwdAdd || MODE == kBwdAddGres;
+  constexpr bool GRES = MODE == kBwdGres || MODE == kBwdAddGres;
   constexpr bool GATED = MODE == kBwdGatedSilu || MODE == kBwdGatedSigmoid;
   constexpr int ACT = MODE == kBwdGatedSigmoid ? kGateSigmoid : kGateSilu;
   constexpr int RPW = 64 / LPR;
   constexpr int U = bwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
-  constexpr bool LEAN = bwd_lean(VPL, GATED);
+  constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
@@ -153,6 +160,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     u32x4 gq[U][VPL], xq[U][VPL];
     u32x4 rq_res[GRES ? U : 1][GRES ? VPL : 1];  // residual-branch gradient
     u32x4 zq[GATED ? U : 1][GATED ? VPL : 1];     // gate input
+    u32x4 hq[ADD ? U : 1][ADD ? VPL : 1];         // fused add: residual input
     float rq[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -185,7 +193,28 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16<kLoadStream>(rz, voff(v, a.ld_z));
       }
+      if constexpr (ADD) {  // the forward read it too: x's policy
+        const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
+        if (a.x_stream) {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) hq[u][v] = buf_load16<kLoadStream>(rh, voff(v, a.ld_rin));
+        } else {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) hq[u][v] = buf_load16(rh, voff(v, a.ld_rin));
+        }
+      }
     }
+    // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
+    // rounding, as in the forward).
+    auto row_values = [&](int u, int v, float (&f)[8]) {
+      unpack8(xq[u][v], f);
+      if constexpr (ADD) {
+        float rf[8];
+        unpack8(hq[u][v], rf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = f[k] + rf[k];
+      }
+    };
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -207,7 +236,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         if (MASKED && v * LPR + l >= nv) continue;  // no such vector (weights unset)
         float gf[8], xf[8], w8[8];
         unpack8(gq[u][v], gf);
-        unpack8(xq[u][v], xf);
+        row_values(u, v, xf);
         weights(wbase, v, w8);
         if constexpr (GATED) {
           float zf[8], dz8[8];
@@ -247,6 +276,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
           opaque(gq[u][v]);
           opaque(xq[u][v]);
           if constexpr (GATED) opaque(zq[u][v]);
+          if constexpr (ADD) opaque(hq[u][v]);
         }
         asm("" : "+v"(wbase));
       }
@@ -258,7 +288,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         if (MASKED && v * LPR + l >= nv) continue;
         float gf[8], xf[8], w8[8], o[8];
         unpack8(gq[u][v], gf);
-        unpack8(xq[u][v], xf);
+        row_values(u, v, xf);
         weights(wbase, v, w8);
         if constexpr (GATED) {
           float zf[8];
@@ -352,8 +382,9 @@ namespace bwd_detail {
 
 template <int LPR, int VPL, bool MASKED, int MODE>
 int launch_inst(const BwdArgs& a, void* stream) {
-  constexpr bool GATED = MODE == kBwdGatedSilu || MODE == kBwdGatedSigmoid;
-  const size_t lds = sizeof(float) * bwd_rows_lds_floats(a.D, a.part != nullptr, GATED);
+  constexpr bool THREE = MODE == kBwdGatedSilu || MODE == kBwdGatedSigmoid || MODE == kBwdAdd ||
+                         MODE == kBwdAddGres;
+  const size_t lds = sizeof(float) * bwd_rows_lds_floats(a.D, a.part != nullptr, THREE);
   hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, MODE>),
                      dim3(static_cast<unsigned>(a.chunks)), dim3(kBlock), lds,
                      static_cast<hipStream_t>(stream), a);

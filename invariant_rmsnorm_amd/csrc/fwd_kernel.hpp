@@ -33,20 +33,24 @@ namespace rmsn {
 
 // GATE: 0 = no gate; otherwise 1 + activation + 2 * cast, where cast selects
 // the convention that rounds the normalised and the weighted value to bf16
-// before the next multiply.
+// before the next multiply; kFwdAdd = the fused add-norm.
 constexpr int fwd_gate_code(bool gated, int act, bool cast) { return gated ? 1 + act + 2 * cast : 0; }
+constexpr int kFwdAdd = 5;
 
 template <int LPR, int VPL, bool MASKED, int GATE>
 __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
-  constexpr bool GATED = GATE != 0;
+  constexpr bool ADD = GATE == kFwdAdd;
+  constexpr bool GATED = GATE != 0 && !ADD;
   constexpr int ACT = GATED ? (GATE - 1) & 1 : 0;
   constexpr bool CAST = GATED && (GATE - 1) >= 2;
   constexpr int RPW = 64 / LPR;
   constexpr int U = fwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
-  constexpr int ZU = GATED ? U : 1;
-  constexpr int ZV = GATED ? VPL : 1;
+  // second input stream: the gate z, or the fused add's residual input
+  constexpr bool TWO = GATED || ADD;
+  constexpr int ZU = TWO ? U : 1;
+  constexpr int ZV = TWO ? VPL : 1;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -82,6 +86,22 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16(rz, voff(v, a.ld_z));
       }
+      if constexpr (ADD) {
+        const auto rr = rows_rsrc(a.rin, first, a.T, RPW, a.ld_rin, a.D);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16(rr, voff(v, a.ld_rin));
+      }
+    }
+  };
+  // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
+  // rounding).
+  auto row_values = [&](const u32x4& xv, const u32x4& rv, float (&f)[8]) {
+    unpack8(xv, f);
+    if constexpr (ADD) {
+      float rf[8];
+      unpack8(rv, rf);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) f[k] = f[k] + rf[k];
     }
   };
 
@@ -92,12 +112,13 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
       const int64_t row = first + slot;
 
       // sum of squares: this lane's elements in (vector, element) order, then
-      // the row's fixed butterfly. Squares of bf16 values are exact in fp32.
+      // the row's fixed butterfly. Squares of bf16 values are exact in fp32;
+      // those of the fused add's h are rounded to fp32 once.
       acc_t ssa = 0;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         float f[8];
-        unpack8(xq[u][v], f);
+        row_values(xq[u][v], zq[ADD ? u : 0][ADD ? v : 0], f);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float sq = f[k] * f[k];
@@ -107,7 +128,10 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
       const float ss = static_cast<float>(row_sum<LPR>(ssa));
       const float r = rstd_of(ss, Df, a.eps);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) opaque(xq[u][v]);
+      for (int v = 0; v < VPL; ++v) {
+        opaque(xq[u][v]);
+        if constexpr (ADD) opaque(zq[u][v]);
+      }
 
       if (a.rstd != nullptr && l == 0 && row < a.T) a.rstd[row] = r;
       // rows past T: the resources below are empty and drop the stores
@@ -115,7 +139,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         float f[8], o[8];
-        unpack8(xq[u][v], f);
+        row_values(xq[u][v], zq[ADD ? u : 0][ADD ? v : 0], f);
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] = f[k] * r;
         if constexpr (CAST) round8_bf16(o);
@@ -131,9 +155,18 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
         buf_store16_nt(pack8(o), ry, voff(v, a.ld_y));
       }
       if (a.res != nullptr) {
+        // residual output: a byte copy of x, or for the fused add bf16(h)
         const auto rr = rows_rsrc(a.res, first, a.T, RPW, a.ld_res, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) buf_store16_nt(xq[u][v], rr, voff(v, a.ld_res));
+        for (int v = 0; v < VPL; ++v) {
+          if constexpr (ADD) {
+            float f[8];
+            row_values(xq[u][v], zq[u][v], f);
+            buf_store16_nt(pack8(f), rr, voff(v, a.ld_res));
+          } else {
+            buf_store16_nt(xq[u][v], rr, voff(v, a.ld_res));
+          }
+        }
       }
     }
   };

@@ -22,9 +22,11 @@ struct FwdArgs {
   int D;
   uint16_t* y;
   int64_t ld_y;
-  uint16_t* res;  // residual copy, or nullptr
+  uint16_t* res;  // residual copy (bf16(x + rin) when rin is set), or nullptr
   int64_t ld_res;
   float* rstd;  // or nullptr
+  const uint16_t* rin;  // fused add: residual input, normalise x + rin; or nullptr
+  int64_t ld_rin;
 };
 
 struct BwdArgs {
@@ -51,13 +53,17 @@ struct BwdArgs {
   uint16_t* dz;  // or nullptr
   int64_t ld_dz;
   int x_stream;  // read x with the non-temporal hint (set by the launcher)
+  const uint16_t* rin;  // fused add: residual input (h = x + rin); or nullptr
+  int64_t ld_rin;
 };
 
 // Each returns 0 on success or the HIP error code of a refused launch.
 int launch_fwd(const FwdArgs& a, void* stream);
 int launch_fwd_gated(const FwdArgs& a, void* stream);  // a.z != nullptr
+int launch_fwd_add(const FwdArgs& a, void* stream);    // a.rin != nullptr
 int launch_bwd_rows(const BwdArgs& a, void* stream);
 int launch_bwd_rows_gated(const BwdArgs& a, void* stream);  // a.z != nullptr
+int launch_bwd_rows_add(const BwdArgs& a, void* stream);    // a.rin != nullptr
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
 
 }  // namespace rmsn

@@ -362,16 +362,18 @@ def add_fwd(x, residual, gamma, zero_centered=False, eps=1e-6, mode=R64):
     return y, rout, rstd
 
 
-def add_bwd(g, x, residual, rstd, gamma, zero_centered=False, g_rout=None, mode=R64):
-    """(dh bf16, dgamma fp32): dh is the gradient of x and of residual."""
+def add_bwd(g, x, residual, rstd, gamma, zero_centered=False, g_rout=None, mode=R64,
+            want_dh=True, want_dgamma=True):
+    """(dh bf16, dgamma fp32) (each None unless wanted): dh is the gradient of
+    x and of residual."""
     g, x, residual = _bf16_2d(g), _bf16_2d(x), _bf16_2d(residual)
     T, D = x.shape
     rstd = np.ascontiguousarray(rstd, dtype=np.float32)
     gamma = np.ascontiguousarray(gamma, dtype=np.float32)
     if g_rout is not None:
         g_rout = _bf16_2d(g_rout)
-    dh = np.empty((T, D), dtype=np.uint16)
-    dg = np.empty(D, dtype=np.float32)
+    dh = np.empty((T, D), dtype=np.uint16) if want_dh else None
+    dg = np.empty(D, dtype=np.float32) if want_dgamma else None
     _check(_load().oracle_rmsnorm_add_bwd(mode, _p(g), _ld(g), _p(x), _ld(x), _p(residual),
                                           _ld(residual), _p(rstd), _p(gamma),
                                           int(zero_centered), T, D, _p(g_rout),

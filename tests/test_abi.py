@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 3
+    assert irn.rmsnorm_abi_version() == 4
 
 
 def test_status_strings():
@@ -254,3 +254,79 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(irn, "LIB_PATH", tmp_path / "missing.so")
     with pytest.raises(ImportError):
         irn.load()
+
+
+# ---- fused add-norm ---------------------------------------------------------------
+
+F = A + (7 << 36)
+
+
+def add_fwd(**kw):
+    a = dict(x=A, ld_x=4096, res=B, ld_res=4096, gamma=GAM, zc=0, eps=1e-6, T=8, D=4096, y=C,
+             ld_y=4096, rout=E, ld_rout=4096, rstd=RS)
+    a.update(kw)
+    return irn.load().rmsnorm_add_fwd(a["x"], a["ld_x"], a["res"], a["ld_res"], a["gamma"],
+                                      a["zc"], a["eps"], a["T"], a["D"], a["y"], a["ld_y"],
+                                      a["rout"], a["ld_rout"], a["rstd"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), irn.RMSN_ERR_NULL),
+    (dict(res=None), irn.RMSN_ERR_NULL),
+    (dict(y=None), irn.RMSN_ERR_NULL),
+    (dict(rout=None), irn.RMSN_ERR_NULL),
+    (dict(gamma=None), irn.RMSN_ERR_NULL),
+    (dict(T=-1), irn.RMSN_ERR_SHAPE),
+    (dict(ld_res=4000), irn.RMSN_ERR_SHAPE),
+    (dict(D=100, ld_x=104, ld_res=104, ld_y=104, ld_rout=104), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(res=B + 2), irn.RMSN_ERR_MISALIGNED),
+    (dict(rout=E + 8), irn.RMSN_ERR_MISALIGNED),
+    (dict(eps=-1.0), irn.RMSN_ERR_EPS),
+    (dict(y=B), irn.RMSN_ERR_ALIASING),                     # y over the residual input
+    (dict(rout=A), irn.RMSN_ERR_ALIASING),                  # residual_out over x
+    (dict(y=A + 2 * 4096 * 2), irn.RMSN_ERR_ALIASING),      # y over x, shifted a row
+    (dict(y=A, ld_y=4104), irn.RMSN_ERR_ALIASING),          # same base, other stride
+    (dict(rout=B + 16), irn.RMSN_ERR_ALIASING),             # residual_out shifted
+    (dict(y=E), irn.RMSN_ERR_ALIASING),                     # the two outputs
+    (dict(rstd=A + 64), irn.RMSN_ERR_ALIASING),
+    (dict(x=A, res=A, y=A), irn.RMSN_ERR_ALIASING),         # in place over x, which is res too
+    (dict(y=A, rout=A), irn.RMSN_ERR_ALIASING),             # both outputs on x
+])
+def test_add_forward_rejections(kw, code):
+    # (accepted in-place calls launch kernels, so they are tested on the GPU)
+    assert add_fwd(**kw) == code
+
+
+def add_bwd(**kw):
+    a = dict(g=A, ld_g=4096, x=B, ld_x=4096, res=F, ld_res=4096, rstd=RS, gamma=GAM, zc=0,
+             T=1000, D=4096, gro=None, ld_gro=0, dh=C, ld_dh=4096, dgamma=E, ws=W,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return irn.load().rmsnorm_add_bwd(a["g"], a["ld_g"], a["x"], a["ld_x"], a["res"], a["ld_res"],
+                                      a["rstd"], a["gamma"], a["zc"], a["T"], a["D"], a["gro"],
+                                      a["ld_gro"], a["dh"], a["ld_dh"], a["dgamma"], a["ws"],
+                                      a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dh=None, dgamma=None), irn.RMSN_ERR_NULL),
+    (dict(res=None), irn.RMSN_ERR_NULL),
+    (dict(res=F + 4), irn.RMSN_ERR_MISALIGNED),
+    (dict(ld_res=100), irn.RMSN_ERR_SHAPE),
+    (dict(dh=F), irn.RMSN_ERR_ALIASING),                    # dh over the residual input
+    (dict(dh=B), irn.RMSN_ERR_ALIASING),                    # dh over x (no in-place backward)
+    (dict(ws=F), irn.RMSN_ERR_ALIASING),
+    (dict(gro=F, ld_gro=4096, dh=F), irn.RMSN_ERR_ALIASING),
+    (dict(ws=None), irn.RMSN_ERR_WORKSPACE),
+    (dict(T=-2), irn.RMSN_ERR_SHAPE),
+])
+def test_add_backward_rejections(kw, code):
+    assert add_bwd(**kw) == code
+
+
+def test_add_backward_rows_rejections():
+    lib = irn.load()
+    args = [A, 4096, B, 4096, F, 4096, RS, GAM, 0, 1000, 4096, None, 0]
+    assert lib.rmsnorm_add_bwd_rows(*args, None, 4096, None, 0, None) == irn.RMSN_ERR_NULL
+    assert lib.rmsnorm_add_bwd_rows(*args, F, 4096, None, 0, None) == irn.RMSN_ERR_ALIASING
+    assert lib.rmsnorm_add_bwd_rows(*args, C, 4096, W, 16, None) == irn.RMSN_ERR_WORKSPACE
