@@ -43,7 +43,7 @@
  * alone.
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
- * contiguous. Supported: D a multiple of 8 with 8 <= D <= 8192, and
+ * contiguous. Supported: D a multiple of 8 with 8 <= D <= 32768, and
  * D <= ld <= 2^24 (RMSN_MAX_LD). Every bf16
  * base pointer and ld * 2 bytes must be multiples of 16 bytes; gamma,
  * dgamma and the workspace must be 16-byte aligned; rstd 4-byte aligned.
@@ -73,8 +73,8 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 4
-#define RMSN_MAX_D 8192
+#define RMSN_ABI_VERSION 5
+#define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
 typedef enum rmsn_status {

@@ -219,7 +219,7 @@ const char* rmsnorm_status_string(int status) {
     case RMSN_OK: return "RMSN_OK";
     case RMSN_ERR_NULL: return "RMSN_ERR_NULL: a required pointer is NULL";
     case RMSN_ERR_SHAPE: return "RMSN_ERR_SHAPE: T < 0, D <= 0, ld < D or ld > 2^24";
-    case RMSN_ERR_UNSUPPORTED_D: return "RMSN_ERR_UNSUPPORTED_D: D must be a multiple of 8 in [8, 8192]";
+    case RMSN_ERR_UNSUPPORTED_D: return "RMSN_ERR_UNSUPPORTED_D: D must be a multiple of 8 in [8, 32768]";
     case RMSN_ERR_MISALIGNED: return "RMSN_ERR_MISALIGNED: pointers and row strides must be 16-byte aligned";
     case RMSN_ERR_EPS: return "RMSN_ERR_EPS: eps must be finite and >= 0";
     case RMSN_ERR_ALIASING: return "RMSN_ERR_ALIASING: an output overlaps an input or another output";

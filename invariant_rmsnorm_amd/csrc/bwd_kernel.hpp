@@ -64,7 +64,10 @@ constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 5 ? 1 : 2; }
 inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
   const RowGeom g = row_geom(D);
   const size_t w = bwd_lean(g.vpl, three_inputs) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
-  const size_t m = want_part ? 2 * static_cast<size_t>(D) : 0;
+  // merge space: 2 rows of D floats with one wave per row, 1 with two, none
+  // with four
+  const int wpr = waves_per_row(g.lpr);
+  const size_t m = want_part ? static_cast<size_t>(D) * (wpr == 1 ? 2 : wpr == 2 ? 1 : 0) : 0;
   return w > m ? w : m;
 }
 
@@ -75,17 +78,24 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr bool GRES = MODE == kBwdGres || MODE == kBwdAddGres;
   constexpr bool GATED = MODE == kBwdGatedSilu || MODE == kBwdGatedSigmoid;
   constexpr int ACT = MODE == kBwdGatedSigmoid ? kGateSigmoid : kGateSilu;
-  constexpr int RPW = 64 / LPR;
+  constexpr int RPW = rows_per_wave(LPR);
+  constexpr int WPR = waves_per_row(LPR);
   constexpr int U = bwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
-  constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
+  constexpr int ROWS_BLOCK = rows_per_block(LPR, U);
+  static_assert(WPR == 1 || (U == 1 && VPL >= kMinVplMulti), "multi-wave rows: one row per step");
   constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int slot = lane / LPR;
-  const int l = lane % LPR;
+  // the wave's row group and, within its row, the lane's index l (rows
+  // spread over WPR waves: l = 64 * (wave % WPR) + lane)
+  const int group = wave / WPR;
+  const int slot = LPR >= 64 ? 0 : lane / LPR;
+  const int l = LPR >= 64 ? (wave % WPR) * 64 + lane : lane % LPR;
+  __shared__ double xch[2][kWaves];  // row-sum exchange of multi-wave rows
+  int xstep = 0;
   const int nv = a.D >> 3;
   const float Df = static_cast<float>(a.D);
   const bool want_part = a.part != nullptr;
@@ -164,7 +174,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     float rq[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t first = step + wave * ROWS_WAVE + u * RPW;
+      const int64_t first = step + group * ROWS_WAVE + u * RPW;
       rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
       const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
       const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
@@ -218,7 +228,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t first = step + wave * ROWS_WAVE + u * RPW;
+      const int64_t first = step + group * ROWS_WAVE + u * RPW;
       const float r = rq[u];
       int wbase = 0;
       if constexpr (LEAN) asm("" : "+v"(wbase));
@@ -264,7 +274,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         // whole row up front and the kernel runs ~10% slower (measured)
         __builtin_amdgcn_sched_barrier(0);
       }
-      const float s = static_cast<float>(row_sum<LPR>(sa));
+      const float s = static_cast<float>(row_total<LPR>(sa, xch, xstep));
       const float rr = r * r;
       const float r3 = rr * r;
       const float r3s = r3 * s;
@@ -326,54 +336,85 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[v][k] = acc[v][k] + __shfl_xor(acc[v][k], m);
 
-  // Waves: ((w0 + w2) + (w1 + w3)) through two LDS rows of D floats (the
-  // weights' space is reused, hence the barrier first).
-  __syncthreads();
+  auto put = [&](float* d, int v) {
+    *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+  };
+  auto add_from = [&](const float* d, int v) {
+    const float4 p0 = *reinterpret_cast<const float4*>(d);
+    const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
+    acc[v][0] = acc[v][0] + p0.x; acc[v][1] = acc[v][1] + p0.y;
+    acc[v][2] = acc[v][2] + p0.z; acc[v][3] = acc[v][3] + p0.w;
+    acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
+    acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
+  };
+  float* const out = a.part + static_cast<int64_t>(blockIdx.x) * a.D;
   const bool writer = slot == 0;
-  auto lds_row = [&](int b) { return lds + b * a.D; };
-  if (wave >= 2 && writer) {
+
+  if constexpr (WPR == 4) {
+    // Four waves per row: every wave owns distinct columns.
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int c = v * LPR + l;
       if (MASKED && c >= nv) continue;
-      float* d = lds_row(wave - 2) + 8 * c;
-      *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-      *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+      put(out + 8 * c, v);
     }
-  }
-  __syncthreads();
-  if (wave < 2 && writer) {
+  } else if constexpr (WPR == 2) {
+    // Two waves per row: waves 0 and 2 hold the same columns, as do 1 and 3;
+    // w0 + w2 and w1 + w3 through one LDS row of D floats (the weights'
+    // space is reused, hence the barrier first).
+    __syncthreads();
+    if (wave >= 2) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int c = v * LPR + l;
-      if (MASKED && c >= nv) continue;
-      float* d = lds_row(wave) + 8 * c;
-      const float4 p0 = *reinterpret_cast<const float4*>(d);
-      const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
-      acc[v][0] = acc[v][0] + p0.x; acc[v][1] = acc[v][1] + p0.y;
-      acc[v][2] = acc[v][2] + p0.z; acc[v][3] = acc[v][3] + p0.w;
-      acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
-      acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
-      if (wave == 1) {  // the same wave read this row just above
-        *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-        *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+      for (int v = 0; v < VPL; ++v) {
+        const int c = v * LPR + l;
+        if (MASKED && c >= nv) continue;
+        put(lds + 8 * c, v);
       }
     }
-  }
-  __syncthreads();
-  if (wave == 0 && writer) {
-    float* out = a.part + static_cast<int64_t>(blockIdx.x) * a.D;
+    __syncthreads();
+    if (wave < 2) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int c = v * LPR + l;
-      if (MASKED && c >= nv) continue;
-      const float* d = lds_row(1) + 8 * c;
-      const float4 p0 = *reinterpret_cast<const float4*>(d);
-      const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
-      const float4 o0 = make_float4(acc[v][0] + p0.x, acc[v][1] + p0.y, acc[v][2] + p0.z, acc[v][3] + p0.w);
-      const float4 o1 = make_float4(acc[v][4] + p1.x, acc[v][5] + p1.y, acc[v][6] + p1.z, acc[v][7] + p1.w);
-      *reinterpret_cast<float4*>(out + 8 * c) = o0;
-      *reinterpret_cast<float4*>(out + 8 * c + 4) = o1;
+      for (int v = 0; v < VPL; ++v) {
+        const int c = v * LPR + l;
+        if (MASKED && c >= nv) continue;
+        add_from(lds + 8 * c, v);
+        put(out + 8 * c, v);
+      }
+    }
+  } else {
+    // One wave per row: ((w0 + w2) + (w1 + w3)) through two LDS rows of D
+    // floats (the weights' space is reused, hence the barrier first).
+    __syncthreads();
+    auto lds_row = [&](int b) { return lds + b * a.D; };
+    if (wave >= 2 && writer) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int c = v * LPR + l;
+        if (MASKED && c >= nv) continue;
+        put(lds_row(wave - 2) + 8 * c, v);
+      }
+    }
+    __syncthreads();
+    if (wave < 2 && writer) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int c = v * LPR + l;
+        if (MASKED && c >= nv) continue;
+        float* d = lds_row(wave) + 8 * c;
+        add_from(d, v);
+        if (wave == 1) put(d, v);  // the same wave read this row just above
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && writer) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int c = v * LPR + l;
+        if (MASKED && c >= nv) continue;
+        add_from(lds_row(1) + 8 * c, v);
+        put(out + 8 * c, v);
+      }
     }
   }
 }
@@ -385,6 +426,16 @@ int launch_inst(const BwdArgs& a, void* stream) {
   constexpr bool THREE = MODE == kBwdGatedSilu || MODE == kBwdGatedSigmoid || MODE == kBwdAdd ||
                          MODE == kBwdAddGres;
   const size_t lds = sizeof(float) * bwd_rows_lds_floats(a.D, a.part != nullptr, THREE);
+  // Rows past 8192 elements may need more than 64 KiB of LDS (at most
+  // 128 KiB, within gfx950's 160 KiB): raise the kernel's limit once.
+  if (lds > 64 * 1024) {
+    static const int lds_ok = [] {
+      return static_cast<int>(hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, MODE>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024));
+    }();
+    if (lds_ok != 0) return lds_ok;
+  }
   hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, MODE>),
                      dim3(static_cast<unsigned>(a.chunks)), dim3(kBlock), lds,
                      static_cast<hipStream_t>(stream), a);
@@ -404,9 +455,23 @@ RowsLaunch pick_wide(int vpl, bool masked) {
   }
 }
 
+// Rows over several waves (D > 8192): 9 to 16 vectors per lane.
+template <int MODE, int LPR, int VPL = kMinVplMulti>
+RowsLaunch pick_multi(int vpl, bool masked) {
+  if constexpr (VPL > kMaxVpl) {
+    return nullptr;
+  } else {
+    if (vpl == VPL)
+      return masked ? &launch_inst<LPR, VPL, true, MODE> : &launch_inst<LPR, VPL, false, MODE>;
+    return pick_multi<MODE, LPR, VPL + 1>(vpl, masked);
+  }
+}
+
 template <int MODE>
 RowsLaunch pick(const RowGeom& g) {
   switch (g.lpr) {
+    case 256: return pick_multi<MODE, 256>(g.vpl, g.masked);
+    case 128: return pick_multi<MODE, 128>(g.vpl, g.masked);
     case 64: return pick_wide<MODE>(g.vpl, g.masked);
     case 32: return g.masked ? &launch_inst<32, 1, true, MODE> : &launch_inst<32, 1, false, MODE>;
     case 16: return g.masked ? &launch_inst<16, 1, true, MODE> : &launch_inst<16, 1, false, MODE>;

@@ -167,6 +167,33 @@ __device__ __forceinline__ double row_sum(double v) {
   return v;
 }
 
+// Sum of v over all LPR lanes of a row, returned to each of them with
+// identical bits. Up to 64 lanes this is row_sum. A row spread over W = LPR/64
+// wavefronts first reduces within each wave, then adds the W wave totals in
+// a fixed tree, (t0 + t1) or ((t0 + t1) + (t2 + t3)), through LDS: `xch`
+// holds two buffers of kWaves doubles, used alternately (`step` counts the
+// exchanges), so a buffer is rewritten only after every wave has passed the
+// next exchange's barrier and hence finished reading it. Every wave of the
+// workgroup must make the same sequence of calls (each holds a barrier).
+template <int LPR>
+__device__ __forceinline__ double row_total(double v, double (*xch)[kWaves], int& step) {
+  if constexpr (LPR <= 64) {
+    return row_sum<LPR>(v);
+  } else {
+    constexpr int W = LPR / 64;
+    static_assert(W == 2 || W == 4, "rows span 2 or 4 waves");
+    const double t = row_sum<64>(v);
+    const int wave = wave_id();
+    double* b = xch[step & 1];
+    ++step;
+    b[wave] = t;  // every lane holds t; no branch around the store
+    __syncthreads();
+    const int first = (wave / W) * W;
+    if constexpr (W == 2) return b[first] + b[first + 1];
+    else return (b[first] + b[first + 1]) + (b[first + 2] + b[first + 3]);
+  }
+}
+
 // Row reductions accumulate fp32 terms (squares of bf16 values, which are
 // exact, and the fp32 products gw*x) in fp64 along the fixed tree above, and
 // round the total to fp32 once. The fp64 sum of such terms is exact, or

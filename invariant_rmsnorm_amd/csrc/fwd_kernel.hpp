@@ -43,10 +43,12 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   constexpr bool GATED = GATE != 0 && !ADD;
   constexpr int ACT = GATED ? (GATE - 1) & 1 : 0;
   constexpr bool CAST = GATED && (GATE - 1) >= 2;
-  constexpr int RPW = 64 / LPR;
+  constexpr int RPW = rows_per_wave(LPR);
+  constexpr int WPR = waves_per_row(LPR);
   constexpr int U = fwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
-  constexpr int ROWS_BLOCK = kWaves * ROWS_WAVE;
+  constexpr int ROWS_BLOCK = rows_per_block(LPR, U);
+  static_assert(WPR == 1 || (U == 1 && VPL >= kMinVplMulti), "multi-wave rows: one row per step");
   // second input stream: the gate z, or the fused add's residual input
   constexpr bool TWO = GATED || ADD;
   constexpr int ZU = TWO ? U : 1;
@@ -54,8 +56,13 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int slot = lane / LPR;
-  const int l = lane % LPR;
+  // the wave's row group and, within its row, the lane's index l (rows
+  // spread over WPR waves: l = 64 * (wave % WPR) + lane)
+  const int group = wave / WPR;
+  const int slot = LPR >= 64 ? 0 : lane / LPR;
+  const int l = LPR >= 64 ? (wave % WPR) * 64 + lane : lane % LPR;
+  __shared__ double xch[2][kWaves];  // row-sum exchange of multi-wave rows
+  int xstep = 0;
   const int nv = a.D >> 3;
   const float Df = static_cast<float>(a.D);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS_BLOCK;
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   };
   // Rows first .. first+RPW-1 form row group u of the wave; `first` is
   // wave-uniform.
-  auto group_first = [&](int64_t base, int u) { return base + wave * ROWS_WAVE + u * RPW; };
+  auto group_first = [&](int64_t base, int u) { return base + group * ROWS_WAVE + u * RPW; };
 
   auto load_step = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
 #pragma unroll
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
           ssa = acc_add(ssa, sq);
         }
       }
-      const float ss = static_cast<float>(row_sum<LPR>(ssa));
+      const float ss = static_cast<float>(row_total<LPR>(ssa, xch, xstep));
       const float r = rstd_of(ss, Df, a.eps);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
@@ -196,7 +203,7 @@ inline int cu_count() {
 
 template <int LPR, int VPL, bool MASKED, int GATE>
 int launch_inst(const FwdArgs& a, void* stream) {
-  constexpr int ROWS_BLOCK = kWaves * fwd_unroll(LPR, VPL) * (64 / LPR);
+  constexpr int ROWS_BLOCK = rows_per_block(LPR, fwd_unroll(LPR, VPL));
   auto kern = rmsnorm_fwd_kernel<LPR, VPL, MASKED, GATE>;
   static const int per_cu = [&] {
     int b = 0;
@@ -228,9 +235,23 @@ FwdLaunch pick_wide(int vpl, bool masked) {
   }
 }
 
+// Rows over several waves (D > 8192): 9 to 16 vectors per lane.
+template <int GATE, int LPR, int VPL = kMinVplMulti>
+FwdLaunch pick_multi(int vpl, bool masked) {
+  if constexpr (VPL > kMaxVpl) {
+    return nullptr;
+  } else {
+    if (vpl == VPL)
+      return masked ? &launch_inst<LPR, VPL, true, GATE> : &launch_inst<LPR, VPL, false, GATE>;
+    return pick_multi<GATE, LPR, VPL + 1>(vpl, masked);
+  }
+}
+
 template <int GATE>
 FwdLaunch pick(const RowGeom& g) {
   switch (g.lpr) {
+    case 256: return pick_multi<GATE, 256>(g.vpl, g.masked);
+    case 128: return pick_multi<GATE, 128>(g.vpl, g.masked);
     case 64: return pick_wide<GATE>(g.vpl, g.masked);
     case 32: return g.masked ? &launch_inst<32, 1, true, GATE> : &launch_inst<32, 1, false, GATE>;
     case 16: return g.masked ? &launch_inst<16, 1, true, GATE> : &launch_inst<16, 1, false, GATE>;

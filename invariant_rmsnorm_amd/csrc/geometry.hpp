@@ -5,12 +5,16 @@
 // Invariant Kernels", sections 2-3: the reduction layout must come from the
 // problem's fixed dimensions, never from the batch dimension).
 //
-// A row of D bf16 values is NV = D/8 vectors of 16 bytes. LPR lanes of a
-// 64-lane wavefront share one row: LPR = 64 when NV >= 64 (each lane then
-// holds VPL = ceil(NV/64) vectors), otherwise the smallest power of two
-// >= NV (VPL = 1, and a wave carries 64/LPR rows side by side). Lane l of a
-// row owns the vectors c = v*LPR + l, v = 0..VPL-1; MASKED marks geometries
-// where the last of those vectors is missing on some lanes.
+// A row of D bf16 values is NV = D/8 vectors of 16 bytes, shared by LPR
+// lanes:
+//  - NV > 1024 (D > 8192): LPR = 128 or 256, the lanes of 2 or 4 wavefronts
+//    of one workgroup (VPL = ceil(NV/LPR) <= 16 vectors each);
+//  - 64 <= NV <= 1024: LPR = 64, one wavefront (VPL = ceil(NV/64));
+//  - NV < 64: LPR = the smallest power of two >= NV, VPL = 1, and a wave
+//    carries 64/LPR rows side by side.
+// Lane l of a row (l = 64 * (wave within the row) + lane) owns the vectors
+// c = v*LPR + l, v = 0..VPL-1; MASKED marks geometries where the last of
+// those vectors is missing on some lanes.
 #pragma once
 
 #include <stdint.h>
@@ -19,8 +23,9 @@ namespace rmsn {
 
 constexpr int kWaves = 4;            // wavefronts per workgroup
 constexpr int kBlock = 64 * kWaves;  // threads per workgroup
-constexpr int kMaxD = 8192;
-constexpr int kMaxVpl = kMaxD / 512;
+constexpr int kMaxD = 32768;
+constexpr int kMaxVpl = 16;      // vectors per lane, in every geometry
+constexpr int kMinVplMulti = 9;  // a row spans several waves only past 1024 vectors
 // The backward splits the batch into at most this many chunks of rows; one
 // workgroup per chunk, one per compute unit on a 256-CU part (measured
 // faster than two: fewer concurrent row streams per HBM channel).
@@ -30,13 +35,21 @@ constexpr int kMaxVpl = kMaxD / 512;
 constexpr int64_t kTargetChunks = RMSN_TARGET_CHUNKS;
 
 struct RowGeom {
-  int lpr;     // lanes per row (1, 2, 4, ..., 64)
+  int lpr;     // lanes per row (1, 2, 4, ..., 64, 128, 256)
   int vpl;     // 16-byte vectors per lane (1..16)
   bool masked; // some lanes lack their last vector
 };
 
+// Wavefronts that share one row, and rows side by side in one wavefront.
+constexpr int waves_per_row(int lpr) { return lpr > 64 ? lpr / 64 : 1; }
+constexpr int rows_per_wave(int lpr) { return lpr >= 64 ? 1 : 64 / lpr; }
+
 inline RowGeom row_geom(int64_t D) {
   const int64_t nv = D / 8;
+  if (nv > 1024) {
+    const int lpr = nv <= 2048 ? 128 : 256;
+    return {lpr, static_cast<int>((nv + lpr - 1) / lpr), (nv % lpr) != 0};
+  }
   if (nv >= 64) return {64, static_cast<int>((nv + 63) / 64), (nv % 64) != 0};
   int lpr = 1;
   while (lpr < nv) lpr <<= 1;
@@ -58,13 +71,20 @@ constexpr int64_t kCacheBytes = int64_t{256} << 20;
 constexpr int fwd_unroll(int lpr, int vpl) {
   return lpr < 64 ? RMSN_FWD_UNROLL_NARROW : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
 }
+static_assert(RMSN_FWD_UNROLL_NARROW >= 1, "unroll");
 constexpr int bwd_unroll(int lpr, int vpl) {
   return lpr < 64 ? 4 : (vpl == 1 ? 4 : vpl == 2 ? 2 : 1);
 }
 
+// Rows one workgroup step covers: (waves / waves per row) row groups of
+// U unrolled steps of rows_per_wave rows.
+constexpr int rows_per_block(int lpr, int unroll) {
+  return kWaves / waves_per_row(lpr) * unroll * rows_per_wave(lpr);
+}
+
 inline int64_t bwd_rows_per_step(int64_t D) {
   const RowGeom g = row_geom(D);
-  return static_cast<int64_t>(kWaves) * bwd_unroll(g.lpr, g.vpl) * (64 / g.lpr);
+  return rows_per_block(g.lpr, bwd_unroll(g.lpr, g.vpl));
 }
 
 // Row blocks per group of the backward's traversal (0: one contiguous group

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 4
+    assert irn.rmsnorm_abi_version() == 5
 
 
 def test_status_strings():
@@ -61,7 +61,7 @@ def fwd(**kw):
     (dict(D=0), irn.RMSN_ERR_SHAPE),
     (dict(D=-8), irn.RMSN_ERR_SHAPE),
     (dict(D=100, ld_x=100, ld_y=104), irn.RMSN_ERR_UNSUPPORTED_D),
-    (dict(D=8200, ld_x=8200, ld_y=8200), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=32776, ld_x=32776, ld_y=32776), irn.RMSN_ERR_UNSUPPORTED_D),
     (dict(ld_x=4000), irn.RMSN_ERR_SHAPE),
     (dict(ld_y=4088), irn.RMSN_ERR_SHAPE),
     (dict(x=A + 2), irn.RMSN_ERR_MISALIGNED),
@@ -141,7 +141,7 @@ def test_workspace_and_chunking_contract():
     assert irn.rmsnorm_bwd_workspace_bytes(0, 4096) == 0
     assert irn.rmsnorm_bwd_workspace_bytes(10, 100) == 0
     for T, D in ((1, 128), (16, 128), (32768, 4096), (262144, 4096), (262144, 128), (1000, 2048),
-                 (7, 8), (12345, 8192)):
+                 (7, 8), (12345, 8192), (5000, 16384), (300, 32768), (777, 8200)):
         R, S, K = irn.rmsnorm_bwd_partials_layout(T, D)
         assert R > 0 and S > 0 and 0 < K <= 256
         assert irn.rmsnorm_bwd_workspace_bytes(T, D) == K * D * 4

@@ -22,7 +22,8 @@ from synth import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-WIDTHS = [8, 16, 24, 64, 96, 128, 136, 256, 520, 1024, 2048, 2560, 4096, 4104, 5120, 8192]
+WIDTHS = [8, 16, 24, 64, 96, 128, 136, 256, 520, 1024, 2048, 2560, 4096, 4104, 5120, 8192,
+          8200, 12288, 16384, 20480, 32768]
 
 
 def _run(p, with_gro, zc=None):
@@ -62,7 +63,7 @@ def test_add_tiny_fixture(gpu, zc, with_gro):
 @pytest.mark.parametrize("D", WIDTHS)
 def test_add_widths(gpu, D):
     """Every geometry class at a T spanning several steps plus a ragged tail."""
-    T = 1037 if D <= 2048 else 261
+    T = 1037 if D <= 2048 else 261 if D <= 8192 else 97
     p = wl.tiny(D % 16 == 8, T=T, D=D, seed=8500 + D, with_gres=True, with_residual=True)
     _assert_parity(_run(p, True), _oracle(p, True), D)
 

@@ -28,11 +28,12 @@ pytestmark = pytest.mark.gpu
 ACTS = [(irn.RMSN_GATE_SILU, oracle.SILU), (irn.RMSN_GATE_SIGMOID, oracle.SIGMOID)]
 ROUNDINGS = [(irn.RMSN_GATED_ROUND_FP32, oracle.FP32_WEIGHT),
              (irn.RMSN_GATED_ROUND_CAST, oracle.CAST_INPUT)]
-WIDTHS = [8, 64, 96, 128, 136, 1024, 2560, 4096, 4104, 5632, 6144, 8192]
+WIDTHS = [8, 64, 96, 128, 136, 1024, 2560, 4096, 4104, 5632, 6144, 8192, 8200, 16384, 18440,
+          32768]
 
 
 def _rows_for(D):
-    return 1037 if D <= 2048 else 261
+    return 1037 if D <= 2048 else 261 if D <= 8192 else 97
 
 
 def _gpu_bwd(p, act, rstd=None, **kw):

@@ -81,6 +81,20 @@ def test_prefix_and_offset_slices(gpu, D):
         assert torch.equal(ys, y[a:b]) and torch.equal(rs, r[a:b]) and torch.equal(dxs, dx[a:b])
 
 
+@pytest.mark.parametrize("D", [12288, 32768])
+def test_wide_rows_across_batches(gpu, D):
+    """Rows spread over 2 and 4 waves: a row's y, rstd and dx are the same
+    bytes in batches of 1, 2, 3, 7 and 40 rows at every position."""
+    T = 40
+    x = dev_bf16(synth.normal_bf16(6300 + D, 1, T, D))
+    g = dev_bf16(synth.normal_bf16(6300 + D, 2, T, D))
+    gamma = dev_f32(wl.gamma_for(6300 + D, D, False))
+    y, r, dx = _fwd_bwd(x, g, gamma)
+    for a, b in ((0, 1), (5, 6), (39, 40), (3, 5), (10, 13), (20, 27), (0, 40)):
+        ys, rs, dxs = _fwd_bwd(x[a:b], g[a:b], gamma)
+        assert torch.equal(ys, y[a:b]) and torch.equal(rs, r[a:b]) and torch.equal(dxs, dx[a:b])
+
+
 @pytest.mark.parametrize("D", [128, 1000, 4096])
 def test_strided_rows(gpu, D):
     """Rows with a stride larger than D give the packed result bytewise."""

@@ -55,14 +55,17 @@ def test_token_and_width_grid(gpu, T, D, zc):
 
 
 WIDTHS = [8, 16, 24, 40, 64, 96, 128, 136, 256, 264, 384, 512, 520, 1024, 1536, 2048, 2560,
-          3072, 4096, 4104, 5120, 6144, 7168, 8192]
+          3072, 4096, 4104, 5120, 6144, 7168, 8192,
+          # rows over 2 waves (8192 < D <= 16384) and 4 waves (D <= 32768)
+          8200, 9216, 12288, 16384, 16392, 18432, 24576, 32768]
 
 
 @pytest.mark.parametrize("D", WIDTHS)
 def test_widths(gpu, D):
-    """Every geometry class (lanes per row 1..64, 1..16 vectors per lane,
-    masked and unmasked) at a T spanning several steps plus a ragged tail."""
-    T = 1037 if D <= 2048 else 261
+    """Every geometry class (lanes per row 1..64 in one wave, 128 and 256
+    over 2 and 4 waves; 1..16 vectors per lane, masked and unmasked) at a T
+    spanning several steps plus a ragged tail."""
+    T = 1037 if D <= 2048 else 261 if D <= 8192 else 97
     p = wl.tiny(D % 16 == 8, T=T, D=D, seed=8000 + D, with_gres=True)
     assert_parity(p, run_fwd_bwd(p, True), oracle_all(p, True), True, D)
 
@@ -165,7 +168,7 @@ def _exact_problem(T, D, seed, zc):
                                              .astype(np.float32)))
 
 
-@pytest.mark.parametrize("D", [8, 128, 2048, 4096, 8192])
+@pytest.mark.parametrize("D", [8, 128, 2048, 4096, 8192, 16384, 32768])
 @pytest.mark.parametrize("zc", [False, True])
 def test_exact_arithmetic_bitwise(gpu, D, zc):
     p = _exact_problem(301, D, D + zc, zc)
