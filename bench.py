@@ -74,7 +74,7 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def make_inputs(workload: str, torch, dev, rows: int = 0):
+def make_inputs(workload: str, torch, dev, rows: int = 0, dim: int = 0):
     import numpy as np
     from synth import workloads as wl
 
@@ -82,16 +82,16 @@ def make_inputs(workload: str, torch, dev, rows: int = 0):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     if workload in ("token", "token_gres"):
-        p = wl.residual(T=rows or 32768, with_gres=(workload == "token_gres"))
-        desc = (f"token RMSNorm fwd+bwd with dgamma, T={p.T}, D=4096, bf16 x ~N(0,1) with 1% "
+        p = wl.residual(T=rows or 32768, D=dim or 4096, with_gres=(workload == "token_gres"))
+        desc = (f"token RMSNorm fwd+bwd with dgamma, T={p.T}, D={p.D}, bf16 x ~N(0,1) with 1% "
                 "outlier rows x50, g ~N(0,1), fp32 gamma=1+N(0,0.1), eps=1e-6")
     elif workload == "large":
         p = wl.large()
         desc = ("RMSNorm fwd+bwd with dgamma, T=262144, D=4096, zero-centred gamma, "
                 "g ~0.01 N(0,1), eps=1e-6")
     elif workload == "add":
-        p = wl.fused_add(T=rows or 32768)
-        desc = (f"fused add-RMSNorm fwd+bwd with dgamma, T={p.T}, D=4096: h = x + residual "
+        p = wl.fused_add(T=rows or 32768, D=dim or 4096)
+        desc = (f"fused add-RMSNorm fwd+bwd with dgamma, T={p.T}, D={p.D}: h = x + residual "
                 "(fp32), bf16 x, residual, g, residual-output gradient ~N(0,1), fp32 "
                 "gamma=1+N(0,0.1), eps=1e-6")
     elif workload == "gated":
@@ -175,6 +175,8 @@ def main():
                     choices=["token", "token_gres", "large", "gated", "add"])
     ap.add_argument("--rows", type=int, default=0,
                     help="token workloads: batch rows T (default 32768, the metric's size)")
+    ap.add_argument("--dim", type=int, default=0,
+                    help="token and add workloads: row length D (default 4096)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time of the CPU-oracle baseline (whole passes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -200,7 +202,7 @@ def main():
     irn.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    p, t, desc = make_inputs(args.workload, torch, dev, args.rows)
+    p, t, desc = make_inputs(args.workload, torch, dev, args.rows, args.dim)
     T, D = p.T, p.D
     zc, eps = p.zero_centered, p.eps
     x, gamma = t["x"], t["gamma"]
@@ -300,7 +302,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic() if (args.workload == "token" and T == 32768) else None
+    traffic = measured_traffic() if (args.workload == "token" and T == 32768 and D == 4096) else None
 
     nev = 2 if gated else 4
 
@@ -351,8 +353,8 @@ def main():
                          f"{dt:.1f} s wall"}
 
     out = {
-        "metric": (METRIC if args.workload == "token" and T == 32768
-                   else f"{METRIC} [workload: {args.workload}, T={T}]"),
+        "metric": (METRIC if args.workload == "token" and T == 32768 and D == 4096
+                   else f"{METRIC} [workload: {args.workload}, T={T}, D={D}]"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

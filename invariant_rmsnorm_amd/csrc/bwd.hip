@@ -32,7 +32,8 @@ __global__ __launch_bounds__(64 * kFinishWaves) void rmsnorm_bwd_finish_kernel(
   const int64_t per = (chunks + kFinishSlices - 1) / kFinishSlices;
   const int64_t k0 = s * per;
   const int64_t k1 = k0 + per < chunks ? k0 + per : chunks;
-  // One resource over all partials (at most 256 x 8192 floats = 8 MiB);
+  // One resource over all partials (at most 512 x 2048 or 256 x 32768
+  // floats, 32 MiB);
   // lanes past D and chunks past the slice's range get an offset beyond it
   // and read zeros, so the loads need no branches.
   const bool ok = col4 < d4;

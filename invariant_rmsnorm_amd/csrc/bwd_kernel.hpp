@@ -55,7 +55,6 @@ enum : int {
 // weights move to LDS and the second pass unpacks the raw vectors again.
 // The gated form holds a third input row (z), so it goes lean from 11.
 constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_inputs ? 11 : 13); }
-constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 5 ? 1 : 2; }
 
 // LDS floats the rows kernel needs: the weights when held in LDS (one float4
 // pair per vector slot, laid out so that consecutive lanes read consecutive

@@ -26,13 +26,15 @@ constexpr int kBlock = 64 * kWaves;  // threads per workgroup
 constexpr int kMaxD = 32768;
 constexpr int kMaxVpl = 16;      // vectors per lane, in every geometry
 constexpr int kMinVplMulti = 9;  // a row spans several waves only past 1024 vectors
-// The backward splits the batch into at most this many chunks of rows; one
-// workgroup per chunk, one per compute unit on a 256-CU part (measured
-// faster than two: fewer concurrent row streams per HBM channel).
-#ifndef RMSN_TARGET_CHUNKS
-#define RMSN_TARGET_CHUNKS 256
-#endif
-constexpr int64_t kTargetChunks = RMSN_TARGET_CHUNKS;
+// The backward splits the batch into at most kCus * (its occupancy in
+// workgroups per CU) chunks of rows, one workgroup per chunk. Rows of 5 or
+// more vectors per lane use the whole register file (one workgroup per CU);
+// narrower rows run two per CU, which measured faster (D = 128: 124 us
+// instead of 161 us per 256 MiB step), while two per CU at D >= 4096 was
+// slower.
+constexpr int64_t kCus = 256;
+constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 5 ? 1 : 2; }
+constexpr int64_t kMaxChunks = 2 * kCus;
 
 struct RowGeom {
   int lpr;     // lanes per row (1, 2, 4, ..., 64, 128, 256)
@@ -72,8 +74,11 @@ constexpr int fwd_unroll(int lpr, int vpl) {
   return lpr < 64 ? RMSN_FWD_UNROLL_NARROW : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
 }
 static_assert(RMSN_FWD_UNROLL_NARROW >= 1, "unroll");
+#ifndef RMSN_BWD_UNROLL_NARROW
+#define RMSN_BWD_UNROLL_NARROW 4
+#endif
 constexpr int bwd_unroll(int lpr, int vpl) {
-  return lpr < 64 ? 4 : (vpl == 1 ? 4 : vpl == 2 ? 2 : 1);
+  return lpr < 64 ? RMSN_BWD_UNROLL_NARROW : (vpl == 1 ? 4 : vpl == 2 ? 2 : 1);
 }
 
 // Rows one workgroup step covers: (waves / waves per row) row groups of
@@ -103,17 +108,26 @@ inline int64_t bwd_rows_per_step(int64_t D) {
 // grouping may depend on T; the per-row outputs never do.)
 struct BwdPlan {
   int64_t block_rows;    // R
-  int64_t chunks;        // K <= kTargetChunks
+  int64_t chunks;        // K <= bwd_target_chunks(D)
   int64_t group_blocks;  // S
 };
 
+#ifndef RMSN_BWD_BLOCKS_PER_CU
+#define RMSN_BWD_BLOCKS_PER_CU 0  // 0: the kernel's occupancy
+#endif
+inline int64_t bwd_target_chunks(int64_t D) {
+  return kCus * (RMSN_BWD_BLOCKS_PER_CU > 0 ? RMSN_BWD_BLOCKS_PER_CU
+                                            : bwd_waves_per_eu(row_geom(D).vpl));
+}
+
 inline BwdPlan bwd_plan(int64_t T, int64_t D) {
   const int64_t R = bwd_rows_per_step(D);
+  const int64_t target = bwd_target_chunks(D);
   if (T <= 0) return {R, 0, 1};
   const int64_t blocks = (T + R - 1) / R;
-  const int64_t S = RMSN_BWD_GROUP > 0 ? RMSN_BWD_GROUP : (blocks + kTargetChunks - 1) / kTargetChunks;
+  const int64_t S = RMSN_BWD_GROUP > 0 ? RMSN_BWD_GROUP : (blocks + target - 1) / target;
   const int64_t groups = (blocks + S - 1) / S;
-  return {R, groups < kTargetChunks ? groups : kTargetChunks, S};
+  return {R, groups < target ? groups : target, S};
 }
 
 }  // namespace rmsn
