@@ -65,7 +65,7 @@ int launch_bwd_rows(const BwdArgs& a, void* stream) {
   if (a.T == 0 || a.chunks == 0) return 0;
   if (a.z != nullptr) return launch_bwd_rows_gated(a, stream);
   if (a.rin != nullptr) return launch_bwd_rows_add(a, stream);
-  const RowGeom g = row_geom(a.D);
+  const RowGeom g = bwd_geom(a.D);
   const bwd_detail::RowsLaunch f =
       a.gres != nullptr ? bwd_detail::pick<kBwdGres>(g) : bwd_detail::pick<kBwdPlain>(g);
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);

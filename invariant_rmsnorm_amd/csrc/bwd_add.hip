@@ -8,7 +8,7 @@
 namespace rmsn {
 
 int launch_bwd_rows_add(const BwdArgs& a, void* stream) {
-  const RowGeom g = row_geom(a.D);
+  const RowGeom g = bwd_geom(a.D);
   const bwd_detail::RowsLaunch f =
       a.gres != nullptr ? bwd_detail::pick<kBwdAddGres>(g) : bwd_detail::pick<kBwdAdd>(g);
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);

@@ -7,7 +7,7 @@
 namespace rmsn {
 
 int launch_bwd_rows_gated(const BwdArgs& a, void* stream) {
-  const RowGeom g = row_geom(a.D);
+  const RowGeom g = bwd_geom(a.D);
   bwd_detail::RowsLaunch f = nullptr;
   if (a.act == kGateSilu) f = bwd_detail::pick<kBwdGatedSilu>(g);
   else if (a.act == kGateSigmoid) f = bwd_detail::pick<kBwdGatedSigmoid>(g);

@@ -55,13 +55,24 @@ enum : int {
 // weights move to LDS and the second pass unpacks the raw vectors again.
 // The gated form holds a third input row (z), so it goes lean from 11.
 constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_inputs ? 11 : 13); }
+// Load the next step while computing this one (two register sets that swap
+// roles), for rows over 4 waves whose loaded step fits the register file
+// twice: input streams x vectors per lane <= 18 with the whole register file
+// (plain: VPL <= 9; three streams: 6; four: 4), <= 8 at two waves per SIMD.
+// Without it the four waves of a row, held together by the exchange
+// barrier, load and compute in lock step and leave the memory pipe idle
+// while they compute.
+constexpr bool bwd_prefetch(int lpr, int vpl, int mode) {
+  const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
+  return lpr > 64 && streams * vpl <= (bwd_waves_per_eu(vpl) == 1 ? 18 : 8);
+}
 
 // LDS floats the rows kernel needs: the weights when held in LDS (one float4
 // pair per vector slot, laid out so that consecutive lanes read consecutive
 // 16 bytes) and, after the rows are done, two rows of D floats for the wave
 // merge (which reuse the same space).
 inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
-  const RowGeom g = row_geom(D);
+  const RowGeom g = bwd_geom(D);
   const size_t w = bwd_lean(g.vpl, three_inputs) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
   // merge space: 2 rows of D floats with one wave per row, 1 with two, none
   // with four
@@ -82,8 +93,9 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr int U = bwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = rows_per_block(LPR, U);
-  static_assert(WPR == 1 || (U == 1 && VPL >= kMinVplMulti), "multi-wave rows: one row per step");
+  static_assert(WPR == 1 || (U == 1 && VPL >= kBwdMinVplMulti), "multi-wave rows: one row per step");
   constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
+  constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE);
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
@@ -161,20 +173,25 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
 
-  for (int64_t j = 0; j < mine; ++j) {
-    // j-th block of the chunk from the top: group (mine-1-j)/S from the
-    // chunk's first, block S-1-(j%S) within it (the last group may be short)
-    const int64_t jj = mine - 1 - j;
-    const int64_t step = ((k + (jj / S) * K) * S + jj % S) * ROWS_BLOCK;
+  // One workgroup step's loaded rows (U row groups of each input stream).
+  struct StepRegs {
     u32x4 gq[U][VPL], xq[U][VPL];
-    u32x4 rq_res[GRES ? U : 1][GRES ? VPL : 1];  // residual-branch gradient
-    u32x4 zq[GATED ? U : 1][GATED ? VPL : 1];     // gate input
-    u32x4 hq[ADD ? U : 1][ADD ? VPL : 1];         // fused add: residual input
+    u32x4 rres[GRES ? U : 1][GRES ? VPL : 1];  // residual-branch gradient
+    u32x4 zq[GATED ? U : 1][GATED ? VPL : 1];   // gate input
+    u32x4 hq[ADD ? U : 1][ADD ? VPL : 1];       // fused add: residual input
     float rq[U];
+  };
+  // j-th block of the chunk from the top: group (mine-1-j)/S from the
+  // chunk's first, block S-1-(j%S) within it (the last group may be short)
+  auto step_of = [&](int64_t j) -> int64_t {
+    const int64_t jj = mine - 1 - j;
+    return ((k + (jj / S) * K) * S + jj % S) * ROWS_BLOCK;
+  };
+  auto load_step = [&](int64_t step, StepRegs& b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t first = step + group * ROWS_WAVE + u * RPW;
-      rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
+      b.rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
       const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
       const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
       // g (and gres, z) are read once: streaming hint. x takes it only when
@@ -182,53 +199,54 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       if (a.x_stream) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
-          xq[u][v] = buf_load16<kLoadStream>(rx, voff(v, a.ld_x));
+          b.gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
+          b.xq[u][v] = buf_load16<kLoadStream>(rx, voff(v, a.ld_x));
         }
       } else {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
-          xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
+          b.gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
+          b.xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
         }
       }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) rq_res[u][v] = buf_load16<kLoadStream>(rgr, voff(v, a.ld_gres));
+        for (int v = 0; v < VPL; ++v) b.rres[u][v] = buf_load16<kLoadStream>(rgr, voff(v, a.ld_gres));
       }
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, end, RPW, a.ld_z, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = buf_load16<kLoadStream>(rz, voff(v, a.ld_z));
+        for (int v = 0; v < VPL; ++v) b.zq[u][v] = buf_load16<kLoadStream>(rz, voff(v, a.ld_z));
       }
       if constexpr (ADD) {  // the forward read it too: x's policy
         const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
         if (a.x_stream) {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) hq[u][v] = buf_load16<kLoadStream>(rh, voff(v, a.ld_rin));
+          for (int v = 0; v < VPL; ++v) b.hq[u][v] = buf_load16<kLoadStream>(rh, voff(v, a.ld_rin));
         } else {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) hq[u][v] = buf_load16(rh, voff(v, a.ld_rin));
+          for (int v = 0; v < VPL; ++v) b.hq[u][v] = buf_load16(rh, voff(v, a.ld_rin));
         }
       }
     }
+  };
+  auto process_step = [&](int64_t step, StepRegs& b) {
     // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
     // rounding, as in the forward).
     auto row_values = [&](int u, int v, float (&f)[8]) {
-      unpack8(xq[u][v], f);
+      unpack8(b.xq[u][v], f);
       if constexpr (ADD) {
         float rf[8];
-        unpack8(hq[u][v], rf);
+        unpack8(b.hq[u][v], rf);
 #pragma unroll
         for (int k = 0; k < 8; ++k) f[k] = f[k] + rf[k];
       }
     };
-
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t first = step + group * ROWS_WAVE + u * RPW;
-      const float r = rq[u];
+      const float r = b.rq[u];
       int wbase = 0;
       if constexpr (LEAN) asm("" : "+v"(wbase));
       // Pass 1: the lane partial of s = sum_i (g_i * w_i) * x_i in (vector,
@@ -244,12 +262,12 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       for (int v = 0; v < VPL; ++v) {
         if (MASKED && v * LPR + l >= nv) continue;  // no such vector (weights unset)
         float gf[8], xf[8], w8[8];
-        unpack8(gq[u][v], gf);
+        unpack8(b.gq[u][v], gf);
         row_values(u, v, xf);
         weights(wbase, v, w8);
         if constexpr (GATED) {
           float zf[8], dz8[8];
-          unpack8(zq[u][v], zf);
+          unpack8(b.zq[u][v], zf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             float ag, dag;
@@ -282,10 +300,10 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       if constexpr (LEAN) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          opaque(gq[u][v]);
-          opaque(xq[u][v]);
-          if constexpr (GATED) opaque(zq[u][v]);
-          if constexpr (ADD) opaque(hq[u][v]);
+          opaque(b.gq[u][v]);
+          opaque(b.xq[u][v]);
+          if constexpr (GATED) opaque(b.zq[u][v]);
+          if constexpr (ADD) opaque(b.hq[u][v]);
         }
         asm("" : "+v"(wbase));
       }
@@ -296,12 +314,12 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       for (int v = 0; v < VPL; ++v) {
         if (MASKED && v * LPR + l >= nv) continue;
         float gf[8], xf[8], w8[8], o[8];
-        unpack8(gq[u][v], gf);
+        unpack8(b.gq[u][v], gf);
         row_values(u, v, xf);
         weights(wbase, v, w8);
         if constexpr (GATED) {
           float zf[8];
-          unpack8(zq[u][v], zf);
+          unpack8(b.zq[u][v], zf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) gf[k] = gf[k] * gate<ACT>(zf[k]);
         }
@@ -314,13 +332,37 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         }
         if constexpr (GRES) {
           float rf[8];
-          unpack8(rq_res[u][v], rf);
+          unpack8(b.rres[u][v], rf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
         }
         buf_store16_nt(pack8(o), rdx, voff(v, a.ld_dx));
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+  };
+
+  if constexpr (PREFETCH) {
+    // Software pipeline over two register sets that swap roles each step
+    // (no copy between them: a copy would wait for every outstanding memory
+    // operation, the previous step's stores included): the next step's
+    // loads are in flight while this step computes.
+    StepRegs ra, rb;
+    if (mine > 0) load_step(step_of(0), ra);
+    for (int64_t j = 0; j < mine; j += 2) {
+      if (j + 1 < mine) load_step(step_of(j + 1), rb);
+      process_step(step_of(j), ra);
+      if (j + 1 < mine) {
+        if (j + 2 < mine) load_step(step_of(j + 2), ra);
+        process_step(step_of(j + 1), rb);
+      }
+    }
+  } else {
+    for (int64_t j = 0; j < mine; ++j) {
+      StepRegs cur;
+      const int64_t step = step_of(j);
+      load_step(step, cur);
+      process_step(step, cur);
     }
   }
 
@@ -454,8 +496,8 @@ RowsLaunch pick_wide(int vpl, bool masked) {
   }
 }
 
-// Rows over several waves (D > 8192): 9 to 16 vectors per lane.
-template <int MODE, int LPR, int VPL = kMinVplMulti>
+// Rows over 4 waves (D > 4096): 3 to 16 vectors per lane.
+template <int MODE, int LPR, int VPL = kBwdMinVplMulti>
 RowsLaunch pick_multi(int vpl, bool masked) {
   if constexpr (VPL > kMaxVpl) {
     return nullptr;
@@ -470,7 +512,6 @@ template <int MODE>
 RowsLaunch pick(const RowGeom& g) {
   switch (g.lpr) {
     case 256: return pick_multi<MODE, 256>(g.vpl, g.masked);
-    case 128: return pick_multi<MODE, 128>(g.vpl, g.masked);
     case 64: return pick_wide<MODE>(g.vpl, g.masked);
     case 32: return g.masked ? &launch_inst<32, 1, true, MODE> : &launch_inst<32, 1, false, MODE>;
     case 16: return g.masked ? &launch_inst<16, 1, true, MODE> : &launch_inst<16, 1, false, MODE>;

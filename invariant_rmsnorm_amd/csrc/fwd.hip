@@ -9,7 +9,7 @@ int launch_fwd(const FwdArgs& a, void* stream) {
   if (a.T == 0) return 0;
   if (a.z != nullptr) return launch_fwd_gated(a, stream);
   if (a.rin != nullptr) return launch_fwd_add(a, stream);
-  const fwd_detail::FwdLaunch f = fwd_detail::pick<0>(row_geom(a.D));
+  const fwd_detail::FwdLaunch f = fwd_detail::pick<0>(fwd_geom(a.D));
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);
   return f(a, stream);
 }

@@ -7,7 +7,7 @@
 namespace rmsn {
 
 int launch_fwd_add(const FwdArgs& a, void* stream) {
-  const fwd_detail::FwdLaunch f = fwd_detail::pick<kFwdAdd>(row_geom(a.D));
+  const fwd_detail::FwdLaunch f = fwd_detail::pick<kFwdAdd>(fwd_geom(a.D));
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);
   return f(a, stream);
 }

@@ -7,7 +7,7 @@ namespace rmsn {
 
 int launch_fwd_gated(const FwdArgs& a, void* stream) {
   using namespace fwd_detail;
-  const RowGeom g = row_geom(a.D);
+  const RowGeom g = fwd_geom(a.D);
   FwdLaunch f = nullptr;
   switch (fwd_gate_code(true, a.act, a.cast != 0)) {
     case fwd_gate_code(true, kGateSilu, false): f = pick<fwd_gate_code(true, kGateSilu, false)>(g); break;

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   constexpr int U = fwd_unroll(LPR, VPL);
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = rows_per_block(LPR, U);
-  static_assert(WPR == 1 || (U == 1 && VPL >= kMinVplMulti), "multi-wave rows: one row per step");
+  static_assert(WPR == 1 || (U == 1 && VPL >= kFwdMinVplMulti), "multi-wave rows: one row per step");
   // second input stream: the gate z, or the fused add's residual input
   constexpr bool TWO = GATED || ADD;
   constexpr int ZU = TWO ? U : 1;
@@ -236,7 +236,7 @@ FwdLaunch pick_wide(int vpl, bool masked) {
 }
 
 // Rows over several waves (D > 8192): 9 to 16 vectors per lane.
-template <int GATE, int LPR, int VPL = kMinVplMulti>
+template <int GATE, int LPR, int VPL = kFwdMinVplMulti>
 FwdLaunch pick_multi(int vpl, bool masked) {
   if constexpr (VPL > kMaxVpl) {
     return nullptr;

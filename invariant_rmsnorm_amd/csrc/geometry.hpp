@@ -7,9 +7,12 @@
 //
 // A row of D bf16 values is NV = D/8 vectors of 16 bytes, shared by LPR
 // lanes:
-//  - NV > 1024 (D > 8192): LPR = 128 or 256, the lanes of 2 or 4 wavefronts
-//    of one workgroup (VPL = ceil(NV/LPR) <= 16 vectors each);
-//  - 64 <= NV <= 1024: LPR = 64, one wavefront (VPL = ceil(NV/64));
+//  - long rows span several wavefronts of one workgroup: LPR = 128 or 256
+//    (VPL = ceil(NV/LPR) <= 16 vectors each). The forward does this past
+//    1024 vectors (D > 8192), over 2 waves up to 2048 vectors and 4 beyond;
+//    the backward past 512 vectors (D > 4096), always over 4 waves, which
+//    keeps VPL small enough for its software pipeline (fwd_geom, bwd_geom);
+//  - 64 <= NV: LPR = 64, one wavefront (VPL = ceil(NV/64));
 //  - NV < 64: LPR = the smallest power of two >= NV, VPL = 1, and a wave
 //    carries 64/LPR rows side by side.
 // Lane l of a row (l = 64 * (wave within the row) + lane) owns the vectors
@@ -25,7 +28,9 @@ constexpr int kWaves = 4;            // wavefronts per workgroup
 constexpr int kBlock = 64 * kWaves;  // threads per workgroup
 constexpr int kMaxD = 32768;
 constexpr int kMaxVpl = 16;      // vectors per lane, in every geometry
-constexpr int kMinVplMulti = 9;  // a row spans several waves only past 1024 vectors
+// Vectors per lane of multi-wave rows: forward 9..16, backward 3..16.
+constexpr int kFwdMinVplMulti = 9;
+constexpr int kBwdMinVplMulti = 3;
 // The backward splits the batch into at most kCus * (its occupancy in
 // workgroups per CU) chunks of rows, one workgroup per chunk. Rows of 5 or
 // more vectors per lane use the whole register file (one workgroup per CU);
@@ -46,16 +51,34 @@ struct RowGeom {
 constexpr int waves_per_row(int lpr) { return lpr > 64 ? lpr / 64 : 1; }
 constexpr int rows_per_wave(int lpr) { return lpr >= 64 ? 1 : 64 / lpr; }
 
-inline RowGeom row_geom(int64_t D) {
-  const int64_t nv = D / 8;
-  if (nv > 1024) {
-    const int lpr = nv <= 2048 ? 128 : 256;
-    return {lpr, static_cast<int>((nv + lpr - 1) / lpr), (nv % lpr) != 0};
-  }
+// One wave or fewer per row (NV <= 1024).
+inline RowGeom single_wave_geom(int64_t nv) {
   if (nv >= 64) return {64, static_cast<int>((nv + 63) / 64), (nv % 64) != 0};
   int lpr = 1;
   while (lpr < nv) lpr <<= 1;
   return {lpr, 1, lpr != nv};
+}
+
+inline RowGeom multi_wave_geom(int64_t nv, int lpr) {
+  return {lpr, static_cast<int>((nv + lpr - 1) / lpr), (nv % lpr) != 0};
+}
+
+// Forward: past 1024 vectors (D > 8192), 2 waves per row up to 2048 vectors,
+// 4 beyond.
+inline RowGeom fwd_geom(int64_t D) {
+  const int64_t nv = D / 8;
+  if (nv > 1024) return multi_wave_geom(nv, nv <= 2048 ? 128 : 256);
+  return single_wave_geom(nv);
+}
+
+// Backward: past 512 vectors (D > 4096), 4 waves per row. Measured on the
+// rows kernel per 256 MiB of x against one wave per row (2 waves past 8192):
+// D = 8192 147 -> 124 us, 12288 163 -> 132, 16384 168 -> 134 (the software
+// pipeline needs VPL <= 9 to fit the register file); D = 5120 within 2%.
+inline RowGeom bwd_geom(int64_t D) {
+  const int64_t nv = D / 8;
+  if (nv > 512) return multi_wave_geom(nv, 256);
+  return single_wave_geom(nv);
 }
 
 // Rows a wave keeps in flight per step: enough that each lane has about
@@ -71,14 +94,15 @@ inline RowGeom row_geom(int64_t D) {
 constexpr int64_t kCacheBytes = int64_t{256} << 20;
 
 constexpr int fwd_unroll(int lpr, int vpl) {
-  return lpr < 64 ? RMSN_FWD_UNROLL_NARROW : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
+  return lpr < 64 ? RMSN_FWD_UNROLL_NARROW
+                  : lpr > 64 ? 1 : (vpl == 1 ? 8 : vpl == 2 ? 4 : vpl <= 4 ? 2 : 1);
 }
 static_assert(RMSN_FWD_UNROLL_NARROW >= 1, "unroll");
 #ifndef RMSN_BWD_UNROLL_NARROW
 #define RMSN_BWD_UNROLL_NARROW 4
 #endif
 constexpr int bwd_unroll(int lpr, int vpl) {
-  return lpr < 64 ? RMSN_BWD_UNROLL_NARROW : (vpl == 1 ? 4 : vpl == 2 ? 2 : 1);
+  return lpr < 64 ? RMSN_BWD_UNROLL_NARROW : lpr > 64 ? 1 : (vpl == 1 ? 4 : vpl == 2 ? 2 : 1);
 }
 
 // Rows one workgroup step covers: (waves / waves per row) row groups of
@@ -88,7 +112,7 @@ constexpr int rows_per_block(int lpr, int unroll) {
 }
 
 inline int64_t bwd_rows_per_step(int64_t D) {
-  const RowGeom g = row_geom(D);
+  const RowGeom g = bwd_geom(D);
   return rows_per_block(g.lpr, bwd_unroll(g.lpr, g.vpl));
 }
 
@@ -117,7 +141,7 @@ struct BwdPlan {
 #endif
 inline int64_t bwd_target_chunks(int64_t D) {
   return kCus * (RMSN_BWD_BLOCKS_PER_CU > 0 ? RMSN_BWD_BLOCKS_PER_CU
-                                            : bwd_waves_per_eu(row_geom(D).vpl));
+                                            : bwd_waves_per_eu(bwd_geom(D).vpl));
 }
 
 inline BwdPlan bwd_plan(int64_t T, int64_t D) {
