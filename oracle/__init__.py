@@ -21,6 +21,7 @@ _LIB_PATH = _HERE / "liboracle_rmsnorm.so"
 _lib = None
 
 R64, A32 = 0, 1
+BF16, F16, F32 = 0, 1, 2        # storage types of activations and weights
 SILU, SIGMOID = 0, 1          # gate activations
 FP32_WEIGHT, CAST_INPUT = 0, 1  # gated-norm rounding conventions
 
@@ -78,6 +79,12 @@ def _load():
                                     vp, i64, vp], i),
         "oracle_rmsnorm_add_fwd_f64": ([vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
         "oracle_rmsnorm_add_bwd_f64": ([vp, vp, vp, vp, i, d, i64, i64, vp, vp, vp], i),
+        "oracle_f16_decode": ([vp, i64, vp], None),
+        "oracle_f16_encode": ([vp, i64, vp], None),
+        "oracle_rmsnorm_fwd_dt": ([i, i, i, vp, i64, vp, i, f, i64, i64, vp, i64, vp], i),
+        "oracle_rmsnorm_bwd_dx_dt": ([i, i, i, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp,
+                                      i64], i),
+        "oracle_rmsnorm_dgamma_dt": ([i, i, vp, i64, vp, i64, vp, i64, i64, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -402,3 +409,59 @@ def add_bwd_f64(g, x, residual, gamma, zero_centered=False, eps=1e-6, g_rout=Non
                                               int(zero_centered), eps, T, D, _p(g_rout), _p(dh),
                                               _p(dg)), "add_bwd_f64")
     return dh, dg
+
+
+# ---- activation and weight dtypes ----------------------------------------------
+
+def f16_decode(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float32)
+    _load().oracle_f16_decode(_p(bits), bits.size, _p(out))
+    return out
+
+
+def f16_encode(vals: np.ndarray) -> np.ndarray:
+    vals = np.ascontiguousarray(vals, dtype=np.float32)
+    out = np.empty(vals.shape, dtype=np.uint16)
+    _load().oracle_f16_encode(_p(vals), vals.size, _p(out))
+    return out
+
+
+def _weights(gamma, weight_dtype):
+    """gamma as stored: fp32 values, or 16-bit patterns (uint16) for BF16/F16."""
+    dt = np.float32 if weight_dtype == F32 else np.uint16
+    return np.ascontiguousarray(gamma, dtype=dt)
+
+
+def fwd_dt(x, gamma, zero_centered=False, eps=1e-6, act_dtype=BF16, weight_dtype=F32, mode=R64):
+    """(y [T, D] in the activation type's bits, rstd fp32)."""
+    x = _bf16_2d(x)
+    T, D = x.shape
+    gamma = _weights(gamma, weight_dtype)
+    y = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_fwd_dt(mode, act_dtype, weight_dtype, _p(x), _ld(x), _p(gamma),
+                                         int(zero_centered), eps, T, D, _p(y), D, _p(rstd)),
+           "fwd_dt")
+    return y, rstd
+
+
+def bwd_dt(g, x, rstd, gamma, zero_centered=False, gres=None, act_dtype=BF16,
+           weight_dtype=F32, mode=R64):
+    """(dx in the activation type's bits, dgamma fp32)."""
+    g, x = _bf16_2d(g), _bf16_2d(x)
+    T, D = x.shape
+    rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+    gamma = _weights(gamma, weight_dtype)
+    if gres is not None:
+        gres = _bf16_2d(gres)
+    dx = np.empty((T, D), dtype=np.uint16)
+    dg = np.empty(D, dtype=np.float32)
+    lib = _load()
+    _check(lib.oracle_rmsnorm_bwd_dx_dt(mode, act_dtype, weight_dtype, _p(g), _ld(g), _p(x),
+                                        _ld(x), _p(rstd), _p(gamma), int(zero_centered), T, D,
+                                        _p(gres), 0 if gres is None else _ld(gres), _p(dx), D),
+           "bwd_dx_dt")
+    _check(lib.oracle_rmsnorm_dgamma_dt(mode, act_dtype, _p(g), _ld(g), _p(x), _ld(x), _p(rstd),
+                                        T, D, _p(dg)), "dgamma_dt")
+    return dx, dg

@@ -461,6 +461,177 @@ int oracle_rmsnorm_add_bwd(int mode, const uint16_t* g, int64_t ld_g, const uint
   return 0;
 }
 
+// ---- activation and weight dtypes ---------------------------------------------
+// fp16 activations and bf16 / fp16 weights (RL-Kernel PR "C1: zero-centred
+// RMSNorm references and CUDA kernel" checks fp16 as well as bf16; Megatron-LM
+// PR "Fix the batch-invariant RMSNorm forward ...", item 1: the weight is cast
+// to fp32 and only then offset by 1). Every storage type widens to fp32
+// exactly; the arithmetic is that of the bf16 / fp32 functions above.
+
+}  // extern "C"
+
+namespace {
+
+// IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+float f16_to_f32(uint16_t h) {
+  const uint32_t sign = static_cast<uint32_t>(h & 0x8000u) << 16;
+  const int e = (h >> 10) & 0x1F;
+  const uint32_t frac = h & 0x3FFu;
+  float mag;
+  if (e == 31) {  // inf, or NaN (quieted, payload kept in the top fraction bits)
+    uint32_t u = sign | 0x7F800000u | (frac << 13) | (frac ? 0x00400000u : 0u);
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+  }
+  if (e == 0)
+    mag = std::ldexp(static_cast<float>(frac), -24);          // subnormal: frac * 2^-24
+  else
+    mag = std::ldexp(static_cast<float>(frac | 0x400u), e - 25);  // (1024 + frac) * 2^(e-25)
+  uint32_t u;
+  std::memcpy(&u, &mag, 4);
+  u |= sign;
+  std::memcpy(&mag, &u, 4);
+  return mag;
+}
+
+// Round to the nearest binary16, ties to even (the significand rounded with
+// nearbyint under the default rounding mode, in exact double arithmetic);
+// subnormals kept; |f| >= 65520 (halfway past the largest finite, 65504)
+// becomes infinity; NaN becomes a quiet NaN of the same sign.
+uint16_t f32_to_f16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  const uint16_t sign = static_cast<uint16_t>((u >> 16) & 0x8000u);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return static_cast<uint16_t>(sign | 0x7E00u | ((a >> 13) & 0x1FFu));
+  const double af = std::fabs(static_cast<double>(f));
+  if (af >= 65520.0) return static_cast<uint16_t>(sign | 0x7C00u);
+  if (af < std::ldexp(1.0, -14)) {  // subnormal range: m * 2^-24
+    const double m = std::nearbyint(af * std::ldexp(1.0, 24));
+    return static_cast<uint16_t>(sign | static_cast<uint16_t>(m));  // m = 1024 is the smallest normal
+  }
+  int e;
+  const double fr = std::frexp(af, &e);  // af = fr * 2^e, fr in [0.5, 1)
+  double sm = std::nearbyint(fr * 2048.0);  // 11-bit significand in [1024, 2048]
+  if (sm == 2048.0) {
+    sm = 1024.0;
+    e += 1;
+  }
+  const int biased = e + 14;  // af = (sm / 1024) * 2^(e - 1)
+  if (biased >= 31) return static_cast<uint16_t>(sign | 0x7C00u);
+  return static_cast<uint16_t>(sign | (biased << 10) | (static_cast<uint32_t>(sm) - 1024u));
+}
+
+float act_to_f32(int dt, uint16_t b) { return dt == ORACLE_F16 ? f16_to_f32(b) : bf16_to_f32(b); }
+uint16_t f32_to_act(int dt, float f) { return dt == ORACLE_F16 ? f32_to_f16(f) : f32_to_bf16(f); }
+bool bad_act_dt(int dt) { return dt != ORACLE_BF16 && dt != ORACLE_F16; }
+bool bad_weight_dt(int dt) { return dt != ORACLE_F32 && dt != ORACLE_BF16 && dt != ORACLE_F16; }
+
+// The weight in fp32 (exact widening), then + 1.0f in fp32 when zero-centred.
+float weight_eff_dt(int wdt, const void* gamma, int zc, int64_t j) {
+  float w;
+  if (wdt == ORACLE_F32)
+    w = static_cast<const float*>(gamma)[j];
+  else
+    w = act_to_f32(wdt, static_cast<const uint16_t*>(gamma)[j]);
+  if (zc) w = w + 1.0f;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+void oracle_f16_decode(const uint16_t* in, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f16_to_f32(in[i]);
+}
+
+void oracle_f16_encode(const float* in, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16(in[i]);
+}
+
+int oracle_rmsnorm_fwd_dt(int mode, int act_dtype, int weight_dtype, const uint16_t* x,
+                          int64_t ld_x, const void* gamma, int zero_centered, float eps, int64_t T,
+                          int64_t D, uint16_t* y, int64_t ld_y, float* rstd) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || bad_weight_dt(weight_dtype) || T < 0 || D <= 0 ||
+      !gamma || bad_2d(x, ld_x, D) || bad_2d(y, ld_y, D))
+    return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + t * ld_x;
+    Sum ss(mode);
+    for (int64_t j = 0; j < D; ++j) {
+      const float xf = act_to_f32(act_dtype, xr[j]);
+      const float sq = xf * xf;  // exact for bf16 and fp16 inputs
+      ss.add(sq);
+    }
+    const float mean = ss.value() / static_cast<float>(D);
+    const float v = mean + eps;
+    const float r = rsqrt_ref(v);
+    if (rstd) rstd[t] = r;
+    for (int64_t j = 0; j < D; ++j) {
+      const float n = row_normed(act_to_f32(act_dtype, xr[j]), r,
+                                 weight_eff_dt(weight_dtype, gamma, zero_centered, j));
+      y[t * ld_y + j] = f32_to_act(act_dtype, n);
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_bwd_dx_dt(int mode, int act_dtype, int weight_dtype, const uint16_t* g,
+                             int64_t ld_g, const uint16_t* x, int64_t ld_x, const float* rstd,
+                             const void* gamma, int zero_centered, int64_t T, int64_t D,
+                             const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || bad_weight_dt(weight_dtype) || T < 0 || D <= 0 ||
+      !gamma || !rstd || bad_2d(g, ld_g, D) || bad_2d(x, ld_x, D) || bad_2d(dx, ld_dx, D) ||
+      (gres && ld_gres < D))
+    return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* gr = g + t * ld_g;
+    const uint16_t* xr = x + t * ld_x;
+    const float r = rstd[t];
+    Sum s(mode);
+    for (int64_t i = 0; i < D; ++i) {
+      const float gw = act_to_f32(act_dtype, gr[i]) *
+                       weight_eff_dt(weight_dtype, gamma, zero_centered, i);
+      const float term = gw * act_to_f32(act_dtype, xr[i]);
+      s.add(term);
+    }
+    const float r2 = r * r;
+    const float r3 = r2 * r;
+    const float r3s = r3 * s.value();
+    const float c = r3s / static_cast<float>(D);
+    for (int64_t k = 0; k < D; ++k) {
+      const float w = weight_eff_dt(weight_dtype, gamma, zero_centered, k);
+      const float gw = act_to_f32(act_dtype, gr[k]) * w;
+      const float t1 = gw * r;
+      const float t2 = act_to_f32(act_dtype, xr[k]) * c;
+      float d = t1 - t2;
+      if (gres) d = d + act_to_f32(act_dtype, gres[t * ld_gres + k]);
+      dx[t * ld_dx + k] = f32_to_act(act_dtype, d);
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_dgamma_dt(int mode, int act_dtype, const uint16_t* g, int64_t ld_g,
+                             const uint16_t* x, int64_t ld_x, const float* rstd, int64_t T,
+                             int64_t ncols, float* dgamma) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || T < 0 || ncols <= 0 || !dgamma ||
+      bad_2d(g, ld_g, ncols) || bad_2d(x, ld_x, ncols) || (T > 0 && !rstd))
+    return -1;
+  for (int64_t j = 0; j < ncols; ++j) {
+    Sum acc(mode);
+    for (int64_t t = 0; t < T; ++t) {
+      const float gx = act_to_f32(act_dtype, g[t * ld_g + j]) * act_to_f32(act_dtype, x[t * ld_x + j]);
+      const float term = gx * rstd[t];
+      acc.add(term);
+    }
+    dgamma[j] = acc.value();
+  }
+  return 0;
+}
+
 // ---- exact double forms ----------------------------------------------------
 
 static double weight_eff_d(const double* gamma, int zc, int64_t j) {

@@ -220,6 +220,32 @@ int oracle_rmsnorm_add_bwd_f64(const double* g, const double* x,
                                int64_t D, const double* g_rout, double* dh,
                                double* dgamma);
 
+/* ---- Activation and weight dtypes --------------------------------------
+ * Storage types: activations (x, g, gres, y, dx) ORACLE_BF16 or ORACLE_F16,
+ * weights ORACLE_F32, ORACLE_BF16 or ORACLE_F16 (gamma points at that type).
+ * Each widens to fp32 exactly; the weight offset (+1.0f) follows the cast
+ * ([MEG] item 1). Results round to the activation type (RNE; binary16:
+ * subnormals kept, |v| >= 65520 -> inf). The arithmetic is that of
+ * oracle_rmsnorm_fwd / _bwd_dx / _dgamma (squares and g*x of fp16 inputs
+ * are exact in fp32 too), which equal the _dt forms with (BF16, F32). */
+enum { ORACLE_BF16 = 0, ORACLE_F16 = 1, ORACLE_F32 = 2 };
+void oracle_f16_decode(const uint16_t* in, int64_t n, float* out);
+void oracle_f16_encode(const float* in, int64_t n, uint16_t* out);
+int oracle_rmsnorm_fwd_dt(int mode, int act_dtype, int weight_dtype,
+                          const uint16_t* x, int64_t ld_x, const void* gamma,
+                          int zero_centered, float eps, int64_t T, int64_t D,
+                          uint16_t* y, int64_t ld_y, float* rstd);
+int oracle_rmsnorm_bwd_dx_dt(int mode, int act_dtype, int weight_dtype,
+                             const uint16_t* g, int64_t ld_g, const uint16_t* x,
+                             int64_t ld_x, const float* rstd, const void* gamma,
+                             int zero_centered, int64_t T, int64_t D,
+                             const uint16_t* gres, int64_t ld_gres, uint16_t* dx,
+                             int64_t ld_dx);
+int oracle_rmsnorm_dgamma_dt(int mode, int act_dtype, const uint16_t* g,
+                             int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                             const float* rstd, int64_t T, int64_t ncols,
+                             float* dgamma);
+
 /* Test-only defect planting, so the tests can show that their checks catch
  * the two defects [MEG] fixes: 0 = none; 1 = the forward ignores the
  * zero-centred offset (the backward still honours it); 2 = the second term
