@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 5
+#define RMSN_ABI_VERSION 6
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -87,8 +87,14 @@ typedef enum rmsn_status {
   RMSN_ERR_ALIASING = 6,       /* an output overlaps an input or another output */
   RMSN_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than required */
   RMSN_ERR_HIP = 8,            /* the HIP runtime refused a launch */
-  RMSN_ERR_MODE = 9            /* unknown gate activation or rounding convention */
+  RMSN_ERR_MODE = 9            /* unknown gate activation, rounding convention or dtype */
 } rmsn_status;
+
+/* Storage types for the _dt entry points: activations are RMSN_DTYPE_BF16
+ * or RMSN_DTYPE_F16, weights any of the three. */
+#define RMSN_DTYPE_BF16 0
+#define RMSN_DTYPE_F16 1
+#define RMSN_DTYPE_F32 2
 
 /* Gate activations of the gated norm (RL-Kernel PR "C1: zero-centred RMSNorm
  * references and CUDA kernel" names both; silu is its default). */
@@ -237,6 +243,33 @@ rmsn_status rmsnorm_gated_bwd(const uint16_t* g, int64_t ld_g,
                               uint16_t* dz, int64_t ld_dz, float* dgamma,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * rmsnorm_fwd and rmsnorm_bwd for other storage types. act_dtype
+ * (RMSN_DTYPE_BF16 or RMSN_DTYPE_F16) is the type of x, y, g, g_residual
+ * and dx; weight_dtype (RMSN_DTYPE_F32, _BF16 or _F16) that of gamma. Every
+ * type widens to fp32 exactly and the arithmetic is rmsnorm_fwd's /
+ * rmsnorm_bwd's; the zero-centred offset is added after the cast to fp32
+ * (Megatron-LM PR "Fix the batch-invariant RMSNorm forward ...", item 1).
+ * fp16 results round to nearest even, subnormals kept, |v| >= 65520 to
+ * infinity (RL-Kernel PR "C1: zero-centred RMSNorm references and CUDA
+ * kernel" checks fp16 beside bf16). rstd and dgamma stay fp32. gamma must be
+ * 16-byte aligned whatever its type. Unknown types return RMSN_ERR_MODE;
+ * everything else as rmsnorm_fwd / rmsnorm_bwd.
+ */
+rmsn_status rmsnorm_fwd_dt(int act_dtype, int weight_dtype, const void* x,
+                           int64_t ld_x, const void* gamma,
+                           int zero_centered_gamma, float eps, int64_t T,
+                           int64_t D, void* y, int64_t ld_y, float* rstd,
+                           void* stream);
+
+rmsn_status rmsnorm_bwd_dt(int act_dtype, int weight_dtype, const void* g,
+                           int64_t ld_g, const void* x, int64_t ld_x,
+                           const float* rstd, const void* gamma,
+                           int zero_centered_gamma, int64_t T, int64_t D,
+                           const void* g_residual, int64_t ld_gres, void* dx,
+                           int64_t ld_dx, float* dgamma, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Fused add-norm forward (RL-Kernel PR "C1: zero-centred RMSNorm references

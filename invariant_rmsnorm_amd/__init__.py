@@ -30,6 +30,12 @@ RMSN_ERR_WORKSPACE = 7
 RMSN_ERR_HIP = 8
 RMSN_ERR_MODE = 9
 
+RMSN_DTYPE_BF16 = 0
+RMSN_DTYPE_F16 = 1
+RMSN_DTYPE_F32 = 2
+_DTYPES = {torch.bfloat16: RMSN_DTYPE_BF16, torch.float16: RMSN_DTYPE_F16,
+           torch.float32: RMSN_DTYPE_F32}
+
 RMSN_GATE_SILU = 0
 RMSN_GATE_SIGMOID = 1
 RMSN_GATED_ROUND_FP32 = 0
@@ -40,6 +46,7 @@ EXPORTED = (
     "rmsnorm_gated_fwd", "rmsnorm_gated_fwd_ex", "rmsnorm_bwd_workspace_bytes",
     "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
     "rmsnorm_gated_bwd", "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_rows",
+    "rmsnorm_fwd_dt", "rmsnorm_bwd_dt",
 )
 
 
@@ -78,6 +85,9 @@ def load():
                              vp, sz, vp], i),
         "rmsnorm_add_bwd_rows": ([vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp,
                                   i64, vp, sz, vp], i),
+        "rmsnorm_fwd_dt": ([i, i, vp, i64, vp, i, f, i64, i64, vp, i64, vp, vp], i),
+        "rmsnorm_bwd_dt": ([i, i, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, vp,
+                            sz, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -344,3 +354,51 @@ def rmsnorm_add_bwd_rows(g, x, residual, rstd, gamma, zero_centered_gamma=False,
         int(zero_centered_gamma), T, D, _ptr(g_residual_out), _ld(g_residual_out), _ptr(dh),
         _ld(dh), _ptr(workspace), nbytes, _stream(x, stream)))
     return dh, workspace
+
+
+def _dt_of(t, name, allowed):
+    dt = _DTYPES.get(t.dtype)
+    if dt is None or dt not in allowed:
+        raise TypeError(f"{name}: unsupported dtype {t.dtype}")
+    return dt
+
+
+def rmsnorm_fwd_dt(x, gamma, zero_centered_gamma=False, eps=1e-6, *, y=None, rstd=None,
+                   want_rstd=True, stream=None):
+    """rmsnorm_fwd for bf16 or fp16 x (y of the same type) and fp32, bf16 or
+    fp16 gamma; returns (y, rstd or None)."""
+    adt = _dt_of(x, "x", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16))
+    wdt = _dt_of(gamma, "gamma", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16, RMSN_DTYPE_F32))
+    T, D = x.shape
+    y = torch.empty((T, D), dtype=x.dtype, device=x.device) if y is None else y
+    if rstd is None and want_rstd:
+        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check("rmsnorm_fwd_dt", load().rmsnorm_fwd_dt(
+        adt, wdt, _ptr(x), _ld(x), _ptr(gamma), int(zero_centered_gamma), eps, T, D, _ptr(y),
+        _ld(y), _ptr(rstd), _stream(x, stream)))
+    return y, rstd
+
+
+def rmsnorm_bwd_dt(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=None, dx=None,
+                   dgamma=None, want_dx=True, want_dgamma=True, workspace=None, stream=None):
+    """rmsnorm_bwd for bf16 or fp16 activations and fp32, bf16 or fp16
+    gamma; returns (dx or None, dgamma fp32 or None)."""
+    adt = _dt_of(x, "x", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16))
+    wdt = _dt_of(gamma, "gamma", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16, RMSN_DTYPE_F32))
+    if g.dtype != x.dtype:
+        raise TypeError("g and x must have the same dtype")
+    T, D = x.shape
+    if dx is None and want_dx:
+        dx = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty(D, dtype=torch.float32, device=x.device)
+    ws, nbytes = (None, 0)
+    if dgamma is not None:
+        if workspace is None:
+            workspace, _ = workspace_for(T, D, x.device)
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    _check("rmsnorm_bwd_dt", load().rmsnorm_bwd_dt(
+        adt, wdt, _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(rstd), _ptr(gamma),
+        int(zero_centered_gamma), T, D, _ptr(g_residual), _ld(g_residual), _ptr(dx), _ld(dx),
+        _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
+    return dx, dgamma

@@ -22,7 +22,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "fwd_add.hip", "bwd.hip", "bwd_gated.hip", "bwd_add.hip"]
+HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "fwd_add.hip", "fwd_f16.hip", "bwd.hip", "bwd_gated.hip",
+               "bwd_add.hip", "bwd_f16.hip"]
 CXX_SOURCES = ["api.cpp"]
 
 

@@ -86,12 +86,31 @@ rmsn_status check_f32(const float* p, uintptr_t align, bool required) {
 
 rmsn_status hip_status(int rc) { return rc == 0 ? RMSN_OK : RMSN_ERR_HIP; }
 
+// Storage types of one call: activations (bf16 or fp16) and weights (bf16,
+// fp16 or fp32). The entry points without a _dt suffix use bf16 / fp32.
+struct Types {
+  int dt = RMSN_DTYPE_BF16;
+  int wdt = RMSN_DTYPE_F32;
+};
+bool bad_types(const Types& t) {
+  return (t.dt != RMSN_DTYPE_BF16 && t.dt != RMSN_DTYPE_F16) ||
+         (t.wdt != RMSN_DTYPE_BF16 && t.wdt != RMSN_DTYPE_F16 && t.wdt != RMSN_DTYPE_F32);
+}
+int64_t weight_bytes(const Types& t) { return t.wdt == RMSN_DTYPE_F32 ? 4 : 2; }
+
+rmsn_status check_ptr(const void* p, uintptr_t align, bool required) {
+  if (p == nullptr) return required ? RMSN_ERR_NULL : RMSN_OK;
+  return aligned(p, align) ? RMSN_OK : RMSN_ERR_MISALIGNED;
+}
+
 bool bad_activation(int act) { return act != RMSN_GATE_SILU && act != RMSN_GATE_SIGMOID; }
 
 rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64_t ld_z,
-                       bool gated, int act, int rounding, const float* gamma, int zc, float eps,
+                       bool gated, int act, int rounding, const void* gamma, int zc, float eps,
                        int64_t T, int64_t D, uint16_t* y, int64_t ld_y, uint16_t* res,
-                       int64_t ld_res, bool residual, float* rstd, void* stream) {
+                       int64_t ld_res, bool residual, float* rstd, void* stream,
+                       Types ty = Types{}) {
+  if (bad_types(ty)) return RMSN_ERR_MODE;
   if (gated && (bad_activation(act) ||
                 (rounding != RMSN_GATED_ROUND_FP32 && rounding != RMSN_GATED_ROUND_CAST)))
     return RMSN_ERR_MODE;
@@ -103,16 +122,16 @@ rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64
   if (residual) RMSN_TRY(check_mat(res, ld_res, T, D, true));
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return RMSN_ERR_EPS;
   if (T == 0) return RMSN_OK;
-  RMSN_TRY(check_f32(gamma, 16, true));
+  RMSN_TRY(check_ptr(gamma, 16, true));
   RMSN_TRY(check_f32(rstd, 4, false));
   const Range outs[] = {mat_range(y, T, ld_y, D, 2), mat_range(res, T, ld_res, D, 2),
                         vec_range(rstd, T, 4)};
   const Range ins[] = {mat_range(x, T, ld_x, D, 2), mat_range(z, T, ld_z, D, 2),
-                       vec_range(gamma, D, 4)};
+                       vec_range(gamma, D, weight_bytes(ty))};
   if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
 
   rmsn::FwdArgs a{x, ld_x, gated ? z : nullptr, ld_z, act, rounding == RMSN_GATED_ROUND_CAST,
-                  gamma, zc != 0, eps, T, static_cast<int>(D), y, ld_y,
+                  gamma, ty.wdt, ty.dt, zc != 0, eps, T, static_cast<int>(D), y, ld_y,
                   residual ? res : nullptr, ld_res, rstd, nullptr, 0};
   return hip_status(rmsn::launch_fwd(a, stream));
 }
@@ -152,11 +171,13 @@ struct GateIO {
 // Checks shared by the backward entry points; `dgamma` is only checked for
 // aliasing here (rmsnorm_bwd_rows passes nullptr).
 rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
-                      const float* rstd, const float* gamma, int64_t T, int64_t D,
+                      const float* rstd, const void* gamma, int64_t T, int64_t D,
                       const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
                       bool want_part, const float* dgamma, void* ws, size_t ws_bytes,
                       bool gated = false, const GateIO& gate = GateIO{},
-                      const uint16_t* rin = nullptr, int64_t ld_rin = 0, bool add = false) {
+                      const uint16_t* rin = nullptr, int64_t ld_rin = 0, bool add = false,
+                      Types ty = Types{}) {
+  if (bad_types(ty)) return RMSN_ERR_MODE;
   if (T < 0) return RMSN_ERR_SHAPE;
   RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(g, ld_g, T, D, true));
@@ -172,7 +193,7 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
   RMSN_TRY(check_f32(rstd, 4, true));
   // The rows kernel loads the weights whatever it writes, so gamma is
   // required even for a weight-gradient-only call.
-  RMSN_TRY(check_f32(gamma, 16, true));
+  RMSN_TRY(check_ptr(gamma, 16, true));
   if (want_part) {
     if (ws == nullptr || ws_bytes < workspace_bytes(T, D)) return RMSN_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return RMSN_ERR_MISALIGNED;
@@ -182,7 +203,7 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
                                   : Range{},
                         vec_range(dgamma, D, 4), mat_range(gate.dz, T, gate.ld_dz, D, 2)};
   const Range ins[] = {mat_range(g, T, ld_g, D, 2), mat_range(x, T, ld_x, D, 2),
-                       vec_range(rstd, T, 4), vec_range(gamma, D, 4),
+                       vec_range(rstd, T, 4), vec_range(gamma, D, weight_bytes(ty)),
                        mat_range(gres, T, ld_gres, D, 2), mat_range(gate.z, T, gate.ld_z, D, 2),
                        mat_range(add ? rin : nullptr, T, ld_rin, D, 2)};
   if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
@@ -190,12 +211,12 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
 }
 
 rmsn::BwdArgs bwd_args(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
-                       const float* rstd, const float* gamma, int zc, int64_t T, int64_t D,
+                       const float* rstd, const void* gamma, int zc, int64_t T, int64_t D,
                        const uint16_t* gres, int64_t ld_gres, uint16_t* dx, int64_t ld_dx,
                        void* ws, const GateIO& gate = GateIO{}, int act = 0,
-                       const uint16_t* rin = nullptr, int64_t ld_rin = 0) {
+                       const uint16_t* rin = nullptr, int64_t ld_rin = 0, Types ty = Types{}) {
   const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
-  return rmsn::BwdArgs{g, ld_g, x, ld_x, rstd, gamma, zc != 0, T, static_cast<int>(D),
+  return rmsn::BwdArgs{g, ld_g, x, ld_x, rstd, gamma, ty.wdt, ty.dt, zc != 0, T, static_cast<int>(D),
                        dx ? gres : nullptr, ld_gres, dx, ld_dx, static_cast<float*>(ws),
                        p.chunks, p.group_blocks, gate.z, gate.ld_z, act, gate.dz, gate.ld_dz,
                        T * D * 2 > rmsn::kCacheBytes, rin, ld_rin};
@@ -360,7 +381,8 @@ rmsn_status rmsnorm_add_fwd(const uint16_t* x, int64_t ld_x, const uint16_t* res
   RMSN_TRY(check_f32(rstd, 4, false));
   if (add_fwd_alias(x, ld_x, residual, ld_res, gamma, T, D, y, ld_y, residual_out, ld_rout, rstd))
     return RMSN_ERR_ALIASING;
-  const rmsn::FwdArgs a{x, ld_x, nullptr, 0, 0, 0, gamma, zero_centered_gamma != 0, eps, T,
+  const rmsn::FwdArgs a{x, ld_x, nullptr, 0, 0, 0, gamma, RMSN_DTYPE_F32, RMSN_DTYPE_BF16,
+                        zero_centered_gamma != 0, eps, T,
                         static_cast<int>(D), y, ld_y, residual_out, ld_rout, rstd, residual,
                         ld_res};
   return hip_status(rmsn::launch_fwd(a, stream));
@@ -399,6 +421,41 @@ rmsn_status rmsnorm_add_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, 
                                      g_residual_out, ld_gro, dh, ld_dh,
                                      dgamma != nullptr ? workspace : nullptr, GateIO{}, 0,
                                      residual, ld_res);
+    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
+  }
+  if (dgamma == nullptr) return RMSN_OK;
+  return finish_dgamma(workspace, T, D, dgamma, stream);
+}
+
+rmsn_status rmsnorm_fwd_dt(int act_dtype, int weight_dtype, const void* x, int64_t ld_x,
+                           const void* gamma, int zero_centered_gamma, float eps, int64_t T,
+                           int64_t D, void* y, int64_t ld_y, float* rstd, void* stream) {
+  return fwd_common(static_cast<const uint16_t*>(x), ld_x, nullptr, 0, false, 0, 0, gamma,
+                    zero_centered_gamma, eps, T, D, static_cast<uint16_t*>(y), ld_y, nullptr, 0,
+                    false, rstd, stream, Types{act_dtype, weight_dtype});
+}
+
+rmsn_status rmsnorm_bwd_dt(int act_dtype, int weight_dtype, const void* g, int64_t ld_g,
+                           const void* x, int64_t ld_x, const float* rstd, const void* gamma,
+                           int zero_centered_gamma, int64_t T, int64_t D, const void* g_residual,
+                           int64_t ld_gres, void* dx, int64_t ld_dx, float* dgamma,
+                           void* workspace, size_t workspace_bytes_, void* stream) {
+  const Types ty{act_dtype, weight_dtype};
+  if (bad_types(ty)) return RMSN_ERR_MODE;
+  if (dx == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
+  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
+  const auto* g16 = static_cast<const uint16_t*>(g);
+  const auto* x16 = static_cast<const uint16_t*>(x);
+  const auto* gr16 = static_cast<const uint16_t*>(g_residual);
+  auto* dx16 = static_cast<uint16_t*>(dx);
+  RMSN_TRY(check_bwd(g16, ld_g, x16, ld_x, rstd, gamma, T, D, gr16, ld_gres, dx16, ld_dx,
+                     dgamma != nullptr, dgamma, workspace, workspace_bytes_, false, GateIO{},
+                     nullptr, 0, false, ty));
+  if (T > 0) {
+    const rmsn::BwdArgs a = bwd_args(g16, ld_g, x16, ld_x, rstd, gamma, zero_centered_gamma, T, D,
+                                     gr16, ld_gres, dx16, ld_dx,
+                                     dgamma != nullptr ? workspace : nullptr, GateIO{}, 0, nullptr,
+                                     0, ty);
     RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
   }
   if (dgamma == nullptr) return RMSN_OK;

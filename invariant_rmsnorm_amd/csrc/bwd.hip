@@ -1,6 +1,7 @@
 // Backward launchers: the plain and residual-gradient rows kernels (the
 // template is in bwd_kernel.hpp; the gated forms are in bwd_gated.hip, the
-// fused add-norm forms in bwd_add.hip) and the dgamma finish kernel.
+// fused add-norm forms in bwd_add.hip, fp16 activations in bwd_f16.hip) and
+// the dgamma finish kernel.
 //
 // Finish: dgamma[j] = a fixed tree over 16 slices, each slice an ascending
 // sum over a contiguous range of the chunk partials. The grouping depends on
@@ -65,6 +66,7 @@ int launch_bwd_rows(const BwdArgs& a, void* stream) {
   if (a.T == 0 || a.chunks == 0) return 0;
   if (a.z != nullptr) return launch_bwd_rows_gated(a, stream);
   if (a.rin != nullptr) return launch_bwd_rows_add(a, stream);
+  if (a.dt == kF16) return launch_bwd_rows_f16(a, stream);
   const RowGeom g = bwd_geom(a.D);
   const bwd_detail::RowsLaunch f =
       a.gres != nullptr ? bwd_detail::pick<kBwdGres>(g) : bwd_detail::pick<kBwdPlain>(g);

@@ -81,7 +81,7 @@ inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
   return w > m ? w : m;
 }
 
-template <int LPR, int VPL, bool MASKED, int MODE>
+template <int LPR, int VPL, bool MASKED, int MODE, int DT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL))))
 void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr bool ADD = MODE == kBwdAdd || MODE == kBwdAddGres;
@@ -116,15 +116,19 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   float4* const wl4 = reinterpret_cast<float4*>(lds);
   if constexpr (LEAN) {
     // float4 h (0/1) of vector c = v*LPR + l goes to slot (2v + h)*LPR + l
-    for (int j = threadIdx.x; j < 2 * nv; j += kBlock) {
-      const int c = j >> 1, h = j & 1;
-      float4 q = reinterpret_cast<const float4*>(a.gamma)[j];
-      if (a.zc) { q.x = q.x + 1.0f; q.y = q.y + 1.0f; q.z = q.z + 1.0f; q.w = q.w + 1.0f; }
-      wl4[((c / LPR) * 2 + h) * LPR + (c % LPR)] = q;
+    for (int c = threadIdx.x; c < nv; c += kBlock) {
+      float w8[8];
+      weights8(a.gamma, a.wdt, c, w8);
+      if (a.zc) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w8[k] = w8[k] + 1.0f;
+      }
+      wl4[((c / LPR) * 2) * LPR + (c % LPR)] = make_float4(w8[0], w8[1], w8[2], w8[3]);
+      wl4[((c / LPR) * 2 + 1) * LPR + (c % LPR)] = make_float4(w8[4], w8[5], w8[6], w8[7]);
     }
     __syncthreads();
   } else {
-    load_weights<LPR, (LEAN ? 1 : VPL), MASKED>(a.gamma, a.zc, nv, l, wreg);
+    load_weights<LPR, (LEAN ? 1 : VPL), MASKED>(a.gamma, a.wdt, a.zc, nv, l, wreg);
   }
   // In the lean plan `base` is an opaque zero, so that the LDS reads stay
   // inside the row loop instead of being hoisted into registers.
@@ -235,10 +239,10 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
     // rounding, as in the forward).
     auto row_values = [&](int u, int v, float (&f)[8]) {
-      unpack8(b.xq[u][v], f);
+      unpack8<DT>(b.xq[u][v], f);
       if constexpr (ADD) {
         float rf[8];
-        unpack8(b.hq[u][v], rf);
+        unpack8<DT>(b.hq[u][v], rf);
 #pragma unroll
         for (int k = 0; k < 8; ++k) f[k] = f[k] + rf[k];
       }
@@ -262,12 +266,12 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       for (int v = 0; v < VPL; ++v) {
         if (MASKED && v * LPR + l >= nv) continue;  // no such vector (weights unset)
         float gf[8], xf[8], w8[8];
-        unpack8(b.gq[u][v], gf);
+        unpack8<DT>(b.gq[u][v], gf);
         row_values(u, v, xf);
         weights(wbase, v, w8);
         if constexpr (GATED) {
           float zf[8], dz8[8];
-          unpack8(b.zq[u][v], zf);
+          unpack8<DT>(b.zq[u][v], zf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             float ag, dag;
@@ -278,7 +282,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
             dz8[k] = gnw * dag;
             gf[k] = gf[k] * ag;
           }
-          buf_store16_nt(pack8(dz8), rdz, voff(v, a.ld_dz));
+          buf_store16_nt(pack8<DT>(dz8), rdz, voff(v, a.ld_dz));
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -314,12 +318,12 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       for (int v = 0; v < VPL; ++v) {
         if (MASKED && v * LPR + l >= nv) continue;
         float gf[8], xf[8], w8[8], o[8];
-        unpack8(b.gq[u][v], gf);
+        unpack8<DT>(b.gq[u][v], gf);
         row_values(u, v, xf);
         weights(wbase, v, w8);
         if constexpr (GATED) {
           float zf[8];
-          unpack8(b.zq[u][v], zf);
+          unpack8<DT>(b.zq[u][v], zf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) gf[k] = gf[k] * gate<ACT>(zf[k]);
         }
@@ -332,11 +336,11 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         }
         if constexpr (GRES) {
           float rf[8];
-          unpack8(b.rres[u][v], rf);
+          unpack8<DT>(b.rres[u][v], rf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
         }
-        buf_store16_nt(pack8(o), rdx, voff(v, a.ld_dx));
+        buf_store16_nt(pack8<DT>(o), rdx, voff(v, a.ld_dx));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -462,7 +466,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 
 namespace bwd_detail {
 
-template <int LPR, int VPL, bool MASKED, int MODE>
+template <int LPR, int VPL, bool MASKED, int MODE, int DT>
 int launch_inst(const BwdArgs& a, void* stream) {
   constexpr bool THREE = MODE == kBwdGatedSilu || MODE == kBwdGatedSigmoid || MODE == kBwdAdd ||
                          MODE == kBwdAddGres;
@@ -472,12 +476,12 @@ int launch_inst(const BwdArgs& a, void* stream) {
   if (lds > 64 * 1024) {
     static const int lds_ok = [] {
       return static_cast<int>(hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, MODE>),
+          reinterpret_cast<const void*>(&rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, MODE, DT>),
           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024));
     }();
     if (lds_ok != 0) return lds_ok;
   }
-  hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, MODE>),
+  hipLaunchKernelGGL((rmsnorm_bwd_rows_kernel<LPR, VPL, MASKED, MODE, DT>),
                      dim3(static_cast<unsigned>(a.chunks)), dim3(kBlock), lds,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
@@ -485,40 +489,40 @@ int launch_inst(const BwdArgs& a, void* stream) {
 
 using RowsLaunch = int (*)(const BwdArgs&, void*);
 
-template <int MODE, int VPL = 1>
+template <int MODE, int DT, int VPL = 1>
 RowsLaunch pick_wide(int vpl, bool masked) {
   if constexpr (VPL > kMaxVpl) {
     return nullptr;
   } else {
     if (vpl == VPL)
-      return masked ? &launch_inst<64, VPL, true, MODE> : &launch_inst<64, VPL, false, MODE>;
-    return pick_wide<MODE, VPL + 1>(vpl, masked);
+      return masked ? &launch_inst<64, VPL, true, MODE, DT> : &launch_inst<64, VPL, false, MODE, DT>;
+    return pick_wide<MODE, DT, VPL + 1>(vpl, masked);
   }
 }
 
 // Rows over 4 waves (D > 4096): 3 to 16 vectors per lane.
-template <int MODE, int LPR, int VPL = kBwdMinVplMulti>
+template <int MODE, int DT, int LPR, int VPL = kBwdMinVplMulti>
 RowsLaunch pick_multi(int vpl, bool masked) {
   if constexpr (VPL > kMaxVpl) {
     return nullptr;
   } else {
     if (vpl == VPL)
-      return masked ? &launch_inst<LPR, VPL, true, MODE> : &launch_inst<LPR, VPL, false, MODE>;
-    return pick_multi<MODE, LPR, VPL + 1>(vpl, masked);
+      return masked ? &launch_inst<LPR, VPL, true, MODE, DT> : &launch_inst<LPR, VPL, false, MODE, DT>;
+    return pick_multi<MODE, DT, LPR, VPL + 1>(vpl, masked);
   }
 }
 
-template <int MODE>
+template <int MODE, int DT = kBf16>
 RowsLaunch pick(const RowGeom& g) {
   switch (g.lpr) {
-    case 256: return pick_multi<MODE, 256>(g.vpl, g.masked);
-    case 64: return pick_wide<MODE>(g.vpl, g.masked);
-    case 32: return g.masked ? &launch_inst<32, 1, true, MODE> : &launch_inst<32, 1, false, MODE>;
-    case 16: return g.masked ? &launch_inst<16, 1, true, MODE> : &launch_inst<16, 1, false, MODE>;
-    case 8: return g.masked ? &launch_inst<8, 1, true, MODE> : &launch_inst<8, 1, false, MODE>;
-    case 4: return g.masked ? &launch_inst<4, 1, true, MODE> : &launch_inst<4, 1, false, MODE>;
-    case 2: return &launch_inst<2, 1, false, MODE>;
-    case 1: return &launch_inst<1, 1, false, MODE>;
+    case 256: return pick_multi<MODE, DT, 256>(g.vpl, g.masked);
+    case 64: return pick_wide<MODE, DT>(g.vpl, g.masked);
+    case 32: return g.masked ? &launch_inst<32, 1, true, MODE, DT> : &launch_inst<32, 1, false, MODE, DT>;
+    case 16: return g.masked ? &launch_inst<16, 1, true, MODE, DT> : &launch_inst<16, 1, false, MODE, DT>;
+    case 8: return g.masked ? &launch_inst<8, 1, true, MODE, DT> : &launch_inst<8, 1, false, MODE, DT>;
+    case 4: return g.masked ? &launch_inst<4, 1, true, MODE, DT> : &launch_inst<4, 1, false, MODE, DT>;
+    case 2: return &launch_inst<2, 1, false, MODE, DT>;
+    case 1: return &launch_inst<1, 1, false, MODE, DT>;
     default: return nullptr;
   }
 }

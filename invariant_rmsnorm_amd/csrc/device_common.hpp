@@ -11,6 +11,11 @@ namespace rmsn {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Storage types (the ABI's RMSN_DTYPE_* values): activations are bf16 or
+// fp16, weights bf16, fp16 or fp32.
+enum : int { kBf16 = 0, kF16 = 1, kF32 = 2 };
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
@@ -25,6 +30,23 @@ __device__ __forceinline__ void unpack8(const u32x4& q, float (&f)[8]) {
   f[6] = bf16_lo(q.w); f[7] = bf16_hi(q.w);
 }
 
+// fp16 pair -> fp32 pair (exact, v_cvt_f32_f16), the low half first.
+__device__ __forceinline__ f32x2 f16_pair(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
+
+// Unpack 8 activations of storage type DT (kBf16 or kF16).
+template <int DT>
+__device__ __forceinline__ void unpack8(const u32x4& q, float (&f)[8]) {
+  if constexpr (DT == kBf16) {
+    unpack8(q, f);
+  } else {
+    const f32x2 a = f16_pair(q.x), b = f16_pair(q.y), c = f16_pair(q.z), d = f16_pair(q.w);
+    f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y;
+    f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+  }
+}
+
 // fp32 pair -> packed bf16 pair with round-to-nearest-even (one
 // v_cvt_pk_bf16_f32 on gfx950); the first value lands in the low half.
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -35,6 +57,24 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
   return u32x4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+}
+
+// fp32 pair -> fp16 pair, round to nearest even (the default rounding mode;
+// fp16 subnormals are kept, overflow goes to infinity).
+__device__ __forceinline__ uint32_t pack2_f16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Pack 8 fp32 values to storage type DT with one rounding each.
+template <int DT>
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  if constexpr (DT == kBf16) {
+    return pack8(f);
+  } else {
+    return u32x4{pack2_f16(f[0], f[1]), pack2_f16(f[2], f[3]), pack2_f16(f[4], f[5]),
+                 pack2_f16(f[6], f[7])};
+  }
 }
 
 // ---- buffer access -----------------------------------------------------------
@@ -290,19 +330,33 @@ __device__ __forceinline__ void gate_and_grad(float z, float& a, float& da) {
 // Rounds 8 fp32 values to bf16 and back (round to nearest even).
 __device__ __forceinline__ void round8_bf16(float (&f)[8]) { unpack8(pack8(f), f); }
 
-// Loads this lane's weights w_eff = gamma (+1.0f in fp32 when zero-centred)
-// for its vectors c = v*LPR + l; columns past D read as zero.
+// The 8 weights of vector c in fp32, widened exactly from their storage
+// type `wdt` (the weights are read once per workgroup, so the type is a
+// run-time choice).
+__device__ __forceinline__ void weights8(const void* __restrict__ gamma, int wdt, int c,
+                                         float (&w)[8]) {
+  if (wdt == kF32) {
+    const float4 a = reinterpret_cast<const float4*>(gamma)[2 * c];
+    const float4 b = reinterpret_cast<const float4*>(gamma)[2 * c + 1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else {
+    const u32x4 q = reinterpret_cast<const u32x4*>(gamma)[c];
+    if (wdt == kF16) unpack8<kF16>(q, w);
+    else unpack8<kBf16>(q, w);
+  }
+}
+
+// Loads this lane's weights w_eff = fp32(gamma) (+1.0f in fp32 when
+// zero-centred) for its vectors c = v*LPR + l; columns past D read as zero.
 template <int LPR, int VPL, bool MASKED>
-__device__ __forceinline__ void load_weights(const float* __restrict__ gamma, int zc, int nv,
-                                             int l, float (&w)[VPL][8]) {
+__device__ __forceinline__ void load_weights(const void* __restrict__ gamma, int wdt, int zc,
+                                             int nv, int l, float (&w)[VPL][8]) {
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int c = v * LPR + l;
     if (!MASKED || c < nv) {
-      const float4 a = *reinterpret_cast<const float4*>(gamma + 8 * c);
-      const float4 b = *reinterpret_cast<const float4*>(gamma + 8 * c + 4);
-      w[v][0] = a.x; w[v][1] = a.y; w[v][2] = a.z; w[v][3] = a.w;
-      w[v][4] = b.x; w[v][5] = b.y; w[v][6] = b.z; w[v][7] = b.w;
+      weights8(gamma, wdt, c, w[v]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) w[v][k] = 0.0f;

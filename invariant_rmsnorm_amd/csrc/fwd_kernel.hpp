@@ -37,7 +37,7 @@ namespace rmsn {
 constexpr int fwd_gate_code(bool gated, int act, bool cast) { return gated ? 1 + act + 2 * cast : 0; }
 constexpr int kFwdAdd = 5;
 
-template <int LPR, int VPL, bool MASKED, int GATE>
+template <int LPR, int VPL, bool MASKED, int GATE, int DT>
 __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   constexpr bool ADD = GATE == kFwdAdd;
   constexpr bool GATED = GATE != 0 && !ADD;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS_BLOCK;
 
   float w[VPL][8];
-  load_weights<LPR, VPL, MASKED>(a.gamma, a.zc, nv, l, w);
+  load_weights<LPR, VPL, MASKED>(a.gamma, a.wdt, a.zc, nv, l, w);
 
   // Byte offset of this lane's vector v within its row group, per tensor;
   // vectors past D get an offset no resource reaches.
@@ -103,10 +103,10 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
   // rounding).
   auto row_values = [&](const u32x4& xv, const u32x4& rv, float (&f)[8]) {
-    unpack8(xv, f);
+    unpack8<DT>(xv, f);
     if constexpr (ADD) {
       float rf[8];
-      unpack8(rv, rf);
+      unpack8<DT>(rv, rf);
 #pragma unroll
       for (int k = 0; k < 8; ++k) f[k] = f[k] + rf[k];
     }
@@ -155,11 +155,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
         if constexpr (GATED) {
           if constexpr (CAST) round8_bf16(o);
           float zf[8];
-          unpack8(zq[u][v], zf);
+          unpack8<DT>(zq[u][v], zf);
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] * gate_fast<ACT>(zf[k]);
         }
-        buf_store16_nt(pack8(o), ry, voff(v, a.ld_y));
+        buf_store16_nt(pack8<DT>(o), ry, voff(v, a.ld_y));
       }
       if (a.res != nullptr) {
         // residual output: a byte copy of x, or for the fused add bf16(h)
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
           if constexpr (ADD) {
             float f[8];
             row_values(xq[u][v], zq[u][v], f);
-            buf_store16_nt(pack8(f), rr, voff(v, a.ld_res));
+            buf_store16_nt(pack8<DT>(f), rr, voff(v, a.ld_res));
           } else {
             buf_store16_nt(xq[u][v], rr, voff(v, a.ld_res));
           }
@@ -201,10 +201,10 @@ inline int cu_count() {
   return n;
 }
 
-template <int LPR, int VPL, bool MASKED, int GATE>
+template <int LPR, int VPL, bool MASKED, int GATE, int DT>
 int launch_inst(const FwdArgs& a, void* stream) {
   constexpr int ROWS_BLOCK = rows_per_block(LPR, fwd_unroll(LPR, VPL));
-  auto kern = rmsnorm_fwd_kernel<LPR, VPL, MASKED, GATE>;
+  auto kern = rmsnorm_fwd_kernel<LPR, VPL, MASKED, GATE, DT>;
   static const int per_cu = [&] {
     int b = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, kBlock, 0) != hipSuccess || b < 1)
@@ -224,41 +224,41 @@ int launch_inst(const FwdArgs& a, void* stream) {
 
 using FwdLaunch = int (*)(const FwdArgs&, void*);
 
-template <int GATE, int VPL = 1>
+template <int GATE, int DT, int VPL = 1>
 FwdLaunch pick_wide(int vpl, bool masked) {
   if constexpr (VPL > kMaxVpl) {
     return nullptr;
   } else {
     if (vpl == VPL)
-      return masked ? &launch_inst<64, VPL, true, GATE> : &launch_inst<64, VPL, false, GATE>;
-    return pick_wide<GATE, VPL + 1>(vpl, masked);
+      return masked ? &launch_inst<64, VPL, true, GATE, DT> : &launch_inst<64, VPL, false, GATE, DT>;
+    return pick_wide<GATE, DT, VPL + 1>(vpl, masked);
   }
 }
 
 // Rows over several waves (D > 8192): 9 to 16 vectors per lane.
-template <int GATE, int LPR, int VPL = kFwdMinVplMulti>
+template <int GATE, int DT, int LPR, int VPL = kFwdMinVplMulti>
 FwdLaunch pick_multi(int vpl, bool masked) {
   if constexpr (VPL > kMaxVpl) {
     return nullptr;
   } else {
     if (vpl == VPL)
-      return masked ? &launch_inst<LPR, VPL, true, GATE> : &launch_inst<LPR, VPL, false, GATE>;
-    return pick_multi<GATE, LPR, VPL + 1>(vpl, masked);
+      return masked ? &launch_inst<LPR, VPL, true, GATE, DT> : &launch_inst<LPR, VPL, false, GATE, DT>;
+    return pick_multi<GATE, DT, LPR, VPL + 1>(vpl, masked);
   }
 }
 
-template <int GATE>
+template <int GATE, int DT = kBf16>
 FwdLaunch pick(const RowGeom& g) {
   switch (g.lpr) {
-    case 256: return pick_multi<GATE, 256>(g.vpl, g.masked);
-    case 128: return pick_multi<GATE, 128>(g.vpl, g.masked);
-    case 64: return pick_wide<GATE>(g.vpl, g.masked);
-    case 32: return g.masked ? &launch_inst<32, 1, true, GATE> : &launch_inst<32, 1, false, GATE>;
-    case 16: return g.masked ? &launch_inst<16, 1, true, GATE> : &launch_inst<16, 1, false, GATE>;
-    case 8: return g.masked ? &launch_inst<8, 1, true, GATE> : &launch_inst<8, 1, false, GATE>;
-    case 4: return g.masked ? &launch_inst<4, 1, true, GATE> : &launch_inst<4, 1, false, GATE>;
-    case 2: return &launch_inst<2, 1, false, GATE>;
-    case 1: return &launch_inst<1, 1, false, GATE>;
+    case 256: return pick_multi<GATE, DT, 256>(g.vpl, g.masked);
+    case 128: return pick_multi<GATE, DT, 128>(g.vpl, g.masked);
+    case 64: return pick_wide<GATE, DT>(g.vpl, g.masked);
+    case 32: return g.masked ? &launch_inst<32, 1, true, GATE, DT> : &launch_inst<32, 1, false, GATE, DT>;
+    case 16: return g.masked ? &launch_inst<16, 1, true, GATE, DT> : &launch_inst<16, 1, false, GATE, DT>;
+    case 8: return g.masked ? &launch_inst<8, 1, true, GATE, DT> : &launch_inst<8, 1, false, GATE, DT>;
+    case 4: return g.masked ? &launch_inst<4, 1, true, GATE, DT> : &launch_inst<4, 1, false, GATE, DT>;
+    case 2: return &launch_inst<2, 1, false, GATE, DT>;
+    case 1: return &launch_inst<1, 1, false, GATE, DT>;
     default: return nullptr;
   }
 }

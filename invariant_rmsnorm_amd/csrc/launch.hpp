@@ -15,7 +15,9 @@ struct FwdArgs {
   int64_t ld_z;
   int act;   // gate activation: 0 silu, 1 sigmoid
   int cast;  // gated rounding convention: 0 weight multiply in fp32, 1 casts
-  const float* gamma;
+  const void* gamma;  // weights of storage type wdt
+  int wdt;            // kBf16, kF16 or kF32
+  int dt;             // activation storage type: kBf16 or kF16
   int zc;
   float eps;
   int64_t T;
@@ -35,7 +37,9 @@ struct BwdArgs {
   const uint16_t* x;
   int64_t ld_x;
   const float* rstd;
-  const float* gamma;
+  const void* gamma;  // weights of storage type wdt
+  int wdt;            // kBf16, kF16 or kF32
+  int dt;             // activation storage type: kBf16 or kF16
   int zc;
   int64_t T;
   int D;
@@ -61,9 +65,11 @@ struct BwdArgs {
 int launch_fwd(const FwdArgs& a, void* stream);
 int launch_fwd_gated(const FwdArgs& a, void* stream);  // a.z != nullptr
 int launch_fwd_add(const FwdArgs& a, void* stream);    // a.rin != nullptr
+int launch_fwd_f16(const FwdArgs& a, void* stream);    // a.dt == fp16 (plain, residual copy)
 int launch_bwd_rows(const BwdArgs& a, void* stream);
 int launch_bwd_rows_gated(const BwdArgs& a, void* stream);  // a.z != nullptr
 int launch_bwd_rows_add(const BwdArgs& a, void* stream);    // a.rin != nullptr
+int launch_bwd_rows_f16(const BwdArgs& a, void* stream);    // a.dt == fp16 (plain, gres)
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
 
 }  // namespace rmsn

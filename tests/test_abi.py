@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 5
+    assert irn.rmsnorm_abi_version() == 6
 
 
 def test_status_strings():
@@ -330,3 +330,22 @@ def test_add_backward_rows_rejections():
     assert lib.rmsnorm_add_bwd_rows(*args, None, 4096, None, 0, None) == irn.RMSN_ERR_NULL
     assert lib.rmsnorm_add_bwd_rows(*args, F, 4096, None, 0, None) == irn.RMSN_ERR_ALIASING
     assert lib.rmsnorm_add_bwd_rows(*args, C, 4096, W, 16, None) == irn.RMSN_ERR_WORKSPACE
+
+
+# ---- storage types ------------------------------------------------------------------
+
+def test_dtype_entry_points_reject_bad_types():
+    lib = irn.load()
+    ok = (A, 4096, GAM, 0, 1e-6, 8, 4096, B, 4096, RS, None)
+    for adt, wdt in ((2, 2), (3, 2), (-1, 2), (0, 3), (1, 7)):
+        assert lib.rmsnorm_fwd_dt(adt, wdt, *ok) == irn.RMSN_ERR_MODE
+    assert lib.rmsnorm_fwd_dt(1, 0, A, 4096, GAM + 8, 0, 1e-6, 8, 4096, B, 4096, RS,
+                              None) == irn.RMSN_ERR_MISALIGNED
+    # rstd 8 KiB past gamma overlaps an fp32 weight vector of 4096 (16 KiB)
+    assert lib.rmsnorm_fwd_dt(1, 2, A, 4096, GAM, 0, 1e-6, 8, 4096, B, 4096, GAM + 8192,
+                              None) == irn.RMSN_ERR_ALIASING
+    bargs = (A, 4096, B, 4096, RS, GAM, 0, 1000, 4096, None, 0, C, 4096, E, W, 1 << 30, None)
+    assert lib.rmsnorm_bwd_dt(5, 2, *bargs) == irn.RMSN_ERR_MODE
+    assert lib.rmsnorm_bwd_dt(1, 9, *bargs) == irn.RMSN_ERR_MODE
+    assert lib.rmsnorm_bwd_dt(1, 2, A, 4096, B, 4096, RS, GAM, 0, 1000, 4096, None, 0, None, 0,
+                              None, W, 1 << 30, None) == irn.RMSN_ERR_NULL
