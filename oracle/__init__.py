@@ -85,6 +85,7 @@ def _load():
         "oracle_rmsnorm_bwd_dx_dt": ([i, i, i, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp,
                                       i64], i),
         "oracle_rmsnorm_dgamma_dt": ([i, i, vp, i64, vp, i64, vp, i64, i64, vp], i),
+        "oracle_gemm_xwt": ([vp, i64, vp, i64, i64, i64, i64, vp, i64, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -465,3 +466,19 @@ def bwd_dt(g, x, rstd, gamma, zero_centered=False, gres=None, act_dtype=BF16,
     _check(lib.oracle_rmsnorm_dgamma_dt(mode, act_dtype, _p(g), _ld(g), _p(x), _ld(x), _p(rstd),
                                         T, D, _p(dg)), "dgamma_dt")
     return dx, dg
+
+
+# ---- batch-invariant GEMM --------------------------------------------------------
+
+def gemm_xwt(x, w):
+    """(Y bf16 [M, N], exact double sums [M, N]) of Y = X @ W.T for bf16
+    X [M, K] and W [N, K]."""
+    x, w = _bf16_2d(x), _bf16_2d(w)
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape[1] == K
+    y = np.empty((M, N), dtype=np.uint16)
+    ye = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_gemm_xwt(_p(x), _ld(x) if M > 1 else K, _p(w), _ld(w) if N > 1 else K,
+                                   M, N, K, _p(y), N, _p(ye)), "gemm_xwt")
+    return y, ye

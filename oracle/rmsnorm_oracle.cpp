@@ -632,6 +632,29 @@ int oracle_rmsnorm_dgamma_dt(int mode, int act_dtype, const uint16_t* g, int64_t
   return 0;
 }
 
+// ---- batch-invariant GEMM ----------------------------------------------------
+// TransformerEngine issue "Expose Batch Invariant Kernels", point 3: BF16,
+// Y = X @ W.T over contiguous 2-D operands. The plain definition: each
+// output is the dot product of a row of X and a row of W; here it is summed
+// in double in ascending k (the products of bf16 values are exact in double),
+// rounded to fp32 and then to bf16.
+
+int oracle_gemm_xwt(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, int64_t M,
+                    int64_t N, int64_t K, uint16_t* Y, int64_t ldy, double* Y_exact) {
+  if (M < 0 || N < 0 || K < 0 || !X || !W || !Y || ldx < K || ldw < K || ldy < N) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        acc += static_cast<double>(bf16_to_f32(X[i * ldx + k])) *
+               static_cast<double>(bf16_to_f32(W[j * ldw + k]));
+      if (Y_exact) Y_exact[i * N + j] = acc;
+      Y[i * ldy + j] = f32_to_bf16(static_cast<float>(acc));
+    }
+  }
+  return 0;
+}
+
 // ---- exact double forms ----------------------------------------------------
 
 static double weight_eff_d(const double* gamma, int zc, int64_t j) {

@@ -16,6 +16,8 @@
  *         the +1 of the zero-centred weight is an fp32 operation; the gated
  *         norm's SiLU gate with the weight multiply in fp32; the backward
  *         reuses the forward's saved rstd.
+ *  [TE]   TransformerEngine issue "Expose Batch Invariant Kernels": the
+ *         batch-invariant BF16 GEMM Y = X @ W.T (point 3).
  *  [RES]  RL-Kernel PR "[DSv4][P1-5] rmsnorm_residual", sections "Summary",
  *         "Implementation" and the review comment: output is RMSNorm(x) plus
  *         a byte copy of x; bf16 activations, fp32 gamma, fp32 saved inverse
@@ -245,6 +247,14 @@ int oracle_rmsnorm_dgamma_dt(int mode, int act_dtype, const uint16_t* g,
                              int64_t ld_g, const uint16_t* x, int64_t ld_x,
                              const float* rstd, int64_t T, int64_t ncols,
                              float* dgamma);
+
+/* ---- Batch-invariant GEMM ([TE] point 3: BF16 Y = X @ W.T) -------------
+ * X bf16 [M, K] (row stride ldx), W bf16 [N, K] (ldw), Y bf16 [M, N] (ldy):
+ * Y[i][j] = bf16(fp32(sum over k ascending of X[i][k] * W[j][k])), the sum in
+ * double. Y_exact (may be NULL, contiguous [M, N]) receives the double sums. */
+int oracle_gemm_xwt(const uint16_t* X, int64_t ldx, const uint16_t* W,
+                    int64_t ldw, int64_t M, int64_t N, int64_t K, uint16_t* Y,
+                    int64_t ldy, double* Y_exact);
 
 /* Test-only defect planting, so the tests can show that their checks catch
  * the two defects [MEG] fixes: 0 = none; 1 = the forward ignores the
