@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 6
+#define RMSN_ABI_VERSION 7
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -324,6 +324,27 @@ rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g,
                                  const uint16_t* g_residual_out, int64_t ld_gro,
                                  uint16_t* dh, int64_t ld_dh, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Batch-invariant BF16 GEMM, Y = X @ W.T (TransformerEngine issue "Expose
+ * Batch Invariant Kernels", point 3: the library GEMM chose its algorithm,
+ * and so its reduction order, from the whole shape; fixed tiles and a fixed
+ * K loop make a row of Y independent of the other rows and of M).
+ * X bf16 [M, K] and W bf16 [N, K], row-major with K contiguous; Y bf16
+ * [M, N] row-major. Each output is a dot product accumulated in fp32 over K
+ * in ascending steps of 32 on the matrix cores (the same tile geometry for
+ * every shape; no split-K) and rounded once to bf16. Every row of Y is
+ * bitwise identical whatever M, the row's position and the other rows are.
+ * Supported: K a positive multiple of 32; K <= ld_x, ld_w <= 2^21 and
+ * ld_x, ld_w multiples of 8 with X and W 16-byte aligned; ld_y >= N, Y
+ * 2-byte aligned. Errors: RMSN_ERR_SHAPE (negative sizes, strides),
+ * RMSN_ERR_UNSUPPORTED_D (K not a positive multiple of 32), RMSN_ERR_NULL,
+ * RMSN_ERR_MISALIGNED, RMSN_ERR_ALIASING (Y overlaps X or W), RMSN_ERR_HIP.
+ * M = 0 or N = 0 enqueue nothing. No workspace; one kernel on `stream`.
+ */
+rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w,
+                            int64_t ld_w, int64_t M, int64_t N, int64_t K,
+                            uint16_t* y, int64_t ld_y, void* stream);
 
 #ifdef __cplusplus
 }

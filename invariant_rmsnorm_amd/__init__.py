@@ -46,7 +46,7 @@ EXPORTED = (
     "rmsnorm_gated_fwd", "rmsnorm_gated_fwd_ex", "rmsnorm_bwd_workspace_bytes",
     "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
     "rmsnorm_gated_bwd", "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_rows",
-    "rmsnorm_fwd_dt", "rmsnorm_bwd_dt",
+    "rmsnorm_fwd_dt", "rmsnorm_bwd_dt", "bigemm_bf16_xwt",
 )
 
 
@@ -88,6 +88,7 @@ def load():
         "rmsnorm_fwd_dt": ([i, i, vp, i64, vp, i, f, i64, i64, vp, i64, vp, vp], i),
         "rmsnorm_bwd_dt": ([i, i, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, vp,
                             sz, vp], i),
+        "bigemm_bf16_xwt": ([vp, i64, vp, i64, i64, i64, i64, vp, i64, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -402,3 +403,18 @@ def rmsnorm_bwd_dt(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=N
         int(zero_centered_gamma), T, D, _ptr(g_residual), _ld(g_residual), _ptr(dx), _ld(dx),
         _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
     return dx, dgamma
+
+
+def bigemm_bf16_xwt(x, w, *, y=None, stream=None):
+    """Y = X @ W.T for bf16 X [M, K] and W [N, K] (K a multiple of 32), each
+    row of Y independent of the batch around it."""
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(w, torch.bfloat16, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w must have the same K")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _check("bigemm_bf16_xwt", load().bigemm_bf16_xwt(
+        _ptr(x), _ld(x), _ptr(w), _ld(w), M, N, K, _ptr(y), _ld(y), _stream(x, stream)))
+    return y

@@ -462,4 +462,23 @@ rmsn_status rmsnorm_bwd_dt(int act_dtype, int weight_dtype, const void* g, int64
   return finish_dgamma(workspace, T, D, dgamma, stream);
 }
 
+rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w, int64_t ld_w,
+                            int64_t M, int64_t N, int64_t K, uint16_t* y, int64_t ld_y,
+                            void* stream) {
+  if (M < 0 || N < 0 || K < 0) return RMSN_ERR_SHAPE;
+  if (K == 0 || K % 32 != 0) return RMSN_ERR_UNSUPPORTED_D;
+  constexpr int64_t kMaxGemmLd = int64_t{1} << 21;  // keeps 256-row byte counts below 2^30
+  if (ld_x < K || ld_w < K || ld_y < N || ld_x > kMaxGemmLd || ld_w > kMaxGemmLd)
+    return RMSN_ERR_SHAPE;
+  if (M == 0 || N == 0) return RMSN_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return RMSN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || ld_x % 8 != 0 || ld_w % 8 != 0 || !aligned(y, 2))
+    return RMSN_ERR_MISALIGNED;
+  const Range outs[] = {mat_range(y, M, ld_y, N, 2)};
+  const Range ins[] = {mat_range(x, M, ld_x, K, 2), mat_range(w, N, ld_w, K, 2)};
+  if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
+  const rmsn::GemmArgs a{x, ld_x, w, ld_w, M, N, K, y, ld_y};
+  return hip_status(rmsn::launch_gemm(a, stream));
+}
+
 }  // extern "C"

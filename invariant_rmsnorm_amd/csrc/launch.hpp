@@ -61,6 +61,16 @@ struct BwdArgs {
   int64_t ld_rin;
 };
 
+struct GemmArgs {
+  const uint16_t* x;  // bf16 [M, K]
+  int64_t ld_x;
+  const uint16_t* w;  // bf16 [N, K]
+  int64_t ld_w;
+  int64_t M, N, K;
+  uint16_t* y;  // bf16 [M, N]
+  int64_t ld_y;
+};
+
 // Each returns 0 on success or the HIP error code of a refused launch.
 int launch_fwd(const FwdArgs& a, void* stream);
 int launch_fwd_gated(const FwdArgs& a, void* stream);  // a.z != nullptr
@@ -71,5 +81,6 @@ int launch_bwd_rows_gated(const BwdArgs& a, void* stream);  // a.z != nullptr
 int launch_bwd_rows_add(const BwdArgs& a, void* stream);    // a.rin != nullptr
 int launch_bwd_rows_f16(const BwdArgs& a, void* stream);    // a.dt == fp16 (plain, gres)
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
+int launch_gemm(const GemmArgs& a, void* stream);
 
 }  // namespace rmsn

@@ -28,7 +28,7 @@ RS = A + (6 << 36)
 
 def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(rmsnorm_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:rmsnorm|bigemm)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 6
+    assert irn.rmsnorm_abi_version() == 7
 
 
 def test_status_strings():
@@ -349,3 +349,35 @@ def test_dtype_entry_points_reject_bad_types():
     assert lib.rmsnorm_bwd_dt(1, 9, *bargs) == irn.RMSN_ERR_MODE
     assert lib.rmsnorm_bwd_dt(1, 2, A, 4096, B, 4096, RS, GAM, 0, 1000, 4096, None, 0, None, 0,
                               None, W, 1 << 30, None) == irn.RMSN_ERR_NULL
+
+
+# ---- batch-invariant GEMM -------------------------------------------------------------
+
+def gemm(**kw):
+    a = dict(x=A, ld_x=4096, w=B, ld_w=4096, M=64, N=4096, K=4096, y=C, ld_y=4096)
+    a.update(kw)
+    return irn.load().bigemm_bf16_xwt(a["x"], a["ld_x"], a["w"], a["ld_w"], a["M"], a["N"],
+                                      a["K"], a["y"], a["ld_y"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), irn.RMSN_ERR_SHAPE),
+    (dict(K=4008, ld_x=4008, ld_w=4008), irn.RMSN_ERR_UNSUPPORTED_D),   # K % 32 == 8
+    (dict(K=0), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(ld_x=4088), irn.RMSN_ERR_SHAPE),
+    (dict(ld_y=4000), irn.RMSN_ERR_SHAPE),
+    (dict(ld_w=(1 << 21) + 8), irn.RMSN_ERR_SHAPE),
+    (dict(x=None), irn.RMSN_ERR_NULL),
+    (dict(y=None), irn.RMSN_ERR_NULL),
+    (dict(x=A + 8), irn.RMSN_ERR_MISALIGNED),
+    (dict(ld_w=4100), irn.RMSN_ERR_MISALIGNED),
+    (dict(y=A + 1024), irn.RMSN_ERR_ALIASING),
+    (dict(y=B), irn.RMSN_ERR_ALIASING),
+])
+def test_gemm_rejections(kw, code):
+    assert gemm(**kw) == code
+
+
+def test_gemm_empty_is_a_noop():
+    assert gemm(M=0, x=None, y=None) == irn.RMSN_OK
+    assert gemm(N=0, w=None, y=None) == irn.RMSN_OK

@@ -1,0 +1,121 @@
+"""GPU checks of the batch-invariant BF16 GEMM (bigemm_bf16_xwt) against
+the CPU oracle, following TransformerEngine issue "Expose Batch Invariant
+Kernels", point 3: one anchor row placed first / in the middle / last in
+batches of M in {1, 2, 17, 33, 128, 257, 1024}, a shuffled batch and a
+non-tile-aligned M = 1000, compared bytewise with the M = 1 result; accuracy
+against an exact (double) product.
+
+Tolerance against the oracle's exact sums: the fp32 accumulation over K
+terms is within gamma_K = K u / (1 - K u) of sum |x w| (u = 2^-24), so the
+bf16 result must be a correct rounding of a value within that bound of the
+exact sum (numerics.rounding_consistent). Integer inputs whose sums are
+exact in fp32 must match the oracle bitwise.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import invariant_rmsnorm_amd as irn
+import oracle
+import synth
+from gpu_util import dev_bf16, host_bits
+from numerics import U32, bf16_to_f64, f32_to_bf16_torch, rounding_consistent
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_parity(x, w, y_bits):
+    _, ye = oracle.gemm_xwt(x, w)
+    K = x.shape[1]
+    scale = np.abs(bf16_to_f64(x)) @ np.abs(bf16_to_f64(w)).T
+    gamma = K * U32 / (1 - K * U32)
+    ok = rounding_consistent(y_bits, ye, gamma * scale)
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} outside the accumulation bound"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 32), (5, 64, 64), (17, 300, 256), (256, 128, 96),
+                                   (300, 257, 512), (257, 1000, 1024), (1000, 1024, 2048)])
+def test_gemm_parity(gpu, M, N, K):
+    x = synth.normal_bf16(2100 + M, 1, M, K)
+    w = synth.normal_bf16(2100 + M, 2, N, K)
+    y = irn.bigemm_bf16_xwt(dev_bf16(x), dev_bf16(w))
+    torch.cuda.synchronize()
+    _check_parity(x, w, host_bits(y))
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 40, 32), (300, 200, 640), (129, 1030, 1024)])
+def test_gemm_exact_integers_bitwise(gpu, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    xi = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    wi = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
+    x, w = f32_to_bf16_torch(xi), f32_to_bf16_torch(wi)
+    y = irn.bigemm_bf16_xwt(dev_bf16(x), dev_bf16(w))
+    ref, _ = oracle.gemm_xwt(x, w)
+    assert np.array_equal(host_bits(y), ref)
+
+
+def test_gemm_strided_operands(gpu):
+    M, N, K = 200, 300, 256
+    x = synth.normal_bf16(2120, 1, M, K)
+    w = synth.normal_bf16(2120, 2, N, K)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    xs = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros((N, K + 32), dtype=torch.bfloat16, device="cuda")
+    xs[:, :K] = xd
+    ws[:, 32:] = wd
+    ys = torch.zeros((M, N + 3), dtype=torch.bfloat16, device="cuda")
+    irn.bigemm_bf16_xwt(xs[:, :K], ws[:, 32:], y=ys[:, :N])
+    y = irn.bigemm_bf16_xwt(xd, wd)
+    assert torch.equal(ys[:, :N], y)
+    assert torch.all(ys[:, N:] == 0)  # nothing written past N
+
+
+M_SET = (1, 2, 17, 33, 128, 257, 1024)
+
+
+def test_gemm_anchor_rows_across_batches(gpu):
+    """The page's check: anchor rows, bitwise equal to their M = 1 result in
+    every batch size and position; padding and shuffles; M = 1000."""
+    N = K = 2048
+    w = dev_bf16(synth.normal_bf16(2130, 2, N, K))
+    filler = synth.normal_bf16(2131, 1, 1024, K)
+    for a in range(3):
+        anchor = synth.normal_bf16(2132 + a, 1, 1, K)
+        ref = irn.bigemm_bf16_xwt(dev_bf16(anchor), w)
+        _check_parity(anchor, host_bits(w), host_bits(ref))
+        for M in M_SET + (1000,):
+            for pos in sorted({0, M // 2, M - 1}):
+                xb = filler[:M].copy()
+                xb[pos] = anchor[0]
+                y = irn.bigemm_bf16_xwt(dev_bf16(xb), w)
+                assert torch.equal(y[pos:pos + 1], ref), (a, M, pos)
+        # shuffled batch with zero padding rows appended
+        perm = np.random.default_rng(2140 + a).permutation(300)
+        xb = np.concatenate([filler[:299], anchor, np.zeros((7, K), np.uint16)])[perm.tolist() + list(range(300, 307))]
+        pos = int(np.where(perm == 299)[0][0])
+        y = irn.bigemm_bf16_xwt(dev_bf16(xb), w)
+        assert torch.equal(y[pos:pos + 1], ref)
+        assert torch.all(y[300:].float() == 0)
+
+
+def test_gemm_row_slices_equal_full_batch(gpu):
+    """Every slice of a batch gives the same bytes as the full batch."""
+    M, N, K = 1024, 1024, 1024
+    x = dev_bf16(synth.normal_bf16(2150, 1, M, K))
+    w = dev_bf16(synth.normal_bf16(2150, 2, N, K))
+    full = irn.bigemm_bf16_xwt(x, w)
+    for a, b in ((0, 1), (3, 5), (255, 257), (100, 1000), (1000, 1024), (0, 1024)):
+        assert torch.equal(irn.bigemm_bf16_xwt(x[a:b], w), full[a:b]), (a, b)
+
+
+@pytest.mark.slow
+def test_gemm_full_size_sampled(gpu):
+    """M = N = K = 4096: 64 sampled rows against the oracle."""
+    M = N = K = 4096
+    x = synth.normal_bf16(2160, 1, M, K)
+    w = synth.normal_bf16(2160, 2, N, K)
+    y = irn.bigemm_bf16_xwt(dev_bf16(x), dev_bf16(w))
+    rows = np.random.default_rng(2160).choice(M, 64, replace=False)
+    _check_parity(x[rows], w, host_bits(y)[rows])
