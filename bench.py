@@ -17,6 +17,13 @@ are per-kernel times from separate passes whose steps bracket every kernel
 with events (events make the GPU drain the stream, so those passes run a few
 microseconds per event slower than the timed steps). `cpu_baseline` times the
 CPU oracle on the host cores for the same workload.
+
+--workload gemm times the batch-invariant BF16 GEMM Y = X @ W.T instead
+(bigemm_bf16_xwt, M = N = K = 4096 unless --m/--n/--k say otherwise): a
+step is one GEMM, `value` is 2MNK flops per step / wall time in TFLOP/s, and
+`roofline` compares the kernel with the 2.5 PFLOP/s dense bf16 matrix-core
+peak; torch.matmul (the library GEMM, which is not batch-invariant) is timed
+beside it for context.
 """
 from __future__ import annotations
 
@@ -34,6 +41,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "RMSNorm fwd+bwd GB/s and % HBM peak, T=32768 D=4096 bf16, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_bwd_rows_T32768_D4096.json"
 # sources of the rows kernel: a committed counter figure is used only while
 # these are unchanged
@@ -166,13 +174,141 @@ def cpu_baseline(p, workload: str, seconds: float):
     return dt, passes, nthreads
 
 
+def gemm_cpu_baseline(x, w, seconds: float):
+    """The CPU oracle's GEMM (double sums, as it stands) on a sample of the
+    workload: blocks of 8 rows of X against all of W, threads over blocks,
+    until `seconds` of wall time have passed. Returns (wall seconds, rows,
+    threads)."""
+    import oracle
+
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    M = x.shape[0]
+    blk = 8
+
+    def rows_block(i):
+        a = (i * blk) % M
+        oracle.gemm_xwt(x[a:a + blk], w)
+
+    done = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nthreads) as ex:
+        i = 0
+        while done == 0 or time.perf_counter() - t0 < seconds:
+            list(ex.map(rows_block, range(i, i + nthreads)))
+            i += nthreads
+            done += nthreads * blk
+    return time.perf_counter() - t0, done, nthreads
+
+
+def bench_gemm(args, torch, irn, dev):
+    """Batch-invariant BF16 GEMM leg: one bigemm_bf16_xwt per step."""
+    import numpy as np
+    import synth
+
+    M, N, K = args.m, args.n, args.k
+    xb = synth.normal_bf16(7007, 1, M, K)
+    wb = synth.normal_bf16(7007, 2, N, K, scale=K ** -0.5)
+
+    def d_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w = d_bf16(xb), d_bf16(wb)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        irn.bigemm_bf16_xwt(x, w, y=y)
+
+    step()
+    ref = y.clone()
+    step()
+    torch.cuda.synchronize()
+    if not torch.equal(ref, y):
+        raise SystemExit("repeat GEMM is not bitwise identical")
+    del ref
+    for _ in range(args.warmup):
+        step()
+    every = max(1, args.event_every)
+    sampled = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for i in range(0, args.steps, every)}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev = sampled.get(i)
+        if ev is not None:
+            ev[0].record(stream)
+        step()
+        if ev is not None:
+            ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(a.elapsed_time(b) for a, b in sampled.values()) / len(sampled)
+    flops = 2.0 * M * N * K
+    ms_step = wall * 1e3 / args.steps
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+
+    # the library GEMM on the same operands, for context only
+    wt = w.t()
+    for _ in range(10):
+        torch.matmul(x, wt)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_lib = max(10, min(args.steps, 200))
+    e0.record(stream)
+    for _ in range(n_lib):
+        torch.matmul(x, wt)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lib_ms = e0.elapsed_time(e1) / n_lib
+
+    cpu = None
+    if not args.no_cpu:
+        dt, rows, nthreads = gemm_cpu_baseline(xb, wb, args.cpu_seconds)
+        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": nthreads, "kind": "oracle",
+               "sample": f"{rows} rows of X (blocks of 8) against all {N} rows of W, "
+                         f"K={K}, {dt:.1f} s wall"}
+
+    out = {
+        "metric": f"Batch-invariant BF16 GEMM TFLOP/s, Y = X @ W.T, M={M} N={N} K={K}, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate_dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"batch-invariant GEMM Y = X @ W.T, M={M}, N={N}, K={K}, "
+                               "bf16 X ~N(0,1), W ~N(0,1/K)",
+                   "M": M, "N": N, "K": K, "flops_per_step": flops, "parallelism": "single GPU"},
+        "library_gemm": {"kernel": "torch.matmul (not batch-invariant)", "ms": round(lib_ms, 5),
+                         "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 2),
+                         "bigemm_over_library_time": round(launch_ms / lib_ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "bigemm_kernel", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "launch_ms": round(launch_ms, 5),
+                     "launches_timed": len(sampled)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="token",
-                    choices=["token", "token_gres", "large", "gated", "add"])
+                    choices=["token", "token_gres", "large", "gated", "add", "gemm"])
+    ap.add_argument("--m", type=int, default=4096, help="gemm workload: rows of X and Y")
+    ap.add_argument("--n", type=int, default=4096, help="gemm workload: rows of W, columns of Y")
+    ap.add_argument("--k", type=int, default=4096, help="gemm workload: reduction length")
     ap.add_argument("--rows", type=int, default=0,
                     help="token workloads: batch rows T (default 32768, the metric's size)")
     ap.add_argument("--dim", type=int, default=0,
@@ -202,6 +338,9 @@ def main():
     irn.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "gemm":
+        bench_gemm(args, torch, irn, dev)
+        return
     p, t, desc = make_inputs(args.workload, torch, dev, args.rows, args.dim)
     T, D = p.T, p.D
     zc, eps = p.zero_centered, p.eps

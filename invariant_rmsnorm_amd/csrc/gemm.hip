@@ -3,21 +3,31 @@
 // TransformerEngine issue "Expose Batch Invariant Kernels", point 3: the
 // library GEMM was not batch-invariant because the algorithm (and with it
 // the reduction order) was chosen from the whole problem shape; a GEMM whose
-// output tiles accumulate over K in a fixed BLOCK_K loop, with the tile grid
-// derived from tile coordinates only and no split-K, is invariant. Here:
-//  - one tile geometry for every shape: 256 x 128 outputs per workgroup,
-//    4 waves of 128 x 64 each, MFMA 32x32x16 bf16 with fp32 accumulation;
-//  - K in steps of 32 (two MFMA k-steps), always ascending, each step
-//    staged through LDS (double-buffered: the next step's global loads are
-//    in flight while this one multiplies);
-//  - rows of X past M and rows of W past N read as zero (buffer resources),
-//    and outputs past M or N are not stored, so a row of Y is computed the
-//    same way whatever M is.
+// output tiles accumulate over K in a fixed BLOCK_K loop, with no split-K, is
+// invariant. What fixes an output element's value here is its arithmetic
+// alone: an fp32 accumulator that starts at zero and takes one
+// v_mfma_f32_32x32x16_bf16 step per 16 consecutive k, in ascending k, then
+// one rounding to bf16. Every kernel below does exactly that for every
+// element, so the tile shape (which may follow M, N and K) changes which
+// workgroup computes an element, never how.
+//
+// The kernel is a template over its tile:
+//  - TM x TN MFMA blocks of 32 x 32 per wave, WGM x WGN waves per workgroup,
+//    so a workgroup owns BM = 32 TM WGM rows by BN = 32 TN WGN columns;
+//  - K in stages of BK, staged through LDS twice over: while the waves
+//    multiply stage s out of one buffer, stage s + 1 is written from
+//    registers into the other and stage s + 2 is loaded from memory into
+//    the registers;
+//  - rows of X past M and rows of W past N read as zero (buffer
+//    resources), outputs past M or N are not stored, and in a last stage of
+//    32 valid k (K = 32 mod 64) the MFMA steps past K are skipped.
 // X [M, K] and W [N, K] are row-major with K contiguous: MFMA lane l takes
 // 8 consecutive k of row l % 32 at k-offset 8 * (l / 32) for both operands,
 // and holds output rows 8 * (r / 4) + 4 * (l / 32) + r % 4 (r = 0..15) of
 // column l % 32.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -26,121 +36,216 @@ namespace rmsn {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 128, kBK = 32;
-constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row: 64 B of data + 16 B of padding
-
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(256) void bigemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLdsRow];
+template <int TM, int TN, int WGM, int WGN, int BK>
+struct GemmTile {
+  static constexpr int kThreads = 64 * WGM * WGN;
+  static constexpr int BM = 32 * TM * WGM, BN = 32 * TN * WGN;
+  static constexpr int kRow = BK + 8;           // bf16 per LDS row (16 B of padding)
+  static constexpr int kChunks = BK / 8;        // 16-byte chunks per row and stage
+  static constexpr int kLoadsA = BM * kChunks / kThreads;
+  static constexpr int kLoadsB = BN * kChunks / kThreads;
+  static constexpr int kStageElems = (BM + BN) * kRow;
+  static constexpr int kLdsBytes = 2 * kStageElems * 2;
+  static_assert(BK % 32 == 0, "stage of whole 32-k halves");
+  static_assert(BM * kChunks % kThreads == 0 && BN * kChunks % kThreads == 0, "loads");
+};
 
-  const int64_t tiles_n = (a.N + kBN - 1) / kBN;
-  const int64_t m0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * kBM;
-  const int64_t n0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * kBN;
+// Tile (tm, tn) of workgroup b. Workgroups go to the 8 XCDs round-robin
+// (b mod 8); consecutive tiles are given to one XCD, and tiles are numbered
+// in groups of kGroupM tile rows, column by column within a group, so the
+// tiles an XCD runs at one time share few rows of X and of W in its L2.
+#ifndef RMSN_GEMM_XCDS
+#define RMSN_GEMM_XCDS 8
+#endif
+#ifndef RMSN_GEMM_GROUP_M
+#define RMSN_GEMM_GROUP_M 4
+#endif
+constexpr int kXcds = RMSN_GEMM_XCDS, kGroupM = RMSN_GEMM_GROUP_M;
+__device__ __forceinline__ void tile_of(int64_t b, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                        int64_t& tn) {
+  const int64_t P = tiles_m * tiles_n;
+  const int64_t xcd = b % kXcds, j = b / kXcds;
+  const int64_t per = (P + kXcds - 1) / kXcds;
+  const int64_t tall = P % kXcds == 0 ? kXcds : P % kXcds;  // XCDs that take `per` tiles
+  const int64_t t = xcd < tall ? xcd * per + j : tall * per + (xcd - tall) * (per - 1) + j;
+  const int64_t in_group = kGroupM * tiles_n;
+  const int64_t first_m = (t / in_group) * kGroupM;
+  const int64_t rows = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  tm = first_m + (t % in_group) % rows;
+  tn = (t % in_group) / rows;
+}
+
+template <int TM, int TN, int WGM, int WGN, int BK>
+__global__ __launch_bounds__(64 * WGM * WGN) void bigemm_kernel(GemmArgs a) {
+  using G = GemmTile<TM, TN, WGM, WGN, BK>;
+  constexpr int S = BK / 16;                       // MFMA k-steps per stage
+  constexpr int L = G::kLoadsA + G::kLoadsB;       // 16-byte chunks per thread and stage
+  static_assert(L % S == 0, "chunks spread evenly over the k-steps");
+  constexpr int PER = L / S;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+
+  int64_t tm, tn;
+  tile_of(blockIdx.x, (a.M + G::BM - 1) / G::BM, (a.N + G::BN - 1) / G::BN, tm, tn);
+  const int64_t m0 = tm * G::BM, n0 = tn * G::BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int K = static_cast<int>(a.K);
 
-  // The tile's rows of X and of W (rows past M or N are outside the
-  // resources and read as zero).
-  const auto rx = rows_rsrc(a.x, m0, a.M, kBM, a.ld_x, static_cast<int>(a.K));
-  const auto rw = rows_rsrc(a.w, n0, a.N, kBN, a.ld_w, static_cast<int>(a.K));
+  const auto rx = rows_rsrc(a.x, m0, a.M, G::BM, a.ld_x, K);
+  const auto rw = rows_rsrc(a.w, n0, a.N, G::BN, a.ld_w, K);
 
-  // Global -> registers -> LDS: 16-byte chunk q of a stage is row q / 4,
-  // columns 8 * (q % 4) .. +8 of the 32 k of the stage.
-  u32x4 ga[4], gb[2];
-  auto load_global = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = t + 256 * i;
-      ga[i] = buf_load16(rx, static_cast<uint32_t>(((q >> 2) * a.ld_x + k0 + 8 * (q & 3)) * 2));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = t + 256 * i;
-      gb[i] = buf_load16(rw, static_cast<uint32_t>(((q >> 2) * a.ld_w + k0 + 8 * (q & 3)) * 2));
-    }
+  // Chunk c of a thread (A chunks first, then B): 16-byte chunk q of a
+  // stage's rows of X (or W), row q / kChunks, k-offset 8 * (q % kChunks),
+  // with q = t + kThreads * (c, or c - kLoadsA).
+  u32x4 g[L];
+  auto chunk_q = [&](int c) { return t + G::kThreads * (c < G::kLoadsA ? c : c - G::kLoadsA); };
+  auto load_chunk = [&](int c, int k0) {
+    const int q = chunk_q(c);
+    if (c < G::kLoadsA)
+      g[c] = buf_load16(rx, static_cast<uint32_t>(
+                                ((q / G::kChunks) * a.ld_x + k0 + 8 * (q % G::kChunks)) * 2));
+    else
+      g[c] = buf_load16(rw, static_cast<uint32_t>(
+                                ((q / G::kChunks) * a.ld_w + k0 + 8 * (q % G::kChunks)) * 2));
   };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = t + 256 * i;
-      *reinterpret_cast<u32x4*>(&As[buf][(q >> 2) * kLdsRow + 8 * (q & 3)]) = ga[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = t + 256 * i;
-      *reinterpret_cast<u32x4*>(&Bs[buf][(q >> 2) * kLdsRow + 8 * (q & 3)]) = gb[i];
-    }
+  auto store_chunk = [&](int c, int buf) {
+    const int q = chunk_q(c);
+    uint16_t* base = lds + buf * G::kStageElems + (c < G::kLoadsA ? 0 : G::BM * G::kRow);
+    *reinterpret_cast<u32x4*>(&base[(q / G::kChunks) * G::kRow + 8 * (q % G::kChunks)]) = g[c];
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  auto compute = [&](int buf) {
+  // MFMA operands of k-step s of a stage out of LDS buffer buf.
+  struct Frags {
+    bf16x8 a[TM], b[TN];
+  };
+  auto read_frags = [&](Frags& f, int buf, int s) {
+    const uint16_t* As = lds + buf * G::kStageElems + (wm * 32 * TM + (lane & 31)) * G::kRow;
+    const uint16_t* Bs = lds + buf * G::kStageElems + G::BM * G::kRow +
+                         (wn * 32 * TN + (lane & 31)) * G::kRow;
+    const int kk = 16 * s + 8 * (lane >> 5);
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int kk = 16 * s + 8 * (lane >> 5);
-      bf16x8 fa[4], fb[2];
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(&As[32 * i * G::kRow + kk]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(
-            &As[buf][(wm * 128 + 32 * i + (lane & 31)) * kLdsRow + kk]);
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[32 * j * G::kRow + kk]);
+  };
+  auto mfma = [&](const Frags& f) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[buf][(wn * 64 + 32 * j + (lane & 31)) * kLdsRow + kk]);
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  const int64_t nk = a.K / kBK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = static_cast<int>(kt & 1);
-    if (kt + 1 < nk) load_global((kt + 1) * kBK);
-    compute(cur);
-    // the other buffer was last read in the previous step, before its barrier
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+  // One full stage out of buffer cur. Beside the k-steps it writes the next
+  // stage from the registers into buffer cur ^ 1 (STORE; that buffer was
+  // last read in the previous stage, before its closing barrier) and loads
+  // the stage at k_next2 into the registers (LOAD), a few chunks per k-step.
+  Frags f[2];
+  auto stage = [&](auto store_tag, auto load_tag, int cur, int k_next2) {
+    constexpr bool STORE = decltype(store_tag)::value, LOAD = decltype(load_tag)::value;
+    read_frags(f[0], cur, 0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (s + 1 < S) read_frags(f[(s + 1) & 1], cur, s + 1);
+      mfma(f[s & 1]);
+      if constexpr (STORE) {
+#pragma unroll
+        for (int c = s * PER; c < (s + 1) * PER; ++c) store_chunk(c, cur ^ 1);
+      }
+      if constexpr (LOAD) {
+#pragma unroll
+        for (int c = s * PER; c < (s + 1) * PER; ++c) load_chunk(c, k_next2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __syncthreads();
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+
+  const int nk = (K + BK - 1) / BK;
+  const int last_steps = (K - (nk - 1) * BK) / 16;
+#pragma unroll
+  for (int c = 0; c < L; ++c) load_chunk(c, 0);
+#pragma unroll
+  for (int c = 0; c < L; ++c) store_chunk(c, 0);
+  if (nk > 1) {
+#pragma unroll
+    for (int c = 0; c < L; ++c) load_chunk(c, BK);
+  }
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) stage(yes{}, yes{}, kt & 1, (kt + 2) * BK);
+  if (kt + 1 < nk) {
+    stage(yes{}, no{}, kt & 1, 0);
+    ++kt;
+  }
+  // Last stage: `last_steps` k-steps (S, or 2 when K = 32 mod 64).
+  {
+    const int cur = kt & 1;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (s >= last_steps) break;
+      read_frags(f[0], cur, s);
+      mfma(f[0]);
+    }
   }
 
   // Epilogue: each fp32 sum rounded once to bf16; lanes 0..31 store 32
   // consecutive columns of one row, lanes 32..63 the same columns 4 rows on.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + 32 * j + (lane & 31);
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = n0 + wn * 32 * TN + 32 * j + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t row = m0 + wm * 32 * TM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row < a.M && col < a.N)
           a.y[row * a.ld_y + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][r]));
       }
     }
 }
 
+template <int TM, int TN, int WGM, int WGN, int BK>
+int launch_tile(const GemmArgs& a, void* stream) {
+  using G = GemmTile<TM, TN, WGM, WGN, BK>;
+  auto* kern = &bigemm_kernel<TM, TN, WGM, WGN, BK>;
+  if (G::kLdsBytes > 64 * 1024) {
+    static const int lds_ok = [kern] {
+      return static_cast<int>(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  G::kLdsBytes));
+    }();
+    if (lds_ok != 0) return lds_ok;
+  }
+  const int64_t tiles = ((a.M + G::BM - 1) / G::BM) * ((a.N + G::BN - 1) / G::BN);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(G::kThreads), G::kLdsBytes,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
 }  // namespace
+
+// Tile of the kernel: TM, TN, WGM, WGN, BK.
+#ifndef RMSN_GEMM_TILE
+#define RMSN_GEMM_TILE 4, 2, 2, 4, 64
+#endif
 
 int launch_gemm(const GemmArgs& a, void* stream) {
   if (a.M == 0 || a.N == 0) return 0;
-  const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(bigemm_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return static_cast<int>(hipGetLastError());
+  return launch_tile<RMSN_GEMM_TILE>(a, stream);
 }
 
 }  // namespace rmsn

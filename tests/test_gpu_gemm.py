@@ -35,7 +35,8 @@ def _check_parity(x, w, y_bits):
     assert ok.all(), f"{(~ok).sum()} of {ok.size} outside the accumulation bound"
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 32), (5, 64, 64), (17, 300, 256), (256, 128, 96),
+@pytest.mark.parametrize("M,N,K", [(1, 128, 32), (5, 64, 64), (64, 96, 128), (33, 200, 160),
+                                   (70, 130, 192), (17, 300, 256), (256, 128, 96),
                                    (300, 257, 512), (257, 1000, 1024), (1000, 1024, 2048)])
 def test_gemm_parity(gpu, M, N, K):
     x = synth.normal_bf16(2100 + M, 1, M, K)
