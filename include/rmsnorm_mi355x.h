@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 7
+#define RMSN_ABI_VERSION 8
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -331,20 +331,31 @@ rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g,
  * and so its reduction order, from the whole shape; fixed tiles and a fixed
  * K loop make a row of Y independent of the other rows and of M).
  * X bf16 [M, K] and W bf16 [N, K], row-major with K contiguous; Y bf16
- * [M, N] row-major. Each output is a dot product accumulated in fp32 over K
- * in ascending steps of 32 on the matrix cores (the same tile geometry for
- * every shape; no split-K) and rounded once to bf16. Every row of Y is
- * bitwise identical whatever M, the row's position and the other rows are.
+ * [M, N] row-major. Each output is a dot product accumulated in fp32 from
+ * zero over K in ascending steps of 16 (one 32x32x16 bf16 matrix-core step
+ * each; no split-K) and rounded once to bf16. The output tile a workgroup
+ * computes follows M and N (bigemm_bf16_tile), but an output's arithmetic
+ * does not, so every row of Y is bitwise identical whatever M, the row's
+ * position and the other rows are.
  * Supported: K a positive multiple of 32; K <= ld_x, ld_w <= 2^21 and
  * ld_x, ld_w multiples of 8 with X and W 16-byte aligned; ld_y >= N, Y
- * 2-byte aligned. Errors: RMSN_ERR_SHAPE (negative sizes, strides),
- * RMSN_ERR_UNSUPPORTED_D (K not a positive multiple of 32), RMSN_ERR_NULL,
- * RMSN_ERR_MISALIGNED, RMSN_ERR_ALIASING (Y overlaps X or W), RMSN_ERR_HIP.
+ * 2-byte aligned. Errors: RMSN_ERR_SHAPE (negative sizes, strides, or more
+ * than 2^31 - 1 tiles of 32 x 64), RMSN_ERR_UNSUPPORTED_D (K not a positive
+ * multiple of 32), RMSN_ERR_NULL, RMSN_ERR_MISALIGNED, RMSN_ERR_ALIASING
+ * (Y overlaps X or W), RMSN_ERR_HIP.
  * M = 0 or N = 0 enqueue nothing. No workspace; one kernel on `stream`.
  */
 rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w,
                             int64_t ld_w, int64_t M, int64_t N, int64_t K,
                             uint16_t* y, int64_t ld_y, void* stream);
+
+/* The output tile (rows of Y x columns of Y per workgroup) bigemm_bf16_xwt
+ * uses for an M x N product: the largest of 256x256, 128x256, 128x128,
+ * 64x128, 32x128 that gives at least 256 tiles (one per compute unit),
+ * else 32x64. A host-side query: it enqueues nothing and needs no GPU.
+ * Errors: RMSN_ERR_SHAPE (M or N negative), RMSN_ERR_NULL (an output
+ * pointer is NULL). */
+rmsn_status bigemm_bf16_tile(int64_t M, int64_t N, int64_t* tile_m, int64_t* tile_n);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,7 @@ EXPORTED = (
     "rmsnorm_gated_fwd", "rmsnorm_gated_fwd_ex", "rmsnorm_bwd_workspace_bytes",
     "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
     "rmsnorm_gated_bwd", "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_rows",
-    "rmsnorm_fwd_dt", "rmsnorm_bwd_dt", "bigemm_bf16_xwt",
+    "rmsnorm_fwd_dt", "rmsnorm_bwd_dt", "bigemm_bf16_xwt", "bigemm_bf16_tile",
 )
 
 
@@ -89,6 +89,7 @@ def load():
         "rmsnorm_bwd_dt": ([i, i, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, vp,
                             sz, vp], i),
         "bigemm_bf16_xwt": ([vp, i64, vp, i64, i64, i64, i64, vp, i64, vp], i),
+        "bigemm_bf16_tile": ([i64, i64, vp, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -418,3 +419,10 @@ def bigemm_bf16_xwt(x, w, *, y=None, stream=None):
     _check("bigemm_bf16_xwt", load().bigemm_bf16_xwt(
         _ptr(x), _ld(x), _ptr(w), _ld(w), M, N, K, _ptr(y), _ld(y), _stream(x, stream)))
     return y
+
+
+def bigemm_bf16_tile(M: int, N: int):
+    """(rows, columns) of the output tile bigemm_bf16_xwt uses for M x N."""
+    out = [ctypes.c_int64(0) for _ in range(2)]
+    _check("bigemm_bf16_tile", load().bigemm_bf16_tile(M, N, *(ctypes.byref(v) for v in out)))
+    return tuple(v.value for v in out)

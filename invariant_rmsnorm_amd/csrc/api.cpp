@@ -471,6 +471,8 @@ rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w, 
   if (ld_x < K || ld_w < K || ld_y < N || ld_x > kMaxGemmLd || ld_w > kMaxGemmLd)
     return RMSN_ERR_SHAPE;
   if (M == 0 || N == 0) return RMSN_OK;
+  // the launch grid has one workgroup per tile, at most 2^31 - 1
+  if ((M + 31) / 32 > INT32_MAX / ((N + 63) / 64)) return RMSN_ERR_SHAPE;
   if (x == nullptr || w == nullptr || y == nullptr) return RMSN_ERR_NULL;
   if (!aligned(x, 16) || !aligned(w, 16) || ld_x % 8 != 0 || ld_w % 8 != 0 || !aligned(y, 2))
     return RMSN_ERR_MISALIGNED;
@@ -479,6 +481,13 @@ rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w, 
   if (any_alias(outs, ins)) return RMSN_ERR_ALIASING;
   const rmsn::GemmArgs a{x, ld_x, w, ld_w, M, N, K, y, ld_y};
   return hip_status(rmsn::launch_gemm(a, stream));
+}
+
+rmsn_status bigemm_bf16_tile(int64_t M, int64_t N, int64_t* tile_m, int64_t* tile_n) {
+  if (M < 0 || N < 0) return RMSN_ERR_SHAPE;
+  if (tile_m == nullptr || tile_n == nullptr) return RMSN_ERR_NULL;
+  rmsn::gemm_tile(M, N, tile_m, tile_n);
+  return RMSN_OK;
 }
 
 }  // extern "C"

@@ -83,8 +83,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void bigemm_kernel(GemmArgs a) {
   using G = GemmTile<TM, TN, WGM, WGN, BK>;
   constexpr int S = BK / 16;                       // MFMA k-steps per stage
   constexpr int L = G::kLoadsA + G::kLoadsB;       // 16-byte chunks per thread and stage
-  static_assert(L % S == 0, "chunks spread evenly over the k-steps");
-  constexpr int PER = L / S;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   int64_t tm, tn;
@@ -99,7 +97,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void bigemm_kernel(GemmArgs a) {
   const auto rx = rows_rsrc(a.x, m0, a.M, G::BM, a.ld_x, K);
   const auto rw = rows_rsrc(a.w, n0, a.N, G::BN, a.ld_w, K);
 
-  // Chunk c of a thread (A chunks first, then B): 16-byte chunk q of a
+  // Chunk c of a thread (A chunks first, then B; k-step s of a stage moves
+  // the chunks s L / S .. (s + 1) L / S - 1): 16-byte chunk q of a
   // stage's rows of X (or W), row q / kChunks, k-offset 8 * (q % kChunks),
   // with q = t + kThreads * (c, or c - kLoadsA).
   u32x4 g[L];
@@ -161,11 +160,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void bigemm_kernel(GemmArgs a) {
       mfma(f[s & 1]);
       if constexpr (STORE) {
 #pragma unroll
-        for (int c = s * PER; c < (s + 1) * PER; ++c) store_chunk(c, cur ^ 1);
+        for (int c = s * L / S; c < (s + 1) * L / S; ++c) store_chunk(c, cur ^ 1);
       }
       if constexpr (LOAD) {
 #pragma unroll
-        for (int c = s * PER; c < (s + 1) * PER; ++c) load_chunk(c, k_next2);
+        for (int c = s * L / S; c < (s + 1) * L / S; ++c) load_chunk(c, k_next2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -236,16 +235,44 @@ int launch_tile(const GemmArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
+// The tiles, largest first: (TM, TN, WGM, WGN), BK = 64 for all.
+//   256 x 256: 8 waves of 128 x 64    128 x 256: 8 waves of 64 x 64
+//   128 x 128: 4 waves of 64 x 64     64 x 128: 4 waves of 32 x 64
+//   32 x 128: 4 waves of 32 x 32      32 x 64: 2 waves of 32 x 32
+// A launch takes the largest tile that still gives every compute unit a
+// tile of its own (at least kCus tiles), else the smallest: measured at
+// N = K = 4096, M = 1 / 128 / 512 / 1024 / 2048 / 4096 run fastest with
+// 32x64 / 32x128-or-32x64 / 64x128 / 128x128 / 128x256 / 256x256.
+struct TileInfo {
+  int bm, bn;
+  int (*launch)(const GemmArgs&, void*);
+};
+constexpr int kTiles = 6;
+const TileInfo kTileTable[kTiles] = {
+    {256, 256, &launch_tile<4, 2, 2, 4, 64>}, {128, 256, &launch_tile<2, 2, 2, 4, 64>},
+    {128, 128, &launch_tile<2, 2, 2, 2, 64>}, {64, 128, &launch_tile<1, 2, 2, 2, 64>},
+    {32, 128, &launch_tile<1, 1, 1, 4, 64>},  {32, 64, &launch_tile<1, 1, 1, 2, 64>},
+};
+
+const TileInfo& pick_tile(int64_t M, int64_t N) {
+  for (int i = 0; i < kTiles - 1; ++i) {
+    const TileInfo& t = kTileTable[i];
+    if (((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) >= kCus) return t;
+  }
+  return kTileTable[kTiles - 1];
+}
+
 }  // namespace
 
-// Tile of the kernel: TM, TN, WGM, WGN, BK.
-#ifndef RMSN_GEMM_TILE
-#define RMSN_GEMM_TILE 4, 2, 2, 4, 64
-#endif
+void gemm_tile(int64_t M, int64_t N, int64_t* bm, int64_t* bn) {
+  const TileInfo& t = pick_tile(M, N);
+  *bm = t.bm;
+  *bn = t.bn;
+}
 
 int launch_gemm(const GemmArgs& a, void* stream) {
   if (a.M == 0 || a.N == 0) return 0;
-  return launch_tile<RMSN_GEMM_TILE>(a, stream);
+  return pick_tile(a.M, a.N).launch(a, stream);
 }
 
 }  // namespace rmsn

@@ -82,5 +82,7 @@ int launch_bwd_rows_add(const BwdArgs& a, void* stream);    // a.rin != nullptr
 int launch_bwd_rows_f16(const BwdArgs& a, void* stream);    // a.dt == fp16 (plain, gres)
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
 int launch_gemm(const GemmArgs& a, void* stream);
+// The output tile launch_gemm uses for an M x N product (host only).
+void gemm_tile(int64_t M, int64_t N, int64_t* bm, int64_t* bn);
 
 }  // namespace rmsn

@@ -8,6 +8,7 @@ sent elsewhere) and RL-Kernel PR "[DSv4][P1-5] rmsnorm_residual",
 "Correctness / Tests" (invalid inputs)."""
 from __future__ import annotations
 
+import ctypes
 import re
 from pathlib import Path
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 7
+    assert irn.rmsnorm_abi_version() == 8
 
 
 def test_status_strings():
@@ -373,6 +374,7 @@ def gemm(**kw):
     (dict(ld_w=4100), irn.RMSN_ERR_MISALIGNED),
     (dict(y=A + 1024), irn.RMSN_ERR_ALIASING),
     (dict(y=B), irn.RMSN_ERR_ALIASING),
+    (dict(M=1 << 31), irn.RMSN_ERR_SHAPE),   # 2^32 tiles of 32 x 64: more than a grid holds
 ])
 def test_gemm_rejections(kw, code):
     assert gemm(**kw) == code
@@ -381,3 +383,28 @@ def test_gemm_rejections(kw, code):
 def test_gemm_empty_is_a_noop():
     assert gemm(M=0, x=None, y=None) == irn.RMSN_OK
     assert gemm(N=0, w=None, y=None) == irn.RMSN_OK
+
+
+GEMM_TILES = [(256, 256), (128, 256), (128, 128), (64, 128), (32, 128), (32, 64)]
+
+
+@pytest.mark.parametrize("M,N,tile", [
+    (1, 4096, (32, 64)), (200, 4096, (32, 64)), (300, 4096, (32, 128)), (500, 4096, (64, 128)),
+    (1000, 4096, (128, 128)), (2000, 4096, (128, 256)), (4000, 4096, (256, 256)),
+    (4096, 11008, (256, 256)), (1024, 2048, (64, 128)), (0, 0, (32, 64)),
+])
+def test_gemm_tile_choice(M, N, tile):
+    """The largest tile giving at least 256 tiles (one per compute unit),
+    else the smallest."""
+    assert irn.bigemm_bf16_tile(M, N) == tile
+    count = lambda t: -(-M // t[0]) * -(-N // t[1])
+    i = GEMM_TILES.index(tile)
+    assert all(count(t) < 256 for t in GEMM_TILES[:i])
+    assert tile == GEMM_TILES[-1] or count(tile) >= 256
+
+
+def test_gemm_tile_rejections():
+    lib = irn.load()
+    v = ctypes.c_int64(0)
+    assert lib.bigemm_bf16_tile(-1, 4, ctypes.byref(v), ctypes.byref(v)) == irn.RMSN_ERR_SHAPE
+    assert lib.bigemm_bf16_tile(4, 4, None, ctypes.byref(v)) == irn.RMSN_ERR_NULL

@@ -111,6 +111,27 @@ def test_gemm_row_slices_equal_full_batch(gpu):
         assert torch.equal(irn.bigemm_bf16_xwt(x[a:b], w), full[a:b]), (a, b)
 
 
+def test_gemm_every_tile_gives_the_same_rows(gpu):
+    """Batch sizes chosen so that each of the six output tiles is used
+    (N = 4000 and M not multiples of any tile; K = 544 ends in a half
+    stage): the first and the last M rows of the 4000-row batch computed
+    alone equal the same rows of the full batch bitwise, and sampled rows
+    agree with the oracle."""
+    Mfull, N, K = 4000, 4000, 544
+    Ms = (1, 200, 300, 500, 1000, 2000, 3900)
+    assert {irn.bigemm_bf16_tile(M, N) for M in Ms} == {
+        (256, 256), (128, 256), (128, 128), (64, 128), (32, 128), (32, 64)}
+    xh = synth.normal_bf16(2170, 1, Mfull, K)
+    wh = synth.normal_bf16(2170, 2, N, K)
+    x, w = dev_bf16(xh), dev_bf16(wh)
+    full = irn.bigemm_bf16_xwt(x, w)
+    for M in Ms:
+        assert torch.equal(irn.bigemm_bf16_xwt(x[:M], w), full[:M]), M
+        assert torch.equal(irn.bigemm_bf16_xwt(x[Mfull - M:], w), full[Mfull - M:]), M
+    rows = [0, 31, 255, 1999, 3998, 3999]
+    _check_parity(xh[rows], wh, host_bits(full)[rows])
+
+
 @pytest.mark.slow
 def test_gemm_full_size_sampled(gpu):
     """M = N = K = 4096: 64 sampled rows against the oracle."""
