@@ -46,6 +46,8 @@ TRAFFIC_FILE = ROOT / "profiles" / "traffic_bwd_rows_T32768_D4096.json"
 # sources of the rows kernel: a committed counter figure is used only while
 # these are unchanged
 BWD_SOURCES = ["bwd.hip", "bwd_kernel.hpp", "device_common.hpp", "geometry.hpp", "launch.hpp"]
+GEMM_TRAFFIC_FILE = ROOT / "profiles" / "traffic_bigemm_M4096_N4096_K4096.json"
+GEMM_SOURCES = ["gemm.hip", "device_common.hpp", "geometry.hpp", "launch.hpp"]
 
 
 def algo_bytes(kind: str, T: int, D: int) -> int:
@@ -63,21 +65,21 @@ def algo_bytes(kind: str, T: int, D: int) -> int:
     }[kind]
 
 
-def bwd_source_hash() -> str:
+def source_hash(names=BWD_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in BWD_SOURCES:
+    for name in names:
         h.update((ROOT / "invariant_rmsnorm_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the rows kernel from committed rocprofv3
-    counter runs, or None if absent or taken on a different kernel source."""
+def measured_traffic(path=TRAFFIC_FILE, names=BWD_SOURCES):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counter
+    runs, or None if absent or taken on a different kernel source."""
     try:
-        rec = json.loads(TRAFFIC_FILE.read_text())
+        rec = json.loads(path.read_text())
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != bwd_source_hash():
+    if rec.get("source_sha256") != source_hash(names):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -174,6 +176,18 @@ def cpu_baseline(p, workload: str, seconds: float):
     return dt, passes, nthreads
 
 
+def calibration_copy(torch, dev):
+    """Five plain 256 MiB device copies: the known byte count that scales
+    the HBM traffic counters."""
+    src = torch.empty(1 << 27, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("calibration copy: 5 x 268435456 bytes read + written", file=sys.stderr, flush=True)
+    del src, dst
+
+
 def gemm_cpu_baseline(x, w, seconds: float):
     """The CPU oracle's GEMM (double sums, as it stands) on a sample of the
     workload: blocks of 8 rows of X against all of W, threads over blocks,
@@ -226,6 +240,8 @@ def bench_gemm(args, torch, irn, dev):
     if not torch.equal(ref, y):
         raise SystemExit("repeat GEMM is not bitwise identical")
     del ref
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
     for _ in range(args.warmup):
         step()
     every = max(1, args.event_every)
@@ -291,7 +307,10 @@ def bench_gemm(args, torch, irn, dev):
                          "bigemm_over_library_time": round(launch_ms / lib_ms, 4)},
         "roofline": {"bound": "mfma", "kernel": "bigemm_kernel", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": (measured_traffic(GEMM_TRAFFIC_FILE, GEMM_SOURCES)
+                                 if (M, N, K) == (4096, 4096, 4096) else None),
+                     "bytes_per_launch": 2 * (M * K + N * K + M * N),
                      "flops_per_launch": flops, "launch_ms": round(launch_ms, 5),
                      "launches_timed": len(sampled)},
         "cpu_baseline": cpu,
@@ -402,13 +421,7 @@ def main():
     del ref
 
     if args.calibrate_copy:
-        src = torch.empty(1 << 27, dtype=torch.int16, device=dev)  # 256 MiB
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print("calibration copy: 5 x 268435456 bytes read + written", file=sys.stderr, flush=True)
-        del src, dst
+        calibration_copy(torch, dev)
 
     for _ in range(args.warmup):
         step()
