@@ -43,10 +43,16 @@
  * alone.
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
- * contiguous. Supported: D a multiple of 8 with 8 <= D <= 32768, and
- * D <= ld <= 2^24 (RMSN_MAX_LD). Every bf16
- * base pointer and ld * 2 bytes must be multiples of 16 bytes; gamma,
- * dgamma and the workspace must be 16-byte aligned; rstd 4-byte aligned.
+ * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD). Supported: 1 <= D <= 32768 for
+ * the plain, residual and residual-gradient entry points (rmsnorm_fwd,
+ * rmsnorm_residual_fwd, rmsnorm_bwd and its stages, the _dt forms); D a
+ * multiple of 8 for the gated and fused-add entry points. When D is a
+ * multiple of 8, rows move as 16-byte vectors: every bf16 / fp16 base
+ * pointer and ld * 2 bytes must be multiples of 16 bytes. Other D move
+ * element by element through the same kernels, reduction trees and
+ * arithmetic: bases need 2-byte alignment only, and any ld >= D will do.
+ * gamma, dgamma and the workspace must be 16-byte aligned; rstd 4-byte
+ * aligned.
  *
  * Ownership and streams. Every pointer is device memory owned by the caller.
  * The library never allocates, never synchronises, never changes the
@@ -73,7 +79,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 8
+#define RMSN_ABI_VERSION 9
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -81,8 +87,11 @@ typedef enum rmsn_status {
   RMSN_OK = 0,
   RMSN_ERR_NULL = 1,           /* a required pointer is NULL */
   RMSN_ERR_SHAPE = 2,          /* T < 0, D <= 0, ld < D or ld > RMSN_MAX_LD */
-  RMSN_ERR_UNSUPPORTED_D = 3,  /* D not a multiple of 8, or D > RMSN_MAX_D */
-  RMSN_ERR_MISALIGNED = 4,     /* pointer or ld*2 not 16-byte aligned */
+  RMSN_ERR_UNSUPPORTED_D = 3,  /* D > RMSN_MAX_D; D not a multiple of 8 for the
+                                  gated and fused-add forms; GEMM K not a
+                                  positive multiple of 32 */
+  RMSN_ERR_MISALIGNED = 4,     /* a pointer or ld*2 below the alignment its
+                                  operand needs (see Layout) */
   RMSN_ERR_EPS = 5,            /* eps negative or not finite */
   RMSN_ERR_ALIASING = 6,       /* an output overlaps an input or another output */
   RMSN_ERR_WORKSPACE = 7,      /* workspace NULL or smaller than required */
@@ -163,8 +172,9 @@ rmsn_status rmsnorm_gated_fwd_ex(const uint16_t* x, int64_t ld_x,
                                  int activation, int rounding, uint16_t* out,
                                  int64_t ld_out, float* rstd, void* stream);
 
-/* Bytes of workspace the backward entry points need for dgamma
- * (0 when T == 0). Depends on T and D only. */
+/* Bytes of workspace the backward entry points need for dgamma: chunks x
+ * (D rounded up to a multiple of 8) x 4 (0 when T == 0, or D invalid).
+ * Depends on T and D only. */
 size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D);
 
 /*
@@ -203,8 +213,9 @@ rmsn_status rmsnorm_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x,
 /*
  * The two stages of rmsnorm_bwd, for callers that schedule them apart.
  * rmsnorm_bwd_rows writes dx (if non-NULL) and, if workspace is non-NULL,
- * the dgamma partials: workspace[k][j] (fp32, [K][D], K = ceil(T / C)) is
- * the sum over chunk k's rows in a fixed order. rmsnorm_bwd_finish sums the
+ * the dgamma partials: workspace[k][j] (fp32, [K][Dp], Dp = D rounded up to
+ * a multiple of 8, K and the chunks from rmsnorm_bwd_partials_layout) is the
+ * sum over chunk k's rows in a fixed order; columns D..Dp-1 hold zeros. rmsnorm_bwd_finish sums the
  * K partials of each column in a fixed order into dgamma[D].
  * rmsnorm_bwd(...) == rmsnorm_bwd_rows(...) then rmsnorm_bwd_finish(...).
  */

@@ -256,7 +256,8 @@ def rmsnorm_bwd(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=None
 def rmsnorm_bwd_rows(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=None, dx=None,
                      workspace=None, stream=None):
     """Stage 1 of the backward: dx (if given) and the dgamma partials into
-    ``workspace`` (if given, fp32 [chunks, D] viewed flat)."""
+    ``workspace`` (if given, fp32 [chunks, D rounded up to a multiple of 8]
+    viewed flat)."""
     T, D = x.shape
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("rmsnorm_bwd_rows", load().rmsnorm_bwd_rows(

@@ -23,7 +23,7 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "fwd_add.hip", "fwd_f16.hip", "bwd.hip", "bwd_gated.hip",
-               "bwd_add.hip", "bwd_f16.hip", "gemm.hip"]
+               "bwd_add.hip", "bwd_f16.hip", "gemm.hip", "fwd_elem.hip", "bwd_elem.hip", "bwd_elem_f16.hip"]
 CXX_SOURCES = ["api.cpp"]
 
 

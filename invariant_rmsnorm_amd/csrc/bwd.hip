@@ -11,13 +11,14 @@
 
 namespace rmsn {
 
-// dgamma from the chunk partials. A workgroup is two waves covering 32
-// columns (one 128-byte line of each partial row, so no line is fetched by
-// two workgroups); in wave w, lane = 16*q + s, where q picks one of the
-// wave's 4 float4 groups and s one of 16 slices. Slice s sums its contiguous
-// range of chunks in ascending order (its loads issued together), then the
-// 16 slice sums meet in the fixed DPP butterfly over the 16 lanes that share
-// q. chunks == 0 writes zeros (the empty sum).
+// dgamma from the chunk partials (rows of Dp = part_stride(D) floats). A
+// workgroup is two waves covering 32 columns (one 128-byte line of each
+// partial row, so no line is fetched by two workgroups); in wave w, lane =
+// 16*q + s, where q picks one of the wave's 4 float4 groups and s one of 16
+// slices. Slice s sums its contiguous range of chunks in ascending order
+// (its loads issued together), then the 16 slice sums meet in the fixed DPP
+// butterfly over the 16 lanes that share q. chunks == 0 writes zeros (the
+// empty sum).
 constexpr int kFinishSlices = 16;
 constexpr int kFinishQuads = 64 / kFinishSlices;  // float4 groups per wave
 constexpr int kFinishWaves = 2;
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(64 * kFinishWaves) void rmsnorm_bwd_finish_kernel(
   const int q = lane / kFinishSlices;
   const int s = lane % kFinishSlices;
   const int col4 = (blockIdx.x * kFinishWaves + wave_id()) * kFinishQuads + q;
-  const int d4 = D >> 2;
+  const int d4 = static_cast<int>(part_stride(D)) >> 2;
   const int64_t per = (chunks + kFinishSlices - 1) / kFinishSlices;
   const int64_t k0 = s * per;
   const int64_t k1 = k0 + per < chunks ? k0 + per : chunks;
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(64 * kFinishWaves) void rmsnorm_bwd_finish_kernel(
   // lanes past D and chunks past the slice's range get an offset beyond it
   // and read zeros, so the loads need no branches.
   const bool ok = col4 < d4;
-  const auto rp = f32_rsrc(part, 0, chunks * D, 0x7FFFFFFF / 4);
+  const auto rp = f32_rsrc(part, 0, chunks * d4 * 4, 0x7FFFFFFF / 4);
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int64_t kb = k0; kb < k1; kb += kFinishLoads) {
     u32x4 t[kFinishLoads];
@@ -59,13 +60,22 @@ __global__ __launch_bounds__(64 * kFinishWaves) void rmsnorm_bwd_finish_kernel(
   acc.y = row_sum<kFinishSlices>(acc.y);
   acc.z = row_sum<kFinishSlices>(acc.z);
   acc.w = row_sum<kFinishSlices>(acc.w);
-  if (s == 0 && ok) reinterpret_cast<float4*>(dgamma)[col4] = acc;
+  if (s == 0 && ok) {
+    if (4 * col4 + 4 <= D) {
+      reinterpret_cast<float4*>(dgamma)[col4] = acc;
+    } else {
+      // the columns of the last group that lie inside the row
+      const float v[4] = {acc.x, acc.y, acc.z, acc.w};
+      for (int e = 0; e < 4 && 4 * col4 + e < D; ++e) dgamma[4 * col4 + e] = v[e];
+    }
+  }
 }
 
 int launch_bwd_rows(const BwdArgs& a, void* stream) {
   if (a.T == 0 || a.chunks == 0) return 0;
   if (a.z != nullptr) return launch_bwd_rows_gated(a, stream);
   if (a.rin != nullptr) return launch_bwd_rows_add(a, stream);
+  if (a.D % 8 != 0) return launch_bwd_rows_elem(a, stream);
   if (a.dt == kF16) return launch_bwd_rows_f16(a, stream);
   const RowGeom g = bwd_geom(a.D);
   const bwd_detail::RowsLaunch f =
@@ -76,7 +86,7 @@ int launch_bwd_rows(const BwdArgs& a, void* stream) {
 
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream) {
   const int cols_per_block = 4 * kFinishQuads * kFinishWaves;
-  const int grid = (D + cols_per_block - 1) / cols_per_block;
+  const int grid = static_cast<int>((part_stride(D) + cols_per_block - 1) / cols_per_block);
   hipLaunchKernelGGL(rmsnorm_bwd_finish_kernel, dim3(grid), dim3(64 * kFinishWaves), 0,
                      static_cast<hipStream_t>(stream), part, chunks, D, dgamma);
   return static_cast<int>(hipGetLastError());

@@ -54,7 +54,9 @@ enum : int {
 // reused by the second. Beyond that the registers would spill, so the
 // weights move to LDS and the second pass unpacks the raw vectors again.
 // The gated form holds a third input row (z), so it goes lean from 11.
-constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_inputs ? 11 : 13); }
+constexpr bool bwd_lean(int vpl, bool three_inputs, bool elem = false) {
+  return vpl >= (elem ? 3 : three_inputs ? 11 : 13);
+}
 // Load the next step while computing this one (two register sets that swap
 // roles), for rows over 4 waves whose loaded step fits the register file
 // twice: input streams x vectors per lane <= 18 with the whole register file
@@ -62,7 +64,11 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 // Without it the four waves of a row, held together by the exchange
 // barrier, load and compute in lock step and leave the memory pipe idle
 // while they compute.
-constexpr bool bwd_prefetch(int lpr, int vpl, int mode) {
+// Element-wise row storage holds each loaded element in a register of its
+// own until the group is packed, twice the registers of a 16-byte vector:
+// it takes neither the second register set nor the values kept for pass 2.
+constexpr bool bwd_prefetch(int lpr, int vpl, int mode, bool elem = false) {
+  if (elem) return false;
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
   return lpr > 64 && streams * vpl <= (bwd_waves_per_eu(vpl) == 1 ? 18 : 8);
 }
@@ -73,11 +79,13 @@ constexpr bool bwd_prefetch(int lpr, int vpl, int mode) {
 // merge (which reuse the same space).
 inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
   const RowGeom g = bwd_geom(D);
-  const size_t w = bwd_lean(g.vpl, three_inputs) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
-  // merge space: 2 rows of D floats with one wave per row, 1 with two, none
-  // with four
+  const size_t w = bwd_lean(g.vpl, three_inputs, D % 8 != 0)
+                       ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
+  // merge space: 2 rows of Dp = part_stride(D) floats with one wave per
+  // row, 1 with two, none with four
   const int wpr = waves_per_row(g.lpr);
-  const size_t m = want_part ? static_cast<size_t>(D) * (wpr == 1 ? 2 : wpr == 2 ? 1 : 0) : 0;
+  const size_t m =
+      want_part ? static_cast<size_t>(part_stride(D)) * (wpr == 1 ? 2 : wpr == 2 ? 1 : 0) : 0;
   return w > m ? w : m;
 }
 
@@ -94,8 +102,8 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = rows_per_block(LPR, U);
   static_assert(WPR == 1 || (U == 1 && VPL >= kBwdMinVplMulti), "multi-wave rows: one row per step");
-  constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
-  constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE);
+  constexpr bool LEAN = bwd_lean(VPL, GATED || ADD, elem_dt(DT));
+  constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE, elem_dt(DT));
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
@@ -107,7 +115,8 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   const int l = LPR >= 64 ? (wave % WPR) * 64 + lane : lane % LPR;
   __shared__ double xch[2][kWaves];  // row-sum exchange of multi-wave rows
   int xstep = 0;
-  const int nv = a.D >> 3;
+  const int nv = (a.D + 7) >> 3;  // groups of 8 elements (the last may be partial)
+  const int Dp = 8 * nv;           // floats per partial row
   const float Df = static_cast<float>(a.D);
   const bool want_part = a.part != nullptr;
 
@@ -118,7 +127,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     // float4 h (0/1) of vector c = v*LPR + l goes to slot (2v + h)*LPR + l
     for (int c = threadIdx.x; c < nv; c += kBlock) {
       float w8[8];
-      weights8(a.gamma, a.wdt, c, w8);
+      weights_group<elem_dt(DT)>(a.gamma, a.wdt, c, a.D, w8);
       if (a.zc) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) w8[k] = w8[k] + 1.0f;
@@ -128,7 +137,8 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     }
     __syncthreads();
   } else {
-    load_weights<LPR, (LEAN ? 1 : VPL), MASKED>(a.gamma, a.wdt, a.zc, nv, l, wreg);
+    load_weights<LPR, (LEAN ? 1 : VPL), MASKED, elem_dt(DT)>(a.gamma, a.wdt, a.zc, nv, a.D, l,
+                                                            wreg);
   }
   // In the lean plan `base` is an opaque zero, so that the LDS reads stay
   // inside the row loop instead of being hoisted into registers.
@@ -176,6 +186,9 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (MASKED && c >= nv) return kOutOfRange;
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
+  // Elements of this lane's group v inside the row (8 or more but for a
+  // partial last group; used by element-wise storage only).
+  auto valid = [&](int v) { return a.D - 8 * (v * LPR + l); };
 
   // One workgroup step's loaded rows (U row groups of each input stream).
   struct StepRegs {
@@ -203,34 +216,37 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       if (a.x_stream) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
-          b.xq[u][v] = buf_load16<kLoadStream>(rx, voff(v, a.ld_x));
+          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
+          b.xq[u][v] = load_row8<DT, kLoadStream>(rx, voff(v, a.ld_x), valid(v));
         }
       } else {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = buf_load16<kLoadStream>(rg, voff(v, a.ld_g));
-          b.xq[u][v] = buf_load16(rx, voff(v, a.ld_x));
+          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
+          b.xq[u][v] = load_row8<DT>(rx, voff(v, a.ld_x), valid(v));
         }
       }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) b.rres[u][v] = buf_load16<kLoadStream>(rgr, voff(v, a.ld_gres));
+        for (int v = 0; v < VPL; ++v)
+          b.rres[u][v] = load_row8<DT, kLoadStream>(rgr, voff(v, a.ld_gres), valid(v));
       }
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, end, RPW, a.ld_z, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) b.zq[u][v] = buf_load16<kLoadStream>(rz, voff(v, a.ld_z));
+        for (int v = 0; v < VPL; ++v)
+          b.zq[u][v] = load_row8<DT, kLoadStream>(rz, voff(v, a.ld_z), valid(v));
       }
       if constexpr (ADD) {  // the forward read it too: x's policy
         const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
         if (a.x_stream) {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) b.hq[u][v] = buf_load16<kLoadStream>(rh, voff(v, a.ld_rin));
+          for (int v = 0; v < VPL; ++v)
+            b.hq[u][v] = load_row8<DT, kLoadStream>(rh, voff(v, a.ld_rin), valid(v));
         } else {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) b.hq[u][v] = buf_load16(rh, voff(v, a.ld_rin));
+          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT>(rh, voff(v, a.ld_rin), valid(v));
         }
       }
     }
@@ -282,7 +298,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
             dz8[k] = gnw * dag;
             gf[k] = gf[k] * ag;
           }
-          buf_store16_nt(pack8<DT>(dz8), rdz, voff(v, a.ld_dz));
+          store_row8<DT>(pack8<DT>(dz8), rdz, voff(v, a.ld_dz), valid(v));
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -340,7 +356,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
         }
-        buf_store16_nt(pack8<DT>(o), rdx, voff(v, a.ld_dx));
+        store_row8<DT>(pack8<DT>(o), rdx, voff(v, a.ld_dx), valid(v));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -393,7 +409,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
     acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
   };
-  float* const out = a.part + static_cast<int64_t>(blockIdx.x) * a.D;
+  float* const out = a.part + static_cast<int64_t>(blockIdx.x) * Dp;
   const bool writer = slot == 0;
 
   if constexpr (WPR == 4) {
@@ -431,7 +447,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     // One wave per row: ((w0 + w2) + (w1 + w3)) through two LDS rows of D
     // floats (the weights' space is reused, hence the barrier first).
     __syncthreads();
-    auto lds_row = [&](int b) { return lds + b * a.D; };
+    auto lds_row = [&](int b) { return lds + b * Dp; };
     if (wave >= 2 && writer) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {

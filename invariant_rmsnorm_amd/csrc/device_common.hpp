@@ -16,6 +16,14 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // Storage types (the ABI's RMSN_DTYPE_* values): activations are bf16 or
 // fp16, weights bf16, fp16 or fp32.
 enum : int { kBf16 = 0, kF16 = 1, kF32 = 2 };
+// Row storage of a kernel instance: the activation type, plus kElem when
+// rows move element by element. A lane still owns groups of 8 consecutive
+// elements (the same geometry and reduction tree as 16-byte vectors), but
+// each group moves as eight 2-byte accesses: rows of any length D and any
+// 2-byte alignment, elements past D read as zero and are never written.
+enum : int { kElem = 8, kBf16E = kBf16 | kElem, kF16E = kF16 | kElem };
+constexpr int value_dt(int DT) { return DT & ~kElem; }
+constexpr bool elem_dt(int DT) { return (DT & kElem) != 0; }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
@@ -35,10 +43,11 @@ __device__ __forceinline__ f32x2 f16_pair(uint32_t w) {
   return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
 }
 
-// Unpack 8 activations of storage type DT (kBf16 or kF16).
+// Unpack 8 activations of storage type DT (kBf16 or kF16, with or without
+// kElem).
 template <int DT>
 __device__ __forceinline__ void unpack8(const u32x4& q, float (&f)[8]) {
-  if constexpr (DT == kBf16) {
+  if constexpr (value_dt(DT) == kBf16) {
     unpack8(q, f);
   } else {
     const f32x2 a = f16_pair(q.x), b = f16_pair(q.y), c = f16_pair(q.z), d = f16_pair(q.w);
@@ -69,7 +78,7 @@ __device__ __forceinline__ uint32_t pack2_f16(float a, float b) {
 // Pack 8 fp32 values to storage type DT with one rounding each.
 template <int DT>
 __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
-  if constexpr (DT == kBf16) {
+  if constexpr (value_dt(DT) == kBf16) {
     return pack8(f);
   } else {
     return u32x4{pack2_f16(f[0], f[1]), pack2_f16(f[2], f[3]), pack2_f16(f[4], f[5]),
@@ -124,6 +133,44 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ void buf_store16_nt(const u32x4& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 2);
 }
+
+// Elements [8c, 8c + 8) of a row at byte offset `off` of a row resource;
+// `valid` = how many of them lie inside the row (8, except in the last group
+// of a row whose length is not a multiple of 8). With 16-byte storage the
+// group is one vector (valid is always 8 there); element-wise storage gives
+// each element past the row an offset beyond the resource, so it reads as
+// zero.
+template <int DT, int POLICY = kLoadDefault>
+__device__ __forceinline__ u32x4 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
+  if constexpr (!elem_dt(DT)) {
+    return buf_load16<POLICY>(r, off);
+  } else {
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      h[e] = __builtin_amdgcn_raw_buffer_load_b16(
+          r, static_cast<int>(e < valid ? off + 2 * e : kOutOfRange), 0, POLICY);
+    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                 h[6] | (h[7] << 16)};
+  }
+}
+// Stores the group (non-temporal); element-wise storage writes only the
+// `valid` elements inside the row.
+template <int DT>
+__device__ __forceinline__ void store_row8(const u32x4& v, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                           int valid) {
+  if constexpr (!elem_dt(DT)) {
+    buf_store16_nt(v, r, off);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      __builtin_amdgcn_raw_buffer_store_b16(
+          static_cast<unsigned short>(w[e >> 1] >> (16 * (e & 1))), r,
+          static_cast<int>(e < valid ? off + 2 * e : kOutOfRange), 0, 2);
+  }
+}
+
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
 }
@@ -347,16 +394,45 @@ __device__ __forceinline__ void weights8(const void* __restrict__ gamma, int wdt
   }
 }
 
+// The weights of a last group with only `valid` < 8 elements inside the
+// row, one element at a time (nothing past gamma's D values is read); the
+// rest are zero.
+__device__ __forceinline__ void weights_part(const void* __restrict__ gamma, int wdt, int c,
+                                             int valid, float (&w)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    w[k] = 0.0f;
+    if (k < valid) {
+      const int j = 8 * c + k;
+      if (wdt == kF32) {
+        w[k] = static_cast<const float*>(gamma)[j];
+      } else {
+        const uint32_t b = static_cast<const uint16_t*>(gamma)[j];
+        w[k] = wdt == kF16 ? f16_pair(b).x : bf16_lo(b);
+      }
+    }
+  }
+}
+
+// The weights of group c of a row of D elements (TAIL: D may not be a
+// multiple of 8).
+template <bool TAIL>
+__device__ __forceinline__ void weights_group(const void* __restrict__ gamma, int wdt, int c, int D,
+                                              float (&w)[8]) {
+  if (TAIL && 8 * c + 8 > D) weights_part(gamma, wdt, c, D - 8 * c, w);
+  else weights8(gamma, wdt, c, w);
+}
+
 // Loads this lane's weights w_eff = fp32(gamma) (+1.0f in fp32 when
 // zero-centred) for its vectors c = v*LPR + l; columns past D read as zero.
-template <int LPR, int VPL, bool MASKED>
+template <int LPR, int VPL, bool MASKED, bool TAIL = false>
 __device__ __forceinline__ void load_weights(const void* __restrict__ gamma, int wdt, int zc,
-                                             int nv, int l, float (&w)[VPL][8]) {
+                                             int nv, int D, int l, float (&w)[VPL][8]) {
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int c = v * LPR + l;
     if (!MASKED || c < nv) {
-      weights8(gamma, wdt, c, w[v]);
+      weights_group<TAIL>(gamma, wdt, c, D, w[v]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) w[v][k] = 0.0f;

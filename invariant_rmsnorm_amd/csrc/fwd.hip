@@ -9,6 +9,7 @@ int launch_fwd(const FwdArgs& a, void* stream) {
   if (a.T == 0) return 0;
   if (a.z != nullptr) return launch_fwd_gated(a, stream);
   if (a.rin != nullptr) return launch_fwd_add(a, stream);
+  if (a.D % 8 != 0) return launch_fwd_elem(a, stream);
   if (a.dt == kF16) return launch_fwd_f16(a, stream);
   const fwd_detail::FwdLaunch f = fwd_detail::pick<0>(fwd_geom(a.D));
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);

@@ -5,8 +5,9 @@
 // Invariant Kernels", sections 2-3: the reduction layout must come from the
 // problem's fixed dimensions, never from the batch dimension).
 //
-// A row of D bf16 values is NV = D/8 vectors of 16 bytes, shared by LPR
-// lanes:
+// A row of D bf16 values is NV = ceil(D/8) groups of 8 elements (16-byte
+// vectors when D is a multiple of 8; otherwise the last group is partial and
+// the rows move element by element), shared by LPR lanes:
 //  - long rows span several wavefronts of one workgroup: LPR = 128 or 256
 //    (VPL = ceil(NV/LPR) <= 16 vectors each). The forward does this past
 //    1024 vectors (D > 8192), over 2 waves up to 2048 vectors and 4 beyond;
@@ -66,7 +67,7 @@ inline RowGeom multi_wave_geom(int64_t nv, int lpr) {
 // Forward: past 1024 vectors (D > 8192), 2 waves per row up to 2048 vectors,
 // 4 beyond.
 inline RowGeom fwd_geom(int64_t D) {
-  const int64_t nv = D / 8;
+  const int64_t nv = (D + 7) / 8;
   if (nv > 1024) return multi_wave_geom(nv, nv <= 2048 ? 128 : 256);
   return single_wave_geom(nv);
 }
@@ -76,10 +77,14 @@ inline RowGeom fwd_geom(int64_t D) {
 // D = 8192 147 -> 124 us, 12288 163 -> 132, 16384 168 -> 134 (the software
 // pipeline needs VPL <= 9 to fit the register file); D = 5120 within 2%.
 inline RowGeom bwd_geom(int64_t D) {
-  const int64_t nv = D / 8;
+  const int64_t nv = (D + 7) / 8;
   if (nv > 512) return multi_wave_geom(nv, 256);
   return single_wave_geom(nv);
 }
+
+// Floats per row of the backward's dgamma partials (and of its LDS merge
+// rows): D rounded up to whole groups of 8.
+constexpr int64_t part_stride(int64_t D) { return (D + 7) / 8 * 8; }
 
 // Rows a wave keeps in flight per step: enough that each lane has about
 // 128 bytes of one input stream outstanding.

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 8
+    assert irn.rmsnorm_abi_version() == 9
 
 
 def test_status_strings():
@@ -61,8 +61,14 @@ def fwd(**kw):
     (dict(T=-1), irn.RMSN_ERR_SHAPE),
     (dict(D=0), irn.RMSN_ERR_SHAPE),
     (dict(D=-8), irn.RMSN_ERR_SHAPE),
-    (dict(D=100, ld_x=100, ld_y=104), irn.RMSN_ERR_UNSUPPORTED_D),
     (dict(D=32776, ld_x=32776, ld_y=32776), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=32769, ld_x=32769, ld_y=32769), irn.RMSN_ERR_UNSUPPORTED_D),
+    # D not a multiple of 8: element-wise rows, 2-byte alignment, any stride
+    (dict(D=100, ld_x=99, ld_y=100), irn.RMSN_ERR_SHAPE),
+    (dict(D=100, ld_x=100, ld_y=101, x=A + 1), irn.RMSN_ERR_MISALIGNED),
+    (dict(D=100, ld_x=100, ld_y=101, y=B + 3), irn.RMSN_ERR_MISALIGNED),
+    (dict(D=100, ld_x=101, ld_y=101, y=A + 2), irn.RMSN_ERR_ALIASING),
+    (dict(D=7, ld_x=7, ld_y=7, gamma=GAM + 4), irn.RMSN_ERR_MISALIGNED),
     (dict(ld_x=4000), irn.RMSN_ERR_SHAPE),
     (dict(ld_y=4088), irn.RMSN_ERR_SHAPE),
     (dict(x=A + 2), irn.RMSN_ERR_MISALIGNED),
@@ -131,7 +137,10 @@ def bwd(**kw):
     (dict(ws=C), irn.RMSN_ERR_ALIASING),
     (dict(gres=C, ld_gres=4096), irn.RMSN_ERR_ALIASING),
     (dict(gres=E + (1 << 30), ld_gres=100), irn.RMSN_ERR_SHAPE),
-    (dict(D=4100, ld_g=4104, ld_x=4104, ld_dx=4104), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=32770, ld_g=32770, ld_x=32770, ld_dx=32770), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=4100, ld_g=4100, ld_x=4100, ld_dx=4100, x=A + 1), irn.RMSN_ERR_MISALIGNED),
+    (dict(D=4100, ld_g=4100, ld_x=4101, ld_dx=4100, dx=A + 6), irn.RMSN_ERR_ALIASING),
+    (dict(D=4100, ld_g=4100, ld_x=4100, ld_dx=4100, ws_bytes=16), irn.RMSN_ERR_WORKSPACE),
     (dict(T=-5), irn.RMSN_ERR_SHAPE),
 ])
 def test_backward_rejections(kw, code):
@@ -140,12 +149,15 @@ def test_backward_rejections(kw, code):
 
 def test_workspace_and_chunking_contract():
     assert irn.rmsnorm_bwd_workspace_bytes(0, 4096) == 0
-    assert irn.rmsnorm_bwd_workspace_bytes(10, 100) == 0
+    assert irn.rmsnorm_bwd_workspace_bytes(10, 0) == 0
+    assert irn.rmsnorm_bwd_workspace_bytes(10, 32769) == 0
     for T, D in ((1, 128), (16, 128), (32768, 4096), (262144, 4096), (262144, 128), (1000, 2048),
-                 (7, 8), (12345, 8192), (5000, 16384), (300, 32768), (777, 8200)):
+                 (7, 8), (12345, 8192), (5000, 16384), (300, 32768), (777, 8200),
+                 (10, 100), (3, 1), (1000, 7), (4000, 4100), (99, 32767)):
         R, S, K = irn.rmsnorm_bwd_partials_layout(T, D)
         assert R > 0 and S > 0 and 0 < K <= 512
-        assert irn.rmsnorm_bwd_workspace_bytes(T, D) == K * D * 4
+        # partial rows of D floats rounded up to a multiple of 8
+        assert irn.rmsnorm_bwd_workspace_bytes(T, D) == K * (-(-D // 8) * 8) * 4
         # R depends on D alone
         assert irn.rmsnorm_bwd_partials_layout(1, D)[0] == R
         # every row belongs to exactly one chunk
@@ -160,7 +172,7 @@ def test_workspace_and_chunking_contract():
 def test_partials_layout_rejections():
     lib = irn.load()
     assert lib.rmsnorm_bwd_partials_layout(-1, 4096, None, None, None) == irn.RMSN_ERR_SHAPE
-    assert lib.rmsnorm_bwd_partials_layout(16, 100, None, None, None) == irn.RMSN_ERR_UNSUPPORTED_D
+    assert lib.rmsnorm_bwd_partials_layout(16, 32769, None, None, None) == irn.RMSN_ERR_UNSUPPORTED_D
     assert lib.rmsnorm_bwd_partials_layout(16, 0, None, None, None) == irn.RMSN_ERR_SHAPE
 
 
@@ -170,7 +182,9 @@ def test_finish_rejections():
     assert lib.rmsnorm_bwd_finish(None, 0, 1000, 4096, E, None) == irn.RMSN_ERR_WORKSPACE
     assert lib.rmsnorm_bwd_finish(W, 64, 1000, 4096, E, None) == irn.RMSN_ERR_WORKSPACE
     assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 4096, W + 64, None) == irn.RMSN_ERR_ALIASING
-    assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 12, E, None) == irn.RMSN_ERR_UNSUPPORTED_D
+    assert lib.rmsnorm_bwd_finish(W, 1 << 30, 1000, 32769, E, None) == irn.RMSN_ERR_UNSUPPORTED_D
+    short = irn.rmsnorm_bwd_workspace_bytes(1000, 12) - 4   # one float short of the partials
+    assert lib.rmsnorm_bwd_finish(W, short, 1000, 12, E, None) == irn.RMSN_ERR_WORKSPACE
 
 
 Z = A + (7 << 36)

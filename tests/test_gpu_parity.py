@@ -260,15 +260,15 @@ def test_rejections_write_nothing(gpu):
     x = dev_bf16(synth.normal_bf16(1, 1, 10, D))
     gamma = torch.ones(D, device="cuda")
     y = torch.full((10, D), 3.0, dtype=torch.bfloat16, device="cuda")
-    cases = [
-        (dict(x=x[:, :100]), irn.RMSN_ERR_UNSUPPORTED_D),     # D % 8 != 0
-        (dict(x=x.view(-1)[1:].as_strided((9, D), (D, 1))), irn.RMSN_ERR_MISALIGNED),
-    ]
-    for kw, code in cases:
-        with pytest.raises(irn.RmsnormError) as e:
-            xx = kw["x"]
-            irn.rmsnorm_fwd(xx, gamma[: xx.shape[1]], y=y[: xx.shape[0], : xx.shape[1]])
-        assert e.value.status == code
+    # a 2-byte offset base is misaligned for rows of a multiple of 8 elements
+    with pytest.raises(irn.RmsnormError) as e:
+        xx = x.view(-1)[1:].as_strided((9, D), (D, 1))
+        irn.rmsnorm_fwd(xx, gamma, y=y[:9])
+    assert e.value.status == irn.RMSN_ERR_MISALIGNED
+    # the gated form needs D a multiple of 8
+    with pytest.raises(irn.RmsnormError) as e:
+        irn.rmsnorm_gated_fwd(x[:, :100], x[:, :100], gamma[:100], out=y[:, :100])
+    assert e.value.status == irn.RMSN_ERR_UNSUPPORTED_D
     with pytest.raises(irn.RmsnormError) as e:
         irn.rmsnorm_fwd(x, gamma, y=x)  # in place
     assert e.value.status == irn.RMSN_ERR_ALIASING

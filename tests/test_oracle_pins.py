@@ -173,7 +173,7 @@ def _fd_errors(xd, gd, gamma, zc, eps, h=1e-5):
     return e_dx, e_dg
 
 
-@pytest.mark.parametrize("T,D", [(1, 8), (2, 16), (3, 128)])
+@pytest.mark.parametrize("T,D", [(1, 8), (2, 16), (3, 128), (1, 5), (2, 13)])
 @pytest.mark.parametrize("zc", [False, True])
 def test_f64_backward_matches_finite_differences(T, D, zc):
     x, g, gamma = _problem(T, D, 100 + T * D, zc)
@@ -282,7 +282,9 @@ def _dx_bound_ok(p, r, gres, dx=None):
     return rounding_consistent(dx, dxd, err)
 
 
-CASES = [(16, 128, 1001), (7, 4096, 17), (5, 200, 18), (3, 8, 19)]
+CASES = [(16, 128, 1001), (7, 4096, 17), (5, 200, 18), (3, 8, 19),
+         # rows whose length is not a multiple of 8
+         (9, 13, 20), (4, 1, 21), (6, 100, 22), (2, 4100, 23)]
 
 
 @pytest.mark.parametrize("T,D,seed", CASES)
@@ -382,6 +384,25 @@ def test_closed_forms_constant_and_one_hot_rows():
         yv = bf16_to_f64(y[0])
         assert yv[j] == bf16_to_f64(f32_to_bf16_torch(np.array([64.0 * gamma[j]], np.float32)))[0]
         assert np.all(np.delete(yv, j) == 0.0)
+
+
+def test_mean_divides_by_D():
+    """The mean is ss / D by one correctly rounded fp32 division, which for D
+    not a power of two differs from multiplying by the rounded 1/D. Constant
+    rows c at eps = 0 have ss = D c^2 exactly, so r = 1/|c| rounded once;
+    for the rows below the multiplication by fl(1/D) would give another r."""
+    decisive = 0
+    for D in (7, 12, 100, 4100):
+        for c in (5.0, 7.0, 11.0, 1.25, 1.75, 2.5, 15.0, 0.625):
+            x = f32_to_bf16_torch(np.full((2, D), c, np.float32))
+            x[1] ^= np.uint16(0x8000)  # -c
+            _, r = oracle.fwd(x, np.ones(D, np.float32), False, 0.0)
+            want = np.float32(1.0 / c)
+            assert r[0] == want and r[1] == want, (D, c)
+            ss = np.float32(D * c * c)
+            by_recip = np.float32(1.0 / np.sqrt(np.float64(np.float32(ss * np.float32(1.0 / D)))))
+            decisive += by_recip != want
+    assert decisive >= 5
 
 
 def test_single_row_dgamma_is_one_rounded_term():
