@@ -66,11 +66,17 @@ constexpr bool bwd_lean(int vpl, bool three_inputs, bool elem = false) {
 // while they compute.
 // Element-wise row storage holds each loaded element in a register of its
 // own until the group is packed, twice the registers of a 16-byte vector:
-// it takes neither the second register set nor the values kept for pass 2.
+// it keeps no values for pass 2 (lean from 3 groups per lane) and takes the
+// second register set only when RMSN_BWD_ELEM_PREFETCH is set (measured no
+// faster at D = 4100).
+#ifndef RMSN_BWD_ELEM_PREFETCH
+#define RMSN_BWD_ELEM_PREFETCH 0
+#endif
 constexpr bool bwd_prefetch(int lpr, int vpl, int mode, bool elem = false) {
-  if (elem) return false;
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
-  return lpr > 64 && streams * vpl <= (bwd_waves_per_eu(vpl) == 1 ? 18 : 8);
+  const int budget = bwd_waves_per_eu(vpl, elem) == 1 ? 18 : 8;
+  if (elem) return RMSN_BWD_ELEM_PREFETCH && lpr > 64 && 2 * streams * vpl <= budget;
+  return lpr > 64 && streams * vpl <= budget;
 }
 
 // LDS floats the rows kernel needs: the weights when held in LDS (one float4
@@ -90,7 +96,8 @@ inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
 }
 
 template <int LPR, int VPL, bool MASKED, int MODE, int DT>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL))))
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL, elem_dt(DT)))))
 void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr bool ADD = MODE == kBwdAdd || MODE == kBwdAddGres;
   constexpr bool GRES = MODE == kBwdGres || MODE == kBwdAddGres;
@@ -121,13 +128,25 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   const bool want_part = a.part != nullptr;
 
   // Weights w_eff = gamma (+1 in fp32 when zero-centred).
+  constexpr bool ELEM = elem_dt(DT);
+  constexpr bool MSK = MASKED && !ELEM;  // lanes without a last group (16-byte rows)
   float wreg[LEAN ? 1 : VPL][8];
   float4* const wl4 = reinterpret_cast<float4*>(lds);
   if constexpr (LEAN) {
-    // float4 h (0/1) of vector c = v*LPR + l goes to slot (2v + h)*LPR + l
-    for (int c = threadIdx.x; c < nv; c += kBlock) {
+    // float4 h (0/1) of group c = v*LPR + l goes to slot (2v + h)*LPR + l;
+    // with element-wise storage every lane's VPL groups are staged (group
+    // v of lane l: elements (8v + e)*LPR + l, zero past D).
+    for (int c = threadIdx.x; c < (ELEM ? VPL * LPR : nv); c += kBlock) {
       float w8[8];
-      weights_group<elem_dt(DT)>(a.gamma, a.wdt, c, a.D, w8);
+      if constexpr (ELEM) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = (8 * (c / LPR) + e) * LPR + c % LPR;
+          w8[e] = j < a.D ? weight_at(a.gamma, a.wdt, j) : 0.0f;
+        }
+      } else {
+        weights8(a.gamma, a.wdt, c, w8);
+      }
       if (a.zc) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) w8[k] = w8[k] + 1.0f;
@@ -137,8 +156,8 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     }
     __syncthreads();
   } else {
-    load_weights<LPR, (LEAN ? 1 : VPL), MASKED, elem_dt(DT)>(a.gamma, a.wdt, a.zc, nv, a.D, l,
-                                                            wreg);
+    if constexpr (ELEM) load_weights_elem<LPR, (LEAN ? 1 : VPL)>(a.gamma, a.wdt, a.zc, a.D, l, wreg);
+    else load_weights<LPR, (LEAN ? 1 : VPL), MASKED>(a.gamma, a.wdt, a.zc, nv, l, wreg);
   }
   // In the lean plan `base` is an opaque zero, so that the LDS reads stay
   // inside the row loop instead of being hoisted into registers.
@@ -181,14 +200,15 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   // Byte offset of this lane's vector v within its row group, per tensor;
   // vectors past D get an offset no resource reaches. Rows past the chunk's
   // end read as zero (and then contribute nothing) and their stores drop.
+  // With element-wise storage the offset is that of the group's first
+  // element 8v*LPR + l, and valid(v) the row's elements from it on.
   auto voff = [&](int v, int64_t ld) -> uint32_t {
+    if constexpr (ELEM) return static_cast<uint32_t>(slot * ld * 2 + 2 * (8 * v * LPR + l));
     const int c = v * LPR + l;
     if (MASKED && c >= nv) return kOutOfRange;
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
-  // Elements of this lane's group v inside the row (8 or more but for a
-  // partial last group; used by element-wise storage only).
-  auto valid = [&](int v) { return a.D - 8 * (v * LPR + l); };
+  auto valid = [&](int v) { return a.D - (8 * v * LPR + l); };
 
   // One workgroup step's loaded rows (U row groups of each input stream).
   struct StepRegs {
@@ -216,37 +236,37 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       if (a.x_stream) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
-          b.xq[u][v] = load_row8<DT, kLoadStream>(rx, voff(v, a.ld_x), valid(v));
+          b.gq[u][v] = load_row8<DT, LPR, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
+          b.xq[u][v] = load_row8<DT, LPR, kLoadStream>(rx, voff(v, a.ld_x), valid(v));
         }
       } else {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
-          b.xq[u][v] = load_row8<DT>(rx, voff(v, a.ld_x), valid(v));
+          b.gq[u][v] = load_row8<DT, LPR, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
+          b.xq[u][v] = load_row8<DT, LPR>(rx, voff(v, a.ld_x), valid(v));
         }
       }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          b.rres[u][v] = load_row8<DT, kLoadStream>(rgr, voff(v, a.ld_gres), valid(v));
+          b.rres[u][v] = load_row8<DT, LPR, kLoadStream>(rgr, voff(v, a.ld_gres), valid(v));
       }
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, end, RPW, a.ld_z, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          b.zq[u][v] = load_row8<DT, kLoadStream>(rz, voff(v, a.ld_z), valid(v));
+          b.zq[u][v] = load_row8<DT, LPR, kLoadStream>(rz, voff(v, a.ld_z), valid(v));
       }
       if constexpr (ADD) {  // the forward read it too: x's policy
         const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
         if (a.x_stream) {
 #pragma unroll
           for (int v = 0; v < VPL; ++v)
-            b.hq[u][v] = load_row8<DT, kLoadStream>(rh, voff(v, a.ld_rin), valid(v));
+            b.hq[u][v] = load_row8<DT, LPR, kLoadStream>(rh, voff(v, a.ld_rin), valid(v));
         } else {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT>(rh, voff(v, a.ld_rin), valid(v));
+          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT, LPR>(rh, voff(v, a.ld_rin), valid(v));
         }
       }
     }
@@ -280,7 +300,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       acc_t sa = 0;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (MASKED && v * LPR + l >= nv) continue;  // no such vector (weights unset)
+        if (MSK && v * LPR + l >= nv) continue;  // no such vector (weights unset)
         float gf[8], xf[8], w8[8];
         unpack8<DT>(b.gq[u][v], gf);
         row_values(u, v, xf);
@@ -298,7 +318,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
             dz8[k] = gnw * dag;
             gf[k] = gf[k] * ag;
           }
-          store_row8<DT>(pack8<DT>(dz8), rdz, voff(v, a.ld_dz), valid(v));
+          store_row8<DT, LPR>(pack8<DT>(dz8), rdz, voff(v, a.ld_dz), valid(v));
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -332,7 +352,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       const auto rdx = rows_rsrc(a.dx, first, a.dx != nullptr ? end : first, RPW, a.ld_dx, a.D);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (MASKED && v * LPR + l >= nv) continue;
+        if (MSK && v * LPR + l >= nv) continue;
         float gf[8], xf[8], w8[8], o[8];
         unpack8<DT>(b.gq[u][v], gf);
         row_values(u, v, xf);
@@ -356,7 +376,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
         }
-        store_row8<DT>(pack8<DT>(o), rdx, voff(v, a.ld_dx), valid(v));
+        store_row8<DT, LPR>(pack8<DT>(o), rdx, voff(v, a.ld_dx), valid(v));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -397,18 +417,41 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[v][k] = acc[v][k] + __shfl_xor(acc[v][k], m);
 
-  auto put = [&](float* d, int v) {
-    *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-    *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+  // Group v of this lane's accumulators to / from a row of Dp floats: the
+  // columns 8c .. 8c+7 of vector c = v*LPR + l, or with element-wise storage
+  // the columns (8v + e)*LPR + l below Dp.
+  auto put = [&](float* row, int v) {
+    if constexpr (ELEM) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = (8 * v + e) * LPR + l;
+        if (j < Dp) row[j] = acc[v][e];
+      }
+    } else {
+      float* d = row + 8 * (v * LPR + l);
+      *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+    }
   };
-  auto add_from = [&](const float* d, int v) {
-    const float4 p0 = *reinterpret_cast<const float4*>(d);
-    const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
-    acc[v][0] = acc[v][0] + p0.x; acc[v][1] = acc[v][1] + p0.y;
-    acc[v][2] = acc[v][2] + p0.z; acc[v][3] = acc[v][3] + p0.w;
-    acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
-    acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
+  auto add_from = [&](const float* row, int v) {
+    if constexpr (ELEM) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = (8 * v + e) * LPR + l;
+        if (j < Dp) acc[v][e] = acc[v][e] + row[j];
+      }
+    } else {
+      const float* d = row + 8 * (v * LPR + l);
+      const float4 p0 = *reinterpret_cast<const float4*>(d);
+      const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
+      acc[v][0] = acc[v][0] + p0.x; acc[v][1] = acc[v][1] + p0.y;
+      acc[v][2] = acc[v][2] + p0.z; acc[v][3] = acc[v][3] + p0.w;
+      acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
+      acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
+    }
   };
+  // lanes without group v (16-byte rows only)
+  auto absent = [&](int v) { return MSK && v * LPR + l >= nv; };
   float* const out = a.part + static_cast<int64_t>(blockIdx.x) * Dp;
   const bool writer = slot == 0;
 
@@ -416,65 +459,58 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     // Four waves per row: every wave owns distinct columns.
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      const int c = v * LPR + l;
-      if (MASKED && c >= nv) continue;
-      put(out + 8 * c, v);
+      if (absent(v)) continue;
+      put(out, v);
     }
   } else if constexpr (WPR == 2) {
     // Two waves per row: waves 0 and 2 hold the same columns, as do 1 and 3;
-    // w0 + w2 and w1 + w3 through one LDS row of D floats (the weights'
+    // w0 + w2 and w1 + w3 through one LDS row of Dp floats (the weights'
     // space is reused, hence the barrier first).
     __syncthreads();
     if (wave >= 2) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int c = v * LPR + l;
-        if (MASKED && c >= nv) continue;
-        put(lds + 8 * c, v);
+        if (absent(v)) continue;
+        put(lds, v);
       }
     }
     __syncthreads();
     if (wave < 2) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int c = v * LPR + l;
-        if (MASKED && c >= nv) continue;
-        add_from(lds + 8 * c, v);
-        put(out + 8 * c, v);
+        if (absent(v)) continue;
+        add_from(lds, v);
+        put(out, v);
       }
     }
   } else {
-    // One wave per row: ((w0 + w2) + (w1 + w3)) through two LDS rows of D
+    // One wave per row: ((w0 + w2) + (w1 + w3)) through two LDS rows of Dp
     // floats (the weights' space is reused, hence the barrier first).
     __syncthreads();
     auto lds_row = [&](int b) { return lds + b * Dp; };
     if (wave >= 2 && writer) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int c = v * LPR + l;
-        if (MASKED && c >= nv) continue;
-        put(lds_row(wave - 2) + 8 * c, v);
+        if (absent(v)) continue;
+        put(lds_row(wave - 2), v);
       }
     }
     __syncthreads();
     if (wave < 2 && writer) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int c = v * LPR + l;
-        if (MASKED && c >= nv) continue;
-        float* d = lds_row(wave) + 8 * c;
-        add_from(d, v);
-        if (wave == 1) put(d, v);  // the same wave read this row just above
+        if (absent(v)) continue;
+        add_from(lds_row(wave), v);
+        if (wave == 1) put(lds_row(wave), v);  // the same wave read this row just above
       }
     }
     __syncthreads();
     if (wave == 0 && writer) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int c = v * LPR + l;
-        if (MASKED && c >= nv) continue;
-        add_from(lds_row(1) + 8 * c, v);
-        put(out + 8 * c, v);
+        if (absent(v)) continue;
+        add_from(lds_row(1), v);
+        put(out, v);
       }
     }
   }

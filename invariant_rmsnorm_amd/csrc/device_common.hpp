@@ -17,10 +17,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // fp16, weights bf16, fp16 or fp32.
 enum : int { kBf16 = 0, kF16 = 1, kF32 = 2 };
 // Row storage of a kernel instance: the activation type, plus kElem when
-// rows move element by element. A lane still owns groups of 8 consecutive
-// elements (the same geometry and reduction tree as 16-byte vectors), but
-// each group moves as eight 2-byte accesses: rows of any length D and any
-// 2-byte alignment, elements past D read as zero and are never written.
+// rows move element by element (rows of any length D and any 2-byte
+// alignment). The geometry (lanes per row, groups of 8 per lane) is that of
+// 16-byte rows with ceil(D/8) groups, but group v of lane l holds the
+// elements (8v + e) * LPR + l, e = 0..7, so that each 2-byte access of the
+// row's lanes covers consecutive elements; elements past D read as zero and
+// are never written.
 enum : int { kElem = 8, kBf16E = kBf16 | kElem, kF16E = kF16 | kElem };
 constexpr int value_dt(int DT) { return DT & ~kElem; }
 constexpr bool elem_dt(int DT) { return (DT & kElem) != 0; }
@@ -134,14 +136,15 @@ __device__ __forceinline__ void buf_store16_nt(const u32x4& v, __amdgpu_buffer_r
   __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 2);
 }
 
-// Elements [8c, 8c + 8) of a row at byte offset `off` of a row resource;
-// `valid` = how many of them lie inside the row (8, except in the last group
-// of a row whose length is not a multiple of 8). With 16-byte storage the
-// group is one vector (valid is always 8 there); element-wise storage gives
-// each element past the row an offset beyond the resource, so it reads as
-// zero.
-template <int DT, int POLICY = kLoadDefault>
-__device__ __forceinline__ u32x4 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off, int valid) {
+// One lane's group of 8 row elements through a row resource. 16-byte
+// storage: elements [8c, 8c + 8) as one vector at byte offset `off`.
+// Element-wise storage: element e of the group is STRIDE elements after
+// element e - 1 (STRIDE = the lanes sharing the row, so that one 2-byte
+// access of all lanes covers consecutive elements), `off` is the byte offset
+// of element 0 and `left` the row's elements from it on; elements past the
+// row get an offset beyond the resource and read as zero.
+template <int DT, int STRIDE, int POLICY = kLoadDefault>
+__device__ __forceinline__ u32x4 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off, int left) {
   if constexpr (!elem_dt(DT)) {
     return buf_load16<POLICY>(r, off);
   } else {
@@ -149,16 +152,16 @@ __device__ __forceinline__ u32x4 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t of
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       h[e] = __builtin_amdgcn_raw_buffer_load_b16(
-          r, static_cast<int>(e < valid ? off + 2 * e : kOutOfRange), 0, POLICY);
+          r, static_cast<int>(e * STRIDE < left ? off + 2 * e * STRIDE : kOutOfRange), 0, POLICY);
     return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                  h[6] | (h[7] << 16)};
   }
 }
-// Stores the group (non-temporal); element-wise storage writes only the
-// `valid` elements inside the row.
-template <int DT>
+// Stores a group the same way (non-temporal); element-wise storage writes
+// only the elements inside the row.
+template <int DT, int STRIDE>
 __device__ __forceinline__ void store_row8(const u32x4& v, __amdgpu_buffer_rsrc_t r, uint32_t off,
-                                           int valid) {
+                                           int left) {
   if constexpr (!elem_dt(DT)) {
     buf_store16_nt(v, r, off);
   } else {
@@ -167,7 +170,7 @@ __device__ __forceinline__ void store_row8(const u32x4& v, __amdgpu_buffer_rsrc_
     for (int e = 0; e < 8; ++e)
       __builtin_amdgcn_raw_buffer_store_b16(
           static_cast<unsigned short>(w[e >> 1] >> (16 * (e & 1))), r,
-          static_cast<int>(e < valid ? off + 2 * e : kOutOfRange), 0, 2);
+          static_cast<int>(e * STRIDE < left ? off + 2 * e * STRIDE : kOutOfRange), 0, 2);
   }
 }
 
@@ -394,45 +397,38 @@ __device__ __forceinline__ void weights8(const void* __restrict__ gamma, int wdt
   }
 }
 
-// The weights of a last group with only `valid` < 8 elements inside the
-// row, one element at a time (nothing past gamma's D values is read); the
-// rest are zero.
-__device__ __forceinline__ void weights_part(const void* __restrict__ gamma, int wdt, int c,
-                                             int valid, float (&w)[8]) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    w[k] = 0.0f;
-    if (k < valid) {
-      const int j = 8 * c + k;
-      if (wdt == kF32) {
-        w[k] = static_cast<const float*>(gamma)[j];
-      } else {
-        const uint32_t b = static_cast<const uint16_t*>(gamma)[j];
-        w[k] = wdt == kF16 ? f16_pair(b).x : bf16_lo(b);
-      }
-    }
-  }
+// Weight j of gamma as fp32 (any weight type).
+__device__ __forceinline__ float weight_at(const void* __restrict__ gamma, int wdt, int j) {
+  if (wdt == kF32) return static_cast<const float*>(gamma)[j];
+  const uint32_t b = static_cast<const uint16_t*>(gamma)[j];
+  return wdt == kF16 ? f16_pair(b).x : bf16_lo(b);
 }
 
-// The weights of group c of a row of D elements (TAIL: D may not be a
-// multiple of 8).
-template <bool TAIL>
-__device__ __forceinline__ void weights_group(const void* __restrict__ gamma, int wdt, int c, int D,
-                                              float (&w)[8]) {
-  if (TAIL && 8 * c + 8 > D) weights_part(gamma, wdt, c, D - 8 * c, w);
-  else weights8(gamma, wdt, c, w);
+// Element-wise storage: the weights of elements (8v + e) * LPR + l of a row
+// of D (zero past D), w_eff = fp32(gamma) (+1.0f in fp32 when zero-centred).
+template <int LPR, int VPL>
+__device__ __forceinline__ void load_weights_elem(const void* __restrict__ gamma, int wdt, int zc,
+                                                  int D, int l, float (&w)[VPL][8]) {
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = (8 * v + e) * LPR + l;
+      w[v][e] = j < D ? weight_at(gamma, wdt, j) : 0.0f;
+      if (zc) w[v][e] = w[v][e] + 1.0f;
+    }
 }
 
 // Loads this lane's weights w_eff = fp32(gamma) (+1.0f in fp32 when
 // zero-centred) for its vectors c = v*LPR + l; columns past D read as zero.
-template <int LPR, int VPL, bool MASKED, bool TAIL = false>
+template <int LPR, int VPL, bool MASKED>
 __device__ __forceinline__ void load_weights(const void* __restrict__ gamma, int wdt, int zc,
-                                             int nv, int D, int l, float (&w)[VPL][8]) {
+                                             int nv, int l, float (&w)[VPL][8]) {
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int c = v * LPR + l;
     if (!MASKED || c < nv) {
-      weights_group<TAIL>(gamma, wdt, c, D, w[v]);
+      weights8(gamma, wdt, c, w[v]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) w[v][k] = 0.0f;

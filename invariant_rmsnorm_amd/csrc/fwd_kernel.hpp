@@ -67,19 +67,23 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   const float Df = static_cast<float>(a.D);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS_BLOCK;
 
+  constexpr bool ELEM = elem_dt(DT);
   float w[VPL][8];
-  load_weights<LPR, VPL, MASKED, elem_dt(DT)>(a.gamma, a.wdt, a.zc, nv, a.D, l, w);
+  if constexpr (ELEM) load_weights_elem<LPR, VPL>(a.gamma, a.wdt, a.zc, a.D, l, w);
+  else load_weights<LPR, VPL, MASKED>(a.gamma, a.wdt, a.zc, nv, l, w);
 
-  // Byte offset of this lane's vector v within its row group, per tensor;
-  // vectors past D get an offset no resource reaches.
+  // Byte offset of this lane's group v within its row group, per tensor:
+  // the vector c = v*LPR + l (vectors past D get an offset no resource
+  // reaches), or with element-wise storage the group's first element
+  // 8v*LPR + l.
   auto voff = [&](int v, int64_t ld) -> uint32_t {
+    if constexpr (ELEM) return static_cast<uint32_t>(slot * ld * 2 + 2 * (8 * v * LPR + l));
     const int c = v * LPR + l;
     if (MASKED && c >= nv) return kOutOfRange;
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
-  // Elements of this lane's group v inside the row (8 or more but for a
-  // partial last group; used by element-wise storage only).
-  auto valid = [&](int v) { return a.D - 8 * (v * LPR + l); };
+  // Element-wise storage: the row's elements from the group's first on.
+  auto valid = [&](int v) { return a.D - (8 * v * LPR + l); };
   // Rows first .. first+RPW-1 form row group u of the wave; `first` is
   // wave-uniform.
   auto group_first = [&](int64_t base, int u) { return base + group * ROWS_WAVE + u * RPW; };
@@ -90,16 +94,16 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
       const int64_t first = group_first(base, u);
       const auto rx = rows_rsrc(a.x, first, a.T, RPW, a.ld_x, a.D);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT>(rx, voff(v, a.ld_x), valid(v));
+      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT, LPR>(rx, voff(v, a.ld_x), valid(v));
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, a.T, RPW, a.ld_z, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT>(rz, voff(v, a.ld_z), valid(v));
+        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, LPR>(rz, voff(v, a.ld_z), valid(v));
       }
       if constexpr (ADD) {
         const auto rr = rows_rsrc(a.rin, first, a.T, RPW, a.ld_rin, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT>(rr, voff(v, a.ld_rin), valid(v));
+        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, LPR>(rr, voff(v, a.ld_rin), valid(v));
       }
     }
   };
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] * gate_fast<ACT>(zf[k]);
         }
-        store_row8<DT>(pack8<DT>(o), ry, voff(v, a.ld_y), valid(v));
+        store_row8<DT, LPR>(pack8<DT>(o), ry, voff(v, a.ld_y), valid(v));
       }
       if (a.res != nullptr) {
         // residual output: a byte copy of x, or for the fused add bf16(h)
@@ -172,9 +176,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
           if constexpr (ADD) {
             float f[8];
             row_values(xq[u][v], zq[u][v], f);
-            store_row8<DT>(pack8<DT>(f), rr, voff(v, a.ld_res), valid(v));
+            store_row8<DT, LPR>(pack8<DT>(f), rr, voff(v, a.ld_res), valid(v));
           } else {
-            store_row8<DT>(xq[u][v], rr, voff(v, a.ld_res), valid(v));
+            store_row8<DT, LPR>(xq[u][v], rr, voff(v, a.ld_res), valid(v));
           }
         }
       }

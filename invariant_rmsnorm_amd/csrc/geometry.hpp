@@ -39,7 +39,17 @@ constexpr int kBwdMinVplMulti = 3;
 // instead of 161 us per 256 MiB step), while two per CU at D >= 4096 was
 // slower.
 constexpr int64_t kCus = 256;
-constexpr int bwd_waves_per_eu(int vpl) { return vpl >= 5 ? 1 : 2; }
+// Rows moved element by element (D not a multiple of 8) keep two
+// workgroups per CU up to this many groups per lane: their loads wait on
+// eight 2-byte accesses per group, and a second workgroup hides that
+// (measured at D = 12290, 7 groups per lane: the rows kernel 2239 ->
+// 3208 GB/s; 2616 -> 2909 with the residual gradient, spills included).
+#ifndef RMSN_BWD_ELEM_TWO_PER_CU_VPL
+#define RMSN_BWD_ELEM_TWO_PER_CU_VPL 8
+#endif
+constexpr int bwd_waves_per_eu(int vpl, bool elem = false) {
+  return vpl < 5 || (elem && vpl <= RMSN_BWD_ELEM_TWO_PER_CU_VPL) ? 2 : 1;
+}
 constexpr int64_t kMaxChunks = 2 * kCus;
 
 struct RowGeom {
@@ -146,7 +156,7 @@ struct BwdPlan {
 #endif
 inline int64_t bwd_target_chunks(int64_t D) {
   return kCus * (RMSN_BWD_BLOCKS_PER_CU > 0 ? RMSN_BWD_BLOCKS_PER_CU
-                                            : bwd_waves_per_eu(bwd_geom(D).vpl));
+                                            : bwd_waves_per_eu(bwd_geom(D).vpl, D % 8 != 0));
 }
 
 inline BwdPlan bwd_plan(int64_t T, int64_t D) {
