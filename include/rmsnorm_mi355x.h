@@ -43,10 +43,8 @@
  * alone.
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
- * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD). Supported: 1 <= D <= 32768 for
- * the plain, residual and residual-gradient entry points (rmsnorm_fwd,
- * rmsnorm_residual_fwd, rmsnorm_bwd and its stages, the _dt forms); D a
- * multiple of 8 for the gated and fused-add entry points. When D is a
+ * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD), 1 <= D <= 32768 (RMSN_MAX_D)
+ * for every entry point. When D is a
  * multiple of 8, rows move as 16-byte vectors: every bf16 / fp16 base
  * pointer and ld * 2 bytes must be multiples of 16 bytes. Other D move
  * element by element through the same kernels, reduction trees and
@@ -79,7 +77,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 9
+#define RMSN_ABI_VERSION 10
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -87,9 +85,8 @@ typedef enum rmsn_status {
   RMSN_OK = 0,
   RMSN_ERR_NULL = 1,           /* a required pointer is NULL */
   RMSN_ERR_SHAPE = 2,          /* T < 0, D <= 0, ld < D or ld > RMSN_MAX_LD */
-  RMSN_ERR_UNSUPPORTED_D = 3,  /* D > RMSN_MAX_D; D not a multiple of 8 for the
-                                  gated and fused-add forms; GEMM K not a
-                                  positive multiple of 32 */
+  RMSN_ERR_UNSUPPORTED_D = 3,  /* D > RMSN_MAX_D; GEMM K not a positive
+                                  multiple of 32 */
   RMSN_ERR_MISALIGNED = 4,     /* a pointer or ld*2 below the alignment its
                                   operand needs (see Layout) */
   RMSN_ERR_EPS = 5,            /* eps negative or not finite */

@@ -55,11 +55,10 @@ bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Row length: 1..32768 for the plain, residual and residual-gradient forms
-// (`any_D`), a multiple of 8 in 8..32768 for the gated and fused-add forms.
-rmsn_status check_D(int64_t D, bool any_D) {
+// Row length: 1..32768 for every form.
+rmsn_status check_D(int64_t D) {
   if (D <= 0) return RMSN_ERR_SHAPE;
-  if (D > kMaxD || (!any_D && D % 8 != 0)) return RMSN_ERR_UNSUPPORTED_D;
+  if (D > kMaxD) return RMSN_ERR_UNSUPPORTED_D;
   return RMSN_OK;
 }
 
@@ -120,7 +119,7 @@ rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64
                 (rounding != RMSN_GATED_ROUND_FP32 && rounding != RMSN_GATED_ROUND_CAST)))
     return RMSN_ERR_MODE;
   if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D, !gated));
+  RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
   if (gated) RMSN_TRY(check_mat(z, ld_z, T, D, true));
   RMSN_TRY(check_mat(y, ld_y, T, D, true));
@@ -160,7 +159,7 @@ bool add_fwd_alias(const uint16_t* x, int64_t ld_x, const uint16_t* rin, int64_t
 }
 
 size_t workspace_bytes(int64_t T, int64_t D) {
-  if (T <= 0 || check_D(D, true) != RMSN_OK) return 0;
+  if (T <= 0 || check_D(D) != RMSN_OK) return 0;
   const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
   return static_cast<size_t>(p.chunks) * static_cast<size_t>(rmsn::part_stride(D)) * sizeof(float);
 }
@@ -184,7 +183,7 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
                       Types ty = Types{}) {
   if (bad_types(ty)) return RMSN_ERR_MODE;
   if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D, !gated && !add));
+  RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(g, ld_g, T, D, true));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
   if (add) RMSN_TRY(check_mat(rin, ld_rin, T, D, true));
@@ -246,8 +245,8 @@ const char* rmsnorm_status_string(int status) {
     case RMSN_ERR_NULL: return "RMSN_ERR_NULL: a required pointer is NULL";
     case RMSN_ERR_SHAPE: return "RMSN_ERR_SHAPE: T < 0, D <= 0, ld < D or ld > 2^24";
     case RMSN_ERR_UNSUPPORTED_D:
-      return "RMSN_ERR_UNSUPPORTED_D: D must be in [1, 32768] (a multiple of 8 for the gated and "
-             "fused-add forms); the GEMM's K a positive multiple of 32";
+      return "RMSN_ERR_UNSUPPORTED_D: D must be in [1, 32768]; the GEMM's K a positive multiple "
+             "of 32";
     case RMSN_ERR_MISALIGNED: return "RMSN_ERR_MISALIGNED: pointers and row strides must be 16-byte aligned";
     case RMSN_ERR_EPS: return "RMSN_ERR_EPS: eps must be finite and >= 0";
     case RMSN_ERR_ALIASING: return "RMSN_ERR_ALIASING: an output overlaps an input or another output";
@@ -293,7 +292,7 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D) { return workspace_byte
 rmsn_status rmsnorm_bwd_partials_layout(int64_t T, int64_t D, int64_t* block_rows,
                                         int64_t* group_blocks, int64_t* chunks) {
   if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D, true));
+  RMSN_TRY(check_D(D));
   const rmsn::BwdPlan p = rmsn::bwd_plan(T, D);
   if (block_rows) *block_rows = p.block_rows;
   if (group_blocks) *group_blocks = p.group_blocks;
@@ -318,7 +317,7 @@ rmsn_status rmsnorm_bwd_rows(const uint16_t* g, int64_t ld_g, const uint16_t* x,
 rmsn_status rmsnorm_bwd_finish(const void* workspace, size_t workspace_bytes_, int64_t T, int64_t D,
                                float* dgamma, void* stream) {
   if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D, true));
+  RMSN_TRY(check_D(D));
   RMSN_TRY(check_f32(dgamma, 16, true));
   const size_t need = workspace_bytes(T, D);
   if (need > 0) {
@@ -377,7 +376,7 @@ rmsn_status rmsnorm_add_fwd(const uint16_t* x, int64_t ld_x, const uint16_t* res
                             int64_t T, int64_t D, uint16_t* y, int64_t ld_y, uint16_t* residual_out,
                             int64_t ld_rout, float* rstd, void* stream) {
   if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D, false));
+  RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
   RMSN_TRY(check_mat(residual, ld_res, T, D, true));
   RMSN_TRY(check_mat(y, ld_y, T, D, true));

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 9
+    assert irn.rmsnorm_abi_version() == 10
 
 
 def test_status_strings():
@@ -211,7 +211,8 @@ def gated_fwd_ex(**kw):
     (dict(ld_z=100), irn.RMSN_ERR_SHAPE),
     (dict(out=Z), irn.RMSN_ERR_ALIASING),
     (dict(rstd=Z + 64), irn.RMSN_ERR_ALIASING),
-    (dict(D=12, ld_x=16, ld_z=16, ld_out=16), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=32769, ld_x=32769, ld_z=32769, ld_out=32769), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=12, ld_x=13, ld_z=16, ld_out=16, z=Z + 1), irn.RMSN_ERR_MISALIGNED),   # 2-byte rule
     (dict(eps=-1.0), irn.RMSN_ERR_EPS),
 ])
 def test_gated_forward_ex_rejections(kw, code):
@@ -249,8 +250,10 @@ def gated_bwd(**kw):
     (dict(dx=Z + 4096), irn.RMSN_ERR_ALIASING),             # partial overlap with z
     (dict(ws=DZ), irn.RMSN_ERR_ALIASING),
     (dict(ws=None), irn.RMSN_ERR_WORKSPACE),
-    (dict(D=4100, ld_g=4104, ld_x=4104, ld_z=4104, ld_dx=4104, ld_dz=4104),
+    (dict(D=32772, ld_g=32772, ld_x=32772, ld_z=32772, ld_dx=32772, ld_dz=32772),
      irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=4100, ld_g=4100, ld_x=4101, ld_z=4100, ld_dx=4100, ld_dz=4100, z=Z + 3),
+     irn.RMSN_ERR_MISALIGNED),
     (dict(T=-1), irn.RMSN_ERR_SHAPE),
 ])
 def test_gated_backward_rejections(kw, code):
@@ -293,7 +296,8 @@ def add_fwd(**kw):
     (dict(gamma=None), irn.RMSN_ERR_NULL),
     (dict(T=-1), irn.RMSN_ERR_SHAPE),
     (dict(ld_res=4000), irn.RMSN_ERR_SHAPE),
-    (dict(D=100, ld_x=104, ld_res=104, ld_y=104, ld_rout=104), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=32769, ld_x=32769, ld_res=32769, ld_y=32769, ld_rout=32769), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(D=100, ld_x=101, ld_res=101, ld_y=101, ld_rout=101, res=B + 1), irn.RMSN_ERR_MISALIGNED),
     (dict(res=B + 2), irn.RMSN_ERR_MISALIGNED),
     (dict(rout=E + 8), irn.RMSN_ERR_MISALIGNED),
     (dict(eps=-1.0), irn.RMSN_ERR_EPS),

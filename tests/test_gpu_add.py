@@ -24,6 +24,8 @@ pytestmark = pytest.mark.gpu
 
 WIDTHS = [8, 16, 24, 64, 96, 128, 136, 256, 520, 1024, 2048, 2560, 4096, 4104, 5120, 8192,
           8200, 12288, 16384, 20480, 32768]
+# not multiples of 8: element-wise rows
+WIDTHS += [3, 13, 100, 1001, 4100, 12290, 20003]
 
 
 def _run(p, with_gro, zc=None):
@@ -101,9 +103,10 @@ def test_add_edge_rows(gpu):
     assert np.array_equal(gr[~fin], rr[~fin]) or np.all(np.isnan(rr[~fin]))
 
 
-def test_add_in_place(gpu):
+@pytest.mark.parametrize("D", [4096, 4100, 13])
+def test_add_in_place(gpu, D):
     """y = x and residual_out = residual in place give the out-of-place bytes."""
-    p = wl.tiny(True, T=777, D=4096, seed=8800, with_residual=True)
+    p = wl.tiny(True, T=777, D=D, seed=8800 + D, with_residual=True)
     x, res, gamma = dev_bf16(p.x), dev_bf16(p.residual), dev_f32(p.gamma)
     y0, rout0, r0 = irn.rmsnorm_add_fwd(x, res, gamma, True, p.eps)
     x2, res2 = x.clone(), res.clone()

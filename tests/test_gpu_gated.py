@@ -29,7 +29,9 @@ ACTS = [(irn.RMSN_GATE_SILU, oracle.SILU), (irn.RMSN_GATE_SIGMOID, oracle.SIGMOI
 ROUNDINGS = [(irn.RMSN_GATED_ROUND_FP32, oracle.FP32_WEIGHT),
              (irn.RMSN_GATED_ROUND_CAST, oracle.CAST_INPUT)]
 WIDTHS = [8, 64, 96, 128, 136, 1024, 2560, 4096, 4104, 5632, 6144, 8192, 8200, 16384, 18440,
-          32768]
+          32768,
+          # not multiples of 8: element-wise rows
+          5, 13, 100, 1001, 4100, 12290, 20003]
 
 
 def _rows_for(D):
