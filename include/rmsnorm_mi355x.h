@@ -44,7 +44,8 @@
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
  * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD), 1 <= D <= 32768 (RMSN_MAX_D)
- * for every entry point. When D is a
+ * for every entry point except rmsnorm_gated_bwd, which needs D a multiple
+ * of 8. When D is a
  * multiple of 8, rows move as 16-byte vectors: every bf16 / fp16 base
  * pointer and ld * 2 bytes must be multiples of 16 bytes. Other D move
  * element by element through the same kernels, reduction trees and
@@ -85,7 +86,8 @@ typedef enum rmsn_status {
   RMSN_OK = 0,
   RMSN_ERR_NULL = 1,           /* a required pointer is NULL */
   RMSN_ERR_SHAPE = 2,          /* T < 0, D <= 0, ld < D or ld > RMSN_MAX_LD */
-  RMSN_ERR_UNSUPPORTED_D = 3,  /* D > RMSN_MAX_D; GEMM K not a positive
+  RMSN_ERR_UNSUPPORTED_D = 3,  /* D > RMSN_MAX_D; D not a multiple of 8 for
+                                  rmsnorm_gated_bwd; GEMM K not a positive
                                   multiple of 32 */
   RMSN_ERR_MISALIGNED = 4,     /* a pointer or ld*2 below the alignment its
                                   operand needs (see Layout) */

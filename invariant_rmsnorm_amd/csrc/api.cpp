@@ -55,10 +55,11 @@ bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Row length: 1..32768 for every form.
-rmsn_status check_D(int64_t D) {
+// Row length: 1..32768, a multiple of 8 for the gated backward (`any_D`
+// false).
+rmsn_status check_D(int64_t D, bool any_D = true) {
   if (D <= 0) return RMSN_ERR_SHAPE;
-  if (D > kMaxD) return RMSN_ERR_UNSUPPORTED_D;
+  if (D > kMaxD || (!any_D && D % 8 != 0)) return RMSN_ERR_UNSUPPORTED_D;
   return RMSN_OK;
 }
 
@@ -89,6 +90,13 @@ rmsn_status check_f32(const float* p, uintptr_t align, bool required) {
   } while (0)
 
 rmsn_status hip_status(int rc) { return rc == 0 ? RMSN_OK : RMSN_ERR_HIP; }
+
+// The forward reads its inputs with the streaming hint when x is larger
+// than the Infinity Cache: the backward could not find them there anyway.
+#ifndef RMSN_FWD_STREAM_X
+#define RMSN_FWD_STREAM_X 1
+#endif
+int fwd_stream(int64_t T, int64_t D) { return RMSN_FWD_STREAM_X && T * D * 2 > rmsn::kCacheBytes; }
 
 // Storage types of one call: activations (bf16 or fp16) and weights (bf16,
 // fp16 or fp32). The entry points without a _dt suffix use bf16 / fp32.
@@ -136,7 +144,7 @@ rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64
 
   rmsn::FwdArgs a{x, ld_x, gated ? z : nullptr, ld_z, act, rounding == RMSN_GATED_ROUND_CAST,
                   gamma, ty.wdt, ty.dt, zc != 0, eps, T, static_cast<int>(D), y, ld_y,
-                  residual ? res : nullptr, ld_res, rstd, nullptr, 0};
+                  residual ? res : nullptr, ld_res, rstd, nullptr, 0, fwd_stream(T, D)};
   return hip_status(rmsn::launch_fwd(a, stream));
 }
 
@@ -183,7 +191,7 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
                       Types ty = Types{}) {
   if (bad_types(ty)) return RMSN_ERR_MODE;
   if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D));
+  RMSN_TRY(check_D(D, !gated));
   RMSN_TRY(check_mat(g, ld_g, T, D, true));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
   if (add) RMSN_TRY(check_mat(rin, ld_rin, T, D, true));
@@ -245,8 +253,8 @@ const char* rmsnorm_status_string(int status) {
     case RMSN_ERR_NULL: return "RMSN_ERR_NULL: a required pointer is NULL";
     case RMSN_ERR_SHAPE: return "RMSN_ERR_SHAPE: T < 0, D <= 0, ld < D or ld > 2^24";
     case RMSN_ERR_UNSUPPORTED_D:
-      return "RMSN_ERR_UNSUPPORTED_D: D must be in [1, 32768]; the GEMM's K a positive multiple "
-             "of 32";
+      return "RMSN_ERR_UNSUPPORTED_D: D must be in [1, 32768] (a multiple of 8 for the gated "
+             "backward); the GEMM's K a positive multiple of 32";
     case RMSN_ERR_MISALIGNED: return "RMSN_ERR_MISALIGNED: pointers and row strides must be 16-byte aligned";
     case RMSN_ERR_EPS: return "RMSN_ERR_EPS: eps must be finite and >= 0";
     case RMSN_ERR_ALIASING: return "RMSN_ERR_ALIASING: an output overlaps an input or another output";
@@ -390,7 +398,7 @@ rmsn_status rmsnorm_add_fwd(const uint16_t* x, int64_t ld_x, const uint16_t* res
   const rmsn::FwdArgs a{x, ld_x, nullptr, 0, 0, 0, gamma, RMSN_DTYPE_F32, RMSN_DTYPE_BF16,
                         zero_centered_gamma != 0, eps, T,
                         static_cast<int>(D), y, ld_y, residual_out, ld_rout, rstd, residual,
-                        ld_res};
+                        ld_res, fwd_stream(T, D)};
   return hip_status(rmsn::launch_fwd(a, stream));
 }
 

@@ -23,6 +23,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <algorithm>
 #include <atomic>
 
@@ -88,24 +90,33 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   // wave-uniform.
   auto group_first = [&](int64_t base, int u) { return base + group * ROWS_WAVE + u * RPW; };
 
-  auto load_step = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
+  // The inputs' cache policy: the default keeps rows the backward reads
+  // next in the Infinity Cache; inputs larger than it take the streaming
+  // hint (a wave-uniform choice).
+  auto load_inputs = [&](auto policy, int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
+    constexpr int P = decltype(policy)::value;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t first = group_first(base, u);
       const auto rx = rows_rsrc(a.x, first, a.T, RPW, a.ld_x, a.D);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT, LPR>(rx, voff(v, a.ld_x), valid(v));
+      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT, LPR, P>(rx, voff(v, a.ld_x), valid(v));
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, a.T, RPW, a.ld_z, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, LPR>(rz, voff(v, a.ld_z), valid(v));
+        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, LPR, P>(rz, voff(v, a.ld_z), valid(v));
       }
       if constexpr (ADD) {
         const auto rr = rows_rsrc(a.rin, first, a.T, RPW, a.ld_rin, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, LPR>(rr, voff(v, a.ld_rin), valid(v));
+        for (int v = 0; v < VPL; ++v)
+          zq[u][v] = load_row8<DT, LPR, P>(rr, voff(v, a.ld_rin), valid(v));
       }
     }
+  };
+  auto load_step = [&](int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
+    if (a.x_stream) load_inputs(std::integral_constant<int, kLoadStream>{}, base, xq, zq);
+    else load_inputs(std::integral_constant<int, kLoadDefault>{}, base, xq, zq);
   };
   // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
   // rounding).

@@ -29,6 +29,7 @@ struct FwdArgs {
   float* rstd;  // or nullptr
   const uint16_t* rin;  // fused add: residual input, normalise x + rin; or nullptr
   int64_t ld_rin;
+  int x_stream;  // read x (z, rin) with the non-temporal hint (set by the caller)
 };
 
 struct BwdArgs {
@@ -85,7 +86,6 @@ int launch_bwd_rows_add(const BwdArgs& a, void* stream);    // a.rin != nullptr
 int launch_bwd_rows_f16(const BwdArgs& a, void* stream);
 int launch_bwd_rows_elem(const BwdArgs& a, void* stream);      // D % 8 != 0 (plain, gres)
 int launch_bwd_rows_elem_f16(const BwdArgs& a, void* stream);  // the same, fp16 activations
-int launch_bwd_rows_gated_elem(const BwdArgs& a, void* stream);  // D % 8 != 0, gated
 int launch_bwd_rows_add_elem(const BwdArgs& a, void* stream);    // D % 8 != 0, fused add    // a.dt == fp16 (plain, gres)
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
 int launch_gemm(const GemmArgs& a, void* stream);

@@ -29,9 +29,10 @@ ACTS = [(irn.RMSN_GATE_SILU, oracle.SILU), (irn.RMSN_GATE_SIGMOID, oracle.SIGMOI
 ROUNDINGS = [(irn.RMSN_GATED_ROUND_FP32, oracle.FP32_WEIGHT),
              (irn.RMSN_GATED_ROUND_CAST, oracle.CAST_INPUT)]
 WIDTHS = [8, 64, 96, 128, 136, 1024, 2560, 4096, 4104, 5632, 6144, 8192, 8200, 16384, 18440,
-          32768,
-          # not multiples of 8: element-wise rows
-          5, 13, 100, 1001, 4100, 12290, 20003]
+          32768]
+# not multiples of 8: element-wise rows (the forward; the gated backward
+# rejects them)
+ODD_WIDTHS = [5, 13, 100, 1001, 4100, 12290, 20003]
 
 
 def _rows_for(D):
@@ -83,7 +84,7 @@ def _check_bwd(p, act, act_o, label):
 
 @pytest.mark.parametrize("rounding,rounding_o", ROUNDINGS)
 @pytest.mark.parametrize("act,act_o", ACTS)
-@pytest.mark.parametrize("D", WIDTHS)
+@pytest.mark.parametrize("D", WIDTHS + ODD_WIDTHS)
 def test_gated_forward_variants(gpu, D, act, act_o, rounding, rounding_o):
     """Every geometry class at a T spanning several steps plus a ragged tail."""
     zc = D % 16 == 8
@@ -242,3 +243,9 @@ def test_gated_repeat_runs_bitwise(gpu):
         for a, b in zip(first, again):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_gated_backward_rejects_odd_rows(gpu):
+    p = wl.tiny(False, T=4, D=100, seed=9500, with_gate=True)
+    with pytest.raises(irn.RmsnormError, match="UNSUPPORTED_D"):
+        _gpu_bwd(p, irn.RMSN_GATE_SILU)
