@@ -1,7 +1,7 @@
 """Writes oracle_tiny_sha256.json: SHA-256 digests of the CPU oracle's
 outputs on the small seeded fixtures (T=16, D=128; both weight conventions;
-residual, gated, residual-gradient and fused add-norm forms), plus digests of
-the inputs.
+residual, gated, residual-gradient and fused add-norm forms; and rows whose
+length is not a multiple of 8, D = 13 and 100), plus digests of the inputs.
 
 It calls only the oracle and the input generator. A later change that moves
 any of these bytes must be explained in the commit that regenerates the file.
@@ -29,8 +29,9 @@ def digest(a) -> str:
 
 def manifest() -> dict:
     m = {}
-    for zc in (False, True):
-        p = wl.tiny(zc, with_gres=True, with_gate=True, with_residual=True)
+    cases = [(zc, 128, 1001) for zc in (False, True)] + [(False, 13, 1013), (True, 100, 1100)]
+    for zc, D, seed in cases:
+        p = wl.tiny(zc, D=D, seed=seed, with_gres=True, with_gate=True, with_residual=True)
         key = p.name
         y, r = oracle.fwd(p.x, p.gamma, zc, p.eps)
         _, res, _ = oracle.residual_fwd(p.x, p.gamma, zc, p.eps)
