@@ -1,7 +1,7 @@
 """GPU parity: the HIP library (through its C-ABI) against the CPU oracle,
 element by element, on seeded inputs small enough for the oracle.
 
-Tolerances (BASELINE): y / gated out <= 1 bf16 ulp, rstd <= 1e-6 relative,
+Tolerances: y / gated out <= 1 bf16 ulp, rstd <= 1e-6 relative,
 dx <= 1 bf16 ulp (with the cancellation rule in numerics.py), dgamma <= 1e-5
 relative in the infinity norm. Exact-arithmetic inputs must match bitwise.
 """
