@@ -133,11 +133,12 @@ def test_gemm_every_tile_gives_the_same_rows(gpu):
 
 
 @pytest.mark.slow
-def test_gemm_full_size_sampled(gpu):
-    """M = N = K = 4096: 64 sampled rows against the oracle."""
-    M = N = K = 4096
-    x = synth.normal_bf16(2160, 1, M, K)
-    w = synth.normal_bf16(2160, 2, N, K)
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (4096, 11008, 4096), (4096, 4096, 11008)])
+def test_gemm_full_size_sampled(gpu, M, N, K):
+    """Shapes of the batch-invariant GEMM cost table: 64 sampled rows
+    against the oracle."""
+    x = synth.normal_bf16(2160 + N + K, 1, M, K)
+    w = synth.normal_bf16(2160 + N + K, 2, N, K)
     y = irn.bigemm_bf16_xwt(dev_bf16(x), dev_bf16(w))
     rows = np.random.default_rng(2160).choice(M, 64, replace=False)
     _check_parity(x[rows], w, host_bits(y)[rows])
