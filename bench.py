@@ -5,7 +5,8 @@ then the backward's two kernels, rmsnorm_bwd_rows (dx and the dgamma chunk
 partials) and rmsnorm_bwd_finish (dgamma). Inputs are resident in HBM before
 timing starts. The default workload is the token norm at T=32768, D=4096
 (bf16 activations with 1% outlier rows, fp32 gamma, eps=1e-6); --workload
-selects the other synthetic workloads.
+selects the other synthetic workloads (`residual`: the same inputs through
+rmsnorm_residual_fwd, which also writes a byte copy of x, then the backward).
 
 Prints one JSON line. `value` is algorithmic bytes per step / wall time per
 step over the K timed steps: each input element read once, each output
@@ -91,10 +92,13 @@ def make_inputs(workload: str, torch, dev, rows: int = 0, dim: int = 0):
     def d_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    if workload in ("token", "token_gres"):
+    if workload in ("token", "token_gres", "residual"):
         p = wl.residual(T=rows or 32768, D=dim or 4096, with_gres=(workload == "token_gres"))
         desc = (f"token RMSNorm fwd+bwd with dgamma, T={p.T}, D={p.D}, bf16 x ~N(0,1) with 1% "
                 "outlier rows x50, g ~N(0,1), fp32 gamma=1+N(0,0.1), eps=1e-6")
+        if workload == "residual":
+            desc = ("rmsnorm_residual fwd (y, rstd and a byte copy of x) + bwd with dgamma"
+                    + desc[len("token RMSNorm fwd+bwd with dgamma"):])
     elif workload == "large":
         p = wl.large()
         desc = ("RMSNorm fwd+bwd with dgamma, T=262144, D=4096, zero-centred gamma, "
@@ -139,6 +143,8 @@ def cpu_baseline(p, workload: str, seconds: float):
         a, b = ix[0], ix[-1] + 1
         if workload == "gated":
             _, r = oracle.gated_fwd(p.x[a:b], p.z[a:b], p.gamma, p.zero_centered, p.eps)
+        elif workload == "residual":
+            _, _, r = oracle.residual_fwd(p.x[a:b], p.gamma, p.zero_centered, p.eps)
         elif workload == "add":
             _, _, r = oracle.add_fwd(p.x[a:b], p.residual[a:b], p.gamma, p.zero_centered, p.eps)
         else:
@@ -324,7 +330,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="token",
-                    choices=["token", "token_gres", "large", "gated", "add", "gemm"])
+                    choices=["token", "token_gres", "residual", "large", "gated", "add", "gemm"])
     ap.add_argument("--m", type=int, default=4096, help="gemm workload: rows of X and Y")
     ap.add_argument("--n", type=int, default=4096, help="gemm workload: rows of W, columns of Y")
     ap.add_argument("--k", type=int, default=4096, help="gemm workload: reduction length")
@@ -368,7 +374,8 @@ def main():
     rstd = torch.empty(T, dtype=torch.float32, device=dev)
     gated = args.workload == "gated"
     add = args.workload == "add"
-    rout = torch.empty_like(x) if add else None
+    resid = args.workload == "residual"
+    rout = torch.empty_like(x) if (add or resid) else None
     if not gated:
         g = t["g"]
         gres = t.get("gres")
@@ -390,6 +397,8 @@ def main():
                 dom[1].record(stream)
         elif add:
             irn.rmsnorm_add_fwd(x, t["residual"], gamma, zc, eps, y=y, residual_out=rout, rstd=rstd)
+        elif resid:
+            irn.rmsnorm_residual_fwd(x, gamma, zc, eps, y=y, residual_out=rout, rstd=rstd)
         else:
             irn.rmsnorm_fwd(x, gamma, zc, eps, y=y, rstd=rstd)
         if evs is not None:
@@ -412,12 +421,14 @@ def main():
 
     # bitwise check before timing (two identical steps)
     step()
-    outs = [y] + ([] if gated else [rstd, dx, dgamma]) + ([rout] if add else [])
+    outs = [y] + ([] if gated else [rstd, dx, dgamma]) + ([rout] if rout is not None else [])
     ref = [o.clone() for o in outs]
     step()
     torch.cuda.synchronize()
     if not all(torch.equal(a, b) for a, b in zip(ref, outs)):
         raise SystemExit("repeat step is not bitwise identical")
+    if resid and not torch.equal(rout.view(torch.int16), x.view(torch.int16)):
+        raise SystemExit("residual_out is not a byte copy of x")
     del ref
 
     if args.calibrate_copy:
@@ -441,7 +452,7 @@ def main():
     wall = time.perf_counter() - t0
     dom_ms = sum(a.elapsed_time(b) for a, b in sampled.values()) / len(sampled)
 
-    fwd_kind = "gated_fwd" if gated else "add_fwd" if add else "fwd"
+    fwd_kind = "gated_fwd" if gated else "add_fwd" if add else "residual_fwd" if resid else "fwd"
     rows_kind = None if gated else (("add_" if add else "") +
                                     ("bwd_rows_gres" if gres is not None else "bwd_rows"))
     step_bytes = algo_bytes(fwd_kind, T, D)
