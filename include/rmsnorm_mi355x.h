@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 10
+#define RMSN_ABI_VERSION 11
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -188,6 +188,23 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t T, int64_t D);
  */
 rmsn_status rmsnorm_bwd_partials_layout(int64_t T, int64_t D, int64_t* block_rows,
                                         int64_t* group_blocks, int64_t* chunks);
+
+/*
+ * Rows R of one block of the dgamma partials (RL-Kernel PR "[DSv4][P1-5]
+ * rmsnorm_residual", "Implementation": fixed-order reductions, no split-K or
+ * stream-K). R is a function of D alone: every chunk of the partials is a
+ * union of whole R-row blocks, and within a block the rows are added in a
+ * fixed order. Which blocks form a chunk (group_blocks S and chunks K of
+ * rmsnorm_bwd_partials_layout) depends on T as well: the backward spreads
+ * the batch over at most one or two workgroups per compute unit, as many as
+ * the batch fills. dgamma is therefore deterministic and bitwise repeatable
+ * for a given (T, D), but its rounding depends on T, and a batch split over
+ * several GPUs at block boundaries does not reproduce the one-GPU dgamma
+ * bits (it stays within the dgamma tolerance). The per-row outputs y, rstd
+ * and dx never depend on T. Returns R, or 0 when D is outside
+ * [1, RMSN_MAX_D]. A host-side query: it enqueues nothing.
+ */
+int rmsnorm_dgamma_chunk_rows(int64_t D);
 
 /*
  * Backward. From the upstream gradient g, the input x and the forward's
@@ -348,9 +365,9 @@ rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g,
  * does not, so every row of Y is bitwise identical whatever M, the row's
  * position and the other rows are.
  * Supported: K a positive multiple of 32; K <= ld_x, ld_w <= 2^21 and
- * ld_x, ld_w multiples of 8 with X and W 16-byte aligned; ld_y >= N, Y
- * 2-byte aligned. Errors: RMSN_ERR_SHAPE (negative sizes, strides, or more
- * than 2^31 - 1 tiles of 32 x 64), RMSN_ERR_UNSUPPORTED_D (K not a positive
+ * ld_x, ld_w multiples of 8 with X and W 16-byte aligned; N <= ld_y <=
+ * 2^62 / M, Y 2-byte aligned. Errors: RMSN_ERR_SHAPE (negative sizes,
+ * strides out of range, or more than 2^31 - 1 tiles of 32 x 64), RMSN_ERR_UNSUPPORTED_D (K not a positive
  * multiple of 32), RMSN_ERR_NULL, RMSN_ERR_MISALIGNED, RMSN_ERR_ALIASING
  * (Y overlaps X or W), RMSN_ERR_HIP.
  * M = 0 or N = 0 enqueue nothing. No workspace; one kernel on `stream`.

@@ -47,6 +47,7 @@ EXPORTED = (
     "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
     "rmsnorm_gated_bwd", "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_rows",
     "rmsnorm_fwd_dt", "rmsnorm_bwd_dt", "bigemm_bf16_xwt", "bigemm_bf16_tile",
+    "rmsnorm_dgamma_chunk_rows",
 )
 
 
@@ -90,6 +91,7 @@ def load():
                             sz, vp], i),
         "bigemm_bf16_xwt": ([vp, i64, vp, i64, i64, i64, i64, vp, i64, vp], i),
         "bigemm_bf16_tile": ([i64, i64, vp, vp], i),
+        "rmsnorm_dgamma_chunk_rows": ([i64], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -118,6 +120,11 @@ def rmsnorm_bwd_partials_layout(T: int, D: int):
     _check("rmsnorm_bwd_partials_layout", load().rmsnorm_bwd_partials_layout(
         T, D, *(ctypes.byref(v) for v in out)))
     return tuple(v.value for v in out)
+
+
+def rmsnorm_dgamma_chunk_rows(D: int) -> int:
+    """Rows R of one dgamma block (a function of D alone; 0 for an invalid D)."""
+    return load().rmsnorm_dgamma_chunk_rows(D)
 
 
 def chunk_rows(k: int, T: int, D: int):
@@ -156,22 +163,86 @@ def _check(fn, status):
         raise RmsnormError(fn, status)
 
 
-def _dtype(t, dt, name):
-    if t is not None and t.dtype != dt:
-        raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+def _arg(t, name, dtypes, shape, required=True):
+    """Checks one tensor argument before its pointer reaches the library:
+    type, dtype (one of `dtypes`), exact shape, and a memory layout the C
+    side can address (1-D contiguous; 2-D with a contiguous last axis).
+    Devices are checked afterwards by _same_device, so that a call with host
+    tensors of the wrong dtype or shape names that mistake first."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dim() == 1 and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() == 2 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have a contiguous last axis")
+    return t
+
+
+def _rows(x, name, dtypes):
+    """The [T, D] activation that fixes a call's shape; returns (T, D)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D torch.Tensor [T, D]")
+    _arg(x, name, dtypes, x.shape)
+    return tuple(x.shape)
+
+
+def _workspace(ws, name="workspace"):
+    """A caller's dgamma workspace: fp32, contiguous; returns its bytes."""
+    if ws is None:
+        return 0
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.float32 or not ws.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous torch.float32 tensor")
+    return ws.numel() * ws.element_size()
+
+
+def _same_device(*named):
+    """Every given tensor must be a CUDA tensor on the first one's device."""
+    ref = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA tensor, got {t.device}")
+        if ref is None:
+            ref = t.device
+        elif t.device != ref:
+            raise ValueError(f"{name} is on {t.device}, the call's other tensors on {ref}")
 
 
 # ---- entry points ----------------------------------------------------------------
+# Each entry point checks every tensor argument (dtype, shape, layout,
+# device) before it calls the library, so a malformed call raises here and
+# never hands the kernels a pointer they would read or write out of bounds.
+
+BF16, F32 = torch.bfloat16, torch.float32
+ACT_DTYPES = (torch.bfloat16, torch.float16)
+WEIGHT_DTYPES = (torch.bfloat16, torch.float16, torch.float32)
+
+
+def _new(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
 
 def rmsnorm_fwd(x, gamma, zero_centered_gamma=False, eps=1e-6, *, y=None, rstd=None,
                 want_rstd=True, stream=None):
     """y = bf16((x * r) * w_eff); returns (y, rstd or None)."""
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(gamma, torch.float32, "gamma")
-    T, D = x.shape
-    y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device) if y is None else y
+    T, D = _rows(x, "x", BF16)
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(y, "y", BF16, (T, D), required=False)
+    _arg(rstd, "rstd", F32, (T,), required=False)
+    _same_device(("x", x), ("gamma", gamma), ("y", y), ("rstd", rstd))
+    y = _new((T, D), BF16, x) if y is None else y
     if rstd is None and want_rstd:
-        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+        rstd = _new(T, F32, x)
     _check("rmsnorm_fwd", load().rmsnorm_fwd(
         _ptr(x), _ld(x), _ptr(gamma), int(zero_centered_gamma), eps, T, D, _ptr(y), _ld(y),
         _ptr(rstd), _stream(x, stream)))
@@ -181,28 +252,41 @@ def rmsnorm_fwd(x, gamma, zero_centered_gamma=False, eps=1e-6, *, y=None, rstd=N
 def rmsnorm_residual_fwd(x, gamma, zero_centered_gamma=False, eps=1e-6, *, y=None,
                          residual_out=None, rstd=None, want_rstd=True, stream=None):
     """(y, residual_out, rstd): the forward plus a byte copy of x."""
-    _dtype(x, torch.bfloat16, "x")
-    T, D = x.shape
-    y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device) if y is None else y
+    T, D = _rows(x, "x", BF16)
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(y, "y", BF16, (T, D), required=False)
+    _arg(residual_out, "residual_out", BF16, (T, D), required=False)
+    _arg(rstd, "rstd", F32, (T,), required=False)
+    _same_device(("x", x), ("gamma", gamma), ("y", y), ("residual_out", residual_out),
+                 ("rstd", rstd))
+    y = _new((T, D), BF16, x) if y is None else y
     if residual_out is None:
-        residual_out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        residual_out = _new((T, D), BF16, x)
     if rstd is None and want_rstd:
-        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+        rstd = _new(T, F32, x)
     _check("rmsnorm_residual_fwd", load().rmsnorm_residual_fwd(
         _ptr(x), _ld(x), _ptr(gamma), int(zero_centered_gamma), eps, T, D, _ptr(y), _ld(y),
         _ptr(residual_out), _ld(residual_out), _ptr(rstd), _stream(x, stream)))
     return y, residual_out, rstd
 
 
+def _gated_args(x, z, gamma, out, rstd):
+    T, D = _rows(x, "x", BF16)
+    _arg(z, "z", BF16, (T, D))
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(out, "out", BF16, (T, D), required=False)
+    _arg(rstd, "rstd", F32, (T,), required=False)
+    _same_device(("x", x), ("z", z), ("gamma", gamma), ("out", out), ("rstd", rstd))
+    return T, D
+
+
 def rmsnorm_gated_fwd(x, z, gamma, zero_centered_gamma=False, eps=1e-6, *, out=None, rstd=None,
                       want_rstd=False, stream=None):
     """(out, rstd or None): out = bf16(((x * r) * w_eff) * silu(z))."""
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(z, torch.bfloat16, "z")
-    T, D = x.shape
-    out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device) if out is None else out
+    T, D = _gated_args(x, z, gamma, out, rstd)
+    out = _new((T, D), BF16, x) if out is None else out
     if rstd is None and want_rstd:
-        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+        rstd = _new(T, F32, x)
     _check("rmsnorm_gated_fwd", load().rmsnorm_gated_fwd(
         _ptr(x), _ld(x), _ptr(z), _ld(z), _ptr(gamma), int(zero_centered_gamma), eps, T, D,
         _ptr(out), _ld(out), _ptr(rstd), _stream(x, stream)))
@@ -214,12 +298,10 @@ def rmsnorm_gated_fwd_ex(x, z, gamma, zero_centered_gamma=False, eps=1e-6, *,
                          rstd=None, want_rstd=False, stream=None):
     """(out, rstd or None): the gated forward with a choice of activation
     (RMSN_GATE_*) and rounding convention (RMSN_GATED_ROUND_*)."""
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(z, torch.bfloat16, "z")
-    T, D = x.shape
-    out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device) if out is None else out
+    T, D = _gated_args(x, z, gamma, out, rstd)
+    out = _new((T, D), BF16, x) if out is None else out
     if rstd is None and want_rstd:
-        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+        rstd = _new(T, F32, x)
     _check("rmsnorm_gated_fwd_ex", load().rmsnorm_gated_fwd_ex(
         _ptr(x), _ld(x), _ptr(z), _ld(z), _ptr(gamma), int(zero_centered_gamma), eps, T, D,
         int(activation), int(rounding), _ptr(out), _ld(out), _ptr(rstd), _stream(x, stream)))
@@ -231,21 +313,34 @@ def workspace_for(T, D, device):
     return torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=device), n
 
 
+def _dgamma_workspace(dgamma, workspace, T, D, like):
+    """(workspace, bytes) for a call that writes dgamma (allocated when the
+    caller gives none), or (None, 0) without dgamma."""
+    if dgamma is None:
+        return None, 0
+    if workspace is None:
+        workspace, _ = workspace_for(T, D, like.device)
+    return workspace, _workspace(workspace)
+
+
 def rmsnorm_bwd(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=None, dx=None,
                 dgamma=None, want_dx=True, want_dgamma=True, workspace=None, stream=None):
     """(dx or None, dgamma or None) from the saved rstd."""
-    _dtype(g, torch.bfloat16, "g")
-    _dtype(x, torch.bfloat16, "x")
-    T, D = x.shape
+    T, D = _rows(x, "x", BF16)
+    _arg(g, "g", BF16, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(g_residual, "g_residual", BF16, (T, D), required=False)
+    _arg(dx, "dx", BF16, (T, D), required=False)
+    _arg(dgamma, "dgamma", F32, (D,), required=False)
+    _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("rstd", rstd), ("gamma", gamma), ("g_residual", g_residual),
+                 ("dx", dx), ("dgamma", dgamma), ("workspace", workspace))
     if dx is None and want_dx:
-        dx = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        dx = _new((T, D), BF16, x)
     if dgamma is None and want_dgamma:
-        dgamma = torch.empty(D, dtype=torch.float32, device=x.device)
-    ws, nbytes = (None, 0)
-    if dgamma is not None:
-        if workspace is None:
-            workspace, _ = workspace_for(T, D, x.device)
-        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+        dgamma = _new(D, F32, x)
+    ws, nbytes = _dgamma_workspace(dgamma, workspace, T, D, x)
     _check("rmsnorm_bwd", load().rmsnorm_bwd(
         _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(rstd), _ptr(gamma), int(zero_centered_gamma),
         T, D, _ptr(g_residual), _ld(g_residual), _ptr(dx), _ld(dx), _ptr(dgamma), _ptr(ws),
@@ -258,8 +353,15 @@ def rmsnorm_bwd_rows(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual
     """Stage 1 of the backward: dx (if given) and the dgamma partials into
     ``workspace`` (if given, fp32 [chunks, D rounded up to a multiple of 8]
     viewed flat)."""
-    T, D = x.shape
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    T, D = _rows(x, "x", BF16)
+    _arg(g, "g", BF16, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(g_residual, "g_residual", BF16, (T, D), required=False)
+    _arg(dx, "dx", BF16, (T, D), required=False)
+    nbytes = _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("rstd", rstd), ("gamma", gamma), ("g_residual", g_residual),
+                 ("dx", dx), ("workspace", workspace))
     _check("rmsnorm_bwd_rows", load().rmsnorm_bwd_rows(
         _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(rstd), _ptr(gamma), int(zero_centered_gamma),
         T, D, _ptr(g_residual), _ld(g_residual), _ptr(dx), _ld(dx), _ptr(workspace), nbytes,
@@ -269,7 +371,9 @@ def rmsnorm_bwd_rows(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual
 
 def rmsnorm_bwd_finish(workspace, T, D, dgamma, stream=None):
     """Stage 2 of the backward: dgamma from the partials."""
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _arg(dgamma, "dgamma", F32, (D,))
+    nbytes = _workspace(workspace)
+    _same_device(("dgamma", dgamma), ("workspace", workspace))
     _check("rmsnorm_bwd_finish", load().rmsnorm_bwd_finish(
         _ptr(workspace), nbytes, T, D, _ptr(dgamma), _stream(dgamma, stream)))
     return dgamma
@@ -280,21 +384,24 @@ def rmsnorm_gated_bwd(g, x, z, rstd, gamma, zero_centered_gamma=False, *,
                       want_dz=True, want_dgamma=True, workspace=None, stream=None):
     """(dx or None, dz or None, dgamma or None): the backward of the gated
     forward (fp32 rounding convention) from the saved rstd."""
-    _dtype(g, torch.bfloat16, "g")
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(z, torch.bfloat16, "z")
-    T, D = x.shape
+    T, D = _rows(x, "x", BF16)
+    _arg(g, "g", BF16, (T, D))
+    _arg(z, "z", BF16, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(dx, "dx", BF16, (T, D), required=False)
+    _arg(dz, "dz", BF16, (T, D), required=False)
+    _arg(dgamma, "dgamma", F32, (D,), required=False)
+    _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("z", z), ("rstd", rstd), ("gamma", gamma), ("dx", dx),
+                 ("dz", dz), ("dgamma", dgamma), ("workspace", workspace))
     if dx is None and want_dx:
-        dx = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        dx = _new((T, D), BF16, x)
     if dz is None and want_dz:
-        dz = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        dz = _new((T, D), BF16, x)
     if dgamma is None and want_dgamma:
-        dgamma = torch.empty(D, dtype=torch.float32, device=x.device)
-    ws, nbytes = (None, 0)
-    if dgamma is not None:
-        if workspace is None:
-            workspace, _ = workspace_for(T, D, x.device)
-        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+        dgamma = _new(D, F32, x)
+    ws, nbytes = _dgamma_workspace(dgamma, workspace, T, D, x)
     _check("rmsnorm_gated_bwd", load().rmsnorm_gated_bwd(
         _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(z), _ld(z), _ptr(rstd), _ptr(gamma),
         int(zero_centered_gamma), T, D, int(activation), _ptr(dx), _ld(dx), _ptr(dz), _ld(dz),
@@ -307,14 +414,19 @@ def rmsnorm_add_fwd(x, residual, gamma, zero_centered_gamma=False, eps=1e-6, *, 
     """(y, residual_out, rstd or None): the norm of h = x + residual (fp32
     sum) and the updated residual bf16(h). ``y=x`` and ``residual_out=residual``
     run in place."""
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(residual, torch.bfloat16, "residual")
-    T, D = x.shape
-    y = torch.empty((T, D), dtype=torch.bfloat16, device=x.device) if y is None else y
+    T, D = _rows(x, "x", BF16)
+    _arg(residual, "residual", BF16, (T, D))
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(y, "y", BF16, (T, D), required=False)
+    _arg(residual_out, "residual_out", BF16, (T, D), required=False)
+    _arg(rstd, "rstd", F32, (T,), required=False)
+    _same_device(("x", x), ("residual", residual), ("gamma", gamma), ("y", y),
+                 ("residual_out", residual_out), ("rstd", rstd))
+    y = _new((T, D), BF16, x) if y is None else y
     if residual_out is None:
-        residual_out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        residual_out = _new((T, D), BF16, x)
     if rstd is None and want_rstd:
-        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+        rstd = _new(T, F32, x)
     _check("rmsnorm_add_fwd", load().rmsnorm_add_fwd(
         _ptr(x), _ld(x), _ptr(residual), _ld(residual), _ptr(gamma), int(zero_centered_gamma),
         eps, T, D, _ptr(y), _ld(y), _ptr(residual_out), _ld(residual_out), _ptr(rstd),
@@ -322,23 +434,32 @@ def rmsnorm_add_fwd(x, residual, gamma, zero_centered_gamma=False, eps=1e-6, *, 
     return y, residual_out, rstd
 
 
+def _add_bwd_args(g, x, residual, rstd, gamma, g_residual_out, dh):
+    T, D = _rows(x, "x", BF16)
+    _arg(g, "g", BF16, (T, D))
+    _arg(residual, "residual", BF16, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(g_residual_out, "g_residual_out", BF16, (T, D), required=False)
+    _arg(dh, "dh", BF16, (T, D), required=False)
+    return T, D
+
+
 def rmsnorm_add_bwd(g, x, residual, rstd, gamma, zero_centered_gamma=False, *,
                     g_residual_out=None, dh=None, dgamma=None, want_dh=True, want_dgamma=True,
                     workspace=None, stream=None):
     """(dh or None, dgamma or None): dh is the gradient of x and of residual."""
-    _dtype(g, torch.bfloat16, "g")
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(residual, torch.bfloat16, "residual")
-    T, D = x.shape
+    T, D = _add_bwd_args(g, x, residual, rstd, gamma, g_residual_out, dh)
+    _arg(dgamma, "dgamma", F32, (D,), required=False)
+    _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("residual", residual), ("rstd", rstd), ("gamma", gamma),
+                 ("g_residual_out", g_residual_out), ("dh", dh), ("dgamma", dgamma),
+                 ("workspace", workspace))
     if dh is None and want_dh:
-        dh = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+        dh = _new((T, D), BF16, x)
     if dgamma is None and want_dgamma:
-        dgamma = torch.empty(D, dtype=torch.float32, device=x.device)
-    ws, nbytes = (None, 0)
-    if dgamma is not None:
-        if workspace is None:
-            workspace, _ = workspace_for(T, D, x.device)
-        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+        dgamma = _new(D, F32, x)
+    ws, nbytes = _dgamma_workspace(dgamma, workspace, T, D, x)
     _check("rmsnorm_add_bwd", load().rmsnorm_add_bwd(
         _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(residual), _ld(residual), _ptr(rstd), _ptr(gamma),
         int(zero_centered_gamma), T, D, _ptr(g_residual_out), _ld(g_residual_out), _ptr(dh),
@@ -350,8 +471,10 @@ def rmsnorm_add_bwd_rows(g, x, residual, rstd, gamma, zero_centered_gamma=False,
                          g_residual_out=None, dh=None, workspace=None, stream=None):
     """Stage 1 of the fused add backward: dh (if given) and the dgamma
     partials into ``workspace`` (if given); rmsnorm_bwd_finish completes it."""
-    T, D = x.shape
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    T, D = _add_bwd_args(g, x, residual, rstd, gamma, g_residual_out, dh)
+    nbytes = _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("residual", residual), ("rstd", rstd), ("gamma", gamma),
+                 ("g_residual_out", g_residual_out), ("dh", dh), ("workspace", workspace))
     _check("rmsnorm_add_bwd_rows", load().rmsnorm_add_bwd_rows(
         _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(residual), _ld(residual), _ptr(rstd), _ptr(gamma),
         int(zero_centered_gamma), T, D, _ptr(g_residual_out), _ld(g_residual_out), _ptr(dh),
@@ -359,26 +482,21 @@ def rmsnorm_add_bwd_rows(g, x, residual, rstd, gamma, zero_centered_gamma=False,
     return dh, workspace
 
 
-def _dt_of(t, name, allowed):
-    dt = _DTYPES.get(t.dtype)
-    if dt is None or dt not in allowed:
-        raise TypeError(f"{name}: unsupported dtype {t.dtype}")
-    return dt
-
-
 def rmsnorm_fwd_dt(x, gamma, zero_centered_gamma=False, eps=1e-6, *, y=None, rstd=None,
                    want_rstd=True, stream=None):
     """rmsnorm_fwd for bf16 or fp16 x (y of the same type) and fp32, bf16 or
     fp16 gamma; returns (y, rstd or None)."""
-    adt = _dt_of(x, "x", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16))
-    wdt = _dt_of(gamma, "gamma", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16, RMSN_DTYPE_F32))
-    T, D = x.shape
-    y = torch.empty((T, D), dtype=x.dtype, device=x.device) if y is None else y
+    T, D = _rows(x, "x", ACT_DTYPES)
+    _arg(gamma, "gamma", WEIGHT_DTYPES, (D,))
+    _arg(y, "y", x.dtype, (T, D), required=False)
+    _arg(rstd, "rstd", F32, (T,), required=False)
+    _same_device(("x", x), ("gamma", gamma), ("y", y), ("rstd", rstd))
+    y = _new((T, D), x.dtype, x) if y is None else y
     if rstd is None and want_rstd:
-        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+        rstd = _new(T, F32, x)
     _check("rmsnorm_fwd_dt", load().rmsnorm_fwd_dt(
-        adt, wdt, _ptr(x), _ld(x), _ptr(gamma), int(zero_centered_gamma), eps, T, D, _ptr(y),
-        _ld(y), _ptr(rstd), _stream(x, stream)))
+        _DTYPES[x.dtype], _DTYPES[gamma.dtype], _ptr(x), _ld(x), _ptr(gamma),
+        int(zero_centered_gamma), eps, T, D, _ptr(y), _ld(y), _ptr(rstd), _stream(x, stream)))
     return y, rstd
 
 
@@ -386,37 +504,39 @@ def rmsnorm_bwd_dt(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=N
                    dgamma=None, want_dx=True, want_dgamma=True, workspace=None, stream=None):
     """rmsnorm_bwd for bf16 or fp16 activations and fp32, bf16 or fp16
     gamma; returns (dx or None, dgamma fp32 or None)."""
-    adt = _dt_of(x, "x", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16))
-    wdt = _dt_of(gamma, "gamma", (RMSN_DTYPE_BF16, RMSN_DTYPE_F16, RMSN_DTYPE_F32))
-    if g.dtype != x.dtype:
-        raise TypeError("g and x must have the same dtype")
-    T, D = x.shape
+    T, D = _rows(x, "x", ACT_DTYPES)
+    _arg(g, "g", x.dtype, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", WEIGHT_DTYPES, (D,))
+    _arg(g_residual, "g_residual", x.dtype, (T, D), required=False)
+    _arg(dx, "dx", x.dtype, (T, D), required=False)
+    _arg(dgamma, "dgamma", F32, (D,), required=False)
+    _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("rstd", rstd), ("gamma", gamma), ("g_residual", g_residual),
+                 ("dx", dx), ("dgamma", dgamma), ("workspace", workspace))
     if dx is None and want_dx:
-        dx = torch.empty((T, D), dtype=x.dtype, device=x.device)
+        dx = _new((T, D), x.dtype, x)
     if dgamma is None and want_dgamma:
-        dgamma = torch.empty(D, dtype=torch.float32, device=x.device)
-    ws, nbytes = (None, 0)
-    if dgamma is not None:
-        if workspace is None:
-            workspace, _ = workspace_for(T, D, x.device)
-        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+        dgamma = _new(D, F32, x)
+    ws, nbytes = _dgamma_workspace(dgamma, workspace, T, D, x)
     _check("rmsnorm_bwd_dt", load().rmsnorm_bwd_dt(
-        adt, wdt, _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(rstd), _ptr(gamma),
-        int(zero_centered_gamma), T, D, _ptr(g_residual), _ld(g_residual), _ptr(dx), _ld(dx),
-        _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
+        _DTYPES[x.dtype], _DTYPES[gamma.dtype], _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(rstd),
+        _ptr(gamma), int(zero_centered_gamma), T, D, _ptr(g_residual), _ld(g_residual),
+        _ptr(dx), _ld(dx), _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
     return dx, dgamma
 
 
 def bigemm_bf16_xwt(x, w, *, y=None, stream=None):
     """Y = X @ W.T for bf16 X [M, K] and W [N, K] (K a multiple of 32), each
     row of Y independent of the batch around it."""
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(w, torch.bfloat16, "w")
-    M, K = x.shape
+    M, K = _rows(x, "x", BF16)
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise ValueError("w must be a 2-D torch.Tensor [N, K]")
     N = w.shape[0]
-    if w.shape[1] != K:
-        raise ValueError("x and w must have the same K")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _arg(w, "w", BF16, (N, K))
+    _arg(y, "y", BF16, (M, N), required=False)
+    _same_device(("x", x), ("w", w), ("y", y))
+    y = _new((M, N), BF16, x) if y is None else y
     _check("bigemm_bf16_xwt", load().bigemm_bf16_xwt(
         _ptr(x), _ld(x), _ptr(w), _ld(w), M, N, K, _ptr(y), _ld(y), _stream(x, stream)))
     return y

@@ -28,19 +28,32 @@ HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "fwd_add.hip", "fwd_f16.hip", "bwd.hi
 CXX_SOURCES = ["api.cpp"]
 
 
-def build(verbose: bool = False) -> Path:
+def _stale(src: Path, obj: Path) -> bool:
+    """An object is stale when it is older than its source or any header it
+    may include (the kernels' headers; the public header for the C++ side)."""
+    if not obj.exists():
+        return True
+    headers = [*CSRC.glob("*.hpp"), *(INCLUDE.glob("*.h") if src.suffix == ".cpp" else [])]
+    return obj.stat().st_mtime < max(f.stat().st_mtime for f in [src, *headers])
+
+
+def build(verbose: bool = False, incremental: bool = False) -> Path:
+    """Compiles every source (or, with `incremental`, only those whose object
+    is older than the source or a header) and links the library."""
     BUILD.mkdir(exist_ok=True)
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
     jobs, objs = [], []
     for src in HIP_SOURCES:
         obj = BUILD / (src + ".o")
         objs.append(obj)
-        jobs.append([HIPCC, *HIP_FLAGS, *inc, "-c", str(CSRC / src), "-o", str(obj)])
+        if not incremental or _stale(CSRC / src, obj):
+            jobs.append([HIPCC, *HIP_FLAGS, *inc, "-c", str(CSRC / src), "-o", str(obj)])
     for src in CXX_SOURCES:
         obj = BUILD / (src + ".o")
         objs.append(obj)
-        jobs.append(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", *inc, "-c",
-                     str(CSRC / src), "-o", str(obj)])
+        if not incremental or _stale(CSRC / src, obj):
+            jobs.append(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", *inc, "-c",
+                         str(CSRC / src), "-o", str(obj)])
     procs = [subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
              for cmd in jobs]
     failed = []
@@ -62,4 +75,5 @@ def build(verbose: bool = False) -> Path:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

@@ -308,6 +308,11 @@ rmsn_status rmsnorm_bwd_partials_layout(int64_t T, int64_t D, int64_t* block_row
   return RMSN_OK;
 }
 
+int rmsnorm_dgamma_chunk_rows(int64_t D) {
+  if (check_D(D) != RMSN_OK) return 0;
+  return static_cast<int>(rmsn::bwd_rows_per_step(D));
+}
+
 rmsn_status rmsnorm_bwd_rows(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
                              const float* rstd, const float* gamma, int zero_centered_gamma,
                              int64_t T, int64_t D, const uint16_t* g_residual, int64_t ld_gres,
@@ -484,6 +489,8 @@ rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w, 
   constexpr int64_t kMaxGemmLd = int64_t{1} << 21;  // keeps 256-row byte counts below 2^30
   if (ld_x < K || ld_w < K || ld_y < N || ld_x > kMaxGemmLd || ld_w > kMaxGemmLd)
     return RMSN_ERR_SHAPE;
+  // Y's element offsets (M - 1) * ld_y + N must fit in int64 with room to spare
+  if (M > 0 && ld_y > (int64_t{1} << 62) / M) return RMSN_ERR_SHAPE;
   if (M == 0 || N == 0) return RMSN_OK;
   // the launch grid has one workgroup per tile, at most 2^31 - 1
   if ((M + 31) / 32 > INT32_MAX / ((N + 63) / 64)) return RMSN_ERR_SHAPE;

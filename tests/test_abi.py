@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 10
+    assert irn.rmsnorm_abi_version() == 11
 
 
 def test_status_strings():
@@ -167,6 +167,19 @@ def test_workspace_and_chunking_contract():
     # the chunk grouping is fixed per (T, D): the same plan on every call
     assert irn.rmsnorm_bwd_partials_layout(32768, 4096) == irn.rmsnorm_bwd_partials_layout(32768, 4096)
     assert irn.rmsnorm_bwd_partials_layout(0, 4096)[2] == 0
+
+
+def test_dgamma_chunk_rows_depends_on_D_only():
+    """rmsnorm_dgamma_chunk_rows(D) is the block height R of the partials
+    layout, the same for every T; invalid D gives 0."""
+    for D in (1, 7, 8, 100, 128, 1024, 2048, 4096, 4100, 8192, 8200, 16384, 32767, 32768):
+        R = irn.rmsnorm_dgamma_chunk_rows(D)
+        assert R > 0
+        for T in (1, 17, 1000, 32768, 262144):
+            assert irn.rmsnorm_bwd_partials_layout(T, D)[0] == R
+    assert irn.rmsnorm_dgamma_chunk_rows(4096) == 4   # one row per wave of a 4-wave step
+    for D in (0, -8, 32769, 1 << 40):
+        assert irn.rmsnorm_dgamma_chunk_rows(D) == 0
 
 
 def test_partials_layout_rejections():
@@ -393,6 +406,8 @@ def gemm(**kw):
     (dict(y=A + 1024), irn.RMSN_ERR_ALIASING),
     (dict(y=B), irn.RMSN_ERR_ALIASING),
     (dict(M=1 << 31), irn.RMSN_ERR_SHAPE),   # 2^32 tiles of 32 x 64: more than a grid holds
+    (dict(ld_y=1 << 61), irn.RMSN_ERR_SHAPE),  # (M - 1) * ld_y would overflow int64
+    (dict(ld_y=(1 << 62) // 64 + 1), irn.RMSN_ERR_SHAPE),  # just past 2^62 / M (M = 64)
 ])
 def test_gemm_rejections(kw, code):
     assert gemm(**kw) == code

@@ -273,3 +273,26 @@ def test_rejections_write_nothing(gpu):
     assert e.value.status == irn.RMSN_ERR_EPS
     torch.cuda.synchronize()
     assert torch.all(y.float() == 3.0)
+
+
+def test_binding_rejects_before_launch(gpu):
+    """Malformed tensors on the GPU (bf16 weights where fp32 is required, an
+    rstd shorter than T, a host gamma beside CUDA activations) raise in the
+    binding; nothing is launched and the outputs keep their contents."""
+    D, T = 256, 10
+    x = dev_bf16(synth.normal_bf16(2, 1, T, D))
+    g = dev_bf16(synth.normal_bf16(2, 2, T, D))
+    gamma = torch.ones(D, device="cuda")
+    y = torch.full((T, D), 3.0, dtype=torch.bfloat16, device="cuda")
+    dx = torch.full((T, D), 3.0, dtype=torch.bfloat16, device="cuda")
+    rstd = torch.ones(T, device="cuda")
+    with pytest.raises(TypeError, match="gamma"):
+        irn.rmsnorm_fwd(x, gamma.to(torch.bfloat16), y=y)
+    with pytest.raises(ValueError, match="rstd"):
+        irn.rmsnorm_bwd(g, x, rstd[: T - 1], gamma, dx=dx)
+    with pytest.raises(ValueError, match="CUDA"):
+        irn.rmsnorm_bwd(g, x, rstd, gamma.cpu(), dx=dx)
+    with pytest.raises(ValueError, match="dx"):
+        irn.rmsnorm_bwd(g, x, rstd, gamma, dx=dx[:, : D - 8])
+    torch.cuda.synchronize()
+    assert torch.all(y.float() == 3.0) and torch.all(dx.float() == 3.0)
