@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 11
+#define RMSN_ABI_VERSION 12
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -225,6 +225,31 @@ rmsn_status rmsnorm_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x,
                         const uint16_t* g_residual, int64_t ld_gres,
                         uint16_t* dx, int64_t ld_dx, float* dgamma,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rmsnorm_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. It calls no allocator (no hipMalloc, no hipFree).
+ * The dgamma chunk partials go to a scratch array of
+ * RMSN_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * copy per GPU, from the first call on that GPU until the process ends. Every
+ * (T, D) the library supports fits in it (rmsnorm_bwd_workspace_bytes never
+ * exceeds it); a layout that did not would return RMSN_ERR_WORKSPACE.
+ * All calls on one GPU share that GPU's array and it keeps the last call's
+ * partials: calls on one stream are safe, but calls that may run at the same
+ * time on one GPU (unordered streams) race on it and may return a wrong
+ * dgamma. The rows kernel writes every partial the finish kernel reads, so
+ * nothing needs clearing between calls. With dgamma NULL (dx only) the array
+ * is not used. Arguments, results and errors otherwise as rmsnorm_bwd;
+ * RMSN_ERR_HIP also when the array's address cannot be obtained on the
+ * current device. Two kernels on `stream`.
+ */
+#define RMSN_NOALLOC_SCRATCH_BYTES (32u << 20)
+rmsn_status rmsnorm_bwd_noalloc(const uint16_t* g, int64_t ld_g, const uint16_t* x,
+                                int64_t ld_x, const float* rstd, const float* gamma,
+                                int zero_centered_gamma, int64_t T, int64_t D,
+                                const uint16_t* g_residual, int64_t ld_gres, uint16_t* dx,
+                                int64_t ld_dx, float* dgamma, void* stream);
 
 /*
  * The two stages of rmsnorm_bwd, for callers that schedule them apart.

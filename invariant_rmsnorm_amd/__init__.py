@@ -47,7 +47,7 @@ EXPORTED = (
     "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
     "rmsnorm_gated_bwd", "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_rows",
     "rmsnorm_fwd_dt", "rmsnorm_bwd_dt", "bigemm_bf16_xwt", "bigemm_bf16_tile",
-    "rmsnorm_dgamma_chunk_rows",
+    "rmsnorm_dgamma_chunk_rows", "rmsnorm_bwd_noalloc",
 )
 
 
@@ -92,6 +92,7 @@ def load():
         "bigemm_bf16_xwt": ([vp, i64, vp, i64, i64, i64, i64, vp, i64, vp], i),
         "bigemm_bf16_tile": ([i64, i64, vp, vp], i),
         "rmsnorm_dgamma_chunk_rows": ([i64], i),
+        "rmsnorm_bwd_noalloc": ([vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -345,6 +346,28 @@ def rmsnorm_bwd(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=None
         _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(rstd), _ptr(gamma), int(zero_centered_gamma),
         T, D, _ptr(g_residual), _ld(g_residual), _ptr(dx), _ld(dx), _ptr(dgamma), _ptr(ws),
         nbytes, _stream(x, stream)))
+    return dx, dgamma
+
+
+def rmsnorm_bwd_noalloc(g, x, rstd, gamma, zero_centered_gamma=False, *, dx, dgamma,
+                        g_residual=None, stream=None):
+    """rmsnorm_bwd with the dgamma partials in the library's own device
+    scratch: no workspace and no allocation, here or in the library. The
+    caller passes the outputs dx and dgamma (either may be None, not both);
+    calls that may overlap on one GPU race on the shared scratch."""
+    T, D = _rows(x, "x", BF16)
+    _arg(g, "g", BF16, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", F32, (D,))
+    _arg(g_residual, "g_residual", BF16, (T, D), required=False)
+    _arg(dx, "dx", BF16, (T, D), required=False)
+    _arg(dgamma, "dgamma", F32, (D,), required=False)
+    _same_device(("x", x), ("g", g), ("rstd", rstd), ("gamma", gamma), ("g_residual", g_residual),
+                 ("dx", dx), ("dgamma", dgamma))
+    _check("rmsnorm_bwd_noalloc", load().rmsnorm_bwd_noalloc(
+        _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(rstd), _ptr(gamma), int(zero_centered_gamma),
+        T, D, _ptr(g_residual), _ld(g_residual), _ptr(dx), _ld(dx), _ptr(dgamma),
+        _stream(x, stream)))
     return dx, dgamma
 
 

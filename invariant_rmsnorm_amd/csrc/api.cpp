@@ -13,10 +13,12 @@
 
 #include "geometry.hpp"
 #include "launch.hpp"
+#include "scratch.hpp"
 
 namespace {
 
 using rmsn::kMaxD;
+static_assert(RMSN_NOALLOC_SCRATCH_BYTES == rmsn::kScratchBytes, "scratch size in the header");
 // Row strides up to 2^24 elements keep every per-lane byte offset of a
 // 64-row group below 2^31 (the kernels address rows through 32-bit offsets).
 constexpr int64_t kMaxLd = int64_t{1} << 24;
@@ -360,6 +362,30 @@ rmsn_status rmsnorm_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int6
   }
   if (dgamma == nullptr) return RMSN_OK;
   return finish_dgamma(workspace, T, D, dgamma, stream);
+}
+
+rmsn_status rmsnorm_bwd_noalloc(const uint16_t* g, int64_t ld_g, const uint16_t* x,
+                                int64_t ld_x, const float* rstd, const float* gamma,
+                                int zero_centered_gamma, int64_t T, int64_t D,
+                                const uint16_t* g_residual, int64_t ld_gres, uint16_t* dx,
+                                int64_t ld_dx, float* dgamma, void* stream) {
+  if (dx == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
+  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
+  // every argument but the workspace, as rmsnorm_bwd checks them
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, g_residual, ld_gres, dx, ld_dx, false,
+                     dgamma, nullptr, 0));
+  void* ws = nullptr;
+  if (dgamma != nullptr && T > 0) {
+    if (workspace_bytes(T, D) > rmsn::kScratchBytes) return RMSN_ERR_WORKSPACE;
+    RMSN_TRY(hip_status(rmsn::scratch_ptr(&ws)));
+  }
+  if (T > 0) {
+    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
+                                     g_residual, ld_gres, dx, ld_dx, ws);
+    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
+  }
+  if (dgamma == nullptr) return RMSN_OK;
+  return finish_dgamma(ws, T, D, dgamma, stream);
 }
 
 rmsn_status rmsnorm_gated_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,

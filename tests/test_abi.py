@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 11
+    assert irn.rmsnorm_abi_version() == 12
 
 
 def test_status_strings():
@@ -441,3 +441,48 @@ def test_gemm_tile_rejections():
     v = ctypes.c_int64(0)
     assert lib.bigemm_bf16_tile(-1, 4, ctypes.byref(v), ctypes.byref(v)) == irn.RMSN_ERR_SHAPE
     assert lib.bigemm_bf16_tile(4, 4, None, ctypes.byref(v)) == irn.RMSN_ERR_NULL
+
+
+def noalloc(**kw):
+    a = dict(g=A, ld_g=4096, x=B, ld_x=4096, rstd=RS, gamma=GAM, zc=0, T=1000, D=4096, gres=None,
+             ld_gres=0, dx=C, ld_dx=4096, dgamma=E)
+    a.update(kw)
+    return irn.load().rmsnorm_bwd_noalloc(a["g"], a["ld_g"], a["x"], a["ld_x"], a["rstd"],
+                                          a["gamma"], a["zc"], a["T"], a["D"], a["gres"],
+                                          a["ld_gres"], a["dx"], a["ld_dx"], a["dgamma"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dx=None, dgamma=None), irn.RMSN_ERR_NULL),
+    (dict(g=None), irn.RMSN_ERR_NULL),
+    (dict(rstd=None), irn.RMSN_ERR_NULL),
+    (dict(gamma=None), irn.RMSN_ERR_NULL),
+    (dict(T=-1), irn.RMSN_ERR_SHAPE),
+    (dict(D=32776, ld_g=32776, ld_x=32776, ld_dx=32776), irn.RMSN_ERR_UNSUPPORTED_D),
+    (dict(ld_x=4000), irn.RMSN_ERR_SHAPE),
+    (dict(dgamma=E + 4), irn.RMSN_ERR_MISALIGNED),
+    (dict(x=B + 2), irn.RMSN_ERR_MISALIGNED),
+    (dict(dx=A), irn.RMSN_ERR_ALIASING),
+    (dict(dgamma=RS), irn.RMSN_ERR_ALIASING),
+])
+def test_noalloc_backward_rejections(kw, code):
+    """The same host checks as rmsnorm_bwd, before the scratch is looked up
+    or anything is launched."""
+    assert noalloc(**kw) == code
+
+
+def test_noalloc_scratch_covers_every_layout():
+    """Every supported (T, D) fits the library's scratch, whatever T: the
+    partials layout caps the chunks, so the largest workspace is reached at
+    moderate T and never grows beyond it."""
+    import re as _re
+    text = HEADER.read_text()
+    cap = int(_re.search(r"#define RMSN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+              .expand(r"\1")) << int(_re.search(r"RMSN_NOALLOC_SCRATCH_BYTES \(\d+u << (\d+)\)",
+                                                text).group(1))
+    assert cap == 32 << 20
+    worst = 0
+    for D in list(range(1, 64)) + list(range(64, 32769, 61)) + [2048, 4096, 8192, 16384, 32768]:
+        for T in (1, 1000, 1 << 20, 1 << 40):
+            worst = max(worst, irn.rmsnorm_bwd_workspace_bytes(T, D))
+    assert 0 < worst <= cap
