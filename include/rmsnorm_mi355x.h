@@ -43,7 +43,8 @@
  * alone.
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
- * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD), 1 <= D <= 32768 (RMSN_MAX_D)
+ * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD) with T * ld <= 2^60, 1 <= D <=
+ * 32768 (RMSN_MAX_D)
  * for every entry point except rmsnorm_gated_bwd, which needs D a multiple
  * of 8. When D is a
  * multiple of 8, rows move as 16-byte vectors: every bf16 / fp16 base
@@ -391,7 +392,7 @@ rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g,
  * position and the other rows are.
  * Supported: K a positive multiple of 32; K <= ld_x, ld_w <= 2^21 and
  * ld_x, ld_w multiples of 8 with X and W 16-byte aligned; N <= ld_y <=
- * 2^62 / M, Y 2-byte aligned. Errors: RMSN_ERR_SHAPE (negative sizes,
+ * 2^60 / M, Y 2-byte aligned. Errors: RMSN_ERR_SHAPE (negative sizes,
  * strides out of range, or more than 2^31 - 1 tiles of 32 x 64), RMSN_ERR_UNSUPPORTED_D (K not a positive
  * multiple of 32), RMSN_ERR_NULL, RMSN_ERR_MISALIGNED, RMSN_ERR_ALIASING
  * (Y overlaps X or W), RMSN_ERR_HIP.

@@ -28,13 +28,28 @@ HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "fwd_add.hip", "fwd_f16.hip", "bwd.hi
 CXX_SOURCES = ["api.cpp"]
 
 
+def _includes(src: Path, seen=None) -> set:
+    """The project headers `src` includes, directly or through other headers
+    (quoted includes found in csrc/ or include/)."""
+    seen = set() if seen is None else seen
+    for line in src.read_text().splitlines():
+        line = line.strip()
+        if line.startswith("#include \""):
+            name = line.split('"')[1]
+            for d in (CSRC, INCLUDE):
+                h = d / name
+                if h.exists() and h not in seen:
+                    seen.add(h)
+                    _includes(h, seen)
+    return seen
+
+
 def _stale(src: Path, obj: Path) -> bool:
-    """An object is stale when it is older than its source or any header it
-    may include (the kernels' headers; the public header for the C++ side)."""
+    """An object is stale when it is older than its source or a header the
+    source includes."""
     if not obj.exists():
         return True
-    headers = [*CSRC.glob("*.hpp"), *(INCLUDE.glob("*.h") if src.suffix == ".cpp" else [])]
-    return obj.stat().st_mtime < max(f.stat().st_mtime for f in [src, *headers])
+    return obj.stat().st_mtime < max(f.stat().st_mtime for f in [src, *_includes(src)])
 
 
 def build(verbose: bool = False, incremental: bool = False) -> Path:

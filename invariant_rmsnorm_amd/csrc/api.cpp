@@ -13,6 +13,7 @@
 
 #include "geometry.hpp"
 #include "launch.hpp"
+#include "plan.hpp"
 #include "scratch.hpp"
 
 namespace {
@@ -69,11 +70,14 @@ rmsn_status check_D(int64_t D, bool any_D = true) {
 // the pointer and its alignment. Rows of a multiple of 8 elements move as
 // 16-byte vectors and need a 16-byte-aligned base and a stride of a
 // multiple of 8; other rows move element by element and need 2-byte
-// alignment only. (T*ld is bounded so byte offsets fit.)
+// alignment only. T * ld is bounded by 2^60 elements, so every byte count
+// the checks below form (an operand's extent, T floats of rstd) stays
+// below 2^62.
+constexpr int64_t kMaxElems = int64_t{1} << 60;
 rmsn_status check_mat(const uint16_t* p, int64_t ld, int64_t T, int64_t D, bool required) {
   if (!required && p == nullptr) return RMSN_OK;
   if (ld < D || ld > kMaxLd) return RMSN_ERR_SHAPE;
-  if (T > 0 && ld > (int64_t{1} << 62) / T) return RMSN_ERR_SHAPE;
+  if (T > 0 && ld > kMaxElems / T) return RMSN_ERR_SHAPE;
   if (T == 0) return RMSN_OK;
   if (p == nullptr) return RMSN_ERR_NULL;
   if (D % 8 == 0 ? (!aligned(p, 16) || (ld % 8) != 0) : !aligned(p, 2)) return RMSN_ERR_MISALIGNED;
@@ -515,8 +519,8 @@ rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w, 
   constexpr int64_t kMaxGemmLd = int64_t{1} << 21;  // keeps 256-row byte counts below 2^30
   if (ld_x < K || ld_w < K || ld_y < N || ld_x > kMaxGemmLd || ld_w > kMaxGemmLd)
     return RMSN_ERR_SHAPE;
-  // Y's element offsets (M - 1) * ld_y + N must fit in int64 with room to spare
-  if (M > 0 && ld_y > (int64_t{1} << 62) / M) return RMSN_ERR_SHAPE;
+  // Y's extent (M - 1) * ld_y + N elements stays below 2^60, its bytes below 2^61
+  if (M > 0 && ld_y > kMaxElems / M) return RMSN_ERR_SHAPE;
   if (M == 0 || N == 0) return RMSN_OK;
   // the launch grid has one workgroup per tile, at most 2^31 - 1
   if ((M + 31) / 32 > INT32_MAX / ((N + 63) / 64)) return RMSN_ERR_SHAPE;

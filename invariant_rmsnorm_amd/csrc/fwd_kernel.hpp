@@ -219,6 +219,8 @@ inline int cu_count() {
   return n;
 }
 
+constexpr int64_t kFwdGridScale = 16;
+
 template <int LPR, int VPL, bool MASKED, int GATE, int DT>
 int launch_inst(const FwdArgs& a, void* stream) {
   constexpr int ROWS_BLOCK = rows_per_block(LPR, fwd_unroll(LPR, VPL));
@@ -229,11 +231,15 @@ int launch_inst(const FwdArgs& a, void* stream) {
       b = 1;
     return b;
   }();
-  // Persistent grid: at most as many workgroups as fit on the device, and
-  // every workgroup given the same number of steps (a grid of `cap` over
-  // 1.6 * cap steps would leave half the device idle for the last step).
+  // Grid: at most kFwdGridScale times as many workgroups as fit on the
+  // device at once (the hardware starts the rest as earlier ones finish, so
+  // the last rows are shared by whichever compute units are free instead of
+  // by a fixed set), and every workgroup given the same number of steps.
+  // Measured at D = 4096 with the cache flushed before each launch, against a
+  // persistent grid of one resident set: T = 32768 103.5 -> 97.3 us,
+  // T = 131072 401 -> 365 us, T = 262144 822 -> 774 us.
   const int64_t blocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu;
+  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu * kFwdGridScale;
   const int64_t steps = (blocks + cap - 1) / cap;
   const int grid = static_cast<int>(std::max<int64_t>(1, (blocks + steps - 1) / steps));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);

@@ -131,42 +131,4 @@ inline int64_t bwd_rows_per_step(int64_t D) {
   return rows_per_block(g.lpr, bwd_unroll(g.lpr, g.vpl));
 }
 
-// Row blocks per group of the backward's traversal (0: one contiguous group
-// per chunk). Groups of 4 blocks keep the workgroups on a front of
-// 256 x 4 blocks (at D = 4096, 32 MiB of each input), measured faster at
-// 1-2 GiB per tensor than 1, 16 or one contiguous group per chunk; all are
-// equal at 256 MiB.
-#ifndef RMSN_BWD_GROUP
-#define RMSN_BWD_GROUP 4
-#endif
-
-// dgamma chunking for a batch of T rows. The batch is cut into blocks of
-// R = bwd_rows_per_step(D) rows (block b = rows [b*R, min(T, (b+1)*R))) and
-// the blocks into groups of S consecutive blocks; chunk k of K holds the
-// groups k, k+K, k+2K, ... (dgamma sums over the whole batch, so its
-// grouping may depend on T; the per-row outputs never do.)
-struct BwdPlan {
-  int64_t block_rows;    // R
-  int64_t chunks;        // K <= bwd_target_chunks(D)
-  int64_t group_blocks;  // S
-};
-
-#ifndef RMSN_BWD_BLOCKS_PER_CU
-#define RMSN_BWD_BLOCKS_PER_CU 0  // 0: the kernel's occupancy
-#endif
-inline int64_t bwd_target_chunks(int64_t D) {
-  return kCus * (RMSN_BWD_BLOCKS_PER_CU > 0 ? RMSN_BWD_BLOCKS_PER_CU
-                                            : bwd_waves_per_eu(bwd_geom(D).vpl, D % 8 != 0));
-}
-
-inline BwdPlan bwd_plan(int64_t T, int64_t D) {
-  const int64_t R = bwd_rows_per_step(D);
-  const int64_t target = bwd_target_chunks(D);
-  if (T <= 0) return {R, 0, 1};
-  const int64_t blocks = (T + R - 1) / R;
-  const int64_t S = RMSN_BWD_GROUP > 0 ? RMSN_BWD_GROUP : (blocks + target - 1) / target;
-  const int64_t groups = (blocks + S - 1) / S;
-  return {R, groups < target ? groups : target, S};
-}
-
 }  // namespace rmsn

@@ -407,7 +407,7 @@ def gemm(**kw):
     (dict(y=B), irn.RMSN_ERR_ALIASING),
     (dict(M=1 << 31), irn.RMSN_ERR_SHAPE),   # 2^32 tiles of 32 x 64: more than a grid holds
     (dict(ld_y=1 << 61), irn.RMSN_ERR_SHAPE),  # (M - 1) * ld_y would overflow int64
-    (dict(ld_y=(1 << 62) // 64 + 1), irn.RMSN_ERR_SHAPE),  # just past 2^62 / M (M = 64)
+    (dict(ld_y=(1 << 60) // 64 + 1), irn.RMSN_ERR_SHAPE),  # just past 2^60 / M (M = 64)
 ])
 def test_gemm_rejections(kw, code):
     assert gemm(**kw) == code

@@ -15,7 +15,9 @@ import invariant_rmsnorm_amd as irn
 import oracle
 import synth
 from gpu_util import dev_bf16, dev_f32, host_bits, run_fwd_bwd
-from numerics import bf16_to_f64, dgamma_rel_err, f32_to_bf16_torch, max_ulp, rstd_rel_err
+from numerics import (bf16_to_f32, bf16_to_f64, dgamma_check, dgamma_rel_err,
+                      dgamma_term_stats, dgamma_terms_f32, f32_to_bf16_torch, max_ulp,
+                      rstd_rel_err)
 from synth import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -134,6 +136,17 @@ def _edge_rows(D, rng):
     return np.stack(rows)
 
 
+def _edge_dgamma_ok(gpu_dg, p, rstd_ref, label):
+    """dgamma of an edge batch under the shared rule (numerics.dgamma_check);
+    the terms are fp32((g*x)*r) per row, rounded as both sides round them."""
+    ref = oracle.dgamma(p.g, p.x, rstd_ref)
+    mag, nonfinite = dgamma_term_stats(
+        dgamma_terms_f32(bf16_to_f32(p.g), bf16_to_f32(p.x), rstd_ref))
+    ok, report = dgamma_check(gpu_dg, ref, mag, nonfinite, p.T + 512)
+    print(f"edge dgamma {label}: {report}", flush=True)
+    assert ok, (label, report)
+
+
 @pytest.mark.parametrize("D", [128, 4096])
 @pytest.mark.parametrize("eps", [1e-6, 0.0])
 def test_edge_values(gpu, D, eps):
@@ -151,6 +164,39 @@ def test_edge_values(gpu, D, eps):
     nan_g = np.isnan(bf16_to_f64(got["dx"]))
     nan_r = np.isnan(bf16_to_f64(ref["dx"]))
     assert np.array_equal(nan_g, nan_r)
+    # dgamma over all edge rows (the NaN row makes every column NaN; with
+    # eps = 0 the zero rows do too), then over the rows without a NaN input
+    _edge_dgamma_ok(got["dgamma"], p, ref["rstd"], (D, eps, "all rows"))
+    finite = np.array([not np.isnan(bf16_to_f64(r)).any() for r in x])
+    q = wl.Problem("edge-finite", int(finite.sum()), D, eps, False, gamma, x[finite], g[finite])
+    _edge_dgamma_ok(run_fwd_bwd(q)["dgamma"], q, oracle_all(q)["rstd"], (D, eps, "finite rows"))
+
+
+@pytest.mark.parametrize("D", [128, 4096])
+def test_dgamma_partial_overflow(gpu, D):
+    """dgamma terms of +-2^126 that cancel: 64 rows of x = 1 carry g = +2^126
+    and 64 more g = -2^126 in their first 2 columns (N(0,1) elsewhere), among
+    N(0,1) rows. The oracle's double sum of those columns is small and finite;
+    an fp32 running sum passes FLT_MAX after four such terms, so the GPU's
+    chunk partials may overflow there. Checked under the shared overflow
+    rule; y, rstd and dx (no sums across rows) against the oracle as usual."""
+    rng = np.random.default_rng(9450 + D)
+    T = 600
+    xf = rng.standard_normal((T, D)).astype(np.float32)
+    gf = rng.standard_normal((T, D)).astype(np.float32)
+    rows = rng.permutation(T)[:128]
+    xf[rows] = 1.0
+    gf[rows[:64], :2] = 2.0 ** 126
+    gf[rows[64:], :2] = -(2.0 ** 126)
+    x, g = f32_to_bf16_torch(xf), f32_to_bf16_torch(gf)
+    gamma = wl.gamma_for(9450, D, False)
+    p = wl.Problem("huge-g", T, D, 1e-6, False, gamma, x, g)
+    got, ref = run_fwd_bwd(p), oracle_all(p)
+    assert max_ulp(got["y"], ref["y"]) <= 1
+    assert rstd_rel_err(got["rstd"], ref["rstd"]) <= 1e-6
+    assert max_ulp(got["dx"], ref["dx"]) <= 1
+    assert np.isfinite(ref["dgamma"][:2]).all()   # the double sums stay finite
+    _edge_dgamma_ok(got["dgamma"], p, ref["rstd"], (D, "huge g"))
 
 
 def _exact_problem(T, D, seed, zc):
