@@ -219,7 +219,22 @@ inline int cu_count() {
   return n;
 }
 
-constexpr int64_t kFwdGridScale = 16;
+// Workgroups per launch, as a multiple of what fits on the device at once
+// (1: a persistent grid). Every workgroup loads the row's weights before its
+// first step, so the multiple shrinks as the weights grow. Measured on the
+// plain forward with the cache flushed before each launch (us, x of 256 MiB;
+// multiples 1 / 2 / 4 / 8 / 16):
+//   D = 128    101.8 101.0  98.3  94.8  93.1
+//   D = 4096   104.4 103.8 100.3  98.2  98.7  (T = 262144: 826 810 800 781 771)
+//   D = 5120   106.5 110.5 103.8 102.1 100.3
+//   D = 8192   114.6 110.4 110.2 118.7 119.6
+//   D = 16384  109.9 106.2 105.7 111.3 111.5
+//   D = 32768  114.1 108.7 109.1 111.0 111.2
+//   D = 4100   222.6 232.1 246.7 275.5 331.4  (element-wise rows: a weight
+//                                              load per element)
+constexpr int64_t fwd_grid_scale(int lpr, int vpl, bool elem) {
+  return elem ? 1 : lpr * vpl >= 1024 ? 2 : 16;
+}
 
 template <int LPR, int VPL, bool MASKED, int GATE, int DT>
 int launch_inst(const FwdArgs& a, void* stream) {
@@ -231,15 +246,12 @@ int launch_inst(const FwdArgs& a, void* stream) {
       b = 1;
     return b;
   }();
-  // Grid: at most kFwdGridScale times as many workgroups as fit on the
+  // Grid: at most fwd_grid_scale times as many workgroups as fit on the
   // device at once (the hardware starts the rest as earlier ones finish, so
   // the last rows are shared by whichever compute units are free instead of
   // by a fixed set), and every workgroup given the same number of steps.
-  // Measured at D = 4096 with the cache flushed before each launch, against a
-  // persistent grid of one resident set: T = 32768 103.5 -> 97.3 us,
-  // T = 131072 401 -> 365 us, T = 262144 822 -> 774 us.
   const int64_t blocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu * kFwdGridScale;
+  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu * fwd_grid_scale(LPR, VPL, elem_dt(DT));
   const int64_t steps = (blocks + cap - 1) / cap;
   const int grid = static_cast<int>(std::max<int64_t>(1, (blocks + steps - 1) / steps));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
