@@ -43,16 +43,16 @@
  * alone.
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
- * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD) with T * ld <= 2^60, 1 <= D <=
- * 32768 (RMSN_MAX_D)
- * for every entry point except rmsnorm_gated_bwd, which needs D a multiple
- * of 8. When D is a
- * multiple of 8, rows move as 16-byte vectors: every bf16 / fp16 base
- * pointer and ld * 2 bytes must be multiples of 16 bytes. Other D move
- * element by element through the same kernels, reduction trees and
- * arithmetic: bases need 2-byte alignment only, and any ld >= D will do.
- * gamma, dgamma and the workspace must be 16-byte aligned; rstd 4-byte
- * aligned.
+ * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD) with T * ld <= 2^60, and
+ * 1 <= D <= 32768 (RMSN_MAX_D) for every entry point except
+ * rmsnorm_gated_bwd, which needs D a multiple of 8. Each lane of a row owns
+ * groups of 8 consecutive elements; every reduction tree is a function of
+ * ceil(D/8) alone. When D is a multiple of 8, rows move as aligned 16-byte
+ * vectors: every bf16 / fp16 base pointer and ld * 2 bytes must be multiples
+ * of 16 bytes. Other D need 2-byte-aligned bases only and take any
+ * ld >= D: full groups move as unaligned 16-byte accesses and the partial
+ * last group of a row element by element. gamma, dgamma and the workspace
+ * must be 16-byte aligned; rstd 4-byte aligned.
  *
  * Ownership and streams. Every pointer is device memory owned by the caller.
  * The library never allocates, never synchronises, never changes the

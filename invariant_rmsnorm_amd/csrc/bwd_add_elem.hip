@@ -1,5 +1,5 @@
 // Fused add-norm backward rows launchers for rows whose length D is not a
-// multiple of 8: the kernel of bwd_kernel.hpp with element-wise row storage
+// multiple of 8: the kernel of bwd_kernel.hpp with rows of any alignment
 // (bf16).
 #include "bwd_kernel.hpp"
 

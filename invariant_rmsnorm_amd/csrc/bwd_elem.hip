@@ -1,6 +1,6 @@
 // Backward rows launchers for rows whose length D is not a multiple of 8,
 // bf16 activations (plain and residual-gradient forms): the kernel of
-// bwd_kernel.hpp with element-wise row storage (fp16 in bwd_elem_f16.hip).
+// bwd_kernel.hpp with rows of any alignment (fp16 in bwd_elem_f16.hip).
 #include "bwd_kernel.hpp"
 
 namespace rmsn {

@@ -54,9 +54,9 @@ enum : int {
 // reused by the second. Beyond that the registers would spill, so the
 // weights move to LDS and the second pass unpacks the raw vectors again.
 // The gated form holds a third input row (z), so it goes lean from 11.
-constexpr bool bwd_lean(int vpl, bool three_inputs, bool elem = false) {
-  return vpl >= (elem ? 3 : three_inputs ? 11 : 13);
-}
+// Rows of any length hold their groups as 16-byte vectors too and take the
+// same plan.
+constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_inputs ? 11 : 13); }
 // Load the next step while computing this one (two register sets that swap
 // roles), for rows over 4 waves whose loaded step fits the register file
 // twice: input streams x vectors per lane <= 18 with the whole register file
@@ -64,18 +64,9 @@ constexpr bool bwd_lean(int vpl, bool three_inputs, bool elem = false) {
 // Without it the four waves of a row, held together by the exchange
 // barrier, load and compute in lock step and leave the memory pipe idle
 // while they compute.
-// Element-wise row storage holds each loaded element in a register of its
-// own until the group is packed, twice the registers of a 16-byte vector:
-// it keeps no values for pass 2 (lean from 3 groups per lane) and takes the
-// second register set only when RMSN_BWD_ELEM_PREFETCH is set (measured no
-// faster at D = 4100).
-#ifndef RMSN_BWD_ELEM_PREFETCH
-#define RMSN_BWD_ELEM_PREFETCH 0
-#endif
-constexpr bool bwd_prefetch(int lpr, int vpl, int mode, bool elem = false) {
+constexpr bool bwd_prefetch(int lpr, int vpl, int mode) {
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
-  const int budget = bwd_waves_per_eu(vpl, elem) == 1 ? 18 : 8;
-  if (elem) return RMSN_BWD_ELEM_PREFETCH && lpr > 64 && 2 * streams * vpl <= budget;
+  const int budget = bwd_waves_per_eu(vpl) == 1 ? 18 : 8;
   return lpr > 64 && streams * vpl <= budget;
 }
 
@@ -85,8 +76,7 @@ constexpr bool bwd_prefetch(int lpr, int vpl, int mode, bool elem = false) {
 // merge (which reuse the same space).
 inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
   const RowGeom g = bwd_geom(D);
-  const size_t w = bwd_lean(g.vpl, three_inputs, D % 8 != 0)
-                       ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
+  const size_t w = bwd_lean(g.vpl, three_inputs) ? static_cast<size_t>(g.vpl) * g.lpr * 8 : 0;
   // merge space: 2 rows of Dp = part_stride(D) floats with one wave per
   // row, 1 with two, none with four
   const int wpr = waves_per_row(g.lpr);
@@ -97,7 +87,7 @@ inline size_t bwd_rows_lds_floats(int D, bool want_part, bool three_inputs) {
 
 template <int LPR, int VPL, bool MASKED, int MODE, int DT>
 __global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL, elem_dt(DT)))))
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu(VPL))))
 void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr bool ADD = MODE == kBwdAdd || MODE == kBwdAddGres;
   constexpr bool GRES = MODE == kBwdGres || MODE == kBwdAddGres;
@@ -109,8 +99,8 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr int ROWS_WAVE = U * RPW;
   constexpr int ROWS_BLOCK = rows_per_block(LPR, U);
   static_assert(WPR == 1 || (U == 1 && VPL >= kBwdMinVplMulti), "multi-wave rows: one row per step");
-  constexpr bool LEAN = bwd_lean(VPL, GATED || ADD, elem_dt(DT));
-  constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE, elem_dt(DT));
+  constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
+  constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE);
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
@@ -129,34 +119,28 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 
   // Weights w_eff = gamma (+1 in fp32 when zero-centred).
   constexpr bool ELEM = elem_dt(DT);
-  constexpr bool MSK = MASKED && !ELEM;  // lanes without a last group (16-byte rows)
+  constexpr bool MSK = MASKED;  // some lanes lack their last group
   float wreg[LEAN ? 1 : VPL][8];
   float4* const wl4 = reinterpret_cast<float4*>(lds);
   if constexpr (LEAN) {
-    // float4 h (0/1) of group c = v*LPR + l goes to slot (2v + h)*LPR + l;
-    // with element-wise storage every lane's VPL groups are staged (group
-    // v of lane l: elements (8v + e)*LPR + l, zero past D).
-    for (int c = threadIdx.x; c < (ELEM ? VPL * LPR : nv); c += kBlock) {
+    // float4 h (0/1) of group c = v*LPR + l goes to slot (2v + h)*LPR + l
+    for (int c = threadIdx.x; c < nv; c += kBlock) {
       float w8[8];
       if constexpr (ELEM) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = (8 * (c / LPR) + e) * LPR + c % LPR;
-          w8[e] = j < a.D ? weight_at(a.gamma, a.wdt, j) : 0.0f;
-        }
+        weights_group(a.gamma, a.wdt, a.zc, a.D, c, w8);
       } else {
         weights8(a.gamma, a.wdt, c, w8);
-      }
-      if (a.zc) {
+        if (a.zc) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) w8[k] = w8[k] + 1.0f;
+          for (int k = 0; k < 8; ++k) w8[k] = w8[k] + 1.0f;
+        }
       }
       wl4[((c / LPR) * 2) * LPR + (c % LPR)] = make_float4(w8[0], w8[1], w8[2], w8[3]);
       wl4[((c / LPR) * 2 + 1) * LPR + (c % LPR)] = make_float4(w8[4], w8[5], w8[6], w8[7]);
     }
     __syncthreads();
   } else {
-    if constexpr (ELEM) load_weights_elem<LPR, (LEAN ? 1 : VPL)>(a.gamma, a.wdt, a.zc, a.D, l, wreg);
+    if constexpr (ELEM) load_weights_any<LPR, (LEAN ? 1 : VPL)>(a.gamma, a.wdt, a.zc, a.D, l, wreg);
     else load_weights<LPR, (LEAN ? 1 : VPL), MASKED>(a.gamma, a.wdt, a.zc, nv, l, wreg);
   }
   // In the lean plan `base` is an opaque zero, so that the LDS reads stay
@@ -197,18 +181,20 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   const int64_t last_group = k + (mine_groups - 1) * K;
   const int64_t mine = mine_groups == 0 ? 0 : (mine_groups - 1) * S + (nblocks - last_group * S < S ? nblocks - last_group * S : S);
 
-  // Byte offset of this lane's vector v within its row group, per tensor;
-  // vectors past D get an offset no resource reaches. Rows past the chunk's
-  // end read as zero (and then contribute nothing) and their stores drop.
-  // With element-wise storage the offset is that of the group's first
-  // element 8v*LPR + l, and valid(v) the row's elements from it on.
+  // Byte offset of this lane's group v (elements [8c, 8c + 8), c = v*LPR + l)
+  // within its row group, per tensor. Rows past the chunk's end read as zero
+  // (and then contribute nothing) and their stores drop. With 16-byte
+  // storage, groups past D get an offset no resource reaches; in rows of any
+  // length the last group's elements are checked one by one
+  // (`valid`: the row's elements from the group's first on; `last`: only a
+  // lane's last group can be partial).
   auto voff = [&](int v, int64_t ld) -> uint32_t {
-    if constexpr (ELEM) return static_cast<uint32_t>(slot * ld * 2 + 2 * (8 * v * LPR + l));
     const int c = v * LPR + l;
-    if (MASKED && c >= nv) return kOutOfRange;
+    if (MSK && c >= nv) return kOutOfRange;
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
-  auto valid = [&](int v) { return a.D - (8 * v * LPR + l); };
+  auto valid = [&](int v) { return a.D - 8 * (v * LPR + l); };
+  auto last = [](int v) { return v == VPL - 1; };
 
   // One workgroup step's loaded rows (U row groups of each input stream).
   struct StepRegs {
@@ -236,37 +222,37 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       if (a.x_stream) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, LPR, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
-          b.xq[u][v] = load_row8<DT, LPR, kLoadStream>(rx, voff(v, a.ld_x), valid(v));
+          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v), last(v));
+          b.xq[u][v] = load_row8<DT, kLoadStream>(rx, voff(v, a.ld_x), valid(v), last(v));
         }
       } else {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, LPR, kLoadStream>(rg, voff(v, a.ld_g), valid(v));
-          b.xq[u][v] = load_row8<DT, LPR>(rx, voff(v, a.ld_x), valid(v));
+          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v), last(v));
+          b.xq[u][v] = load_row8<DT>(rx, voff(v, a.ld_x), valid(v), last(v));
         }
       }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          b.rres[u][v] = load_row8<DT, LPR, kLoadStream>(rgr, voff(v, a.ld_gres), valid(v));
+          b.rres[u][v] = load_row8<DT, kLoadStream>(rgr, voff(v, a.ld_gres), valid(v), last(v));
       }
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, end, RPW, a.ld_z, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          b.zq[u][v] = load_row8<DT, LPR, kLoadStream>(rz, voff(v, a.ld_z), valid(v));
+          b.zq[u][v] = load_row8<DT, kLoadStream>(rz, voff(v, a.ld_z), valid(v), last(v));
       }
       if constexpr (ADD) {  // the forward read it too: x's policy
         const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
         if (a.x_stream) {
 #pragma unroll
           for (int v = 0; v < VPL; ++v)
-            b.hq[u][v] = load_row8<DT, LPR, kLoadStream>(rh, voff(v, a.ld_rin), valid(v));
+            b.hq[u][v] = load_row8<DT, kLoadStream>(rh, voff(v, a.ld_rin), valid(v), last(v));
         } else {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT, LPR>(rh, voff(v, a.ld_rin), valid(v));
+          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT>(rh, voff(v, a.ld_rin), valid(v), last(v));
         }
       }
     }
@@ -318,7 +304,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
             dz8[k] = gnw * dag;
             gf[k] = gf[k] * ag;
           }
-          store_row8<DT, LPR>(pack8<DT>(dz8), rdz, voff(v, a.ld_dz), valid(v));
+          store_row8<DT>(pack8<DT>(dz8), rdz, voff(v, a.ld_dz), valid(v), last(v));
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -376,7 +362,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
         }
-        store_row8<DT, LPR>(pack8<DT>(o), rdx, voff(v, a.ld_dx), valid(v));
+        store_row8<DT>(pack8<DT>(o), rdx, voff(v, a.ld_dx), valid(v), last(v));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -418,39 +404,23 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       for (int k = 0; k < 8; ++k) acc[v][k] = acc[v][k] + __shfl_xor(acc[v][k], m);
 
   // Group v of this lane's accumulators to / from a row of Dp floats: the
-  // columns 8c .. 8c+7 of vector c = v*LPR + l, or with element-wise storage
-  // the columns (8v + e)*LPR + l below Dp.
+  // columns 8c .. 8c+7 of group c = v*LPR + l (Dp = 8 * nv, so a partial last
+  // group's columns past D exist and hold zeros).
   auto put = [&](float* row, int v) {
-    if constexpr (ELEM) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = (8 * v + e) * LPR + l;
-        if (j < Dp) row[j] = acc[v][e];
-      }
-    } else {
-      float* d = row + 8 * (v * LPR + l);
-      *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-      *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
-    }
+    float* d = row + 8 * (v * LPR + l);
+    *reinterpret_cast<float4*>(d) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
   };
   auto add_from = [&](const float* row, int v) {
-    if constexpr (ELEM) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = (8 * v + e) * LPR + l;
-        if (j < Dp) acc[v][e] = acc[v][e] + row[j];
-      }
-    } else {
-      const float* d = row + 8 * (v * LPR + l);
-      const float4 p0 = *reinterpret_cast<const float4*>(d);
-      const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
-      acc[v][0] = acc[v][0] + p0.x; acc[v][1] = acc[v][1] + p0.y;
-      acc[v][2] = acc[v][2] + p0.z; acc[v][3] = acc[v][3] + p0.w;
-      acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
-      acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
-    }
+    const float* d = row + 8 * (v * LPR + l);
+    const float4 p0 = *reinterpret_cast<const float4*>(d);
+    const float4 p1 = *reinterpret_cast<const float4*>(d + 4);
+    acc[v][0] = acc[v][0] + p0.x; acc[v][1] = acc[v][1] + p0.y;
+    acc[v][2] = acc[v][2] + p0.z; acc[v][3] = acc[v][3] + p0.w;
+    acc[v][4] = acc[v][4] + p1.x; acc[v][5] = acc[v][5] + p1.y;
+    acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
   };
-  // lanes without group v (16-byte rows only)
+  // lanes without group v
   auto absent = [&](int v) { return MSK && v * LPR + l >= nv; };
   float* const out = a.part + static_cast<int64_t>(blockIdx.x) * Dp;
   const bool writer = slot == 0;

@@ -17,12 +17,11 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // fp16, weights bf16, fp16 or fp32.
 enum : int { kBf16 = 0, kF16 = 1, kF32 = 2 };
 // Row storage of a kernel instance: the activation type, plus kElem when
-// rows move element by element (rows of any length D and any 2-byte
-// alignment). The geometry (lanes per row, groups of 8 per lane) is that of
-// 16-byte rows with ceil(D/8) groups, but group v of lane l holds the
-// elements (8v + e) * LPR + l, e = 0..7, so that each 2-byte access of the
-// row's lanes covers consecutive elements; elements past D read as zero and
-// are never written.
+// rows may have any length D and any 2-byte alignment. Either way a lane's
+// group c holds the row's elements [8c, 8c + 8) (the last group of a row of
+// D not a multiple of 8 is partial; its elements past D read as zero and are
+// never written), so the lanes' elements, and hence every reduction tree,
+// are those of 16-byte rows of ceil(D/8) groups.
 enum : int { kElem = 8, kBf16E = kBf16 | kElem, kF16E = kF16 | kElem };
 constexpr int value_dt(int DT) { return DT & ~kElem; }
 constexpr bool elem_dt(int DT) { return (DT & kElem) != 0; }
@@ -136,42 +135,40 @@ __device__ __forceinline__ void buf_store16_nt(const u32x4& v, __amdgpu_buffer_r
   __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 2);
 }
 
-// One lane's group of 8 row elements through a row resource. 16-byte
-// storage: elements [8c, 8c + 8) as one vector at byte offset `off`.
-// Element-wise storage: element e of the group is STRIDE elements after
-// element e - 1 (STRIDE = the lanes sharing the row, so that one 2-byte
-// access of all lanes covers consecutive elements), `off` is the byte offset
-// of element 0 and `left` the row's elements from it on; elements past the
-// row get an offset beyond the resource and read as zero.
-template <int DT, int STRIDE, int POLICY = kLoadDefault>
-__device__ __forceinline__ u32x4 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off, int left) {
-  if constexpr (!elem_dt(DT)) {
-    return buf_load16<POLICY>(r, off);
-  } else {
-    uint32_t h[8];
+// One lane's group of 8 row elements [8c, 8c + 8) through a row resource, at
+// byte offset `off` (the group's first element); `left` = D - 8c, the row's
+// elements from there on, and `last` whether the group may be the row's
+// last (only the last of a lane's groups can be; the argument is a constant
+// after unrolling). 16-byte storage: one aligned 16-byte vector.
+// Element-wise storage (any D, any 2-byte alignment): a full group is one
+// 16-byte access at a 2-byte-aligned offset, which the hardware splits into
+// aligned pieces; the row's partial last group moves element by element,
+// elements past D reading as zero (an offset beyond the resource).
+template <int DT, int POLICY = kLoadDefault>
+__device__ __forceinline__ u32x4 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off, int left,
+                                           bool last) {
+  if (!elem_dt(DT) || !last || left >= 8) return buf_load16<POLICY>(r, off);
+  uint32_t h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      h[e] = __builtin_amdgcn_raw_buffer_load_b16(
-          r, static_cast<int>(e * STRIDE < left ? off + 2 * e * STRIDE : kOutOfRange), 0, POLICY);
-    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                 h[6] | (h[7] << 16)};
-  }
+  for (int e = 0; e < 8; ++e)
+    h[e] = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(e < left ? off + 2 * e : kOutOfRange),
+                                                0, POLICY);
+  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
-// Stores a group the same way (non-temporal); element-wise storage writes
-// only the elements inside the row.
-template <int DT, int STRIDE>
+// Stores a group the same way (non-temporal); a partial last group writes
+// only its elements inside the row.
+template <int DT>
 __device__ __forceinline__ void store_row8(const u32x4& v, __amdgpu_buffer_rsrc_t r, uint32_t off,
-                                           int left) {
-  if constexpr (!elem_dt(DT)) {
+                                           int left, bool last) {
+  if (!elem_dt(DT) || !last || left >= 8) {
     buf_store16_nt(v, r, off);
-  } else {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      __builtin_amdgcn_raw_buffer_store_b16(
-          static_cast<unsigned short>(w[e >> 1] >> (16 * (e & 1))), r,
-          static_cast<int>(e * STRIDE < left ? off + 2 * e * STRIDE : kOutOfRange), 0, 2);
+    return;
   }
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[e >> 1] >> (16 * (e & 1))), r,
+                                          static_cast<int>(e < left ? off + 2 * e : kOutOfRange), 0, 2);
 }
 
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -404,19 +401,29 @@ __device__ __forceinline__ float weight_at(const void* __restrict__ gamma, int w
   return wdt == kF16 ? f16_pair(b).x : bf16_lo(b);
 }
 
-// Element-wise storage: the weights of elements (8v + e) * LPR + l of a row
-// of D (zero past D), w_eff = fp32(gamma) (+1.0f in fp32 when zero-centred).
+// The 8 weights of group c (columns 8c .. 8c + 7), zero past D, with the
+// zero-centred offset: a full group as one vector read, the partial last
+// group element by element (so nothing past gamma's D values is read).
+__device__ __forceinline__ void weights_group(const void* __restrict__ gamma, int wdt, int zc, int D,
+                                              int c, float (&w)[8]) {
+  if (8 * c + 8 <= D) {
+    weights8(gamma, wdt, c, w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = 8 * c + e < D ? weight_at(gamma, wdt, 8 * c + e) : 0.0f;
+  }
+  if (zc) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = w[k] + 1.0f;
+  }
+}
+
+// Rows of any length: this lane's weights for its groups c = v*LPR + l.
 template <int LPR, int VPL>
-__device__ __forceinline__ void load_weights_elem(const void* __restrict__ gamma, int wdt, int zc,
-                                                  int D, int l, float (&w)[VPL][8]) {
+__device__ __forceinline__ void load_weights_any(const void* __restrict__ gamma, int wdt, int zc,
+                                                 int D, int l, float (&w)[VPL][8]) {
 #pragma unroll
-  for (int v = 0; v < VPL; ++v)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = (8 * v + e) * LPR + l;
-      w[v][e] = j < D ? weight_at(gamma, wdt, j) : 0.0f;
-      if (zc) w[v][e] = w[v][e] + 1.0f;
-    }
+  for (int v = 0; v < VPL; ++v) weights_group(gamma, wdt, zc, D, v * LPR + l, w[v]);
 }
 
 // Loads this lane's weights w_eff = fp32(gamma) (+1.0f in fp32 when

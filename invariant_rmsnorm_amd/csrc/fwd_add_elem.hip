@@ -1,5 +1,5 @@
 // Fused add-norm forward launcher for rows whose length D is not a multiple
-// of 8: the kernel of fwd_kernel.hpp with element-wise row storage (bf16).
+// of 8: the kernel of fwd_kernel.hpp with rows of any alignment (bf16).
 #include "fwd_kernel.hpp"
 
 namespace rmsn {

@@ -1,7 +1,8 @@
 // Forward launchers for rows whose length D is not a multiple of 8 (plain
 // and residual-copy forms, bf16 or fp16 activations): the kernel of
-// fwd_kernel.hpp with element-wise row storage. The arithmetic and the
-// reduction tree are those of 16-byte rows; only the memory accesses change.
+// fwd_kernel.hpp with rows of any alignment (unaligned 16-byte accesses, the
+// partial last group element by element). The arithmetic and the reduction
+// tree are those of 16-byte rows of ceil(D/8) groups.
 #include "fwd_kernel.hpp"
 
 namespace rmsn {

@@ -71,21 +71,21 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
 
   constexpr bool ELEM = elem_dt(DT);
   float w[VPL][8];
-  if constexpr (ELEM) load_weights_elem<LPR, VPL>(a.gamma, a.wdt, a.zc, a.D, l, w);
+  if constexpr (ELEM) load_weights_any<LPR, VPL>(a.gamma, a.wdt, a.zc, a.D, l, w);
   else load_weights<LPR, VPL, MASKED>(a.gamma, a.wdt, a.zc, nv, l, w);
 
-  // Byte offset of this lane's group v within its row group, per tensor:
-  // the vector c = v*LPR + l (vectors past D get an offset no resource
-  // reaches), or with element-wise storage the group's first element
-  // 8v*LPR + l.
+  // Byte offset of this lane's group v (elements [8c, 8c + 8), c = v*LPR + l)
+  // within its row group, per tensor. With 16-byte storage, groups past D
+  // get an offset no resource reaches; in rows of any length the last
+  // group's elements are checked one by one (`valid`: the row's elements from
+  // the group's first on; `last`: only a lane's last group can be partial).
   auto voff = [&](int v, int64_t ld) -> uint32_t {
-    if constexpr (ELEM) return static_cast<uint32_t>(slot * ld * 2 + 2 * (8 * v * LPR + l));
     const int c = v * LPR + l;
-    if (MASKED && c >= nv) return kOutOfRange;
+    if (!ELEM && MASKED && c >= nv) return kOutOfRange;
     return static_cast<uint32_t>(slot * ld * 2 + 16 * c);
   };
-  // Element-wise storage: the row's elements from the group's first on.
-  auto valid = [&](int v) { return a.D - (8 * v * LPR + l); };
+  auto valid = [&](int v) { return a.D - 8 * (v * LPR + l); };
+  auto last = [](int v) { return v == VPL - 1; };
   // Rows first .. first+RPW-1 form row group u of the wave; `first` is
   // wave-uniform.
   auto group_first = [&](int64_t base, int u) { return base + group * ROWS_WAVE + u * RPW; };
@@ -100,17 +100,17 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
       const int64_t first = group_first(base, u);
       const auto rx = rows_rsrc(a.x, first, a.T, RPW, a.ld_x, a.D);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT, LPR, P>(rx, voff(v, a.ld_x), valid(v));
+      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT, P>(rx, voff(v, a.ld_x), valid(v), last(v));
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, a.T, RPW, a.ld_z, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, LPR, P>(rz, voff(v, a.ld_z), valid(v));
+        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, P>(rz, voff(v, a.ld_z), valid(v), last(v));
       }
       if constexpr (ADD) {
         const auto rr = rows_rsrc(a.rin, first, a.T, RPW, a.ld_rin, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          zq[u][v] = load_row8<DT, LPR, P>(rr, voff(v, a.ld_rin), valid(v));
+          zq[u][v] = load_row8<DT, P>(rr, voff(v, a.ld_rin), valid(v), last(v));
       }
     }
   };
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) o[k] = o[k] * gate_fast<ACT>(zf[k]);
         }
-        store_row8<DT, LPR>(pack8<DT>(o), ry, voff(v, a.ld_y), valid(v));
+        store_row8<DT>(pack8<DT>(o), ry, voff(v, a.ld_y), valid(v), last(v));
       }
       if (a.res != nullptr) {
         // residual output: a byte copy of x, or for the fused add bf16(h)
@@ -187,9 +187,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
           if constexpr (ADD) {
             float f[8];
             row_values(xq[u][v], zq[u][v], f);
-            store_row8<DT, LPR>(pack8<DT>(f), rr, voff(v, a.ld_res), valid(v));
+            store_row8<DT>(pack8<DT>(f), rr, voff(v, a.ld_res), valid(v), last(v));
           } else {
-            store_row8<DT, LPR>(xq[u][v], rr, voff(v, a.ld_res), valid(v));
+            store_row8<DT>(xq[u][v], rr, voff(v, a.ld_res), valid(v), last(v));
           }
         }
       }
@@ -230,11 +230,7 @@ inline int cu_count() {
 //   D = 8192   114.6 110.4 110.2 118.7 119.6
 //   D = 16384  109.9 106.2 105.7 111.3 111.5
 //   D = 32768  114.1 108.7 109.1 111.0 111.2
-//   D = 4100   222.6 232.1 246.7 275.5 331.4  (element-wise rows: a weight
-//                                              load per element)
-constexpr int64_t fwd_grid_scale(int lpr, int vpl, bool elem) {
-  return elem ? 1 : lpr * vpl >= 1024 ? 2 : 16;
-}
+constexpr int64_t fwd_grid_scale(int lpr, int vpl) { return lpr * vpl >= 1024 ? 2 : 16; }
 
 template <int LPR, int VPL, bool MASKED, int GATE, int DT>
 int launch_inst(const FwdArgs& a, void* stream) {
@@ -251,7 +247,7 @@ int launch_inst(const FwdArgs& a, void* stream) {
   // the last rows are shared by whichever compute units are free instead of
   // by a fixed set), and every workgroup given the same number of steps.
   const int64_t blocks = (a.T + ROWS_BLOCK - 1) / ROWS_BLOCK;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu * fwd_grid_scale(LPR, VPL, elem_dt(DT));
+  const int64_t cap = static_cast<int64_t>(cu_count()) * per_cu * fwd_grid_scale(LPR, VPL);
   const int64_t steps = (blocks + cap - 1) / cap;
   const int grid = static_cast<int>(std::max<int64_t>(1, (blocks + steps - 1) / steps));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);

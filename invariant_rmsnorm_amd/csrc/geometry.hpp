@@ -5,9 +5,9 @@
 // Invariant Kernels", sections 2-3: the reduction layout must come from the
 // problem's fixed dimensions, never from the batch dimension).
 //
-// A row of D bf16 values is NV = ceil(D/8) groups of 8 elements (16-byte
-// vectors when D is a multiple of 8; otherwise the last group is partial and
-// the rows move element by element), shared by LPR lanes:
+// A row of D bf16 values is NV = ceil(D/8) groups of 8 consecutive elements
+// (16-byte vectors; when D is not a multiple of 8 the last group is
+// partial), shared by LPR lanes:
 //  - long rows span several wavefronts of one workgroup: LPR = 128 or 256
 //    (VPL = ceil(NV/LPR) <= 16 vectors each). The forward does this past
 //    1024 vectors (D > 8192), over 2 waves up to 2048 vectors and 4 beyond;
@@ -39,17 +39,7 @@ constexpr int kBwdMinVplMulti = 3;
 // instead of 161 us per 256 MiB step), while two per CU at D >= 4096 was
 // slower.
 constexpr int64_t kCus = 256;
-// Rows moved element by element (D not a multiple of 8) keep two
-// workgroups per CU up to this many groups per lane: their loads wait on
-// eight 2-byte accesses per group, and a second workgroup hides that
-// (measured at D = 12290, 7 groups per lane: the rows kernel 2239 ->
-// 3208 GB/s; 2616 -> 2909 with the residual gradient, spills included).
-#ifndef RMSN_BWD_ELEM_TWO_PER_CU_VPL
-#define RMSN_BWD_ELEM_TWO_PER_CU_VPL 8
-#endif
-constexpr int bwd_waves_per_eu(int vpl, bool elem = false) {
-  return vpl < 5 || (elem && vpl <= RMSN_BWD_ELEM_TWO_PER_CU_VPL) ? 2 : 1;
-}
+constexpr int bwd_waves_per_eu(int vpl) { return vpl < 5 ? 2 : 1; }
 constexpr int64_t kMaxChunks = 2 * kCus;
 
 struct RowGeom {

@@ -31,11 +31,11 @@ struct BwdPlan {
 #endif
 inline int64_t bwd_target_chunks(int64_t D) {
   return kCus * (RMSN_BWD_BLOCKS_PER_CU > 0 ? RMSN_BWD_BLOCKS_PER_CU
-                                            : bwd_waves_per_eu(bwd_geom(D).vpl, D % 8 != 0));
+                                            : bwd_waves_per_eu(bwd_geom(D).vpl));
 }
 
-// Rows of one wave with 5 to 8 vectors per lane (2048 < D <= 4096, 16-byte
-// rows) run one workgroup per CU and take their (K, S) from measurement
+// Rows of one wave with 5 to 8 groups per lane (2048 < D <= 4096) run one
+// workgroup per CU and take their (K, S) from measurement
 // (rows kernel, cache flushed before each launch, us; after the forward in
 // brackets):
 //   D     T        K=256 S=4      K=256 S=1      K=512 S=8
@@ -61,8 +61,7 @@ inline BwdPlan bwd_plan(int64_t T, int64_t D) {
   const int64_t blocks = T / R + (T % R != 0);
   int64_t S = RMSN_BWD_GROUP > 0 ? RMSN_BWD_GROUP : blocks / target + (blocks % target != 0);
   const RowGeom g = bwd_geom(D);
-  if (RMSN_BWD_GROUP > 0 && RMSN_BWD_BLOCKS_PER_CU == 0 && D % 8 == 0 && g.lpr == 64 &&
-      g.vpl >= 5) {
+  if (RMSN_BWD_GROUP > 0 && RMSN_BWD_BLOCKS_PER_CU == 0 && g.lpr == 64 && g.vpl >= 5) {
     const bool pow2 = (D & (D - 1)) == 0;
     const bool spread = pow2 && blocks > kBwdDenseBlocksPerCu * kCus;
     S = spread ? 8 : 1;

@@ -7,8 +7,8 @@
 namespace rmsn {
 
 // Bytes of the scratch (one copy per GPU). The dgamma partials need at most
-// 512 chunks x 16384 floats or 256 x 32768 (rmsnorm_bwd_workspace_bytes),
-// 32 MiB, so every supported shape fits.
+// 256 chunks x 32768 floats (rmsnorm_bwd_workspace_bytes; 512 chunks only
+// for rows of at most 2048 elements), 32 MiB, so every supported shape fits.
 constexpr size_t kScratchBytes = size_t{32} << 20;
 
 // The device address of the current device's copy of the scratch (looked up

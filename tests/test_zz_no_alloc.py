@@ -44,11 +44,12 @@ def test_noalloc_matches_bwd_on_two_calls_second_smaller(gpu):
 
 
 def test_noalloc_largest_layouts_and_repeats(gpu):
-    # the two layouts that fill the whole scratch
-    assert irn.rmsnorm_bwd_workspace_bytes(3000, 16383) == 32 << 20   # 512 x 16384 floats
-    assert irn.rmsnorm_bwd_workspace_bytes(1100, 32768) == 32 << 20   # 256 x 32768 floats
-    _compare(3000, 16383, True, 11003, False)
+    # layouts that fill the whole scratch (256 chunks x 32768 floats), the
+    # second with rows not a multiple of 8
+    assert irn.rmsnorm_bwd_workspace_bytes(1100, 32768) == 32 << 20
+    assert irn.rmsnorm_bwd_workspace_bytes(1500, 32767) == 32 << 20
     _compare(1100, 32768, False, 11006, True)
+    _compare(1500, 32767, True, 11003, False)
     _compare(77, 100, False, 11004, True)        # rows not a multiple of 8
     _compare(77, 100, False, 11004, True)        # the same call again: the same bits
 
