@@ -86,6 +86,16 @@ def _load():
                                       i64], i),
         "oracle_rmsnorm_dgamma_dt": ([i, i, vp, i64, vp, i64, vp, i64, i64, vp], i),
         "oracle_gemm_xwt": ([vp, i64, vp, i64, i64, i64, i64, vp, i64, vp], i),
+        "oracle_rmsnorm_gated_fwd_dt": ([i, i, i, i, i, vp, i64, vp, i64, vp, i, f, i64, i64, vp,
+                                         i64, vp], i),
+        "oracle_rmsnorm_gated_bwd_dt": ([i, i, i, i, vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64,
+                                         vp, i64, vp, i64], i),
+        "oracle_rmsnorm_gated_dgamma_dt": ([i, i, i, vp, i64, vp, i64, vp, i64, vp, i64, i64, vp],
+                                           i),
+        "oracle_rmsnorm_add_fwd_dt": ([i, i, i, vp, i64, vp, i64, vp, i, f, i64, i64, vp, i64, vp,
+                                       i64, vp], i),
+        "oracle_rmsnorm_add_bwd_dt": ([i, i, i, vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, vp,
+                                       i64, vp, i64, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -466,6 +476,80 @@ def bwd_dt(g, x, rstd, gamma, zero_centered=False, gres=None, act_dtype=BF16,
     _check(lib.oracle_rmsnorm_dgamma_dt(mode, act_dtype, _p(g), _ld(g), _p(x), _ld(x), _p(rstd),
                                         T, D, _p(dg)), "dgamma_dt")
     return dx, dg
+
+
+def gated_fwd_dt(x, z, gamma, zero_centered=False, eps=1e-6, activation=SILU,
+                 convention=FP32_WEIGHT, act_dtype=BF16, weight_dtype=F32, mode=R64):
+    """(out in the activation type's bits, rstd fp32): the gated forward for
+    bf16 / fp16 activations and fp32 / bf16 / fp16 weights."""
+    x, z = _bf16_2d(x), _bf16_2d(z)
+    T, D = x.shape
+    gamma = _weights(gamma, weight_dtype)
+    out = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_gated_fwd_dt(mode, act_dtype, weight_dtype, activation,
+                                               convention, _p(x), _ld(x), _p(z), _ld(z), _p(gamma),
+                                               int(zero_centered), eps, T, D, _p(out), D,
+                                               _p(rstd)), "gated_fwd_dt")
+    return out, rstd
+
+
+def gated_bwd_dt(g, x, z, rstd, gamma, zero_centered=False, activation=SILU, act_dtype=BF16,
+                 weight_dtype=F32, mode=R64):
+    """(dx, dz in the activation type's bits, dgamma fp32) of the gated norm
+    (fp32 convention)."""
+    g, x, z = _bf16_2d(g), _bf16_2d(x), _bf16_2d(z)
+    T, D = x.shape
+    rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+    gamma = _weights(gamma, weight_dtype)
+    dx = np.empty((T, D), dtype=np.uint16)
+    dz = np.empty((T, D), dtype=np.uint16)
+    dg = np.empty(D, dtype=np.float32)
+    lib = _load()
+    _check(lib.oracle_rmsnorm_gated_bwd_dt(mode, act_dtype, weight_dtype, activation, _p(g),
+                                           _ld(g), _p(x), _ld(x), _p(z), _ld(z), _p(rstd),
+                                           _p(gamma), int(zero_centered), T, D, _p(dx), D, _p(dz),
+                                           D), "gated_bwd_dt")
+    _check(lib.oracle_rmsnorm_gated_dgamma_dt(mode, act_dtype, activation, _p(g), _ld(g), _p(x),
+                                              _ld(x), _p(z), _ld(z), _p(rstd), T, D, _p(dg)),
+           "gated_dgamma_dt")
+    return dx, dz, dg
+
+
+def add_fwd_dt(x, residual, gamma, zero_centered=False, eps=1e-6, act_dtype=BF16,
+               weight_dtype=F32, mode=R64):
+    """(y, residual_out in the activation type's bits, rstd fp32) of the fused
+    add-norm."""
+    x, residual = _bf16_2d(x), _bf16_2d(residual)
+    T, D = x.shape
+    gamma = _weights(gamma, weight_dtype)
+    y = np.empty((T, D), dtype=np.uint16)
+    rout = np.empty((T, D), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_add_fwd_dt(mode, act_dtype, weight_dtype, _p(x), _ld(x),
+                                             _p(residual), _ld(residual), _p(gamma),
+                                             int(zero_centered), eps, T, D, _p(y), D, _p(rout), D,
+                                             _p(rstd)), "add_fwd_dt")
+    return y, rout, rstd
+
+
+def add_bwd_dt(g, x, residual, rstd, gamma, zero_centered=False, g_rout=None, act_dtype=BF16,
+               weight_dtype=F32, mode=R64):
+    """(dh in the activation type's bits, dgamma fp32) of the fused add-norm."""
+    g, x, residual = _bf16_2d(g), _bf16_2d(x), _bf16_2d(residual)
+    T, D = x.shape
+    rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+    gamma = _weights(gamma, weight_dtype)
+    if g_rout is not None:
+        g_rout = _bf16_2d(g_rout)
+    dh = np.empty((T, D), dtype=np.uint16)
+    dg = np.empty(D, dtype=np.float32)
+    _check(_load().oracle_rmsnorm_add_bwd_dt(mode, act_dtype, weight_dtype, _p(g), _ld(g), _p(x),
+                                             _ld(x), _p(residual), _ld(residual), _p(rstd),
+                                             _p(gamma), int(zero_centered), T, D, _p(g_rout),
+                                             0 if g_rout is None else _ld(g_rout), _p(dh), D,
+                                             _p(dg)), "add_bwd_dt")
+    return dh, dg
 
 
 # ---- batch-invariant GEMM --------------------------------------------------------

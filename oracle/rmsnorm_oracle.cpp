@@ -632,6 +632,218 @@ int oracle_rmsnorm_dgamma_dt(int mode, int act_dtype, const uint16_t* g, int64_t
   return 0;
 }
 
+// ---- gated norm and fused add-norm in other storage types ----------------------
+// The same definitions as oracle_rmsnorm_gated_* and oracle_rmsnorm_add_*
+// above, with activations (x, z, g, residual, gradients, outputs) stored as
+// bf16 or fp16 and weights as fp32, bf16 or fp16. Every storage type widens to
+// fp32 exactly; the gated cast convention rounds to the activations' type
+// ("cast to the input dtype", RL-Kernel PR "C1: zero-centred RMSNorm
+// references and CUDA kernel", gated-norm conventions).
+
+static float round_act(int dt, float v) { return act_to_f32(dt, f32_to_act(dt, v)); }
+
+// rstd of a row of stored activations: squares of the widened values (exact
+// for bf16 and fp16) summed in the mode's order.
+static float row_rstd_dt(int mode, int dt, const uint16_t* xr, int64_t D, float eps) {
+  Sum ss(mode);
+  for (int64_t j = 0; j < D; ++j) {
+    const float xf = act_to_f32(dt, xr[j]);
+    const float sq = xf * xf;
+    ss.add(sq);
+  }
+  const float mean = ss.value() / static_cast<float>(D);
+  const float v = mean + eps;
+  return rsqrt_ref(v);
+}
+
+int oracle_rmsnorm_gated_fwd_dt(int mode, int act_dtype, int weight_dtype, int activation,
+                                int convention, const uint16_t* x, int64_t ld_x,
+                                const uint16_t* z, int64_t ld_z, const void* gamma,
+                                int zero_centered, float eps, int64_t T, int64_t D, uint16_t* out,
+                                int64_t ld_out, float* rstd) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || bad_weight_dt(weight_dtype) ||
+      bad_act(activation) || (convention != ORACLE_GATED_FP32 && convention != ORACLE_GATED_CAST) ||
+      T < 0 || D <= 0 || !gamma || bad_2d(x, ld_x, D) || bad_2d(z, ld_z, D) ||
+      bad_2d(out, ld_out, D))
+    return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + t * ld_x;
+    const float r = row_rstd_dt(mode, act_dtype, xr, D, eps);
+    if (rstd) rstd[t] = r;
+    for (int64_t j = 0; j < D; ++j) {
+      const float w = weight_eff_dt(weight_dtype, gamma, zero_centered, j);
+      const float a = static_cast<float>(gate_d(activation, act_to_f32(act_dtype, z[t * ld_z + j])));
+      float n = act_to_f32(act_dtype, xr[j]) * r;
+      if (convention == ORACLE_GATED_CAST) n = round_act(act_dtype, n);
+      float nw = n * w;
+      if (convention == ORACLE_GATED_CAST) nw = round_act(act_dtype, nw);
+      const float o = nw * a;
+      out[t * ld_out + j] = f32_to_act(act_dtype, o);
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_gated_bwd_dt(int mode, int act_dtype, int weight_dtype, int activation,
+                                const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                                const uint16_t* z, int64_t ld_z, const float* rstd,
+                                const void* gamma, int zero_centered, int64_t T, int64_t D,
+                                uint16_t* dx, int64_t ld_dx, uint16_t* dz, int64_t ld_dz) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || bad_weight_dt(weight_dtype) ||
+      bad_act(activation) || T < 0 || D <= 0 || !gamma || !rstd || bad_2d(g, ld_g, D) ||
+      bad_2d(x, ld_x, D) || bad_2d(z, ld_z, D) || (!dx && !dz) || (dx && ld_dx < D) ||
+      (dz && ld_dz < D))
+    return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* gr = g + t * ld_g;
+    const uint16_t* xr = x + t * ld_x;
+    const uint16_t* zr = z + t * ld_z;
+    const float r = rstd[t];
+    Sum s(mode);
+    for (int64_t i = 0; i < D; ++i) {
+      const float a = static_cast<float>(gate_d(activation, act_to_f32(act_dtype, zr[i])));
+      const float gn = act_to_f32(act_dtype, gr[i]) * a;
+      const float gw = gn * weight_eff_dt(weight_dtype, gamma, zero_centered, i);
+      const float term = gw * act_to_f32(act_dtype, xr[i]);
+      s.add(term);
+    }
+    const float r2 = r * r;
+    const float r3 = r2 * r;
+    const float r3s = r3 * s.value();
+    const float c = r3s / static_cast<float>(D);
+    for (int64_t k = 0; k < D; ++k) {
+      const float w = weight_eff_dt(weight_dtype, gamma, zero_centered, k);
+      const float xf = act_to_f32(act_dtype, xr[k]);
+      const float gf = act_to_f32(act_dtype, gr[k]);
+      const double zd = act_to_f32(act_dtype, zr[k]);
+      const float a = static_cast<float>(gate_d(activation, zd));
+      const float da = static_cast<float>(gate_grad_d(activation, zd));
+      if (dz) {
+        const float n = xf * r;
+        const float nw = n * w;
+        const float gnw = gf * nw;
+        dz[t * ld_dz + k] = f32_to_act(act_dtype, gnw * da);
+      }
+      if (dx) {
+        const float gn = gf * a;
+        const float gw = gn * w;
+        const float t1 = gw * r;
+        const float t2 = xf * c;
+        dx[t * ld_dx + k] = f32_to_act(act_dtype, t1 - t2);
+      }
+    }
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_gated_dgamma_dt(int mode, int act_dtype, int activation, const uint16_t* g,
+                                   int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                                   const uint16_t* z, int64_t ld_z, const float* rstd, int64_t T,
+                                   int64_t ncols, float* dgamma) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || bad_act(activation) || T < 0 || ncols <= 0 ||
+      !dgamma || bad_2d(g, ld_g, ncols) || bad_2d(x, ld_x, ncols) || bad_2d(z, ld_z, ncols) ||
+      (T > 0 && !rstd))
+    return -1;
+  for (int64_t j = 0; j < ncols; ++j) {
+    Sum acc(mode);
+    for (int64_t t = 0; t < T; ++t) {
+      const float a =
+          static_cast<float>(gate_d(activation, act_to_f32(act_dtype, z[t * ld_z + j])));
+      const float gn = act_to_f32(act_dtype, g[t * ld_g + j]) * a;
+      const float gx = gn * act_to_f32(act_dtype, x[t * ld_x + j]);
+      const float term = gx * rstd[t];
+      acc.add(term);
+    }
+    dgamma[j] = acc.value();
+  }
+  return 0;
+}
+
+int oracle_rmsnorm_add_fwd_dt(int mode, int act_dtype, int weight_dtype, const uint16_t* x,
+                              int64_t ld_x, const uint16_t* residual, int64_t ld_res,
+                              const void* gamma, int zero_centered, float eps, int64_t T, int64_t D,
+                              uint16_t* y, int64_t ld_y, uint16_t* residual_out, int64_t ld_rout,
+                              float* rstd) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || bad_weight_dt(weight_dtype) || T < 0 || D <= 0 ||
+      !gamma || bad_2d(x, ld_x, D) || bad_2d(residual, ld_res, D) || bad_2d(y, ld_y, D) ||
+      bad_2d(residual_out, ld_rout, D))
+    return -1;
+  float* h = new float[static_cast<size_t>(D)];
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = 0; j < D; ++j)
+      h[j] = act_to_f32(act_dtype, x[t * ld_x + j]) + act_to_f32(act_dtype, residual[t * ld_res + j]);
+    Sum ss(mode);
+    for (int64_t j = 0; j < D; ++j) {
+      const float sq = h[j] * h[j];
+      ss.add(sq);
+    }
+    const float mean = ss.value() / static_cast<float>(D);
+    const float r = rsqrt_ref(mean + eps);
+    if (rstd) rstd[t] = r;
+    for (int64_t j = 0; j < D; ++j) {
+      const float n = row_normed(h[j], r, weight_eff_dt(weight_dtype, gamma, zero_centered, j));
+      y[t * ld_y + j] = f32_to_act(act_dtype, n);
+      residual_out[t * ld_rout + j] = f32_to_act(act_dtype, h[j]);
+    }
+  }
+  delete[] h;
+  return 0;
+}
+
+int oracle_rmsnorm_add_bwd_dt(int mode, int act_dtype, int weight_dtype, const uint16_t* g,
+                              int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                              const uint16_t* residual, int64_t ld_res, const float* rstd,
+                              const void* gamma, int zero_centered, int64_t T, int64_t D,
+                              const uint16_t* g_rout, int64_t ld_gro, uint16_t* dh, int64_t ld_dh,
+                              float* dgamma) {
+  if (bad_mode(mode) || bad_act_dt(act_dtype) || bad_weight_dt(weight_dtype) || T < 0 || D <= 0 ||
+      !gamma || (T > 0 && !rstd) || bad_2d(g, ld_g, D) || bad_2d(x, ld_x, D) ||
+      bad_2d(residual, ld_res, D) || (!dh && !dgamma) || (dh && ld_dh < D) ||
+      (g_rout && ld_gro < D))
+    return -1;
+  auto h_of = [&](int64_t t, int64_t j) {
+    return act_to_f32(act_dtype, x[t * ld_x + j]) + act_to_f32(act_dtype, residual[t * ld_res + j]);
+  };
+  if (dh) {
+    for (int64_t t = 0; t < T; ++t) {
+      const uint16_t* gr = g + t * ld_g;
+      const float r = rstd[t];
+      Sum s(mode);
+      for (int64_t i = 0; i < D; ++i) {
+        const float gw = act_to_f32(act_dtype, gr[i]) *
+                         weight_eff_dt(weight_dtype, gamma, zero_centered, i);
+        const float term = gw * h_of(t, i);
+        s.add(term);
+      }
+      const float r2 = r * r;
+      const float r3 = r2 * r;
+      const float r3s = r3 * s.value();
+      const float c = r3s / static_cast<float>(D);
+      for (int64_t k = 0; k < D; ++k) {
+        const float gw = act_to_f32(act_dtype, gr[k]) *
+                         weight_eff_dt(weight_dtype, gamma, zero_centered, k);
+        const float t1 = gw * r;
+        const float t2 = h_of(t, k) * c;
+        float d = t1 - t2;
+        if (g_rout) d = d + act_to_f32(act_dtype, g_rout[t * ld_gro + k]);
+        dh[t * ld_dh + k] = f32_to_act(act_dtype, d);
+      }
+    }
+  }
+  if (dgamma) {
+    for (int64_t j = 0; j < D; ++j) {
+      Sum acc(mode);
+      for (int64_t t = 0; t < T; ++t) {
+        const float gh = act_to_f32(act_dtype, g[t * ld_g + j]) * h_of(t, j);
+        const float term = gh * rstd[t];
+        acc.add(term);
+      }
+      dgamma[j] = acc.value();
+    }
+  }
+  return 0;
+}
+
 // ---- batch-invariant GEMM ----------------------------------------------------
 // TransformerEngine issue "Expose Batch Invariant Kernels", point 3: BF16,
 // Y = X @ W.T over contiguous 2-D operands. The plain definition: each

@@ -248,6 +248,38 @@ int oracle_rmsnorm_dgamma_dt(int mode, int act_dtype, const uint16_t* g,
                              const float* rstd, int64_t T, int64_t ncols,
                              float* dgamma);
 
+/* The gated norm and the fused add-norm in other storage types: the same
+ * definitions as oracle_rmsnorm_gated_fwd_ex / _gated_bwd / _gated_dgamma and
+ * oracle_rmsnorm_add_fwd / _add_bwd, with activations ORACLE_BF16 or
+ * ORACLE_F16 and weights ORACLE_F32, ORACLE_BF16 or ORACLE_F16 (gamma points at
+ * that type). The gated cast convention rounds to the activations' type. With
+ * (ORACLE_BF16, ORACLE_F32) they equal those functions bitwise. */
+int oracle_rmsnorm_gated_fwd_dt(int mode, int act_dtype, int weight_dtype, int activation,
+                                int convention, const uint16_t* x, int64_t ld_x,
+                                const uint16_t* z, int64_t ld_z, const void* gamma,
+                                int zero_centered, float eps, int64_t T, int64_t D, uint16_t* out,
+                                int64_t ld_out, float* rstd);
+int oracle_rmsnorm_gated_bwd_dt(int mode, int act_dtype, int weight_dtype, int activation,
+                                const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                                const uint16_t* z, int64_t ld_z, const float* rstd,
+                                const void* gamma, int zero_centered, int64_t T, int64_t D,
+                                uint16_t* dx, int64_t ld_dx, uint16_t* dz, int64_t ld_dz);
+int oracle_rmsnorm_gated_dgamma_dt(int mode, int act_dtype, int activation, const uint16_t* g,
+                                   int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                                   const uint16_t* z, int64_t ld_z, const float* rstd, int64_t T,
+                                   int64_t ncols, float* dgamma);
+int oracle_rmsnorm_add_fwd_dt(int mode, int act_dtype, int weight_dtype, const uint16_t* x,
+                              int64_t ld_x, const uint16_t* residual, int64_t ld_res,
+                              const void* gamma, int zero_centered, float eps, int64_t T, int64_t D,
+                              uint16_t* y, int64_t ld_y, uint16_t* residual_out, int64_t ld_rout,
+                              float* rstd);
+int oracle_rmsnorm_add_bwd_dt(int mode, int act_dtype, int weight_dtype, const uint16_t* g,
+                              int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                              const uint16_t* residual, int64_t ld_res, const float* rstd,
+                              const void* gamma, int zero_centered, int64_t T, int64_t D,
+                              const uint16_t* g_rout, int64_t ld_gro, uint16_t* dh, int64_t ld_dh,
+                              float* dgamma);
+
 /* ---- Batch-invariant GEMM ([TE] point 3: BF16 Y = X @ W.T) -------------
  * X bf16 [M, K] (row stride ldx), W bf16 [N, K] (ldw), Y bf16 [M, N] (ldy):
  * Y[i][j] = bf16(fp32(sum over k ascending of X[i][k] * W[j][k])), the sum in

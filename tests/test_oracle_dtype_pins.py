@@ -15,7 +15,13 @@ What pins what:
   * bf16 and fp16 weights: bitwise equal to passing their exact fp32 values;
   * fp16 activations: rounding-aware bounds against the exact (f64) forms,
     whose own pins are finite differences and closed forms; exact-arithmetic
-    inputs; overflow to infinity.
+    inputs; overflow to infinity;
+  * the gated norm and the fused add-norm in these types: with (bf16, fp32)
+    bitwise equal to their bf16 functions; 16-bit weights equal to their fp32
+    values; fp16 within rounding of the exact forms; the cast convention's
+    two intermediate roundings go to the activations' type (a sigmoid gate at
+    z = 0 is exactly 1/2, which exposes them); binary16 overflow of the
+    stored residual sum.
 """
 from __future__ import annotations
 
@@ -158,3 +164,197 @@ def test_f16_exact_arithmetic_and_overflow():
     big = np.full(D, 70000.0, np.float32)
     y, _ = oracle.fwd_dt(_f16_bits(x), big, False, 0.0, oracle.F16)
     assert np.all(np.isinf(_f16_val(y))) and np.array_equal(np.sign(_f16_val(y)), np.sign(x))
+
+
+# ---- gated norm and fused add-norm in other storage types -----------------------
+
+ACTS = [oracle.SILU, oracle.SIGMOID]
+
+
+def _f16_problem(seed, T, D, scales=(1.0, 1.0, 1.0)):
+    """fp16 patterns of N(0, s^2) draws for three operands."""
+    return tuple(_f16_bits(synth.normal_f32(seed, 1 + i, T * D).reshape(T, D) * s)
+                 for i, s in enumerate(scales))
+
+
+@pytest.mark.parametrize("zc", [False, True])
+@pytest.mark.parametrize("act", ACTS)
+def test_gated_dt_forms_equal_the_bf16_functions(zc, act):
+    p = wl.tiny(zc, T=21, D=320, seed=1610, with_gate=True)
+    for conv in (oracle.FP32_WEIGHT, oracle.CAST_INPUT):
+        o, r = oracle.gated_fwd_dt(p.x, p.z, p.gamma, zc, p.eps, act, conv)
+        o0, r0 = oracle.gated_fwd_ex(p.x, p.z, p.gamma, zc, p.eps, act, conv)
+        assert np.array_equal(o, o0) and np.array_equal(r.view(np.uint32), r0.view(np.uint32))
+    dx, dz, dg = oracle.gated_bwd_dt(p.g, p.x, p.z, r, p.gamma, zc, act)
+    dx0, dz0, dg0 = oracle.gated_bwd(p.g, p.x, p.z, r, p.gamma, zc, act)
+    assert np.array_equal(dx, dx0) and np.array_equal(dz, dz0)
+    assert np.array_equal(dg.view(np.uint32), dg0.view(np.uint32))
+
+
+@pytest.mark.parametrize("zc", [False, True])
+@pytest.mark.parametrize("with_gro", [False, True])
+def test_add_dt_forms_equal_the_bf16_functions(zc, with_gro):
+    T, D, seed = 19, 264, 1611
+    x = synth.normal_bf16(seed, 1, T, D)
+    res = synth.normal_bf16(seed, 4, T, D, scale=2.0)
+    g = synth.normal_bf16(seed, 2, T, D)
+    gro = synth.normal_bf16(seed, 5, T, D, scale=0.5) if with_gro else None
+    gamma = wl.gamma_for(seed, D, zc)
+    y, ro, r = oracle.add_fwd_dt(x, res, gamma, zc)
+    y0, ro0, r0 = oracle.add_fwd(x, res, gamma, zc)
+    assert np.array_equal(y, y0) and np.array_equal(ro, ro0)
+    assert np.array_equal(r.view(np.uint32), r0.view(np.uint32))
+    dh, dg = oracle.add_bwd_dt(g, x, res, r, gamma, zc, g_rout=gro)
+    dh0, dg0 = oracle.add_bwd(g, x, res, r, gamma, zc, g_rout=gro)
+    assert np.array_equal(dh, dh0) and np.array_equal(dg.view(np.uint32), dg0.view(np.uint32))
+
+
+def _weights16(w32, weight_dtype):
+    if weight_dtype == oracle.BF16:
+        bits = torch.from_numpy(w32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        val = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    else:
+        bits = _f16_bits(w32)
+        val = bits.view(np.float16).astype(np.float32)
+    return bits, val
+
+
+@pytest.mark.parametrize("weight_dtype", [oracle.BF16, oracle.F16])
+@pytest.mark.parametrize("act_dtype", [oracle.BF16, oracle.F16])
+@pytest.mark.parametrize("zc", [False, True])
+def test_gated_add_16bit_weights_equal_their_fp32_values(weight_dtype, act_dtype, zc):
+    T, D, seed = 12, 256, 1612
+    if act_dtype == oracle.F16:
+        x, z, g = _f16_problem(seed, T, D, (1.0, 3.0, 1.0))
+    else:
+        x, z, g = (synth.normal_bf16(seed, 1 + i, T, D, scale=s)
+                   for i, s in enumerate((1.0, 3.0, 1.0)))
+    wbits, wval = _weights16(wl.gamma_for(seed, D, zc), weight_dtype)
+    F32 = oracle.F32
+    for act in ACTS:
+        for conv in (oracle.FP32_WEIGHT, oracle.CAST_INPUT):
+            o, r = oracle.gated_fwd_dt(x, z, wbits, zc, 1e-6, act, conv, act_dtype, weight_dtype)
+            o0, r0 = oracle.gated_fwd_dt(x, z, wval, zc, 1e-6, act, conv, act_dtype, F32)
+            assert np.array_equal(o, o0) and np.array_equal(r, r0)
+        b = oracle.gated_bwd_dt(g, x, z, r, wbits, zc, act, act_dtype, weight_dtype)
+        b0 = oracle.gated_bwd_dt(g, x, z, r, wval, zc, act, act_dtype, F32)
+        assert all(np.array_equal(u, v) for u, v in zip(b, b0))
+    y, ro, r = oracle.add_fwd_dt(x, z, wbits, zc, 1e-6, act_dtype, weight_dtype)
+    y0, ro0, r0 = oracle.add_fwd_dt(x, z, wval, zc, 1e-6, act_dtype, F32)
+    assert np.array_equal(y, y0) and np.array_equal(ro, ro0) and np.array_equal(r, r0)
+    dh, dg = oracle.add_bwd_dt(g, x, z, r, wbits, zc, g_rout=g, act_dtype=act_dtype,
+                               weight_dtype=weight_dtype)
+    dh0, dg0 = oracle.add_bwd_dt(g, x, z, r, wval, zc, g_rout=g, act_dtype=act_dtype,
+                                 weight_dtype=F32)
+    assert np.array_equal(dh, dh0) and np.array_equal(dg, dg0)
+
+
+def _gate(act, z):
+    import scipy.special
+    s = scipy.special.expit(z)
+    return z * s if act == oracle.SILU else s
+
+
+@pytest.mark.parametrize("T,D,seed", [(16, 128, 1613), (5, 4096, 1614), (7, 200, 1615)])
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("zc", [False, True])
+def test_f16_gated_within_rounding_of_exact(T, D, seed, act, zc):
+    eps = 1e-6
+    x, z, g = _f16_problem(seed, T, D, (1.0, 3.0, 1.0))
+    gamma = wl.gamma_for(seed, D, zc)
+    out, r = oracle.gated_fwd_dt(x, z, gamma, zc, eps, act, act_dtype=oracle.F16)
+    xd, zd, gd = _f16_val(x), _f16_val(z), _f16_val(g)
+    ex = oracle.gated_fwd_ex_f64(xd, zd, gamma, zc, eps, act)
+    rd = oracle.fwd_f64(xd, gamma, zc, eps)[1]
+    assert np.all(np.abs(r - rd) <= 2.6 * U32 * rd)
+    # x*r (r 2.6u + u), *w (u), the gate in fp32 (u), *a (u)
+    assert _f16_rounding_consistent(out, ex, 6.6 * U32 * np.abs(ex)).all()
+    dx, dz, dg = oracle.gated_bwd_dt(g, x, z, r, gamma, zc, act, act_dtype=oracle.F16)
+    edx, edz, edg = oracle.gated_bwd_f64(gd, xd, zd, gamma, zc, eps, act)
+    w = gamma.astype(np.float64) + (1.0 if zc else 0.0)
+    rr = rd[:, None]
+    assert _f16_rounding_consistent(dz, edz, 7.6 * U32 * np.abs(edz)).all()
+    gn = gd * _gate(act, zd)
+    s = (gn * w * xd).sum(axis=1, keepdims=True)
+    s_abs = np.abs(gn * w * xd).sum(axis=1, keepdims=True)
+    err = (6.6 * U32 * np.abs(gn * w) * rr
+           + np.abs(xd) * rr ** 3 / D * (4.1 * U32 * s_abs + 13.0 * U32 * np.abs(s))
+           + 3.1 * U32 * np.abs(edx))
+    assert _f16_rounding_consistent(dx, edx, err).all()
+    bound = 5.6 * U32 * (np.abs(gn * xd) * rr).sum(axis=0) + U32 * np.abs(edg)
+    assert np.all(np.abs(dg - edg) <= bound)
+
+
+@pytest.mark.parametrize("act_dtype", [oracle.BF16, oracle.F16])
+def test_cast_convention_rounds_to_the_activation_type(act_dtype):
+    """A sigmoid gate at z = 0 is exactly 1/2. The cast convention then gives
+    1/2 * q(q(q(x*r) * w)) with q the rounding to the activations' type and
+    q(x*r) the plain forward with unit weight; the fp32 convention gives
+    1/2 * q(x*r*w), the plain forward. Inputs keep every output normal, so
+    halving is exact."""
+    T, D, seed = 12, 256, 1616
+    rng = np.random.default_rng(seed)
+    mag = rng.uniform(0.5, 2.0, (T, D)) * rng.choice([-1.0, 1.0], (T, D))
+    gamma = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    if act_dtype == oracle.F16:
+        x = _f16_bits(mag)
+        val, enc = (lambda b: _f16_val(b)), (lambda v: _f16_bits(v))
+    else:
+        x = torch.from_numpy(mag.astype(np.float32)).bfloat16().view(torch.int16).numpy() \
+            .view(np.uint16)
+        val = lambda b: torch.from_numpy(np.asarray(b).view(np.int16)).view(torch.bfloat16) \
+            .double().numpy()
+        enc = lambda v: torch.from_numpy(np.asarray(v, np.float32)).bfloat16() \
+            .view(torch.int16).numpy().view(np.uint16)
+    z0 = np.zeros_like(x)
+    cast, _ = oracle.gated_fwd_dt(x, z0, gamma, False, 1e-6, oracle.SIGMOID, oracle.CAST_INPUT,
+                                  act_dtype)
+    fp32, _ = oracle.gated_fwd_dt(x, z0, gamma, False, 1e-6, oracle.SIGMOID, oracle.FP32_WEIGHT,
+                                  act_dtype)
+    n, _ = oracle.fwd_dt(x, np.ones(D, np.float32), False, 1e-6, act_dtype)
+    nw = enc((val(n).astype(np.float32) * gamma).astype(np.float32))
+    assert np.array_equal(val(cast), 0.5 * val(nw))
+    y, _ = oracle.fwd_dt(x, gamma, False, 1e-6, act_dtype)
+    assert np.array_equal(val(fp32), 0.5 * val(y))
+    assert (cast != fp32).any()
+
+
+@pytest.mark.parametrize("T,D,seed", [(16, 128, 1617), (7, 4096, 1618), (5, 200, 1619)])
+@pytest.mark.parametrize("zc", [False, True])
+@pytest.mark.parametrize("with_gro", [False, True])
+def test_f16_add_within_rounding_of_exact(T, D, seed, zc, with_gro):
+    eps = 1e-6
+    x, res, g = _f16_problem(seed, T, D, (1.0, 2.0, 1.0))
+    gro = _f16_bits(synth.normal_f32(seed, 5, T * D).reshape(T, D) * 0.5) if with_gro else None
+    gamma = wl.gamma_for(seed, D, zc)
+    y, rout, r = oracle.add_fwd_dt(x, res, gamma, zc, eps, oracle.F16)
+    xd, resd, gd = _f16_val(x), _f16_val(res), _f16_val(g)
+    grod = None if gro is None else _f16_val(gro)
+    yd, hd, rd = oracle.add_fwd_f64(xd, resd, gamma, zc, eps)
+    assert np.all(np.abs(r - rd) <= 3.0 * U32 * rd)
+    assert _f16_rounding_consistent(rout, hd, U32 * np.abs(hd)).all()
+    assert _f16_rounding_consistent(y, yd, 6.1 * U32 * np.abs(yd)).all()
+    dh, dg = oracle.add_bwd_dt(g, x, res, r, gamma, zc, g_rout=gro, act_dtype=oracle.F16)
+    dhd, dgd = oracle.add_bwd_f64(gd, xd, resd, gamma, zc, eps, g_rout=grod)
+    w = gamma.astype(np.float64) + (1.0 if zc else 0.0)
+    rr = rd[:, None]
+    s = (gd * w * hd).sum(axis=1, keepdims=True)
+    s_abs = np.abs(gd * w * hd).sum(axis=1, keepdims=True)
+    err = (7.6 * U32 * np.abs(gd * w) * rr
+           + np.abs(hd) * rr ** 3 / D * (3.1 * U32 * s_abs + 16.0 * U32 * np.abs(s))
+           + 3.1 * U32 * np.abs(dhd))
+    assert _f16_rounding_consistent(dh, dhd, err).all()
+    bound = 6.6 * U32 * (np.abs(gd * hd) * rr).sum(axis=0) + U32 * np.abs(dgd)
+    assert np.all(np.abs(dg - dgd) <= bound)
+
+
+def test_f16_add_residual_out_overflows_to_infinity():
+    """h = x + residual is formed in fp32; past binary16's range the stored
+    residual_out is infinite while y, normalised, stays finite."""
+    D = 64
+    x = _f16_bits(np.full((1, D), 60000.0))
+    res = _f16_bits(np.full((1, D), 30000.0))
+    y, ro, r = oracle.add_fwd_dt(x, res, np.ones(D, np.float32), False, 0.0, oracle.F16)
+    assert np.all(np.isinf(_f16_val(ro)))
+    assert np.array_equal(_f16_val(y), np.ones((1, D)))
+    assert abs(float(r[0]) * 90000.0 - 1.0) <= 3.0 * U32
