@@ -44,8 +44,7 @@
  *
  * Layout. Row-major [T, D] with a row stride ld >= D (in elements), last axis
  * contiguous, D <= ld <= 2^24 (RMSN_MAX_LD) with T * ld <= 2^60, and
- * 1 <= D <= 32768 (RMSN_MAX_D) for every entry point except
- * rmsnorm_gated_bwd, which needs D a multiple of 8. Each lane of a row owns
+ * 1 <= D <= 32768 (RMSN_MAX_D) for every entry point. Each lane of a row owns
  * groups of 8 consecutive elements; every reduction tree is a function of
  * ceil(D/8) alone. When D is a multiple of 8, rows move as aligned 16-byte
  * vectors: every bf16 / fp16 base pointer and ld * 2 bytes must be multiples
@@ -79,7 +78,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 12
+#define RMSN_ABI_VERSION 13
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -87,8 +86,7 @@ typedef enum rmsn_status {
   RMSN_OK = 0,
   RMSN_ERR_NULL = 1,           /* a required pointer is NULL */
   RMSN_ERR_SHAPE = 2,          /* T < 0, D <= 0, ld < D or ld > RMSN_MAX_LD */
-  RMSN_ERR_UNSUPPORTED_D = 3,  /* D > RMSN_MAX_D; D not a multiple of 8 for
-                                  rmsnorm_gated_bwd; GEMM K not a positive
+  RMSN_ERR_UNSUPPORTED_D = 3,  /* D > RMSN_MAX_D; GEMM K not a positive
                                   multiple of 32 */
   RMSN_ERR_MISALIGNED = 4,     /* a pointer or ld*2 below the alignment its
                                   operand needs (see Layout) */

@@ -58,11 +58,10 @@ bool any_alias(const Range (&outs)[NO], const Range (&ins)[NI]) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Row length: 1..32768, a multiple of 8 for the gated backward (`any_D`
-// false).
-rmsn_status check_D(int64_t D, bool any_D = true) {
+// Row length: 1..32768.
+rmsn_status check_D(int64_t D) {
   if (D <= 0) return RMSN_ERR_SHAPE;
-  if (D > kMaxD || (!any_D && D % 8 != 0)) return RMSN_ERR_UNSUPPORTED_D;
+  if (D > kMaxD) return RMSN_ERR_UNSUPPORTED_D;
   return RMSN_OK;
 }
 
@@ -197,7 +196,7 @@ rmsn_status check_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_
                       Types ty = Types{}) {
   if (bad_types(ty)) return RMSN_ERR_MODE;
   if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D, !gated));
+  RMSN_TRY(check_D(D));
   RMSN_TRY(check_mat(g, ld_g, T, D, true));
   RMSN_TRY(check_mat(x, ld_x, T, D, true));
   if (add) RMSN_TRY(check_mat(rin, ld_rin, T, D, true));
@@ -259,8 +258,8 @@ const char* rmsnorm_status_string(int status) {
     case RMSN_ERR_NULL: return "RMSN_ERR_NULL: a required pointer is NULL";
     case RMSN_ERR_SHAPE: return "RMSN_ERR_SHAPE: T < 0, D <= 0, ld < D or ld > 2^24";
     case RMSN_ERR_UNSUPPORTED_D:
-      return "RMSN_ERR_UNSUPPORTED_D: D must be in [1, 32768] (a multiple of 8 for the gated "
-             "backward); the GEMM's K a positive multiple of 32";
+      return "RMSN_ERR_UNSUPPORTED_D: D must be in [1, 32768]; the GEMM's K a positive multiple "
+             "of 32";
     case RMSN_ERR_MISALIGNED: return "RMSN_ERR_MISALIGNED: pointers and row strides must be 16-byte aligned";
     case RMSN_ERR_EPS: return "RMSN_ERR_EPS: eps must be finite and >= 0";
     case RMSN_ERR_ALIASING: return "RMSN_ERR_ALIASING: an output overlaps an input or another output";

@@ -7,6 +7,7 @@
 namespace rmsn {
 
 int launch_bwd_rows_gated(const BwdArgs& a, void* stream) {
+  if (a.D % 8 != 0) return launch_bwd_rows_gated_elem(a, stream);
   const RowGeom g = bwd_geom(a.D);
   bwd_detail::RowsLaunch f = nullptr;
   if (a.act == kGateSilu) f = bwd_detail::pick<kBwdGatedSilu>(g);

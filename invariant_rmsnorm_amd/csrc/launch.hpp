@@ -79,14 +79,15 @@ int launch_fwd_add(const FwdArgs& a, void* stream);    // a.rin != nullptr
 int launch_fwd_f16(const FwdArgs& a, void* stream);
 int launch_fwd_elem(const FwdArgs& a, void* stream);   // D % 8 != 0 (plain, residual copy)
 int launch_fwd_gated_elem(const FwdArgs& a, void* stream);  // D % 8 != 0, gated
-int launch_fwd_add_elem(const FwdArgs& a, void* stream);    // D % 8 != 0, fused add    // a.dt == fp16 (plain, residual copy)
+int launch_fwd_add_elem(const FwdArgs& a, void* stream);    // D % 8 != 0, fused add
 int launch_bwd_rows(const BwdArgs& a, void* stream);
 int launch_bwd_rows_gated(const BwdArgs& a, void* stream);  // a.z != nullptr
+int launch_bwd_rows_gated_elem(const BwdArgs& a, void* stream);  // a.z != nullptr, D % 8 != 0
 int launch_bwd_rows_add(const BwdArgs& a, void* stream);    // a.rin != nullptr
 int launch_bwd_rows_f16(const BwdArgs& a, void* stream);
 int launch_bwd_rows_elem(const BwdArgs& a, void* stream);      // D % 8 != 0 (plain, gres)
 int launch_bwd_rows_elem_f16(const BwdArgs& a, void* stream);  // the same, fp16 activations
-int launch_bwd_rows_add_elem(const BwdArgs& a, void* stream);    // D % 8 != 0, fused add    // a.dt == fp16 (plain, gres)
+int launch_bwd_rows_add_elem(const BwdArgs& a, void* stream);    // D % 8 != 0, fused add
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
 int launch_gemm(const GemmArgs& a, void* stream);
 // The output tile launch_gemm uses for an M x N product (host only).

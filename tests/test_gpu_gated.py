@@ -32,8 +32,7 @@ ROUNDINGS = [(irn.RMSN_GATED_ROUND_FP32, oracle.FP32_WEIGHT),
              (irn.RMSN_GATED_ROUND_CAST, oracle.CAST_INPUT)]
 WIDTHS = [8, 64, 96, 128, 136, 1024, 2560, 4096, 4104, 5632, 6144, 8192, 8200, 16384, 18440,
           32768]
-# not multiples of 8: element-wise rows (the forward; the gated backward
-# rejects them)
+# not multiples of 8: rows of any alignment
 ODD_WIDTHS = [5, 13, 100, 1001, 4100, 12290, 20003]
 
 
@@ -243,7 +242,38 @@ def test_gated_repeat_runs_bitwise(gpu):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-def test_gated_backward_rejects_odd_rows(gpu):
-    p = wl.tiny(False, T=4, D=100, seed=9500, with_gate=True)
-    with pytest.raises(irn.RmsnormError, match="UNSUPPORTED_D"):
-        _gpu_bwd(p, irn.RMSN_GATE_SILU)
+@pytest.mark.parametrize("act,act_o", ACTS)
+@pytest.mark.parametrize("D", ODD_WIDTHS)
+def test_gated_backward_odd_widths(gpu, D, act, act_o):
+    """Rows not a multiple of 8 (any alignment): dx, dz and dgamma against
+    the oracle, over a few steps and a ragged tail."""
+    zc = D % 2 == 1
+    p = wl.tiny(zc, T=_rows_for(D), D=D, seed=9650 + D, with_gate=True)
+    _check_bwd(p, act, act_o, (D, act))
+
+
+@pytest.mark.parametrize("D", [100, 4100])
+def test_gated_backward_odd_rows_strided(gpu, D):
+    """Rows of D not a multiple of 8 in wider buffers at an odd element
+    offset: the same bits as the contiguous call, nothing written outside."""
+    p = wl.tiny(False, T=333, D=D, seed=9660 + D, with_gate=True)
+    dx, dz, dg = _gpu_bwd(p, irn.RMSN_GATE_SILU)
+    ld = D + 3
+
+    def wide(bits):
+        buf = torch.zeros((p.T, ld), dtype=torch.bfloat16, device="cuda")
+        buf[:, 1:1 + D] = dev_bf16(bits)
+        return buf[:, 1:1 + D]
+
+    x, g, z = wide(p.x), wide(p.g), wide(p.z)
+    gamma = dev_f32(p.gamma)
+    _, rstd = irn.rmsnorm_fwd(x, gamma, False, p.eps)
+    dxw = torch.full((p.T, ld), 5.0, dtype=torch.bfloat16, device="cuda")
+    dzw = torch.full((p.T, ld), 5.0, dtype=torch.bfloat16, device="cuda")
+    _, _, dg2 = irn.rmsnorm_gated_bwd(g, x, z, rstd, gamma, activation=irn.RMSN_GATE_SILU,
+                                      dx=dxw[:, 1:1 + D], dz=dzw[:, 1:1 + D])
+    torch.cuda.synchronize()
+    assert torch.equal(dxw[:, 1:1 + D], dx) and torch.equal(dzw[:, 1:1 + D], dz)
+    assert torch.equal(dg2, dg)
+    assert torch.all(dxw[:, 0].float() == 5.0) and torch.all(dxw[:, 1 + D:].float() == 5.0)
+    assert torch.all(dzw[:, 0].float() == 5.0) and torch.all(dzw[:, 1 + D:].float() == 5.0)
