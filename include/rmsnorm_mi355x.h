@@ -23,7 +23,9 @@
  *    unsupported input is rejected, never sent silently down another path.
  *
  * Precision contract. x, y, dx, g, z, dz and residual tensors are bf16,
- * passed as raw uint16_t bits. gamma, rstd and dgamma are fp32. Per row:
+ * passed as raw uint16_t bits (bf16 or fp16 through the _dt entry points).
+ * gamma, rstd and dgamma are fp32 (gamma also bf16 / fp16 through _dt). Per
+ * row:
  *   ss   = sum_j x_j^2: fp32 squares added in fp64 along a fixed reduction
  *          tree chosen by D alone, rounded to fp32 once
  *   r    = 1/sqrt(ss / D + eps): fp32 division and addition, the reciprocal
@@ -78,7 +80,7 @@
 extern "C" {
 #endif
 
-#define RMSN_ABI_VERSION 13
+#define RMSN_ABI_VERSION 14
 #define RMSN_MAX_D 32768
 #define RMSN_MAX_LD (1 << 24)
 
@@ -375,6 +377,58 @@ rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g,
                                  const uint16_t* g_residual_out, int64_t ld_gro,
                                  uint16_t* dh, int64_t ld_dh, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * The gated norm and the fused add-norm for other storage types, as
+ * rmsnorm_fwd_dt / rmsnorm_bwd_dt are for the plain norm. act_dtype
+ * (RMSN_DTYPE_BF16 or RMSN_DTYPE_F16) is the type of every activation
+ * operand: x, z, residual, g, g_residual_out and the outputs out, y,
+ * residual_out, dx, dz and dh; weight_dtype (RMSN_DTYPE_F32, _BF16 or _F16)
+ * that of gamma. Each widens to fp32 exactly and the arithmetic is that of
+ * rmsnorm_gated_fwd_ex, rmsnorm_gated_bwd, rmsnorm_add_fwd and
+ * rmsnorm_add_bwd, with every rounding of a result to bf16 there made to
+ * act_dtype here (fp16: nearest even, subnormals kept, overflow to
+ * infinity). That includes the two intermediate casts of the gated
+ * RMSN_GATED_ROUND_CAST convention, which round to the input dtype
+ * (RL-Kernel PR "C1: zero-centred RMSNorm references and CUDA kernel",
+ * gated-norm conventions; its contract checks fp16 beside bf16). In the
+ * fused add, h = fp32(x) + fp32(residual) and residual_out = act_dtype(h).
+ * rstd and dgamma stay fp32; gamma must be 16-byte aligned whatever its
+ * type. Unknown types return RMSN_ERR_MODE; arguments, aliasing rules,
+ * workspace and errors otherwise as the bf16 entry points named above.
+ */
+rmsn_status rmsnorm_gated_fwd_dt(int act_dtype, int weight_dtype, const void* x,
+                                 int64_t ld_x, const void* z, int64_t ld_z,
+                                 const void* gamma, int zero_centered_gamma,
+                                 float eps, int64_t T, int64_t D, int activation,
+                                 int rounding, void* out, int64_t ld_out,
+                                 float* rstd, void* stream);
+
+rmsn_status rmsnorm_gated_bwd_dt(int act_dtype, int weight_dtype, const void* g,
+                                 int64_t ld_g, const void* x, int64_t ld_x,
+                                 const void* z, int64_t ld_z, const float* rstd,
+                                 const void* gamma, int zero_centered_gamma,
+                                 int64_t T, int64_t D, int activation, void* dx,
+                                 int64_t ld_dx, void* dz, int64_t ld_dz,
+                                 float* dgamma, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+rmsn_status rmsnorm_add_fwd_dt(int act_dtype, int weight_dtype, const void* x,
+                               int64_t ld_x, const void* residual, int64_t ld_res,
+                               const void* gamma, int zero_centered_gamma,
+                               float eps, int64_t T, int64_t D, void* y,
+                               int64_t ld_y, void* residual_out, int64_t ld_rout,
+                               float* rstd, void* stream);
+
+rmsn_status rmsnorm_add_bwd_dt(int act_dtype, int weight_dtype, const void* g,
+                               int64_t ld_g, const void* x, int64_t ld_x,
+                               const void* residual, int64_t ld_res,
+                               const float* rstd, const void* gamma,
+                               int zero_centered_gamma, int64_t T, int64_t D,
+                               const void* g_residual_out, int64_t ld_gro,
+                               void* dh, int64_t ld_dh, float* dgamma,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * Batch-invariant BF16 GEMM, Y = X @ W.T (TransformerEngine issue "Expose

@@ -47,7 +47,8 @@ EXPORTED = (
     "rmsnorm_bwd_partials_layout", "rmsnorm_bwd", "rmsnorm_bwd_rows", "rmsnorm_bwd_finish",
     "rmsnorm_gated_bwd", "rmsnorm_add_fwd", "rmsnorm_add_bwd", "rmsnorm_add_bwd_rows",
     "rmsnorm_fwd_dt", "rmsnorm_bwd_dt", "bigemm_bf16_xwt", "bigemm_bf16_tile",
-    "rmsnorm_dgamma_chunk_rows", "rmsnorm_bwd_noalloc",
+    "rmsnorm_dgamma_chunk_rows", "rmsnorm_bwd_noalloc", "rmsnorm_gated_fwd_dt",
+    "rmsnorm_gated_bwd_dt", "rmsnorm_add_fwd_dt", "rmsnorm_add_bwd_dt",
 )
 
 
@@ -93,6 +94,14 @@ def load():
         "bigemm_bf16_tile": ([i64, i64, vp, vp], i),
         "rmsnorm_dgamma_chunk_rows": ([i64], i),
         "rmsnorm_bwd_noalloc": ([vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp, i64, vp, vp], i),
+        "rmsnorm_gated_fwd_dt": ([i, i, vp, i64, vp, i64, vp, i, f, i64, i64, i, i, vp, i64, vp,
+                                  vp], i),
+        "rmsnorm_gated_bwd_dt": ([i, i, vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, i, vp, i64,
+                                  vp, i64, vp, vp, sz, vp], i),
+        "rmsnorm_add_fwd_dt": ([i, i, vp, i64, vp, i64, vp, i, f, i64, i64, vp, i64, vp, i64, vp,
+                                vp], i),
+        "rmsnorm_add_bwd_dt": ([i, i, vp, i64, vp, i64, vp, i64, vp, vp, i, i64, i64, vp, i64, vp,
+                                i64, vp, vp, sz, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -547,6 +556,113 @@ def rmsnorm_bwd_dt(g, x, rstd, gamma, zero_centered_gamma=False, *, g_residual=N
         _ptr(gamma), int(zero_centered_gamma), T, D, _ptr(g_residual), _ld(g_residual),
         _ptr(dx), _ld(dx), _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
     return dx, dgamma
+
+
+def rmsnorm_gated_fwd_dt(x, z, gamma, zero_centered_gamma=False, eps=1e-6, *,
+                         activation=RMSN_GATE_SILU, rounding=RMSN_GATED_ROUND_FP32, out=None,
+                         rstd=None, want_rstd=False, stream=None):
+    """rmsnorm_gated_fwd_ex for bf16 or fp16 x and z (out of the same type;
+    the cast convention rounds to that type) and fp32, bf16 or fp16 gamma;
+    returns (out, rstd or None)."""
+    T, D = _rows(x, "x", ACT_DTYPES)
+    _arg(z, "z", x.dtype, (T, D))
+    _arg(gamma, "gamma", WEIGHT_DTYPES, (D,))
+    _arg(out, "out", x.dtype, (T, D), required=False)
+    _arg(rstd, "rstd", F32, (T,), required=False)
+    _same_device(("x", x), ("z", z), ("gamma", gamma), ("out", out), ("rstd", rstd))
+    out = _new((T, D), x.dtype, x) if out is None else out
+    if rstd is None and want_rstd:
+        rstd = _new(T, F32, x)
+    _check("rmsnorm_gated_fwd_dt", load().rmsnorm_gated_fwd_dt(
+        _DTYPES[x.dtype], _DTYPES[gamma.dtype], _ptr(x), _ld(x), _ptr(z), _ld(z), _ptr(gamma),
+        int(zero_centered_gamma), eps, T, D, int(activation), int(rounding), _ptr(out), _ld(out),
+        _ptr(rstd), _stream(x, stream)))
+    return out, rstd
+
+
+def rmsnorm_gated_bwd_dt(g, x, z, rstd, gamma, zero_centered_gamma=False, *,
+                         activation=RMSN_GATE_SILU, dx=None, dz=None, dgamma=None, want_dx=True,
+                         want_dz=True, want_dgamma=True, workspace=None, stream=None):
+    """rmsnorm_gated_bwd for bf16 or fp16 activations and fp32, bf16 or fp16
+    gamma; returns (dx or None, dz or None, dgamma fp32 or None)."""
+    T, D = _rows(x, "x", ACT_DTYPES)
+    _arg(g, "g", x.dtype, (T, D))
+    _arg(z, "z", x.dtype, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", WEIGHT_DTYPES, (D,))
+    _arg(dx, "dx", x.dtype, (T, D), required=False)
+    _arg(dz, "dz", x.dtype, (T, D), required=False)
+    _arg(dgamma, "dgamma", F32, (D,), required=False)
+    _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("z", z), ("rstd", rstd), ("gamma", gamma), ("dx", dx),
+                 ("dz", dz), ("dgamma", dgamma), ("workspace", workspace))
+    if dx is None and want_dx:
+        dx = _new((T, D), x.dtype, x)
+    if dz is None and want_dz:
+        dz = _new((T, D), x.dtype, x)
+    if dgamma is None and want_dgamma:
+        dgamma = _new(D, F32, x)
+    ws, nbytes = _dgamma_workspace(dgamma, workspace, T, D, x)
+    _check("rmsnorm_gated_bwd_dt", load().rmsnorm_gated_bwd_dt(
+        _DTYPES[x.dtype], _DTYPES[gamma.dtype], _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(z), _ld(z),
+        _ptr(rstd), _ptr(gamma), int(zero_centered_gamma), T, D, int(activation), _ptr(dx),
+        _ld(dx), _ptr(dz), _ld(dz), _ptr(dgamma), _ptr(ws), nbytes, _stream(x, stream)))
+    return dx, dz, dgamma
+
+
+def rmsnorm_add_fwd_dt(x, residual, gamma, zero_centered_gamma=False, eps=1e-6, *, y=None,
+                       residual_out=None, rstd=None, want_rstd=True, stream=None):
+    """rmsnorm_add_fwd for bf16 or fp16 x and residual (y and residual_out of
+    the same type) and fp32, bf16 or fp16 gamma; returns (y, residual_out,
+    rstd or None). ``y=x`` and ``residual_out=residual`` run in place."""
+    T, D = _rows(x, "x", ACT_DTYPES)
+    _arg(residual, "residual", x.dtype, (T, D))
+    _arg(gamma, "gamma", WEIGHT_DTYPES, (D,))
+    _arg(y, "y", x.dtype, (T, D), required=False)
+    _arg(residual_out, "residual_out", x.dtype, (T, D), required=False)
+    _arg(rstd, "rstd", F32, (T,), required=False)
+    _same_device(("x", x), ("residual", residual), ("gamma", gamma), ("y", y),
+                 ("residual_out", residual_out), ("rstd", rstd))
+    y = _new((T, D), x.dtype, x) if y is None else y
+    if residual_out is None:
+        residual_out = _new((T, D), x.dtype, x)
+    if rstd is None and want_rstd:
+        rstd = _new(T, F32, x)
+    _check("rmsnorm_add_fwd_dt", load().rmsnorm_add_fwd_dt(
+        _DTYPES[x.dtype], _DTYPES[gamma.dtype], _ptr(x), _ld(x), _ptr(residual), _ld(residual),
+        _ptr(gamma), int(zero_centered_gamma), eps, T, D, _ptr(y), _ld(y), _ptr(residual_out),
+        _ld(residual_out), _ptr(rstd), _stream(x, stream)))
+    return y, residual_out, rstd
+
+
+def rmsnorm_add_bwd_dt(g, x, residual, rstd, gamma, zero_centered_gamma=False, *,
+                       g_residual_out=None, dh=None, dgamma=None, want_dh=True, want_dgamma=True,
+                       workspace=None, stream=None):
+    """rmsnorm_add_bwd for bf16 or fp16 activations and fp32, bf16 or fp16
+    gamma; returns (dh or None, dgamma fp32 or None)."""
+    T, D = _rows(x, "x", ACT_DTYPES)
+    _arg(g, "g", x.dtype, (T, D))
+    _arg(residual, "residual", x.dtype, (T, D))
+    _arg(rstd, "rstd", F32, (T,))
+    _arg(gamma, "gamma", WEIGHT_DTYPES, (D,))
+    _arg(g_residual_out, "g_residual_out", x.dtype, (T, D), required=False)
+    _arg(dh, "dh", x.dtype, (T, D), required=False)
+    _arg(dgamma, "dgamma", F32, (D,), required=False)
+    _workspace(workspace)
+    _same_device(("x", x), ("g", g), ("residual", residual), ("rstd", rstd), ("gamma", gamma),
+                 ("g_residual_out", g_residual_out), ("dh", dh), ("dgamma", dgamma),
+                 ("workspace", workspace))
+    if dh is None and want_dh:
+        dh = _new((T, D), x.dtype, x)
+    if dgamma is None and want_dgamma:
+        dgamma = _new(D, F32, x)
+    ws, nbytes = _dgamma_workspace(dgamma, workspace, T, D, x)
+    _check("rmsnorm_add_bwd_dt", load().rmsnorm_add_bwd_dt(
+        _DTYPES[x.dtype], _DTYPES[gamma.dtype], _ptr(g), _ld(g), _ptr(x), _ld(x), _ptr(residual),
+        _ld(residual), _ptr(rstd), _ptr(gamma), int(zero_centered_gamma), T, D,
+        _ptr(g_residual_out), _ld(g_residual_out), _ptr(dh), _ld(dh), _ptr(dgamma), _ptr(ws),
+        nbytes, _stream(x, stream)))
+    return dh, dgamma
 
 
 def bigemm_bf16_xwt(x, w, *, y=None, stream=None):

@@ -25,6 +25,8 @@ HIP_FLAGS = [
 HIP_SOURCES = ["fwd.hip", "fwd_gated.hip", "fwd_add.hip", "fwd_f16.hip", "bwd.hip", "bwd_gated.hip",
                "bwd_add.hip", "bwd_f16.hip", "gemm.hip", "fwd_elem.hip", "bwd_elem.hip", "bwd_elem_f16.hip",
                "fwd_gated_elem.hip", "fwd_add_elem.hip", "bwd_add_elem.hip", "bwd_gated_elem.hip",
+               "fwd_gated_f16.hip", "fwd_gated_elem_f16.hip", "fwd_add_f16.hip", "bwd_gated_f16.hip",
+               "bwd_gated_elem_f16.hip", "bwd_add_f16.hip",
                "scratch.hip"]
 CXX_SOURCES = ["api.cpp"]
 

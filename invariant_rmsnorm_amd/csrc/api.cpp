@@ -158,10 +158,10 @@ rmsn_status fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* z, int64
 // only values it computed from elements it has already loaded at those
 // addresses, and rows do not overlap); any other overlap is rejected.
 bool add_fwd_alias(const uint16_t* x, int64_t ld_x, const uint16_t* rin, int64_t ld_rin,
-                   const float* gamma, int64_t T, int64_t D, const uint16_t* y, int64_t ld_y,
-                   const uint16_t* rout, int64_t ld_rout, const float* rstd) {
+                   const void* gamma, int64_t gamma_elem, int64_t T, int64_t D, const uint16_t* y,
+                   int64_t ld_y, const uint16_t* rout, int64_t ld_rout, const float* rstd) {
   const Range X = mat_range(x, T, ld_x, D, 2), RI = mat_range(rin, T, ld_rin, D, 2),
-              G = vec_range(gamma, D, 4), Y = mat_range(y, T, ld_y, D, 2),
+              G = vec_range(gamma, D, gamma_elem), Y = mat_range(y, T, ld_y, D, 2),
               RO = mat_range(rout, T, ld_rout, D, 2), RS = vec_range(rstd, T, 4);
   const bool y_in_place = y == x && ld_y == ld_x;
   const bool r_in_place = rout == rin && ld_rout == ld_rin;
@@ -246,6 +246,81 @@ rmsn_status finish_dgamma(void* workspace, int64_t T, int64_t D, float* dgamma, 
                                             static_cast<int>(D), dgamma, stream));
 }
 
+// The _dt entry points pass 16-bit activations as untyped pointers.
+const uint16_t* u16(const void* p) { return static_cast<const uint16_t*>(p); }
+uint16_t* u16(void* p) { return static_cast<uint16_t*>(p); }
+
+rmsn_status add_fwd_common(const uint16_t* x, int64_t ld_x, const uint16_t* residual,
+                           int64_t ld_res, const void* gamma, int zc, float eps, int64_t T,
+                           int64_t D, uint16_t* y, int64_t ld_y, uint16_t* residual_out,
+                           int64_t ld_rout, float* rstd, void* stream, Types ty) {
+  if (bad_types(ty)) return RMSN_ERR_MODE;
+  if (T < 0) return RMSN_ERR_SHAPE;
+  RMSN_TRY(check_D(D));
+  RMSN_TRY(check_mat(x, ld_x, T, D, true));
+  RMSN_TRY(check_mat(residual, ld_res, T, D, true));
+  RMSN_TRY(check_mat(y, ld_y, T, D, true));
+  RMSN_TRY(check_mat(residual_out, ld_rout, T, D, true));
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return RMSN_ERR_EPS;
+  if (T == 0) return RMSN_OK;
+  RMSN_TRY(check_ptr(gamma, 16, true));
+  RMSN_TRY(check_f32(rstd, 4, false));
+  if (add_fwd_alias(x, ld_x, residual, ld_res, gamma, weight_bytes(ty), T, D, y, ld_y,
+                    residual_out, ld_rout, rstd))
+    return RMSN_ERR_ALIASING;
+  const rmsn::FwdArgs a{x, ld_x, nullptr, 0, 0, 0, gamma, ty.wdt, ty.dt, zc != 0, eps, T,
+                        static_cast<int>(D), y, ld_y, residual_out, ld_rout, rstd, residual,
+                        ld_res, fwd_stream(T, D)};
+  return hip_status(rmsn::launch_fwd(a, stream));
+}
+
+rmsn_status gated_bwd_common(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                             const uint16_t* z, int64_t ld_z, const float* rstd,
+                             const void* gamma, int zc, int64_t T, int64_t D, int activation,
+                             uint16_t* dx, int64_t ld_dx, uint16_t* dz, int64_t ld_dz,
+                             float* dgamma, void* workspace, size_t ws_bytes, void* stream,
+                             Types ty) {
+  if (bad_types(ty) || bad_activation(activation)) return RMSN_ERR_MODE;
+  if (dx == nullptr && dz == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
+  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
+  const GateIO gate{z, ld_z, dz, ld_dz};
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, nullptr, 0, dx, ld_dx,
+                     dgamma != nullptr, dgamma, workspace, ws_bytes, true, gate, nullptr, 0,
+                     false, ty));
+  if (T > 0) {
+    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zc, T, D, nullptr, 0, dx,
+                                     ld_dx, dgamma != nullptr ? workspace : nullptr, gate,
+                                     activation, nullptr, 0, ty);
+    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
+  }
+  if (dgamma == nullptr) return RMSN_OK;
+  return finish_dgamma(workspace, T, D, dgamma, stream);
+}
+
+// The fused add-norm backward: rows kernel (dh and/or the partials), then
+// the finish kernel when dgamma is wanted.
+rmsn_status add_bwd_common(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
+                           const uint16_t* residual, int64_t ld_res, const float* rstd,
+                           const void* gamma, int zc, int64_t T, int64_t D,
+                           const uint16_t* g_rout, int64_t ld_gro, uint16_t* dh, int64_t ld_dh,
+                           float* dgamma, void* workspace, size_t ws_bytes, void* stream,
+                           Types ty) {
+  if (bad_types(ty)) return RMSN_ERR_MODE;
+  if (dh == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
+  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
+  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, g_rout, ld_gro, dh, ld_dh,
+                     dgamma != nullptr, dgamma, workspace, ws_bytes, false, GateIO{}, residual,
+                     ld_res, true, ty));
+  if (T > 0) {
+    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zc, T, D, g_rout, ld_gro, dh,
+                                     ld_dh, dgamma != nullptr ? workspace : nullptr, GateIO{}, 0,
+                                     residual, ld_res, ty);
+    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
+  }
+  if (dgamma == nullptr) return RMSN_OK;
+  return finish_dgamma(workspace, T, D, dgamma, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,7 +340,7 @@ const char* rmsnorm_status_string(int status) {
     case RMSN_ERR_ALIASING: return "RMSN_ERR_ALIASING: an output overlaps an input or another output";
     case RMSN_ERR_WORKSPACE: return "RMSN_ERR_WORKSPACE: workspace missing or too small";
     case RMSN_ERR_HIP: return "RMSN_ERR_HIP: the HIP runtime refused a kernel launch";
-    case RMSN_ERR_MODE: return "RMSN_ERR_MODE: unknown gate activation or rounding convention";
+    case RMSN_ERR_MODE: return "RMSN_ERR_MODE: unknown gate activation, rounding convention or storage type";
     default: return "unknown rmsn_status";
   }
 }
@@ -397,43 +472,17 @@ rmsn_status rmsnorm_gated_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x
                               int activation, uint16_t* dx, int64_t ld_dx, uint16_t* dz,
                               int64_t ld_dz, float* dgamma, void* workspace,
                               size_t workspace_bytes_, void* stream) {
-  if (bad_activation(activation)) return RMSN_ERR_MODE;
-  if (dx == nullptr && dz == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
-  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
-  const GateIO gate{z, ld_z, dz, ld_dz};
-  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, nullptr, 0, dx, ld_dx,
-                     dgamma != nullptr, dgamma, workspace, workspace_bytes_, true, gate));
-  if (T > 0) {
-    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
-                                     nullptr, 0, dx, ld_dx,
-                                     dgamma != nullptr ? workspace : nullptr, gate, activation);
-    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
-  }
-  if (dgamma == nullptr) return RMSN_OK;
-  return finish_dgamma(workspace, T, D, dgamma, stream);
+  return gated_bwd_common(g, ld_g, x, ld_x, z, ld_z, rstd, gamma, zero_centered_gamma, T, D,
+                          activation, dx, ld_dx, dz, ld_dz, dgamma, workspace, workspace_bytes_,
+                          stream, Types{});
 }
 
 rmsn_status rmsnorm_add_fwd(const uint16_t* x, int64_t ld_x, const uint16_t* residual,
                             int64_t ld_res, const float* gamma, int zero_centered_gamma, float eps,
                             int64_t T, int64_t D, uint16_t* y, int64_t ld_y, uint16_t* residual_out,
                             int64_t ld_rout, float* rstd, void* stream) {
-  if (T < 0) return RMSN_ERR_SHAPE;
-  RMSN_TRY(check_D(D));
-  RMSN_TRY(check_mat(x, ld_x, T, D, true));
-  RMSN_TRY(check_mat(residual, ld_res, T, D, true));
-  RMSN_TRY(check_mat(y, ld_y, T, D, true));
-  RMSN_TRY(check_mat(residual_out, ld_rout, T, D, true));
-  if (!(eps >= 0.0f) || !std::isfinite(eps)) return RMSN_ERR_EPS;
-  if (T == 0) return RMSN_OK;
-  RMSN_TRY(check_f32(gamma, 16, true));
-  RMSN_TRY(check_f32(rstd, 4, false));
-  if (add_fwd_alias(x, ld_x, residual, ld_res, gamma, T, D, y, ld_y, residual_out, ld_rout, rstd))
-    return RMSN_ERR_ALIASING;
-  const rmsn::FwdArgs a{x, ld_x, nullptr, 0, 0, 0, gamma, RMSN_DTYPE_F32, RMSN_DTYPE_BF16,
-                        zero_centered_gamma != 0, eps, T,
-                        static_cast<int>(D), y, ld_y, residual_out, ld_rout, rstd, residual,
-                        ld_res, fwd_stream(T, D)};
-  return hip_status(rmsn::launch_fwd(a, stream));
+  return add_fwd_common(x, ld_x, residual, ld_res, gamma, zero_centered_gamma, eps, T, D, y, ld_y,
+                        residual_out, ld_rout, rstd, stream, Types{});
 }
 
 rmsn_status rmsnorm_add_bwd_rows(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64_t ld_x,
@@ -459,20 +508,9 @@ rmsn_status rmsnorm_add_bwd(const uint16_t* g, int64_t ld_g, const uint16_t* x, 
                             const uint16_t* g_residual_out, int64_t ld_gro, uint16_t* dh,
                             int64_t ld_dh, float* dgamma, void* workspace, size_t workspace_bytes_,
                             void* stream) {
-  if (dh == nullptr && dgamma == nullptr) return RMSN_ERR_NULL;
-  if (dgamma != nullptr) RMSN_TRY(check_f32(dgamma, 16, true));
-  RMSN_TRY(check_bwd(g, ld_g, x, ld_x, rstd, gamma, T, D, g_residual_out, ld_gro, dh, ld_dh,
-                     dgamma != nullptr, dgamma, workspace, workspace_bytes_, false, GateIO{},
-                     residual, ld_res, true));
-  if (T > 0) {
-    const rmsn::BwdArgs a = bwd_args(g, ld_g, x, ld_x, rstd, gamma, zero_centered_gamma, T, D,
-                                     g_residual_out, ld_gro, dh, ld_dh,
-                                     dgamma != nullptr ? workspace : nullptr, GateIO{}, 0,
-                                     residual, ld_res);
-    RMSN_TRY(hip_status(rmsn::launch_bwd_rows(a, stream)));
-  }
-  if (dgamma == nullptr) return RMSN_OK;
-  return finish_dgamma(workspace, T, D, dgamma, stream);
+  return add_bwd_common(g, ld_g, x, ld_x, residual, ld_res, rstd, gamma, zero_centered_gamma, T, D,
+                        g_residual_out, ld_gro, dh, ld_dh, dgamma, workspace, workspace_bytes_,
+                        stream, Types{});
 }
 
 rmsn_status rmsnorm_fwd_dt(int act_dtype, int weight_dtype, const void* x, int64_t ld_x,
@@ -508,6 +546,50 @@ rmsn_status rmsnorm_bwd_dt(int act_dtype, int weight_dtype, const void* g, int64
   }
   if (dgamma == nullptr) return RMSN_OK;
   return finish_dgamma(workspace, T, D, dgamma, stream);
+}
+
+rmsn_status rmsnorm_gated_fwd_dt(int act_dtype, int weight_dtype, const void* x, int64_t ld_x,
+                                 const void* z, int64_t ld_z, const void* gamma,
+                                 int zero_centered_gamma, float eps, int64_t T, int64_t D,
+                                 int activation, int rounding, void* out, int64_t ld_out,
+                                 float* rstd, void* stream) {
+  return fwd_common(u16(x), ld_x, u16(z), ld_z, true, activation, rounding, gamma,
+                    zero_centered_gamma, eps, T, D, u16(out), ld_out, nullptr, 0, false, rstd,
+                    stream, Types{act_dtype, weight_dtype});
+}
+
+rmsn_status rmsnorm_gated_bwd_dt(int act_dtype, int weight_dtype, const void* g, int64_t ld_g,
+                                 const void* x, int64_t ld_x, const void* z, int64_t ld_z,
+                                 const float* rstd, const void* gamma, int zero_centered_gamma,
+                                 int64_t T, int64_t D, int activation, void* dx, int64_t ld_dx,
+                                 void* dz, int64_t ld_dz, float* dgamma, void* workspace,
+                                 size_t workspace_bytes_, void* stream) {
+  return gated_bwd_common(u16(g), ld_g, u16(x), ld_x, u16(z), ld_z, rstd, gamma,
+                          zero_centered_gamma, T, D, activation, u16(dx), ld_dx, u16(dz), ld_dz,
+                          dgamma, workspace, workspace_bytes_, stream,
+                          Types{act_dtype, weight_dtype});
+}
+
+rmsn_status rmsnorm_add_fwd_dt(int act_dtype, int weight_dtype, const void* x, int64_t ld_x,
+                               const void* residual, int64_t ld_res, const void* gamma,
+                               int zero_centered_gamma, float eps, int64_t T, int64_t D, void* y,
+                               int64_t ld_y, void* residual_out, int64_t ld_rout, float* rstd,
+                               void* stream) {
+  return add_fwd_common(u16(x), ld_x, u16(residual), ld_res, gamma, zero_centered_gamma, eps, T,
+                        D, u16(y), ld_y, u16(residual_out), ld_rout, rstd, stream,
+                        Types{act_dtype, weight_dtype});
+}
+
+rmsn_status rmsnorm_add_bwd_dt(int act_dtype, int weight_dtype, const void* g, int64_t ld_g,
+                               const void* x, int64_t ld_x, const void* residual, int64_t ld_res,
+                               const float* rstd, const void* gamma, int zero_centered_gamma,
+                               int64_t T, int64_t D, const void* g_residual_out, int64_t ld_gro,
+                               void* dh, int64_t ld_dh, float* dgamma, void* workspace,
+                               size_t workspace_bytes_, void* stream) {
+  return add_bwd_common(u16(g), ld_g, u16(x), ld_x, u16(residual), ld_res, rstd, gamma,
+                        zero_centered_gamma, T, D, u16(g_residual_out), ld_gro, u16(dh), ld_dh,
+                        dgamma, workspace, workspace_bytes_, stream,
+                        Types{act_dtype, weight_dtype});
 }
 
 rmsn_status bigemm_bf16_xwt(const uint16_t* x, int64_t ld_x, const uint16_t* w, int64_t ld_w,

@@ -8,6 +8,7 @@
 namespace rmsn {
 
 int launch_bwd_rows_add(const BwdArgs& a, void* stream) {
+  if (a.dt == kF16) return launch_bwd_rows_add_f16(a, stream);
   if (a.D % 8 != 0) return launch_bwd_rows_add_elem(a, stream);
   const RowGeom g = bwd_geom(a.D);
   const bwd_detail::RowsLaunch f =

@@ -7,6 +7,7 @@
 namespace rmsn {
 
 int launch_bwd_rows_gated(const BwdArgs& a, void* stream) {
+  if (a.dt == kF16) return launch_bwd_rows_gated_f16(a, stream);
   if (a.D % 8 != 0) return launch_bwd_rows_gated_elem(a, stream);
   const RowGeom g = bwd_geom(a.D);
   bwd_detail::RowsLaunch f = nullptr;

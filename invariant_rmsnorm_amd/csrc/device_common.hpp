@@ -374,8 +374,10 @@ __device__ __forceinline__ void gate_and_grad(float z, float& a, float& da) {
   }
 }
 
-// Rounds 8 fp32 values to bf16 and back (round to nearest even).
-__device__ __forceinline__ void round8_bf16(float (&f)[8]) { unpack8(pack8(f), f); }
+// Rounds 8 fp32 values to the activation storage type DT and back (round
+// to nearest even).
+template <int DT>
+__device__ __forceinline__ void round8(float (&f)[8]) { unpack8<DT>(pack8<DT>(f), f); }
 
 // The 8 weights of vector c in fp32, widened exactly from their storage
 // type `wdt` (the weights are read once per workgroup, so the type is a

@@ -7,6 +7,7 @@
 namespace rmsn {
 
 int launch_fwd_add(const FwdArgs& a, void* stream) {
+  if (a.dt == kF16) return launch_fwd_add_f16(a, stream);
   if (a.D % 8 != 0) return launch_fwd_add_elem(a, stream);
   const fwd_detail::FwdLaunch f = fwd_detail::pick<kFwdAdd>(fwd_geom(a.D));
   if (f == nullptr) return static_cast<int>(hipErrorInvalidValue);

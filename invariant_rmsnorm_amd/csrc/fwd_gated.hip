@@ -6,6 +6,7 @@
 namespace rmsn {
 
 int launch_fwd_gated(const FwdArgs& a, void* stream) {
+  if (a.dt == kF16) return launch_fwd_gated_f16(a, stream);
   if (a.D % 8 != 0) return launch_fwd_gated_elem(a, stream);
   using namespace fwd_detail;
   const RowGeom g = fwd_geom(a.D);

@@ -34,8 +34,9 @@
 namespace rmsn {
 
 // GATE: 0 = no gate; otherwise 1 + activation + 2 * cast, where cast selects
-// the convention that rounds the normalised and the weighted value to bf16
-// before the next multiply; kFwdAdd = the fused add-norm.
+// the convention that rounds the normalised and the weighted value to the
+// activations' storage type before the next multiply; kFwdAdd = the fused
+// add-norm.
 constexpr int fwd_gate_code(bool gated, int act, bool cast) { return gated ? 1 + act + 2 * cast : 0; }
 constexpr int kFwdAdd = 5;
 
@@ -167,11 +168,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
         row_values(xq[u][v], zq[ADD ? u : 0][ADD ? v : 0], f);
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] = f[k] * r;
-        if constexpr (CAST) round8_bf16(o);
+        if constexpr (CAST) round8<DT>(o);
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] = o[k] * w[v][k];
         if constexpr (GATED) {
-          if constexpr (CAST) round8_bf16(o);
+          if constexpr (CAST) round8<DT>(o);
           float zf[8];
           unpack8<DT>(zq[u][v], zf);
 #pragma unroll

@@ -80,6 +80,9 @@ int launch_fwd_f16(const FwdArgs& a, void* stream);
 int launch_fwd_elem(const FwdArgs& a, void* stream);   // D % 8 != 0 (plain, residual copy)
 int launch_fwd_gated_elem(const FwdArgs& a, void* stream);  // D % 8 != 0, gated
 int launch_fwd_add_elem(const FwdArgs& a, void* stream);    // D % 8 != 0, fused add
+int launch_fwd_gated_f16(const FwdArgs& a, void* stream);       // fp16, gated
+int launch_fwd_gated_elem_f16(const FwdArgs& a, void* stream);  // fp16, gated, D % 8 != 0
+int launch_fwd_add_f16(const FwdArgs& a, void* stream);         // fp16, fused add, any D
 int launch_bwd_rows(const BwdArgs& a, void* stream);
 int launch_bwd_rows_gated(const BwdArgs& a, void* stream);  // a.z != nullptr
 int launch_bwd_rows_gated_elem(const BwdArgs& a, void* stream);  // a.z != nullptr, D % 8 != 0
@@ -88,6 +91,9 @@ int launch_bwd_rows_f16(const BwdArgs& a, void* stream);
 int launch_bwd_rows_elem(const BwdArgs& a, void* stream);      // D % 8 != 0 (plain, gres)
 int launch_bwd_rows_elem_f16(const BwdArgs& a, void* stream);  // the same, fp16 activations
 int launch_bwd_rows_add_elem(const BwdArgs& a, void* stream);    // D % 8 != 0, fused add
+int launch_bwd_rows_gated_f16(const BwdArgs& a, void* stream);       // fp16, gated
+int launch_bwd_rows_gated_elem_f16(const BwdArgs& a, void* stream);  // fp16, gated, D % 8 != 0
+int launch_bwd_rows_add_f16(const BwdArgs& a, void* stream);         // fp16, fused add, any D
 int launch_bwd_finish(const float* part, int64_t chunks, int D, float* dgamma, void* stream);
 int launch_gemm(const GemmArgs& a, void* stream);
 // The output tile launch_gemm uses for an M x N product (host only).

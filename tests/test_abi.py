@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(irn.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert irn.rmsnorm_abi_version() == 13
+    assert irn.rmsnorm_abi_version() == 14
 
 
 def test_status_strings():
@@ -379,6 +379,38 @@ def test_dtype_entry_points_reject_bad_types():
     assert lib.rmsnorm_bwd_dt(1, 9, *bargs) == irn.RMSN_ERR_MODE
     assert lib.rmsnorm_bwd_dt(1, 2, A, 4096, B, 4096, RS, GAM, 0, 1000, 4096, None, 0, None, 0,
                               None, W, 1 << 30, None) == irn.RMSN_ERR_NULL
+
+
+def test_gated_and_add_dtype_entry_points_reject_bad_types():
+    lib = irn.load()
+    gf = (A, 4096, B, 4096, GAM, 0, 1e-6, 8, 4096, 0, 0, C, 4096, RS, None)
+    gb = (A, 4096, B, 4096, F, 4096, RS, GAM, 0, 1000, 4096, 0, C, 4096, E, 4096, W + 64,
+          W, 1 << 30, None)
+    af = (A, 4096, B, 4096, GAM, 0, 1e-6, 8, 4096, C, 4096, E, 4096, RS, None)
+    ab = (A, 4096, B, 4096, F, 4096, RS, GAM, 0, 1000, 4096, None, 0, C, 4096, E, W, 1 << 30,
+          None)
+    for adt, wdt in ((2, 2), (3, 2), (-1, 2), (0, 3), (1, 7)):
+        assert lib.rmsnorm_gated_fwd_dt(adt, wdt, *gf) == irn.RMSN_ERR_MODE
+        assert lib.rmsnorm_gated_bwd_dt(adt, wdt, *gb) == irn.RMSN_ERR_MODE
+        assert lib.rmsnorm_add_fwd_dt(adt, wdt, *af) == irn.RMSN_ERR_MODE
+        assert lib.rmsnorm_add_bwd_dt(adt, wdt, *ab) == irn.RMSN_ERR_MODE
+    # activation and rounding are checked as in the bf16 entry points
+    bad_act = gf[:9] + (2,) + gf[10:]
+    assert lib.rmsnorm_gated_fwd_dt(1, 0, *bad_act) == irn.RMSN_ERR_MODE
+    bad_round = gf[:10] + (2,) + gf[11:]
+    assert lib.rmsnorm_gated_fwd_dt(1, 0, *bad_round) == irn.RMSN_ERR_MODE
+    assert lib.rmsnorm_gated_bwd_dt(1, 1, *(gb[:11] + (5,) + gb[12:])) == irn.RMSN_ERR_MODE
+    # 16-bit weights keep the 16-byte alignment rule
+    assert lib.rmsnorm_add_fwd_dt(1, 1, A, 4096, B, 4096, GAM + 8, 0, 1e-6, 8, 4096, C, 4096, E,
+                                  4096, RS, None) == irn.RMSN_ERR_MISALIGNED
+    # the weights' range follows their type: rstd 12 KiB past fp32 weights of
+    # 4096 (16 KiB) overlaps them
+    assert lib.rmsnorm_add_fwd_dt(1, 2, A, 4096, B, 4096, GAM, 0, 1e-6, 8, 4096, C, 4096, E,
+                                  4096, GAM + 12288, None) == irn.RMSN_ERR_ALIASING
+    assert lib.rmsnorm_gated_bwd_dt(1, 2, A, 4096, B, 4096, F, 4096, RS, GAM, 0, 1000, 4096, 0,
+                                    C, 4096, C, 4096, None, None, 0, None) == irn.RMSN_ERR_ALIASING
+    assert lib.rmsnorm_add_bwd_dt(0, 2, A, 4096, B, 4096, F, 4096, RS, GAM, 0, 1000, 4096, None,
+                                  0, None, 0, None, W, 1 << 30, None) == irn.RMSN_ERR_NULL
 
 
 # ---- batch-invariant GEMM -------------------------------------------------------------

@@ -98,6 +98,15 @@ def test_every_entry_point_checks_before_the_call(monkeypatch):
         lambda: irn.rmsnorm_fwd_dt(t2(F16), gamma, y=t2(BF)),          # y must match x's type
         lambda: irn.rmsnorm_bwd_dt(t2(F16), t2(BF), rstd, gamma),       # g and x differ
         lambda: irn.rmsnorm_bwd_dt(t2(F16), t2(F16), rstd, t1(D, torch.int32)),
+        lambda: irn.rmsnorm_gated_fwd_dt(t2(F16), t2(BF), gamma),        # z must match x's type
+        lambda: irn.rmsnorm_gated_fwd_dt(t2(F16), t2(F16), gamma, out=t2(BF)),
+        lambda: irn.rmsnorm_gated_bwd_dt(t2(F16), t2(F16), t2(F16), rstd, t1(D - 8, F16)),
+        lambda: irn.rmsnorm_gated_bwd_dt(t2(F16), t2(F16), t2(F16), rstd, gamma, dz=t2(BF)),
+        lambda: irn.rmsnorm_add_fwd_dt(t2(F16), t2(F16), gamma, residual_out=t2(BF)),
+        lambda: irn.rmsnorm_add_fwd_dt(t2(F32), t2(F32), gamma),         # fp32 activations
+        lambda: irn.rmsnorm_add_bwd_dt(t2(F16), t2(F16), t2(BF), rstd, gamma),
+        lambda: irn.rmsnorm_add_bwd_dt(t2(F16), t2(F16), t2(F16), rstd, gamma,
+                                       g_residual_out=t2(BF)),
         lambda: irn.bigemm_bf16_xwt(t2(shape=(4, 64)), t2(shape=(8, 32))),
         lambda: irn.bigemm_bf16_xwt(t2(shape=(4, 64)), t2(shape=(8, 64)), y=t2(shape=(4, 4))),
         # well-formed but on the host: rejected before the call
@@ -105,6 +114,10 @@ def test_every_entry_point_checks_before_the_call(monkeypatch):
         lambda: irn.rmsnorm_bwd(g, x, rstd, gamma),
         lambda: irn.rmsnorm_gated_bwd(g, x, z, rstd, gamma),
         lambda: irn.rmsnorm_add_bwd(g, x, z, rstd, gamma),
+        lambda: irn.rmsnorm_gated_fwd_dt(t2(F16), t2(F16), t1(D, F16)),
+        lambda: irn.rmsnorm_gated_bwd_dt(t2(F16), t2(F16), t2(F16), rstd, gamma),
+        lambda: irn.rmsnorm_add_fwd_dt(t2(F16), t2(F16), t1(D, BF)),
+        lambda: irn.rmsnorm_add_bwd_dt(t2(F16), t2(F16), t2(F16), rstd, gamma),
         lambda: irn.bigemm_bf16_xwt(t2(shape=(4, 64)), t2(shape=(8, 64))),
     ]
     for i, call in enumerate(calls):
