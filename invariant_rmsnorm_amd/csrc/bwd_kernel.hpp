@@ -120,6 +120,9 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   // Weights w_eff = gamma (+1 in fp32 when zero-centred).
   constexpr bool ELEM = elem_dt(DT);
   constexpr bool MSK = MASKED;  // some lanes lack their last group
+  // rows of any length: a partial last group is read as the row's last 16
+  // bytes, except in rows shorter than one group (LPR == 1)
+  constexpr bool TAIL = LPR > 1;
   float wreg[LEAN ? 1 : VPL][8];
   float4* const wl4 = reinterpret_cast<float4*>(lds);
   if constexpr (LEAN) {
@@ -222,37 +225,37 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       if (a.x_stream) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v), last(v));
-          b.xq[u][v] = load_row8<DT, kLoadStream>(rx, voff(v, a.ld_x), valid(v), last(v));
+          b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
+          b.xq[u][v] = load_row8<DT, kLoadStream, TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
         }
       } else {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, kLoadStream>(rg, voff(v, a.ld_g), valid(v), last(v));
-          b.xq[u][v] = load_row8<DT>(rx, voff(v, a.ld_x), valid(v), last(v));
+          b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
+          b.xq[u][v] = load_row8<DT, kLoadDefault, TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
         }
       }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          b.rres[u][v] = load_row8<DT, kLoadStream>(rgr, voff(v, a.ld_gres), valid(v), last(v));
+          b.rres[u][v] = load_row8<DT, kLoadStream, TAIL>(rgr, voff(v, a.ld_gres), valid(v), last(v));
       }
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, end, RPW, a.ld_z, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          b.zq[u][v] = load_row8<DT, kLoadStream>(rz, voff(v, a.ld_z), valid(v), last(v));
+          b.zq[u][v] = load_row8<DT, kLoadStream, TAIL>(rz, voff(v, a.ld_z), valid(v), last(v));
       }
       if constexpr (ADD) {  // the forward read it too: x's policy
         const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
         if (a.x_stream) {
 #pragma unroll
           for (int v = 0; v < VPL; ++v)
-            b.hq[u][v] = load_row8<DT, kLoadStream>(rh, voff(v, a.ld_rin), valid(v), last(v));
+            b.hq[u][v] = load_row8<DT, kLoadStream, TAIL>(rh, voff(v, a.ld_rin), valid(v), last(v));
         } else {
 #pragma unroll
-          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT>(rh, voff(v, a.ld_rin), valid(v), last(v));
+          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT, kLoadDefault, TAIL>(rh, voff(v, a.ld_rin), valid(v), last(v));
         }
       }
     }
@@ -273,6 +276,14 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t first = step + group * ROWS_WAVE + u * RPW;
       const float r = b.rq[u];
+      {
+        const int lv = valid(VPL - 1);
+        place_row8<DT, TAIL>(b.gq[u][VPL - 1], lv, true);
+        place_row8<DT, TAIL>(b.xq[u][VPL - 1], lv, true);
+        if constexpr (GRES) place_row8<DT, TAIL>(b.rres[u][VPL - 1], lv, true);
+        if constexpr (GATED) place_row8<DT, TAIL>(b.zq[u][VPL - 1], lv, true);
+        if constexpr (ADD) place_row8<DT, TAIL>(b.hq[u][VPL - 1], lv, true);
+      }
       int wbase = 0;
       if constexpr (LEAN) asm("" : "+v"(wbase));
       // Pass 1: the lane partial of s = sum_i (g_i * w_i) * x_i in (vector,

@@ -142,18 +142,39 @@ __device__ __forceinline__ void buf_store16_nt(const u32x4& v, __amdgpu_buffer_r
 // after unrolling). 16-byte storage: one aligned 16-byte vector.
 // Element-wise storage (any D, any 2-byte alignment): a full group is one
 // 16-byte access at a 2-byte-aligned offset, which the hardware splits into
-// aligned pieces; the row's partial last group moves element by element,
-// elements past D reading as zero (an offset beyond the resource).
-template <int DT, int POLICY = kLoadDefault>
+// aligned pieces. The row's partial last group (0 < left < 8) is read as the
+// 16 bytes that end at the row's last element, which lie inside the row
+// whenever D >= 8 (TAIL), and place_row8 moves its elements into place once
+// the data is needed: a single load whose result nothing waits for while
+// the step's other loads are in flight. Rows shorter than 8 elements (not
+// TAIL) read the group element by element, elements past D reading as zero.
+// Groups past the row (left <= 0) read zeros.
+template <int DT, int POLICY = kLoadDefault, bool TAIL = true>
 __device__ __forceinline__ u32x4 load_row8(__amdgpu_buffer_rsrc_t r, uint32_t off, int left,
                                            bool last) {
   if (!elem_dt(DT) || !last || left >= 8) return buf_load16<POLICY>(r, off);
-  uint32_t h[8];
+  if constexpr (TAIL) {
+    return buf_load16<POLICY>(r, left > 0 ? off - 2u * static_cast<uint32_t>(8 - left) : kOutOfRange);
+  } else {
+    uint32_t h[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    h[e] = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(e < left ? off + 2 * e : kOutOfRange),
-                                                0, POLICY);
-  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    for (int e = 0; e < 8; ++e)
+      h[e] = __builtin_amdgcn_raw_buffer_load_b16(
+          r, static_cast<int>(e < left ? off + 2 * e : kOutOfRange), 0, POLICY);
+    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  }
+}
+// Places a group that load_row8 read as a row's tail: its last `left`
+// elements become elements 0 .. left-1, zeros above. Every other group is
+// left as it is.
+template <int DT, bool TAIL = true>
+__device__ __forceinline__ void place_row8(u32x4& q, int left, bool last) {
+  if constexpr (elem_dt(DT) && TAIL) {
+    if (last && left > 0 && left < 8) {
+      const unsigned __int128 w = __builtin_bit_cast(unsigned __int128, q);
+      q = __builtin_bit_cast(u32x4, w >> (16 * (8 - left)));
+    }
+  }
 }
 // Stores a group the same way (non-temporal); a partial last group writes
 // only its elements inside the row.

@@ -71,6 +71,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * ROWS_BLOCK;
 
   constexpr bool ELEM = elem_dt(DT);
+  // rows of any length: a partial last group is read as the row's last 16
+  // bytes, except in rows shorter than one group (LPR == 1)
+  constexpr bool TAIL = LPR > 1;
   float w[VPL][8];
   if constexpr (ELEM) load_weights_any<LPR, VPL>(a.gamma, a.wdt, a.zc, a.D, l, w);
   else load_weights<LPR, VPL, MASKED>(a.gamma, a.wdt, a.zc, nv, l, w);
@@ -101,17 +104,17 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
       const int64_t first = group_first(base, u);
       const auto rx = rows_rsrc(a.x, first, a.T, RPW, a.ld_x, a.D);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT, P>(rx, voff(v, a.ld_x), valid(v), last(v));
+      for (int v = 0; v < VPL; ++v) xq[u][v] = load_row8<DT, P, TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
       if constexpr (GATED) {
         const auto rz = rows_rsrc(a.z, first, a.T, RPW, a.ld_z, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, P>(rz, voff(v, a.ld_z), valid(v), last(v));
+        for (int v = 0; v < VPL; ++v) zq[u][v] = load_row8<DT, P, TAIL>(rz, voff(v, a.ld_z), valid(v), last(v));
       }
       if constexpr (ADD) {
         const auto rr = rows_rsrc(a.rin, first, a.T, RPW, a.ld_rin, a.D);
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          zq[u][v] = load_row8<DT, P>(rr, voff(v, a.ld_rin), valid(v), last(v));
+          zq[u][v] = load_row8<DT, P, TAIL>(rr, voff(v, a.ld_rin), valid(v), last(v));
       }
     }
   };
@@ -136,6 +139,8 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t first = group_first(base, u);
       const int64_t row = first + slot;
+      place_row8<DT, TAIL>(xq[u][VPL - 1], valid(VPL - 1), true);
+      if constexpr (TWO) place_row8<DT, TAIL>(zq[u][VPL - 1], valid(VPL - 1), true);
 
       // sum of squares: this lane's elements in (vector, element) order, then
       // the row's fixed butterfly. Squares of bf16 values are exact in fp32;
