@@ -96,12 +96,23 @@ rmsn_status check_f32(const float* p, uintptr_t align, bool required) {
 
 rmsn_status hip_status(int rc) { return rc == 0 ? RMSN_OK : RMSN_ERR_HIP; }
 
-// The forward reads its inputs with the streaming hint when x is larger
-// than the Infinity Cache: the backward could not find them there anyway.
+// The forward reads its inputs with the streaming hint when x is well past
+// the Infinity Cache (RMSN_STREAM_BYTES): the backward would find little of
+// them there.
 #ifndef RMSN_FWD_STREAM_X
 #define RMSN_FWD_STREAM_X 1
 #endif
-int fwd_stream(int64_t T, int64_t D) { return RMSN_FWD_STREAM_X && T * D * 2 > rmsn::kCacheBytes; }
+// Bytes of x past which both kernels read it with the streaming hint: twice
+// the Infinity Cache. Below that, keeping x's lines pays although x does
+// not fit: the backward still finds part of it (measured, T x 4096 bf16,
+// step with the cache flushed before it, never streaming / streaming past
+// 256 MiB: x = 288 MiB 72.4 / 67.6%, 384 MiB 72.9 / 70.7%, 512 MiB
+// 72.3 / 71.2%, 1 GiB 70.2 / 72.1%).
+#ifndef RMSN_STREAM_BYTES
+#define RMSN_STREAM_BYTES (2 * rmsn::kCacheBytes)
+#endif
+bool streams_x(int64_t T, int64_t D) { return T * D * 2 > static_cast<int64_t>(RMSN_STREAM_BYTES); }
+int fwd_stream(int64_t T, int64_t D) { return RMSN_FWD_STREAM_X && streams_x(T, D); }
 
 // Storage types of one call: activations (bf16 or fp16) and weights (bf16,
 // fp16 or fp32). The entry points without a _dt suffix use bf16 / fp32.
@@ -236,7 +247,7 @@ rmsn::BwdArgs bwd_args(const uint16_t* g, int64_t ld_g, const uint16_t* x, int64
   return rmsn::BwdArgs{g, ld_g, x, ld_x, rstd, gamma, ty.wdt, ty.dt, zc != 0, T, static_cast<int>(D),
                        dx ? gres : nullptr, ld_gres, dx, ld_dx, static_cast<float*>(ws),
                        p.chunks, p.group_blocks, gate.z, gate.ld_z, act, gate.dz, gate.ld_dz,
-                       T * D * 2 > rmsn::kCacheBytes, rin, ld_rin};
+                       streams_x(T, D), rin, ld_rin};
 }
 
 // dgamma from the workspace partials (zeros when T == 0).

@@ -221,7 +221,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
       const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
       // g (and gres, z) are read once: streaming hint. x takes it only when
-      // it does not fit in the Infinity Cache (a wave-uniform branch).
+      // it is well past the Infinity Cache (a wave-uniform branch).
       if (a.x_stream) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {

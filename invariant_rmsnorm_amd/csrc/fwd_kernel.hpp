@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
   auto group_first = [&](int64_t base, int u) { return base + group * ROWS_WAVE + u * RPW; };
 
   // The inputs' cache policy: the default keeps rows the backward reads
-  // next in the Infinity Cache; inputs larger than it take the streaming
+  // next in the Infinity Cache; inputs well past it take the streaming
   // hint (a wave-uniform choice).
   auto load_inputs = [&](auto policy, int64_t base, u32x4 (&xq)[U][VPL], u32x4 (&zq)[ZU][ZV]) {
     constexpr int P = decltype(policy)::value;

@@ -91,11 +91,11 @@ constexpr int64_t part_stride(int64_t D) { return (D + 7) / 8 * 8; }
 #ifndef RMSN_FWD_UNROLL_NARROW
 #define RMSN_FWD_UNROLL_NARROW 2
 #endif
-// Infinity Cache (MALL) capacity of an MI355X. The backward reads x with the
-// non-temporal hint only when x is larger than this: a tensor that fits may
-// be served from the cache when it is read again (the forward just read it;
-// a repeated call reads it next), while a larger one would only evict other
-// lines. The hint changes no result.
+// Infinity Cache (MALL) capacity of an MI355X. Both kernels read x with the
+// non-temporal hint only when x is well past this (the threshold is in
+// api.cpp): up to about twice the capacity the backward still finds enough
+// of x in the cache (the forward just read it) to pay for keeping its lines;
+// beyond that they would only evict other lines. The hint changes no result.
 constexpr int64_t kCacheBytes = int64_t{256} << 20;
 
 constexpr int fwd_unroll(int lpr, int vpl) {
