@@ -384,7 +384,7 @@ def bench_gemm(args, torch, irn, dev):
         "library_gemm": {"kernel": "torch.matmul (not batch-invariant)", "ms": round(lib_ms, 5),
                          "TFLOP/s": round(flops / (lib_ms * 1e-3) / 1e12, 2),
                          "bigemm_over_library_time": round(launch_ms / lib_ms, 4)},
-        "roofline": {"bound": "mfma", "kernel": "bigemm_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(M, N), "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": (measured_traffic(GEMM_TRAFFIC_FILE, GEMM_SOURCES)
@@ -395,6 +395,15 @@ def bench_gemm(args, torch, irn, dev):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def gemm_kernel_name(M: int, N: int) -> str:
+    """The GEMM kernel a launch of M x N runs: the operands-into-LDS kernel
+    for output tiles of 64 rows or more, the register-staged one below."""
+    import invariant_rmsnorm_amd as irn
+    tm, tn = irn.bigemm_bf16_tile(M, N)
+    kind = "bigemm_dl_kernel" if tm >= 64 else "bigemm_kernel"
+    return f"{kind} ({tm}x{tn} tile)"
 
 
 def main():
