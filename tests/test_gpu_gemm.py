@@ -73,6 +73,29 @@ def test_gemm_strided_operands(gpu):
     assert torch.all(ys[:, N:] == 0)  # nothing written past N
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 352), (4096, 4096, 320), (600, 4096, 288)])
+def test_gemm_strided_operands_large_tiles(gpu, M, N, K):
+    """Row strides above K and offset bases on the tiles whose operands go
+    straight into LDS (128 x 128, 256 x 256 and 64 x 128 here; K ends in a
+    half stage in two of them): the same bytes as contiguous operands,
+    nothing written past N."""
+    assert irn.bigemm_bf16_tile(M, N)[0] >= 64
+    x = synth.normal_bf16(2125 + M, 1, M, K)
+    w = synth.normal_bf16(2125 + M, 2, N, K)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    xs = torch.zeros((M, K + 40), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros((N, K + 24), dtype=torch.bfloat16, device="cuda")
+    xs[:, 8:K + 8] = xd
+    ws[:, 24:] = wd
+    ys = torch.zeros((M, N + 5), dtype=torch.bfloat16, device="cuda")
+    irn.bigemm_bf16_xwt(xs[:, 8:K + 8], ws[:, 24:], y=ys[:, :N])
+    y = irn.bigemm_bf16_xwt(xd, wd)
+    assert torch.equal(ys[:, :N], y)
+    assert torch.all(ys[:, N:] == 0)
+    rows = [0, M // 2, M - 1]
+    _check_parity(x[rows], w, host_bits(y)[rows])
+
+
 M_SET = (1, 2, 17, 33, 128, 257, 1024)
 
 
