@@ -551,7 +551,10 @@ def main():
         step_evs[i][1].record(stream)
     torch.cuda.synchronize()
     loop_wall = time.perf_counter() - t0
-    ms_step = sum(a.elapsed_time(b) for a, b in step_evs) / args.steps
+    step_ms = sorted(a.elapsed_time(b) for a, b in step_evs)
+    ms_step = sum(step_ms) / args.steps
+    ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else \
+        0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     # Warm pass: the same K steps back to back (wall clock). A timing event
     # costs the GPU a few microseconds (it waits for the stream to drain), so
@@ -639,6 +642,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(ms_median, 5),
+        "value_median": round(step_bytes / (ms_median * 1e-3) / 1e9, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
