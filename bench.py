@@ -398,12 +398,10 @@ def bench_gemm(args, torch, irn, dev):
 
 
 def gemm_kernel_name(M: int, N: int) -> str:
-    """The GEMM kernel a launch of M x N runs: the operands-into-LDS kernel
-    for output tiles of 64 rows or more, the register-staged one below."""
+    """The GEMM kernel and output tile a launch of M x N runs."""
     import invariant_rmsnorm_amd as irn
     tm, tn = irn.bigemm_bf16_tile(M, N)
-    kind = "bigemm_dl_kernel" if tm >= 64 else "bigemm_kernel"
-    return f"{kind} ({tm}x{tn} tile)"
+    return f"bigemm_dl_kernel ({tm}x{tn} tile)"
 
 
 def main():

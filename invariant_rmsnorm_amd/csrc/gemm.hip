@@ -7,31 +7,24 @@
 // invariant. What fixes an output element's value here is its arithmetic
 // alone: an fp32 accumulator that starts at zero and takes one
 // v_mfma_f32_32x32x16_bf16 step per 16 consecutive k, in ascending k, then
-// one rounding to bf16. Every kernel below does exactly that for every
-// element, so the tile shape (which may follow M, N and K) changes which
+// one rounding to bf16. Every tile instance below does exactly that for
+// every element, so the tile shape (which may follow M and N) changes which
 // workgroup computes an element, never how.
 //
-// Two kernels, each a template over its tile (TM x TN MFMA blocks of 32 x 32
+// The kernel is a template over its tile: TM x TN MFMA blocks of 32 x 32
 // per wave, WGM x WGN waves per workgroup, so a workgroup owns
-// BM = 32 TM WGM rows by BN = 32 TN WGN columns), K in stages of BK:
-//  - bigemm_dl_kernel (tiles of 64 rows and more): operands go from memory
-//    straight into LDS (buffer loads with the LDS bit: lane i's 16 bytes
-//    land 16 i bytes past the wave's LDS pointer), through a ring of NS
-//    stage buffers with one barrier per stage;
-//  - bigemm_kernel (tiles of 32 rows): stages are staged through LDS twice
-//    over: while the waves multiply stage s out of one buffer, stage s + 1
-//    is written from registers into the other and stage s + 2 is loaded from
-//    memory into the registers.
-// In both, rows of X past M and rows of W past N read as zero (buffer
-// resources), outputs past M or N are not stored, and in a last stage of 32
-// valid k (K = 32 mod 64) the MFMA steps past K are skipped.
+// BM = 32 TM WGM rows by BN = 32 TN WGN columns; K in stages of 64. The
+// operands go from memory straight into LDS (buffer loads with the LDS bit:
+// lane i's 16 bytes land 16 i bytes past the wave's LDS pointer), through a
+// ring of NS stage buffers with one barrier per stage. Rows of X past M and
+// rows of W past N read as zero (buffer resources), outputs past M or N are
+// not stored, and in a last stage of 32 valid k (K = 32 mod 64) the MFMA
+// steps past K are skipped.
 // X [M, K] and W [N, K] are row-major with K contiguous: MFMA lane l takes
 // 8 consecutive k of row l % 32 at k-offset 8 * (l / 32) for both operands,
 // and holds output rows 8 * (r / 4) + 4 * (l / 32) + r % 4 (r = 0..15) of
 // column l % 32.
 #include <hip/hip_runtime.h>
-
-#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -42,20 +35,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-template <int TM, int TN, int WGM, int WGN, int BK>
-struct GemmTile {
-  static constexpr int kThreads = 64 * WGM * WGN;
-  static constexpr int BM = 32 * TM * WGM, BN = 32 * TN * WGN;
-  static constexpr int kRow = BK + 8;           // bf16 per LDS row (16 B of padding)
-  static constexpr int kChunks = BK / 8;        // 16-byte chunks per row and stage
-  static constexpr int kLoadsA = BM * kChunks / kThreads;
-  static constexpr int kLoadsB = BN * kChunks / kThreads;
-  static constexpr int kStageElems = (BM + BN) * kRow;
-  static constexpr int kLdsBytes = 2 * kStageElems * 2;
-  static_assert(BK % 32 == 0, "stage of whole 32-k halves");
-  static_assert(BM * kChunks % kThreads == 0 && BN * kChunks % kThreads == 0, "loads");
-};
 
 // Tile (tm, tn) of workgroup b. Workgroups go to the 8 XCDs round-robin
 // (b mod 8); consecutive tiles are given to one XCD, and tiles are numbered
@@ -82,147 +61,6 @@ __device__ __forceinline__ void tile_of(int64_t b, int64_t tiles_m, int64_t tile
   tn = (t % in_group) / rows;
 }
 
-template <int TM, int TN, int WGM, int WGN, int BK>
-__global__ __launch_bounds__(64 * WGM * WGN) void bigemm_kernel(GemmArgs a) {
-  using G = GemmTile<TM, TN, WGM, WGN, BK>;
-  constexpr int S = BK / 16;                       // MFMA k-steps per stage
-  constexpr int L = G::kLoadsA + G::kLoadsB;       // 16-byte chunks per thread and stage
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-
-  int64_t tm, tn;
-  tile_of(blockIdx.x, (a.M + G::BM - 1) / G::BM, (a.N + G::BN - 1) / G::BN, tm, tn);
-  const int64_t m0 = tm * G::BM, n0 = tn * G::BN;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = wave_id();
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int K = static_cast<int>(a.K);
-
-  const auto rx = rows_rsrc(a.x, m0, a.M, G::BM, a.ld_x, K);
-  const auto rw = rows_rsrc(a.w, n0, a.N, G::BN, a.ld_w, K);
-
-  // Chunk c of a thread (A chunks first, then B; k-step s of a stage moves
-  // the chunks s L / S .. (s + 1) L / S - 1): 16-byte chunk q of a
-  // stage's rows of X (or W), row q / kChunks, k-offset 8 * (q % kChunks),
-  // with q = t + kThreads * (c, or c - kLoadsA).
-  u32x4 g[L];
-  auto chunk_q = [&](int c) { return t + G::kThreads * (c < G::kLoadsA ? c : c - G::kLoadsA); };
-  auto load_chunk = [&](int c, int k0) {
-    const int q = chunk_q(c);
-    if (c < G::kLoadsA)
-      g[c] = buf_load16(rx, static_cast<uint32_t>(
-                                ((q / G::kChunks) * a.ld_x + k0 + 8 * (q % G::kChunks)) * 2));
-    else
-      g[c] = buf_load16(rw, static_cast<uint32_t>(
-                                ((q / G::kChunks) * a.ld_w + k0 + 8 * (q % G::kChunks)) * 2));
-  };
-  auto store_chunk = [&](int c, int buf) {
-    const int q = chunk_q(c);
-    uint16_t* base = lds + buf * G::kStageElems + (c < G::kLoadsA ? 0 : G::BM * G::kRow);
-    *reinterpret_cast<u32x4*>(&base[(q / G::kChunks) * G::kRow + 8 * (q % G::kChunks)]) = g[c];
-  };
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-
-  // MFMA operands of k-step s of a stage out of LDS buffer buf.
-  struct Frags {
-    bf16x8 a[TM], b[TN];
-  };
-  auto read_frags = [&](Frags& f, int buf, int s) {
-    const uint16_t* As = lds + buf * G::kStageElems + (wm * 32 * TM + (lane & 31)) * G::kRow;
-    const uint16_t* Bs = lds + buf * G::kStageElems + G::BM * G::kRow +
-                         (wn * 32 * TN + (lane & 31)) * G::kRow;
-    const int kk = 16 * s + 8 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(&As[32 * i * G::kRow + kk]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[32 * j * G::kRow + kk]);
-  };
-  auto mfma = [&](const Frags& f) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-  };
-
-  // One full stage out of buffer cur. Beside the k-steps it writes the next
-  // stage from the registers into buffer cur ^ 1 (STORE; that buffer was
-  // last read in the previous stage, before its closing barrier) and loads
-  // the stage at k_next2 into the registers (LOAD), a few chunks per k-step.
-  Frags f[2];
-  auto stage = [&](auto store_tag, auto load_tag, int cur, int k_next2) {
-    constexpr bool STORE = decltype(store_tag)::value, LOAD = decltype(load_tag)::value;
-    read_frags(f[0], cur, 0);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s + 1 < S) read_frags(f[(s + 1) & 1], cur, s + 1);
-      mfma(f[s & 1]);
-      if constexpr (STORE) {
-#pragma unroll
-        for (int c = s * L / S; c < (s + 1) * L / S; ++c) store_chunk(c, cur ^ 1);
-      }
-      if constexpr (LOAD) {
-#pragma unroll
-        for (int c = s * L / S; c < (s + 1) * L / S; ++c) load_chunk(c, k_next2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-  };
-  using yes = std::integral_constant<bool, true>;
-  using no = std::integral_constant<bool, false>;
-
-  const int nk = (K + BK - 1) / BK;
-  const int last_steps = (K - (nk - 1) * BK) / 16;
-#pragma unroll
-  for (int c = 0; c < L; ++c) load_chunk(c, 0);
-#pragma unroll
-  for (int c = 0; c < L; ++c) store_chunk(c, 0);
-  if (nk > 1) {
-#pragma unroll
-    for (int c = 0; c < L; ++c) load_chunk(c, BK);
-  }
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) stage(yes{}, yes{}, kt & 1, (kt + 2) * BK);
-  if (kt + 1 < nk) {
-    stage(yes{}, no{}, kt & 1, 0);
-    ++kt;
-  }
-  // Last stage: `last_steps` k-steps (S, or 2 when K = 32 mod 64).
-  {
-    const int cur = kt & 1;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s >= last_steps) break;
-      read_frags(f[0], cur, s);
-      mfma(f[0]);
-    }
-  }
-
-  // Epilogue: each fp32 sum rounded once to bf16; lanes 0..31 store 32
-  // consecutive columns of one row, lanes 32..63 the same columns 4 rows on.
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t col = n0 + wn * 32 * TN + 32 * j + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 32 * TM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < a.M && col < a.N)
-          a.y[row * a.ld_y + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][r]));
-      }
-    }
-}
-
-// ---- operands loaded straight into LDS ----------------------------------------
-
 // 16 bytes per lane from a buffer resource into LDS: lane i's bytes land at
 // lds + 16 i (lds is wave-uniform; it becomes M0).
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
@@ -237,14 +75,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
-// Waits until at most `stages` stages of LPS loads each are in flight.
-template <int LPS, int NS>
+// Waits until at most `stages` stages of LPS loads each are in flight (K:
+// the most there can be).
+template <int LPS, int K>
 __device__ __forceinline__ void wait_stages(int stages) {
-  static_assert(NS <= 4, "stages in flight");
-  if constexpr (NS > 3) { if (stages >= 3) { wait_vmcnt<3 * LPS>(); return; } }
-  if constexpr (NS > 2) { if (stages == 2) { wait_vmcnt<2 * LPS>(); return; } }
-  if constexpr (NS > 1) { if (stages == 1) { wait_vmcnt<1 * LPS>(); return; } }
-  wait_vmcnt<0>();
+  if constexpr (K <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (stages >= K) {
+      wait_vmcnt<K * LPS>();
+      return;
+    }
+    wait_stages<LPS, K - 1>(stages);
+  }
 }
 
 // 16-byte chunk of a stage row that holds logical chunk kc of row r: kc xor
@@ -271,6 +114,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void bigemm_dl_kernel(GemmArgs a) {
   constexpr int LA = SA / 1024 / NW, LB = BN * ROWB / 1024 / NW;  // 1 KB loads per wave
   constexpr int LPS = LA + LB;
   static_assert(LA * 1024 * NW == SA && LB * 1024 * NW == BN * ROWB, "whole 1 KB loads per wave");
+  static_assert((NS - 1) * LPS < 64, "loads in flight fit the vmcnt counter");
   extern __shared__ __attribute__((aligned(16))) char lds8[];
 
   int64_t tm, tn;
@@ -352,7 +196,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void bigemm_dl_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < NS; ++j)
     if (j < nk) issue(j, j);
-  wait_stages<LPS, NS>(nk - 1 < NS - 1 ? nk - 1 : NS - 1);  // stage 0 complete
+  wait_stages<LPS, NS - 1>(nk - 1 < NS - 1 ? nk - 1 : NS - 1);  // stage 0 complete
   __syncthreads();
   Frags f[2];
   read_frags(f[0], 0, 0);
@@ -365,7 +209,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void bigemm_dl_kernel(GemmArgs a) {
       pin_step();
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this stage's reads are done
-    wait_stages<LPS, NS>(nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2);  // stage kt + 1 complete
+    wait_stages<LPS, NS - 2>(nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2);  // stage kt + 1 complete
     __syncthreads();
     if (kt + NS < nk) issue(kt + NS, buf);
     __builtin_amdgcn_sched_barrier(0);
@@ -383,7 +227,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void bigemm_dl_kernel(GemmArgs a) {
     }
   }
 
-  // Epilogue as bigemm_kernel's.
+  // Epilogue: each fp32 sum rounded once to bf16; lanes 0..31 store 32
+  // consecutive columns of one row, lanes 32..63 the same columns 4 rows on.
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -416,56 +261,53 @@ int launch_dl_tile(const GemmArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-template <int TM, int TN, int WGM, int WGN, int BK>
-int launch_tile(const GemmArgs& a, void* stream) {
-  using G = GemmTile<TM, TN, WGM, WGN, BK>;
-  auto* kern = &bigemm_kernel<TM, TN, WGM, WGN, BK>;
-  if (G::kLdsBytes > 64 * 1024) {
-    static const int lds_ok = [kern] {
-      return static_cast<int>(hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  G::kLdsBytes));
-    }();
-    if (lds_ok != 0) return lds_ok;
-  }
-  const int64_t tiles = ((a.M + G::BM - 1) / G::BM) * ((a.N + G::BN - 1) / G::BN);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tiles)), dim3(G::kThreads), G::kLdsBytes,
-                     static_cast<hipStream_t>(stream), a);
-  return static_cast<int>(hipGetLastError());
-}
-
-// The tiles, largest first: (TM, TN, WGM, WGN), BK = 64 for all.
-//   256 x 256: 8 waves of 128 x 64, 2 stages (128 KiB of LDS)
+// The tiles, largest first: (TM, TN, WGM, WGN), stages NS, LDS.
+//   256 x 256: 8 waves of 128 x 64, 2 stages (128 KiB)
 //   128 x 256: 8 waves of 64 x 64, 2 stages (96 KiB)
 //   128 x 128: 4 waves of 64 x 64, 3 stages (96 KiB)
-//   64 x 128: 4 waves of 32 x 64, 3 stages (72 KiB)       -- bigemm_dl_kernel
-//   32 x 128: 4 waves of 32 x 32     32 x 64: 2 waves of 32 x 32 -- bigemm_kernel
-// A launch takes the largest tile that still gives every compute unit a
-// tile of its own (at least kCus tiles), else the smallest: measured at
-// N = K = 4096, M = 1 / 128 / 512 / 1024 / 2048 / 4096 run fastest with
-// 32x64 / 32x128-or-32x64 / 64x128 / 128x128 / 128x256 / 256x256.
-// Direct loads into LDS against registers staging (us at N = K = 4096,
-// medians of interleaved timings): 256x256 at M = 4096 113.8 / 117.7,
-// 128x256 at M = 2048 64.0 / 67.7, 128x128 at M = 1024 39.6 / 40.0, 64x128
-// at M = 512 26.2 / 27.2 and at M = 300 24.7 / 29.0; the 32-row tiles ran
-// slower with direct loads (M = 128: 27.9 against 24.0).
+//   64 x 128: 4 waves of 32 x 64, 4 stages (96 KiB)
+//   32 x 64: 2 waves of 32 x 32, 4 stages (48 KiB)
+// A launch takes the tile with the least estimated time: rounds of tiles
+// over the compute units, ceil(tiles / kCus), times the tile's measured
+// time per round at K = 4096 (the same for any K up to a factor, so the
+// choice does not depend on K); ties go to the larger tile. The small
+// tiles run their K loop at a latency-bound pace that barely shrinks with
+// the tile, so a round of bigger tiles often beats more rounds of smaller
+// ones. Per-round times, and the launches they give (us at N = K = 4096,
+// medians of interleaved timings; the library GEMM in brackets): 256x256
+// 113.8 (M = 4096), 128x256 64.0 (M = 2048), 128x128 39.6 (M = 1024),
+// 64x128 25.8 (M = 512: 26.5 [26.0]; M = 300: 24.3 [21.7]), 32x64 19.4
+// (M = 1: 19.3 [19.2]; M = 128: 20.2 [20.1]).
 struct TileInfo {
   int bm, bn;
+  int64_t round_ns;  // time of one round of these tiles at K = 4096
   int (*launch)(const GemmArgs&, void*);
 };
-constexpr int kTiles = 6;
+constexpr int kTiles = 5;
 const TileInfo kTileTable[kTiles] = {
-    {256, 256, &launch_dl_tile<4, 2, 2, 4, 2>}, {128, 256, &launch_dl_tile<2, 2, 2, 4, 2>},
-    {128, 128, &launch_dl_tile<2, 2, 2, 2, 3>}, {64, 128, &launch_dl_tile<1, 2, 2, 2, 3>},
-    {32, 128, &launch_tile<1, 1, 1, 4, 64>},  {32, 64, &launch_tile<1, 1, 1, 2, 64>},
+    {256, 256, 113800, &launch_dl_tile<4, 2, 2, 4, 2>},
+    {128, 256, 64000, &launch_dl_tile<2, 2, 2, 4, 2>},
+    {128, 128, 39600, &launch_dl_tile<2, 2, 2, 2, 3>},
+    {64, 128, 25800, &launch_dl_tile<1, 2, 2, 2, 4>},
+    {32, 64, 19400, &launch_dl_tile<1, 1, 1, 2, 4>},
 };
 
 const TileInfo& pick_tile(int64_t M, int64_t N) {
-  for (int i = 0; i < kTiles - 1; ++i) {
+  int best = kTiles - 1;
+  int64_t best_ns = -1;
+  for (int i = 0; i < kTiles; ++i) {
     const TileInfo& t = kTileTable[i];
-    if (((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) >= kCus) return t;
+    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const int64_t rounds = tiles == 0 ? 1 : (tiles + kCus - 1) / kCus;
+    // rounds <= 2^31 / 256 (the host bounds the 32 x 64 tile count), so
+    // rounds * round_ns stays far below 2^63
+    const int64_t ns = rounds * t.round_ns;
+    if (best_ns < 0 || ns < best_ns) {
+      best = i;
+      best_ns = ns;
+    }
   }
-  return kTileTable[kTiles - 1];
+  return kTileTable[best];
 }
 
 }  // namespace

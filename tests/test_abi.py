@@ -448,22 +448,26 @@ def test_gemm_empty_is_a_noop():
     assert gemm(N=0, w=None, y=None) == irn.RMSN_OK
 
 
-GEMM_TILES = [(256, 256), (128, 256), (128, 128), (64, 128), (32, 128), (32, 64)]
+GEMM_TILES = [(256, 256), (128, 256), (128, 128), (64, 128), (32, 64)]
+GEMM_ROUND_US = [113.8, 64.0, 39.6, 25.8, 19.4]  # per round of 256 tiles, K = 4096
 
 
 @pytest.mark.parametrize("M,N,tile", [
-    (1, 4096, (32, 64)), (200, 4096, (32, 64)), (300, 4096, (32, 128)), (500, 4096, (64, 128)),
-    (1000, 4096, (128, 128)), (2000, 4096, (128, 256)), (4000, 4096, (256, 256)),
-    (4096, 11008, (256, 256)), (1024, 2048, (64, 128)), (0, 0, (32, 64)),
+    (1, 4096, (32, 64)), (128, 4096, (32, 64)), (200, 4096, (64, 128)), (300, 4096, (64, 128)),
+    (500, 4096, (64, 128)), (1000, 4096, (128, 128)), (2000, 4096, (128, 256)),
+    (4000, 4096, (256, 256)), (4096, 11008, (256, 256)), (8192, 4096, (256, 256)),
+    (1024, 2048, (64, 128)), (100, 11008, (64, 128)), (64, 4096, (32, 64)), (0, 0, (32, 64)),
+    (1000, 4100, (128, 256)),  # 264 tiles of 128 x 128 would take two rounds
 ])
 def test_gemm_tile_choice(M, N, tile):
-    """The largest tile giving at least 256 tiles (one per compute unit),
-    else the smallest."""
+    """The tile with the least rounds x per-round time; ties to the larger."""
     assert irn.bigemm_bf16_tile(M, N) == tile
-    count = lambda t: -(-M // t[0]) * -(-N // t[1])
+    def cost(t, us):
+        tiles = -(-M // t[0]) * -(-N // t[1])
+        return max(1, -(-tiles // 256)) * us
+    costs = [cost(t, us) for t, us in zip(GEMM_TILES, GEMM_ROUND_US)]
     i = GEMM_TILES.index(tile)
-    assert all(count(t) < 256 for t in GEMM_TILES[:i])
-    assert tile == GEMM_TILES[-1] or count(tile) >= 256
+    assert costs[i] == min(costs) and all(c > costs[i] for c in costs[:i])
 
 
 def test_gemm_tile_rejections():
