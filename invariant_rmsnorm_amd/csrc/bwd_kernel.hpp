@@ -198,6 +198,14 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   };
   auto valid = [&](int v) { return a.D - 8 * (v * LPR + l); };
   auto last = [](int v) { return v == VPL - 1; };
+  // Lanes without group v. Only a lane's last one can be missing (VPL =
+  // ceil(nv / LPR)); the pipelined rows test only that one. The others test
+  // every vector: the branches also keep the scheduler from holding several
+  // vectors' values at once, and without them their many vectors per lane
+  // no longer fit the register file.
+  auto absent = [&](int v) {
+    return MSK && (!PREFETCH || v == VPL - 1) && v * LPR + l >= nv;
+  };
 
   // One workgroup step's loaded rows (U row groups of each input stream).
   struct StepRegs {
@@ -206,35 +214,58 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     u32x4 zq[GATED ? U : 1][GATED ? VPL : 1];   // gate input
     u32x4 hq[ADD ? U : 1][ADD ? VPL : 1];       // fused add: residual input
     float rq[U];
+    int64_t step;  // first row of the block
   };
-  // j-th block of the chunk from the top: group (mine-1-j)/S from the
-  // chunk's first, block S-1-(j%S) within it (the last group may be short)
-  auto step_of = [&](int64_t j) -> int64_t {
-    const int64_t jj = mine - 1 - j;
-    return ((k + (jj / S) * K) * S + jj % S) * ROWS_BLOCK;
+  // The chunk's blocks from the top: its j-th is block jj % S of the
+  // chunk's group jj / S (jj = mine - 1 - j; the last group may be short).
+  // Walked one block at a time, carrying the quotient and the remainder, so
+  // the loop does no division; past the chunk's last block the walk yields
+  // `end`, whose rows are empty.
+  int64_t walk_left = mine;
+  int64_t walk_q = mine > 0 ? (mine - 1) / S : 0;
+  int64_t walk_r = mine > 0 ? (mine - 1) % S : 0;
+  auto next_step = [&]() -> int64_t {
+    const int64_t st = walk_left > 0 ? ((k + walk_q * K) * S + walk_r) * ROWS_BLOCK : end;
+    const bool wrap = walk_r == 0;
+    walk_r = wrap ? S - 1 : walk_r - 1;
+    walk_q = wrap ? walk_q - 1 : walk_q;
+    walk_left = walk_left - 1;
+    return st;
   };
-  auto load_step = [&](int64_t step, StepRegs& b) {
+  // x's cache policy in load_step: kLoadStream or kLoadDefault fixed at
+  // compile time, or kXRuntime, where a.x_stream picks it each step (a
+  // wave-uniform branch).
+  constexpr int kXRuntime = -1;
+  auto load_step = [&](auto xpol, int64_t step, StepRegs& b) __attribute__((always_inline)) {
+    constexpr int XP = decltype(xpol)::value;
+    b.step = step;
+    // x, and the fused add's rin (the forward read it too), take x's policy
+    auto load_xp = [&](__amdgpu_buffer_rsrc_t r, int64_t ld, u32x4(&dst)[VPL]) __attribute__((always_inline)) {
+      if constexpr (XP == kXRuntime) {
+        if (a.x_stream) {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) dst[v] = load_row8<DT, kLoadStream, TAIL>(r, voff(v, ld), valid(v), last(v));
+        } else {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) dst[v] = load_row8<DT, kLoadDefault, TAIL>(r, voff(v, ld), valid(v), last(v));
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          dst[v] = load_row8<DT, (XP == kXRuntime ? kLoadDefault : XP), TAIL>(r, voff(v, ld), valid(v), last(v));
+      }
+    };
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t first = step + group * ROWS_WAVE + u * RPW;
       b.rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
-      const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
-      const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
       // g (and gres, z) are read once: streaming hint. x takes it only when
-      // it is well past the Infinity Cache (a wave-uniform branch).
-      if (a.x_stream) {
+      // it is well past the Infinity Cache.
+      const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
-          b.xq[u][v] = load_row8<DT, kLoadStream, TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
-          b.xq[u][v] = load_row8<DT, kLoadDefault, TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
-        }
-      }
+      for (int v = 0; v < VPL; ++v)
+        b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
+      load_xp(rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D), a.ld_x, b.xq[u]);
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
@@ -247,20 +278,10 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         for (int v = 0; v < VPL; ++v)
           b.zq[u][v] = load_row8<DT, kLoadStream, TAIL>(rz, voff(v, a.ld_z), valid(v), last(v));
       }
-      if constexpr (ADD) {  // the forward read it too: x's policy
-        const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
-        if (a.x_stream) {
-#pragma unroll
-          for (int v = 0; v < VPL; ++v)
-            b.hq[u][v] = load_row8<DT, kLoadStream, TAIL>(rh, voff(v, a.ld_rin), valid(v), last(v));
-        } else {
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) b.hq[u][v] = load_row8<DT, kLoadDefault, TAIL>(rh, voff(v, a.ld_rin), valid(v), last(v));
-        }
-      }
+      if constexpr (ADD) load_xp(rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D), a.ld_rin, b.hq[u]);
     }
   };
-  auto process_step = [&](int64_t step, StepRegs& b) {
+  auto process_step = [&](int64_t step, StepRegs& b) __attribute__((always_inline)) {
     // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
     // rounding, as in the forward).
     auto row_values = [&](int u, int v, float (&f)[8]) {
@@ -276,14 +297,6 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t first = step + group * ROWS_WAVE + u * RPW;
       const float r = b.rq[u];
-      {
-        const int lv = valid(VPL - 1);
-        place_row8<DT, TAIL>(b.gq[u][VPL - 1], lv, true);
-        place_row8<DT, TAIL>(b.xq[u][VPL - 1], lv, true);
-        if constexpr (GRES) place_row8<DT, TAIL>(b.rres[u][VPL - 1], lv, true);
-        if constexpr (GATED) place_row8<DT, TAIL>(b.zq[u][VPL - 1], lv, true);
-        if constexpr (ADD) place_row8<DT, TAIL>(b.hq[u][VPL - 1], lv, true);
-      }
       int wbase = 0;
       if constexpr (LEAN) asm("" : "+v"(wbase));
       // Pass 1: the lane partial of s = sum_i (g_i * w_i) * x_i in (vector,
@@ -297,33 +310,58 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       acc_t sa = 0;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (MSK && v * LPR + l >= nv) continue;  // no such vector (weights unset)
-        float gf[8], xf[8], w8[8];
-        unpack8<DT>(b.gq[u][v], gf);
-        row_values(u, v, xf);
-        weights(wbase, v, w8);
+        // Lanes without this vector (weights unset) skip its arithmetic. Its
+        // stores stay outside the branch, at an offset no resource reaches,
+        // so every lane issues the same memory operations: a store count
+        // that differed between the branch's paths would leave the compiler
+        // unsure how many are in flight, and it would then wait for the next
+        // step's loads as well.
+        const bool have = !absent(v);
+        // A partial last group read as the row's last 16 bytes moves into
+        // place here, where it is first used (and stays placed for pass 2).
+        // Placed at the top of the step instead, the shifts would stand right
+        // after the next step's loads and the compiler would make them wait
+        // for part of those loads.
+        if (v == VPL - 1) {
+          const int lv = valid(VPL - 1);
+          place_row8<DT, TAIL>(b.gq[u][VPL - 1], lv, true);
+          place_row8<DT, TAIL>(b.xq[u][VPL - 1], lv, true);
+          if constexpr (GATED) place_row8<DT, TAIL>(b.zq[u][VPL - 1], lv, true);
+          if constexpr (ADD) place_row8<DT, TAIL>(b.hq[u][VPL - 1], lv, true);
+        }
+        [[maybe_unused]] float dz8[8];
         if constexpr (GATED) {
-          float zf[8], dz8[8];
-          unpack8<DT>(b.zq[u][v], zf);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) dz8[k] = 0.0f;
+        }
+        if (have) {
+          float gf[8], xf[8], w8[8];
+          unpack8<DT>(b.gq[u][v], gf);
+          row_values(u, v, xf);
+          weights(wbase, v, w8);
+          if constexpr (GATED) {
+            float zf[8];
+            unpack8<DT>(b.zq[u][v], zf);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              float ag, dag;
+              gate_and_grad<ACT>(zf[k], ag, dag);
+              const float xr = xf[k] * r;
+              const float nw = xr * w8[k];
+              const float gnw = gf[k] * nw;
+              dz8[k] = gnw * dag;
+              gf[k] = gf[k] * ag;
+            }
+          }
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            float ag, dag;
-            gate_and_grad<ACT>(zf[k], ag, dag);
-            const float xr = xf[k] * r;
-            const float nw = xr * w8[k];
-            const float gnw = gf[k] * nw;
-            dz8[k] = gnw * dag;
-            gf[k] = gf[k] * ag;
+            const float gw = gf[k] * w8[k];
+            const float t = gw * xf[k];
+            sa = acc_add(sa, t);
+            acc[v][k] = __builtin_fmaf(gf[k] * xf[k], r, acc[v][k]);
           }
-          store_row8<DT>(pack8<DT>(dz8), rdz, voff(v, a.ld_dz), valid(v), last(v));
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float gw = gf[k] * w8[k];
-          const float t = gw * xf[k];
-          sa = acc_add(sa, t);
-          acc[v][k] = __builtin_fmaf(gf[k] * xf[k], r, acc[v][k]);
-        }
+        if constexpr (GATED) store_row8<DT>(pack8<DT>(dz8), rdz, voff(v, a.ld_dz), valid(v), last(v));
         // one vector at a time: without this fence the scheduler unpacks the
         // whole row up front and the kernel runs ~10% slower (measured)
         __builtin_amdgcn_sched_barrier(0);
@@ -349,29 +387,37 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       const auto rdx = rows_rsrc(a.dx, first, a.dx != nullptr ? end : first, RPW, a.ld_dx, a.D);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (MSK && v * LPR + l >= nv) continue;
-        float gf[8], xf[8], w8[8], o[8];
-        unpack8<DT>(b.gq[u][v], gf);
-        row_values(u, v, xf);
-        weights(wbase, v, w8);
-        if constexpr (GATED) {
-          float zf[8];
-          unpack8<DT>(b.zq[u][v], zf);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) gf[k] = gf[k] * gate<ACT>(zf[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float gw = gf[k] * w8[k];
-          const float t1 = gw * r;
-          const float t2 = xf[k] * c;
-          o[k] = t1 - t2;
-        }
+        const bool have = !absent(v);
         if constexpr (GRES) {
-          float rf[8];
-          unpack8<DT>(b.rres[u][v], rf);
+          if (v == VPL - 1) place_row8<DT, TAIL>(b.rres[u][VPL - 1], valid(VPL - 1), true);
+        }
+        float o[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
+        for (int k = 0; k < 8; ++k) o[k] = 0.0f;
+        if (have) {
+          float gf[8], xf[8], w8[8];
+          unpack8<DT>(b.gq[u][v], gf);
+          row_values(u, v, xf);
+          weights(wbase, v, w8);
+          if constexpr (GATED) {
+            float zf[8];
+            unpack8<DT>(b.zq[u][v], zf);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) gf[k] = gf[k] * gate<ACT>(zf[k]);
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float gw = gf[k] * w8[k];
+            const float t1 = gw * r;
+            const float t2 = xf[k] * c;
+            o[k] = t1 - t2;
+          }
+          if constexpr (GRES) {
+            float rf[8];
+            unpack8<DT>(b.rres[u][v], rf);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = o[k] + rf[k];
+          }
         }
         store_row8<DT>(pack8<DT>(o), rdx, voff(v, a.ld_dx), valid(v), last(v));
         __builtin_amdgcn_sched_barrier(0);
@@ -383,23 +429,37 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     // Software pipeline over two register sets that swap roles each step
     // (no copy between them: a copy would wait for every outstanding memory
     // operation, the previous step's stores included): the next step's
-    // loads are in flight while this step computes.
+    // loads are in flight while this step computes. Every load is issued
+    // unconditionally: past the chunk's last step the rows start at `end`,
+    // so the resources are empty and the loads read zeros without touching
+    // memory. A load under a branch would leave the compiler unsure how many
+    // operations are in flight where the paths meet, and it would then wait
+    // for all of them (the next step's loads included) before using the
+    // other set. The loop leaves by `break`, so its back edge carries a
+    // single path.
     StepRegs ra, rb;
-    if (mine > 0) load_step(step_of(0), ra);
-    for (int64_t j = 0; j < mine; j += 2) {
-      if (j + 1 < mine) load_step(step_of(j + 1), rb);
-      process_step(step_of(j), ra);
-      if (j + 1 < mine) {
-        if (j + 2 < mine) load_step(step_of(j + 2), ra);
-        process_step(step_of(j + 1), rb);
+    // x's policy is fixed for the whole loop: a branch between two forms of
+    // the loads inside it would again leave the compiler unsure of the count.
+    auto run = [&](auto xpol) __attribute__((always_inline)) {
+      if (mine > 0) {
+        load_step(xpol, next_step(), ra);
+        for (int64_t j = 0;; j += 2) {
+          load_step(xpol, next_step(), rb);
+          process_step(ra.step, ra);
+          if (j + 1 >= mine) break;
+          load_step(xpol, next_step(), ra);
+          process_step(rb.step, rb);
+          if (j + 2 >= mine) break;
+        }
       }
-    }
+    };
+    if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
+    else run(std::integral_constant<int, kLoadDefault>{});
   } else {
     for (int64_t j = 0; j < mine; ++j) {
       StepRegs cur;
-      const int64_t step = step_of(j);
-      load_step(step, cur);
-      process_step(step, cur);
+      load_step(std::integral_constant<int, kXRuntime>{}, next_step(), cur);
+      process_step(cur.step, cur);
     }
   }
 
@@ -432,7 +492,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     acc[v][6] = acc[v][6] + p1.z; acc[v][7] = acc[v][7] + p1.w;
   };
   // lanes without group v
-  auto absent = [&](int v) { return MSK && v * LPR + l >= nv; };
+  auto absent_part = [&](int v) { return MSK && v * LPR + l >= nv; };
   float* const out = a.part + static_cast<int64_t>(blockIdx.x) * Dp;
   const bool writer = slot == 0;
 
@@ -440,7 +500,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     // Four waves per row: every wave owns distinct columns.
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      if (absent(v)) continue;
+      if (absent_part(v)) continue;
       put(out, v);
     }
   } else if constexpr (WPR == 2) {
@@ -451,7 +511,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (wave >= 2) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (absent(v)) continue;
+        if (absent_part(v)) continue;
         put(lds, v);
       }
     }
@@ -459,7 +519,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (wave < 2) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (absent(v)) continue;
+        if (absent_part(v)) continue;
         add_from(lds, v);
         put(out, v);
       }
@@ -472,7 +532,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (wave >= 2 && writer) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (absent(v)) continue;
+        if (absent_part(v)) continue;
         put(lds_row(wave - 2), v);
       }
     }
@@ -480,7 +540,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (wave < 2 && writer) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (absent(v)) continue;
+        if (absent_part(v)) continue;
         add_from(lds_row(wave), v);
         if (wave == 1) put(lds_row(wave), v);  // the same wave read this row just above
       }
@@ -489,7 +549,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (wave == 0 && writer) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (absent(v)) continue;
+        if (absent_part(v)) continue;
         add_from(lds_row(1), v);
         put(out, v);
       }

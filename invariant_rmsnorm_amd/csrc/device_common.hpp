@@ -26,6 +26,7 @@ enum : int { kElem = 8, kBf16E = kBf16 | kElem, kF16E = kF16 | kElem };
 constexpr int value_dt(int DT) { return DT & ~kElem; }
 constexpr bool elem_dt(int DT) { return (DT & kElem) != 0; }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -177,19 +178,37 @@ __device__ __forceinline__ void place_row8(u32x4& q, int left, bool last) {
   }
 }
 // Stores a group the same way (non-temporal); a partial last group writes
-// only its elements inside the row.
+// only its elements inside the row. A lane's last group in a row of any
+// length goes out as the same four stores on every lane, whatever the group
+// holds: one 16-byte store for a full group, and pieces of 8, 4 and 2 bytes
+// for a partial one (1..7 elements); the stores a lane does not need get an
+// offset no resource reaches. (A number of stores that differed between
+// lanes' branches would leave the compiler unsure how many memory operations
+// are in flight after them, and it would then wait for loads issued ahead
+// for the next rows.)
 template <int DT>
 __device__ __forceinline__ void store_row8(const u32x4& v, __amdgpu_buffer_rsrc_t r, uint32_t off,
                                            int left, bool last) {
-  if (!elem_dt(DT) || !last || left >= 8) {
+  if (!elem_dt(DT) || !last) {
     buf_store16_nt(v, r, off);
     return;
   }
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[e >> 1] >> (16 * (e & 1))), r,
-                                          static_cast<int>(e < left ? off + 2 * e : kOutOfRange), 0, 2);
+  const bool part = left > 0 && left < 8;
+  buf_store16_nt(v, r, left >= 8 ? off : kOutOfRange);
+  // elements 0..3
+  const bool p8 = part && left >= 4;
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, static_cast<int>(p8 ? off : kOutOfRange), 0, 0);
+  // the next two elements, from element b
+  const int b = p8 ? 4 : 0;
+  const bool p4 = part && left - b >= 2;
+  __builtin_amdgcn_raw_buffer_store_b32(p8 ? v.z : v.x, r,
+                                        static_cast<int>(p4 ? off + 2 * b : kOutOfRange), 0, 0);
+  // an odd count's last element e = left - 1 (even: the low half of word e/2)
+  const int e = left - 1;
+  const bool p2 = part && (left & 1) != 0;
+  const uint32_t we = e >= 4 ? (e >= 6 ? v.w : v.z) : (e >= 2 ? v.y : v.x);
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(we & 0xFFFFu), r,
+                                        static_cast<int>(p2 ? off + 2 * e : kOutOfRange), 0, 0);
 }
 
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
