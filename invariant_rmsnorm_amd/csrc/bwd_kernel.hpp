@@ -58,16 +58,24 @@ enum : int {
 // same plan.
 constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_inputs ? 11 : 13); }
 // Load the next step while computing this one (two register sets that swap
-// roles), for rows over 4 waves whose loaded step fits the register file
-// twice: input streams x vectors per lane <= 18 with the whole register file
-// (plain: VPL <= 9; three streams: 6; four: 4), <= 8 at two waves per SIMD.
-// Without it the four waves of a row, held together by the exchange
-// barrier, load and compute in lock step and leave the memory pipe idle
-// while they compute.
-constexpr bool bwd_prefetch(int lpr, int vpl, int mode) {
+// roles) where a wave would otherwise leave the memory pipe idle while it
+// computes, and the loaded step fits the register file twice without
+// scratch (with the whole register file, VPL <= 9 and input streams x VPL
+// <= 21: plain 9, three streams 7, four 5; rows of any length, which hold
+// their tail's shifts too, 18; at two waves per SIMD, streams x VPL <= 8):
+//  - rows over 4 waves: held together by the exchange barrier, the waves
+//    load and compute in lock step;
+//  - one-wave rows from 5 vectors per lane on, where a wave is alone on its
+//    SIMD. Measured against no prefetch (us per 256 MiB of x, cache evicted
+//    / warm): D = 2050 158.2 / 169.3 -> 152.6 / 144.4, 4096 148.3 / 138.2 ->
+//    146.7 / 140.8, 3072 144.5 / 138.0 -> 146.0 / 135.7. With two waves per
+//    SIMD it cost 1-2% (D = 1000, 2048), so narrower rows go without.
+constexpr bool bwd_prefetch(int lpr, int vpl, int mode, int dt) {
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
-  const int budget = bwd_waves_per_eu(vpl) == 1 ? 18 : 8;
-  return lpr > 64 && streams * vpl <= budget;
+  const int cap = elem_dt(dt) ? 18 : 21;
+  const bool fits = bwd_waves_per_eu(vpl) == 1 ? vpl <= 9 && streams * vpl <= cap : streams * vpl <= 8;
+  const bool idle = lpr > 64 || (lpr == 64 && bwd_waves_per_eu(vpl) == 1);
+  return idle && fits;
 }
 
 // LDS floats the rows kernel needs: the weights when held in LDS (one float4
@@ -100,7 +108,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr int ROWS_BLOCK = rows_per_block(LPR, U);
   static_assert(WPR == 1 || (U == 1 && VPL >= kBwdMinVplMulti), "multi-wave rows: one row per step");
   constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
-  constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE);
+  constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE, DT);
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
