@@ -273,7 +273,7 @@ FwdLaunch pick_wide(int vpl, bool masked) {
   }
 }
 
-// Rows over several waves (D > 8192): 9 to 16 vectors per lane.
+// Rows over several waves (D > 4096): 5 to 16 vectors per lane.
 template <int GATE, int DT, int LPR, int VPL = kFwdMinVplMulti>
 FwdLaunch pick_multi(int vpl, bool masked) {
   if constexpr (VPL > kMaxVpl) {

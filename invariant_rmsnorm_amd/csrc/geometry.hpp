@@ -9,10 +9,10 @@
 // (16-byte vectors; when D is not a multiple of 8 the last group is
 // partial), shared by LPR lanes:
 //  - long rows span several wavefronts of one workgroup: LPR = 128 or 256
-//    (VPL = ceil(NV/LPR) <= 16 vectors each). The forward does this past
-//    1024 vectors (D > 8192), over 2 waves up to 2048 vectors and 4 beyond;
-//    the backward past 512 vectors (D > 4096), always over 4 waves, which
-//    keeps VPL small enough for its software pipeline (fwd_geom, bwd_geom);
+//    (VPL = ceil(NV/LPR) <= 16 vectors each). Both kernels do this past 512
+//    vectors (D > 4096): the forward over 2 waves up to 1024 vectors and 4
+//    beyond, the backward always over 4 waves (fwd_geom, bwd_geom); both
+//    keep VPL <= 8 up to 2048 vectors (D = 16384);
 //  - 64 <= NV: LPR = 64, one wavefront (VPL = ceil(NV/64));
 //  - NV < 64: LPR = the smallest power of two >= NV, VPL = 1, and a wave
 //    carries 64/LPR rows side by side.
@@ -29,8 +29,8 @@ constexpr int kWaves = 4;            // wavefronts per workgroup
 constexpr int kBlock = 64 * kWaves;  // threads per workgroup
 constexpr int kMaxD = 32768;
 constexpr int kMaxVpl = 16;      // vectors per lane, in every geometry
-// Vectors per lane of multi-wave rows: forward 9..16, backward 3..16.
-constexpr int kFwdMinVplMulti = 9;
+// Vectors per lane of multi-wave rows: forward 5..16, backward 3..16.
+constexpr int kFwdMinVplMulti = 5;
 constexpr int kBwdMinVplMulti = 3;
 // The backward splits the batch into at most kCus * (its occupancy in
 // workgroups per CU) chunks of rows, one workgroup per chunk. Rows of 5 or
@@ -64,11 +64,16 @@ inline RowGeom multi_wave_geom(int64_t nv, int lpr) {
   return {lpr, static_cast<int>((nv + lpr - 1) / lpr), (nv % lpr) != 0};
 }
 
-// Forward: past 1024 vectors (D > 8192), 2 waves per row up to 2048 vectors,
-// 4 beyond.
+// Forward: past 512 vectors (D > 4096), 2 waves per row up to 1024 vectors,
+// 4 beyond, so a lane holds at most 8 vectors up to D = 16384 and the
+// kernel keeps 4 waves per SIMD (its weights stay in registers). Against one
+// wave per row up to 1024 vectors and 2 up to 2048 (us per 256 MiB of x,
+// cache evicted, same box): D = 5120 98.8 -> 95.6, 6144 105.1 -> 95.9, 8192
+// 108.0 -> 101.6, 10240 109.2 -> 101.8, 12288 103.0 -> 102.2, 16384 104.6
+// -> 101.3; D = 4104 101.3 -> 102.0 (warm 94.3 -> 89.0).
 inline RowGeom fwd_geom(int64_t D) {
   const int64_t nv = (D + 7) / 8;
-  if (nv > 1024) return multi_wave_geom(nv, nv <= 2048 ? 128 : 256);
+  if (nv > 512) return multi_wave_geom(nv, nv <= 1024 ? 128 : 256);
   return single_wave_geom(nv);
 }
 

@@ -81,10 +81,11 @@ def test_prefix_and_offset_slices(gpu, D):
         assert torch.equal(ys, y[a:b]) and torch.equal(rs, r[a:b]) and torch.equal(dxs, dx[a:b])
 
 
-@pytest.mark.parametrize("D", [12288, 32768])
+@pytest.mark.parametrize("D", [4104, 8192, 12288, 32768])
 def test_wide_rows_across_batches(gpu, D):
-    """Rows spread over 2 and 4 waves: a row's y, rstd and dx are the same
-    bytes in batches of 1, 2, 3, 7 and 40 rows at every position."""
+    """Rows spread over 2 waves (forward, D = 4104 and 8192) and 4 waves
+    (forward past 8192, backward past 4096): a row's y, rstd and dx are the
+    same bytes in batches of 1, 2, 3, 7 and 40 rows at every position."""
     T = 40
     x = dev_bf16(synth.normal_bf16(6300 + D, 1, T, D))
     g = dev_bf16(synth.normal_bf16(6300 + D, 2, T, D))
