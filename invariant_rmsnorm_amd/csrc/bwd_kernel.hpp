@@ -61,8 +61,9 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 // roles) where a wave would otherwise leave the memory pipe idle while it
 // computes, and the loaded step fits the register file twice without
 // scratch (with the whole register file, VPL <= 9 and input streams x VPL
-// <= 21: plain 9, three streams 7, four 5; rows of any length, which hold
-// their tail's shifts too, 18; at two waves per SIMD, streams x VPL <= 8):
+// <= 21 for 16-byte rows over 4 waves: plain 9, three streams 7, four 5;
+// 18 for one-wave rows and rows of any length, whose lane offsets and tail
+// shifts take more registers; at two waves per SIMD, streams x VPL <= 8):
 //  - rows over 4 waves: held together by the exchange barrier, the waves
 //    load and compute in lock step;
 //  - one-wave rows from 5 vectors per lane on, where a wave is alone on its
@@ -72,7 +73,7 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 //    SIMD it cost 1-2% (D = 1000, 2048), so narrower rows go without.
 constexpr bool bwd_prefetch(int lpr, int vpl, int mode, int dt) {
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
-  const int cap = elem_dt(dt) ? 18 : 21;
+  const int cap = elem_dt(dt) || lpr <= 64 ? 18 : 21;
   const bool fits = bwd_waves_per_eu(vpl) == 1 ? vpl <= 9 && streams * vpl <= cap : streams * vpl <= 8;
   const bool idle = lpr > 64 || (lpr == 64 && bwd_waves_per_eu(vpl) == 1);
   return idle && fits;
@@ -240,40 +241,26 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     walk_left = walk_left - 1;
     return st;
   };
-  // x's cache policy in load_step: kLoadStream or kLoadDefault fixed at
-  // compile time, or kXRuntime, where a.x_stream picks it each step (a
-  // wave-uniform branch).
-  constexpr int kXRuntime = -1;
+  // One step's loads; x's cache policy (kLoadStream or kLoadDefault) is a
+  // compile-time choice, fixed for a whole loop by its caller.
   auto load_step = [&](auto xpol, int64_t step, StepRegs& b) __attribute__((always_inline)) {
     constexpr int XP = decltype(xpol)::value;
     b.step = step;
-    // x, and the fused add's rin (the forward read it too), take x's policy
-    auto load_xp = [&](__amdgpu_buffer_rsrc_t r, int64_t ld, u32x4(&dst)[VPL]) __attribute__((always_inline)) {
-      if constexpr (XP == kXRuntime) {
-        if (a.x_stream) {
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) dst[v] = load_row8<DT, kLoadStream, TAIL>(r, voff(v, ld), valid(v), last(v));
-        } else {
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) dst[v] = load_row8<DT, kLoadDefault, TAIL>(r, voff(v, ld), valid(v), last(v));
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-          dst[v] = load_row8<DT, (XP == kXRuntime ? kLoadDefault : XP), TAIL>(r, voff(v, ld), valid(v), last(v));
-      }
-    };
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t first = step + group * ROWS_WAVE + u * RPW;
       b.rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
-      // g (and gres, z) are read once: streaming hint. x takes it only when
-      // it is well past the Infinity Cache.
+      // g (and gres, z) are read once: streaming hint. x (and the fused
+      // add's rin, which the forward read too) takes it only when it is well
+      // past the Infinity Cache. g and x alternate, so a vector's pair
+      // arrives together.
       const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
+      const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v)
+      for (int v = 0; v < VPL; ++v) {
         b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
-      load_xp(rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D), a.ld_x, b.xq[u]);
+        b.xq[u][v] = load_row8<DT, XP, TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
+      }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
 #pragma unroll
@@ -286,7 +273,12 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         for (int v = 0; v < VPL; ++v)
           b.zq[u][v] = load_row8<DT, kLoadStream, TAIL>(rz, voff(v, a.ld_z), valid(v), last(v));
       }
-      if constexpr (ADD) load_xp(rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D), a.ld_rin, b.hq[u]);
+      if constexpr (ADD) {
+        const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          b.hq[u][v] = load_row8<DT, XP, TAIL>(rh, voff(v, a.ld_rin), valid(v), last(v));
+      }
     }
   };
   auto process_step = [&](int64_t step, StepRegs& b) __attribute__((always_inline)) {
@@ -464,11 +456,18 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
     else run(std::integral_constant<int, kLoadDefault>{});
   } else {
-    for (int64_t j = 0; j < mine; ++j) {
-      StepRegs cur;
-      load_step(std::integral_constant<int, kXRuntime>{}, next_step(), cur);
-      process_step(cur.step, cur);
-    }
+    // Here too x's policy is fixed for the loop: chosen per step, the
+    // compiler would wait for all of a step's loads before its first
+    // vector's arithmetic instead of for that vector's own.
+    auto run = [&](auto xpol) __attribute__((always_inline)) {
+      for (int64_t j = 0; j < mine; ++j) {
+        StepRegs cur;
+        load_step(xpol, next_step(), cur);
+        process_step(cur.step, cur);
+      }
+    };
+    if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
+    else run(std::integral_constant<int, kLoadDefault>{});
   }
 
   if (!want_part) return;
