@@ -59,7 +59,7 @@ def test_token_and_width_grid(gpu, T, D, zc):
 WIDTHS = [8, 16, 24, 40, 64, 96, 128, 136, 256, 264, 384, 512, 520, 1024, 1536, 2048, 2560,
           3072, 4096, 4104, 5120, 6144, 7168, 8192,
           # rows over 2 waves (8192 < D <= 16384) and 4 waves (D <= 32768)
-          8200, 9216, 12288, 16384, 16392, 18432, 24576, 32768]
+          8200, 9216, 12288, 16384, 16392, 18432, 20480, 24576, 28680, 32768]
 
 
 @pytest.mark.parametrize("D", WIDTHS)
