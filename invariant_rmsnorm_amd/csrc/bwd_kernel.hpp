@@ -241,25 +241,56 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     walk_left = walk_left - 1;
     return st;
   };
-  // One step's loads; x's cache policy (kLoadStream or kLoadDefault) is a
-  // compile-time choice, fixed for a whole loop by its caller.
+  // One step's loads. Two forms, chosen per geometry by measurement (same
+  // box, us per 256 MiB of x, cache evicted; the other form in brackets):
+  //  - x's cache policy fixed for the whole loop (the caller instantiates
+  //    the loop once per policy) and each vector's g and x loads issued
+  //    together: the pipelined rows (D = 4096 145.5 [147.9]) and 16-byte
+  //    rows over 4 waves that keep their weights in registers (D = 20480
+  //    164.0 [177.1], 24576 171.8 [188.4]);
+  //  - x's policy chosen each step (kXRuntime, a wave-uniform branch) and
+  //    all g loads before all x loads: every other row (D = 128 156.9
+  //    [162.4], 2048 152.8 [155.1], 20002 187.1 [199.9], 12290 with the
+  //    residual gradient 236.7 [241.3], 32768 185.0 [198.6]).
+  // x (and the fused add's rin, which the forward read too) takes the
+  // streaming hint only when it is well past the Infinity Cache; g (and
+  // gres, z) always: they are read once.
+  constexpr int kXRuntime = -1;
   auto load_step = [&](auto xpol, int64_t step, StepRegs& b) __attribute__((always_inline)) {
     constexpr int XP = decltype(xpol)::value;
     b.step = step;
+    auto load_xp = [&](__amdgpu_buffer_rsrc_t r, int64_t ld, u32x4(&dst)[VPL]) __attribute__((always_inline)) {
+      if constexpr (XP == kXRuntime) {
+        if (a.x_stream) {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) dst[v] = load_row8<DT, kLoadStream, TAIL>(r, voff(v, ld), valid(v), last(v));
+        } else {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) dst[v] = load_row8<DT, kLoadDefault, TAIL>(r, voff(v, ld), valid(v), last(v));
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          dst[v] = load_row8<DT, (XP == kXRuntime ? kLoadDefault : XP), TAIL>(r, voff(v, ld), valid(v), last(v));
+      }
+    };
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t first = step + group * ROWS_WAVE + u * RPW;
       b.rq[u] = buf_load_f32(f32_rsrc(a.rstd, first, end, RPW), 4 * slot);
-      // g (and gres, z) are read once: streaming hint. x (and the fused
-      // add's rin, which the forward read too) takes it only when it is well
-      // past the Infinity Cache. g and x alternate, so a vector's pair
-      // arrives together.
       const auto rg = rows_rsrc(a.g, first, end, RPW, a.ld_g, a.D);
       const auto rx = rows_rsrc(a.x, first, end, RPW, a.ld_x, a.D);
+      if constexpr (XP == kXRuntime) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
-        b.xq[u][v] = load_row8<DT, XP, TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
+        for (int v = 0; v < VPL; ++v)
+          b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
+        load_xp(rx, a.ld_x, b.xq[u]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          b.gq[u][v] = load_row8<DT, kLoadStream, TAIL>(rg, voff(v, a.ld_g), valid(v), last(v));
+          b.xq[u][v] = load_row8<DT, (XP == kXRuntime ? kLoadDefault : XP), TAIL>(rx, voff(v, a.ld_x), valid(v), last(v));
+        }
       }
       if constexpr (GRES) {
         const auto rgr = rows_rsrc(a.gres, first, end, RPW, a.ld_gres, a.D);
@@ -273,12 +304,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         for (int v = 0; v < VPL; ++v)
           b.zq[u][v] = load_row8<DT, kLoadStream, TAIL>(rz, voff(v, a.ld_z), valid(v), last(v));
       }
-      if constexpr (ADD) {
-        const auto rh = rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D);
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-          b.hq[u][v] = load_row8<DT, XP, TAIL>(rh, voff(v, a.ld_rin), valid(v), last(v));
-      }
+      if constexpr (ADD) load_xp(rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D), a.ld_rin, b.hq[u]);
     }
   };
   auto process_step = [&](int64_t step, StepRegs& b) __attribute__((always_inline)) {
@@ -456,9 +482,6 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
     else run(std::integral_constant<int, kLoadDefault>{});
   } else {
-    // Here too x's policy is fixed for the loop: chosen per step, the
-    // compiler would wait for all of a step's loads before its first
-    // vector's arithmetic instead of for that vector's own.
     auto run = [&](auto xpol) __attribute__((always_inline)) {
       for (int64_t j = 0; j < mine; ++j) {
         StepRegs cur;
@@ -466,8 +489,13 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         process_step(cur.step, cur);
       }
     };
-    if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
-    else run(std::integral_constant<int, kLoadDefault>{});
+    // the load forms above
+    if constexpr (LPR > 64 && !ELEM && !LEAN) {
+      if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
+      else run(std::integral_constant<int, kLoadDefault>{});
+    } else {
+      run(std::integral_constant<int, kXRuntime>{});
+    }
   }
 
   if (!want_part) return;
