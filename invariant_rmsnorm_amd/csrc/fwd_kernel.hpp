@@ -139,15 +139,20 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
     for (int u = 0; u < U; ++u) {
       const int64_t first = group_first(base, u);
       const int64_t row = first + slot;
-      place_row8<DT, TAIL>(xq[u][VPL - 1], valid(VPL - 1), true);
-      if constexpr (TWO) place_row8<DT, TAIL>(zq[u][VPL - 1], valid(VPL - 1), true);
 
       // sum of squares: this lane's elements in (vector, element) order, then
       // the row's fixed butterfly. Squares of bf16 values are exact in fp32;
-      // those of the fused add's h are rounded to fp32 once.
+      // those of the fused add's h are rounded to fp32 once. A partial last
+      // group read as the row's last 16 bytes moves into place where it is
+      // first used: moved at the top of the step, its shifts made the
+      // compiler wait for all of the step's loads before the first vector.
       acc_t ssa = 0;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
+        if (v == VPL - 1) {
+          place_row8<DT, TAIL>(xq[u][VPL - 1], valid(VPL - 1), true);
+          if constexpr (ADD) place_row8<DT, TAIL>(zq[u][VPL - 1], valid(VPL - 1), true);
+        }
         float f[8];
         row_values(xq[u][v], zq[ADD ? u : 0][ADD ? v : 0], f);
 #pragma unroll
@@ -158,6 +163,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_fwd_kernel(FwdArgs a) {
       }
       const float ss = static_cast<float>(row_total<LPR>(ssa, xch, xstep));
       const float r = rstd_of(ss, Df, a.eps);
+      if constexpr (GATED) place_row8<DT, TAIL>(zq[u][VPL - 1], valid(VPL - 1), true);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         opaque(xq[u][v]);
