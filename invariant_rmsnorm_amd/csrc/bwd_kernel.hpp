@@ -61,9 +61,12 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 // roles) where a wave would otherwise leave the memory pipe idle while it
 // computes, and the loaded step fits the register file twice without
 // scratch (with the whole register file, VPL <= 9 and input streams x VPL
-// <= 21 for 16-byte rows over 4 waves: plain 9, three streams 7, four 5;
-// 18 for one-wave rows and rows of any length, whose lane offsets and tail
-// shifts take more registers; at two waves per SIMD, streams x VPL <= 8):
+// <= 21 for rows over 4 waves: plain 9, three streams 7, four 5; 18 for
+// one-wave rows and for fp16 or gated rows of any length, whose lane
+// offsets and tail shifts take more registers; at two waves per SIMD,
+// streams x VPL <= 8). Rows of any length with the residual gradient at 7
+// vectors per lane: D = 12290 233.3 -> 211.1 us per 256 MiB of x (cache
+// evicted) with the larger cap.
 //  - rows over 4 waves: held together by the exchange barrier, the waves
 //    load and compute in lock step;
 //  - one-wave rows from 5 vectors per lane on, where a wave is alone on its
@@ -73,7 +76,8 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 //    SIMD it cost 1-2% (D = 1000, 2048), so narrower rows go without.
 constexpr bool bwd_prefetch(int lpr, int vpl, int mode, int dt) {
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
-  const int cap = elem_dt(dt) || lpr <= 64 ? 18 : 21;
+  const bool wide_cap = lpr > 64 && (!elem_dt(dt) || (dt == kBf16E && mode != kBwdGatedSilu && mode != kBwdGatedSigmoid));
+  const int cap = wide_cap ? 21 : 18;
   const bool fits = bwd_waves_per_eu(vpl) == 1 ? vpl <= 9 && streams * vpl <= cap : streams * vpl <= 8;
   const bool idle = lpr > 64 || (lpr == 64 && bwd_waves_per_eu(vpl) == 1);
   return idle && fits;
