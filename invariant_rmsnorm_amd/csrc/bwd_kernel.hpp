@@ -60,13 +60,15 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 // Load the next step while computing this one (two register sets that swap
 // roles) where a wave would otherwise leave the memory pipe idle while it
 // computes, and the loaded step fits the register file twice without
-// scratch (with the whole register file, VPL <= 9 and input streams x VPL
-// <= 21 for rows over 4 waves: plain 9, three streams 7, four 5; 18 for
-// one-wave rows and for fp16 or gated rows of any length, whose lane
-// offsets and tail shifts take more registers; at two waves per SIMD,
-// streams x VPL <= 8). Rows of any length with the residual gradient at 7
-// vectors per lane: D = 12290 233.3 -> 211.1 us per 256 MiB of x (cache
-// evicted) with the larger cap.
+// scratch, checked with the compiler's resource report for every instance
+// (with the whole register file, VPL <= 9 and input streams x VPL <= 24 for
+// 16-byte rows over 4 waves: plain 9, three streams 8, four 6; 21 for bf16
+// rows of any length over 4 waves without the gate; 18 for one-wave rows
+// and the other rows of any length, whose lane offsets and tail shifts take
+// more registers; at two waves per SIMD, streams x VPL <= 8). Residual
+// gradient, same box, us per 256 MiB of x: D = 12290 (any length, 7
+// vectors) 233.3 -> 211.1 cache evicted with the cap raised from 18 to 21;
+// D = 16384 (8 vectors) 220.3 -> 200.3 after the forward, from 21 to 24.
 //  - rows over 4 waves: held together by the exchange barrier, the waves
 //    load and compute in lock step;
 //  - one-wave rows from 5 vectors per lane on, where a wave is alone on its
@@ -76,8 +78,8 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 //    SIMD it cost 1-2% (D = 1000, 2048), so narrower rows go without.
 constexpr bool bwd_prefetch(int lpr, int vpl, int mode, int dt) {
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
-  const bool wide_cap = lpr > 64 && (!elem_dt(dt) || (dt == kBf16E && mode != kBwdGatedSilu && mode != kBwdGatedSigmoid));
-  const int cap = wide_cap ? 21 : 18;
+  const bool gated = mode == kBwdGatedSilu || mode == kBwdGatedSigmoid;
+  const int cap = lpr <= 64 ? 18 : !elem_dt(dt) ? 24 : dt == kBf16E && !gated ? 21 : 18;
   const bool fits = bwd_waves_per_eu(vpl) == 1 ? vpl <= 9 && streams * vpl <= cap : streams * vpl <= 8;
   const bool idle = lpr > 64 || (lpr == 64 && bwd_waves_per_eu(vpl) == 1);
   return idle && fits;
