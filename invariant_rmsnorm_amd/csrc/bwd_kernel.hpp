@@ -84,6 +84,22 @@ constexpr bool bwd_prefetch(int lpr, int vpl, int mode, int dt) {
   const bool idle = lpr > 64 || (lpr == 64 && bwd_waves_per_eu(vpl) == 1);
   return idle && fits;
 }
+// Rows over 4 waves at one wave per SIMD that do not fit two register sets
+// (longer rows, more input streams) still load the next step early, into
+// the registers this step's second pass frees: once a vector's dx is
+// stored, that vector's loads of the next step are issued into the
+// registers that held it, so the next row streams in while this row's
+// second pass computes and stores. Same box, us per 256 MiB of x, cache
+// evicted, against loading each step after the last one's stores: D =
+// 28672 194.9 -> 175.6, 32768 187.0 -> 172.2, 20002 188.3 -> 180.6, 30002
+// 210.7 -> 197.1; residual gradient D = 24576 224.0 -> 220.0, 32768 224.3
+// -> 217.6; D = 20480-24576 (weights in registers) within 1%. With two
+// workgroups per CU (3 or 4 vectors per lane) the other workgroup already
+// fills the gaps, and it cost: fused add with the residual-output gradient
+// at D = 4100, 248.3 -> 267.9 us.
+constexpr bool bwd_roll(int lpr, int vpl, int mode, int dt) {
+  return lpr > 64 && bwd_waves_per_eu(vpl) == 1 && !bwd_prefetch(lpr, vpl, mode, dt);
+}
 
 // LDS floats the rows kernel needs: the weights when held in LDS (one float4
 // pair per vector slot, laid out so that consecutive lanes read consecutive
@@ -116,6 +132,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   static_assert(WPR == 1 || (U == 1 && VPL >= kBwdMinVplMulti), "multi-wave rows: one row per step");
   constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
   constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE, DT);
+  constexpr bool ROLL = bwd_roll(LPR, VPL, MODE, DT);
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
@@ -251,13 +268,13 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   // box, us per 256 MiB of x, cache evicted; the other form in brackets):
   //  - x's cache policy fixed for the whole loop (the caller instantiates
   //    the loop once per policy) and each vector's g and x loads issued
-  //    together: the pipelined rows (D = 4096 145.5 [147.9]) and 16-byte
-  //    rows over 4 waves that keep their weights in registers (D = 20480
-  //    164.0 [177.1], 24576 171.8 [188.4]);
+  //    together: the pipelined rows (D = 4096 145.5 [147.9]), the rolling
+  //    ones and the other 16-byte rows over 4 waves (before the rolling
+  //    loads: D = 20480 164.0 [177.1], 24576 171.8 [188.4]);
   //  - x's policy chosen each step (kXRuntime, a wave-uniform branch) and
   //    all g loads before all x loads: every other row (D = 128 156.9
-  //    [162.4], 2048 152.8 [155.1], 20002 187.1 [199.9], 12290 with the
-  //    residual gradient 236.7 [241.3], 32768 185.0 [198.6]).
+  //    [162.4], 2048 152.8 [155.1]; before the rolling loads also 20002
+  //    187.1 [199.9] and 32768 185.0 [198.6]).
   // x (and the fused add's rin, which the forward read too) takes the
   // streaming hint only when it is well past the Infinity Cache; g (and
   // gres, z) always: they are read once.
@@ -313,7 +330,31 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       if constexpr (ADD) load_xp(rows_rsrc(a.rin, first, end, RPW, a.ld_rin, a.D), a.ld_rin, b.hq[u]);
     }
   };
-  auto process_step = [&](int64_t step, StepRegs& b) __attribute__((always_inline)) {
+  // Rows of the step after this one, for loads issued while this step's
+  // second pass runs (multi-wave rows without the two-set pipeline).
+  struct NextRows { __amdgpu_buffer_rsrc_t g, x, gr, z, h; };
+  auto roll_begin = [&](int64_t nxt, StepRegs& b) __attribute__((always_inline)) {
+    const int64_t nfirst = nxt + group * ROWS_WAVE;
+    NextRows n;
+    b.step = nxt;
+    b.rq[0] = buf_load_f32(f32_rsrc(a.rstd, nfirst, end, RPW), 4 * slot);
+    n.g = rows_rsrc(a.g, nfirst, end, RPW, a.ld_g, a.D);
+    n.x = rows_rsrc(a.x, nfirst, end, RPW, a.ld_x, a.D);
+    if constexpr (GRES) n.gr = rows_rsrc(a.gres, nfirst, end, RPW, a.ld_gres, a.D);
+    if constexpr (GATED) n.z = rows_rsrc(a.z, nfirst, end, RPW, a.ld_z, a.D);
+    if constexpr (ADD) n.h = rows_rsrc(a.rin, nfirst, end, RPW, a.ld_rin, a.D);
+    return n;
+  };
+  auto roll_load = [&](auto xpol, StepRegs& b, const NextRows& n, int v) __attribute__((always_inline)) {
+    constexpr int XP = decltype(xpol)::value;
+    b.gq[0][v] = load_row8<DT, kLoadStream, TAIL>(n.g, voff(v, a.ld_g), valid(v), last(v));
+    b.xq[0][v] = load_row8<DT, XP, TAIL>(n.x, voff(v, a.ld_x), valid(v), last(v));
+    if constexpr (GRES) b.rres[0][v] = load_row8<DT, kLoadStream, TAIL>(n.gr, voff(v, a.ld_gres), valid(v), last(v));
+    if constexpr (GATED) b.zq[0][v] = load_row8<DT, kLoadStream, TAIL>(n.z, voff(v, a.ld_z), valid(v), last(v));
+    if constexpr (ADD) b.hq[0][v] = load_row8<DT, XP, TAIL>(n.h, voff(v, a.ld_rin), valid(v), last(v));
+  };
+  auto process_step = [&](auto xpol, int64_t step, StepRegs& b, int64_t nxt) __attribute__((always_inline)) {
+    constexpr int XP = decltype(xpol)::value;
     // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
     // rounding, as in the forward).
     auto row_values = [&](int u, int v, float (&f)[8]) {
@@ -417,6 +458,8 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       // Without dx (weight gradient only) the resource is empty and the
       // stores drop; computing dx anyway keeps this loop free of branches.
       const auto rdx = rows_rsrc(a.dx, first, a.dx != nullptr ? end : first, RPW, a.ld_dx, a.D);
+      [[maybe_unused]] NextRows nr;
+      if constexpr (ROLL) nr = roll_begin(nxt, b);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         const bool have = !absent(v);
@@ -452,6 +495,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
           }
         }
         store_row8<DT>(pack8<DT>(o), rdx, voff(v, a.ld_dx), valid(v), last(v));
+        if constexpr (ROLL) roll_load(xpol, b, nr, v);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -477,11 +521,41 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
         load_step(xpol, next_step(), ra);
         for (int64_t j = 0;; j += 2) {
           load_step(xpol, next_step(), rb);
-          process_step(ra.step, ra);
+          process_step(xpol, ra.step, ra, 0);
           if (j + 1 >= mine) break;
           load_step(xpol, next_step(), ra);
-          process_step(rb.step, rb);
+          process_step(xpol, rb.step, rb, 0);
           if (j + 2 >= mine) break;
+        }
+      }
+    };
+    if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
+    else run(std::integral_constant<int, kLoadDefault>{});
+  } else if constexpr (ROLL) {
+    // One register set: pass 2 of each step issues the next step's loads
+    // (roll_load), so each step starts with its rows already in flight. As
+    // in the two-set pipeline, x's policy is fixed for the whole loop and
+    // the loads past the chunk's last step read from empty resources.
+    auto run = [&](auto xpol) __attribute__((always_inline)) {
+      if (mine > 0) {
+        StepRegs cur;
+        // the first step's loads in the order pass 2 issues them, each
+        // vector's after a store that drops (an empty resource), so that
+        // both ways into the loop leave the same operations in flight
+        const NextRows n0 = roll_begin(next_step(), cur);
+        const auto none = rows_rsrc(a.dx, 0, 0, RPW, a.ld_dx, a.D);
+        float zero8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zero8[e] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          store_row8<DT>(pack8<DT>(zero8), none, voff(v, a.ld_dx), valid(v), last(v));
+          roll_load(xpol, cur, n0, v);
+        }
+        for (int64_t j = 0;; ++j) {
+          const int64_t nxt = next_step();
+          process_step(xpol, cur.step, cur, nxt);
+          if (j + 1 >= mine) break;
         }
       }
     };
@@ -492,11 +566,11 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
       for (int64_t j = 0; j < mine; ++j) {
         StepRegs cur;
         load_step(xpol, next_step(), cur);
-        process_step(cur.step, cur);
+        process_step(xpol, cur.step, cur, 0);
       }
     };
     // the load forms above
-    if constexpr (LPR > 64 && !ELEM && !LEAN) {
+    if constexpr (LPR > 64 && !ELEM) {
       if (a.x_stream) run(std::integral_constant<int, kLoadStream>{});
       else run(std::integral_constant<int, kLoadDefault>{});
     } else {
