@@ -242,7 +242,16 @@ inline int cu_count() {
 //   D = 8192   114.6 110.4 110.2 118.7 119.6
 //   D = 16384  109.9 106.2 105.7 111.3 111.5
 //   D = 32768  114.1 108.7 109.1 111.0 111.2
-constexpr int64_t fwd_grid_scale(int lpr, int vpl) { return lpr * vpl >= 1024 ? 2 : 16; }
+// Re-measured on the present kernel, same box, x of 256 MiB, multiples 1 /
+// 2 / 4: D = 8192 103.2 101.7 98.5, 12288 105.2 103.1 98.9, 16384 103.0
+// 101.0 98.1, 20480 106.8 108.7 102.0, 24576 103.8 103.2 103.7, 28672 106.6
+// 105.8 111.2, 32768 113.7 107.4 109.0; 4 against 2 at other batch sizes:
+// D = 8192 T = 65536 394.9 -> 388.5, 10240 T = 13107 101.9 -> 97.0, 12288
+// T = 9000 85.9 -> 81.4, 20480 T = 13107 208.3 -> 206.6, smaller batches
+// within 1 us. Hence 4 up to 2560 groups per row (D = 20480) and 2 beyond.
+constexpr int64_t fwd_grid_scale(int lpr, int vpl) {
+  return lpr * vpl < 1024 ? 16 : lpr * vpl <= 2560 ? 4 : 2;
+}
 
 template <int LPR, int VPL, bool MASKED, int GATE, int DT>
 int launch_inst(const FwdArgs& a, void* stream) {
