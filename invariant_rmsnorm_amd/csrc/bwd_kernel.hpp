@@ -76,11 +76,18 @@ constexpr bool bwd_lean(int vpl, bool three_inputs) { return vpl >= (three_input
 //    / warm): D = 2050 158.2 / 169.3 -> 152.6 / 144.4, 4096 148.3 / 138.2 ->
 //    146.7 / 140.8, 3072 144.5 / 138.0 -> 146.0 / 135.7. With two waves per
 //    SIMD it cost 1-2% (D = 1000, 2048), so narrower rows go without.
+// At two waves per SIMD only the gated rows over 4 waves take a third
+// stream at 3 vectors: their gate arithmetic is long enough that the other
+// workgroup does not hide it (D = 4100 447.1 -> 329.9 us, 4104 446.5 ->
+// 316.1, same box, cache evicted); the residual gradient and the fused add
+// measured slower that way (D = 8192 198.4 -> 206.2, fused add 4104 249.2
+// -> 257.9), and the gated rows at 4 vectors no faster.
 constexpr bool bwd_prefetch(int lpr, int vpl, int mode, int dt) {
   const int streams = 2 + (mode == kBwdPlain ? 0 : 1) + (mode == kBwdAddGres ? 1 : 0);
   const bool gated = mode == kBwdGatedSilu || mode == kBwdGatedSigmoid;
   const int cap = lpr <= 64 ? 18 : !elem_dt(dt) ? 24 : dt == kBf16E && !gated ? 21 : 18;
-  const bool fits = bwd_waves_per_eu(vpl) == 1 ? vpl <= 9 && streams * vpl <= cap : streams * vpl <= 8;
+  const int cap2 = gated && lpr > 64 ? 9 : 8;  // two waves per SIMD
+  const bool fits = bwd_waves_per_eu(vpl) == 1 ? vpl <= 9 && streams * vpl <= cap : streams * vpl <= cap2;
   const bool idle = lpr > 64 || (lpr == 64 && bwd_waves_per_eu(vpl) == 1);
   return idle && fits;
 }
