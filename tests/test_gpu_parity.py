@@ -72,6 +72,15 @@ def test_widths(gpu, D):
     assert_parity(p, run_fwd_bwd(p, True), oracle_all(p, True), True, D)
 
 
+@pytest.mark.parametrize("D", [16392, 18432, 20480, 24576, 28680, 32768])
+def test_long_rows_without_residual_gradient(gpu, D):
+    """Rows over 4 waves past the two-set pipeline (9 to 16 vectors per
+    lane: the next row loaded into the registers the second pass frees),
+    plain backward, 66 chunks of up to 4 row steps each."""
+    p = wl.tiny(D % 16 == 8, T=261, D=D, seed=8500 + D)
+    assert_parity(p, run_fwd_bwd(p, False), oracle_all(p, False), False, D)
+
+
 @pytest.mark.parametrize("D", [128, 4096])
 @pytest.mark.parametrize("T", [2, 3, 4, 5, 31, 63, 64, 65, 127, 129, 511, 513, 2049])
 def test_ragged_batches(gpu, D, T):
