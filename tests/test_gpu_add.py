@@ -26,6 +26,8 @@ WIDTHS = [8, 16, 24, 64, 96, 128, 136, 256, 520, 1024, 2048, 2560, 4096, 4104, 5
           8200, 12288, 16384, 20480, 32768]
 # not multiples of 8: element-wise rows
 WIDTHS += [3, 13, 100, 1001, 4100, 12290, 20003]
+# no lane lacking its last group: 14 and 16 vectors per lane
+WIDTHS += [28671, 32767]
 
 
 def _run(p, with_gro, zc=None):

@@ -33,7 +33,8 @@ ROUNDINGS = [(irn.RMSN_GATED_ROUND_FP32, oracle.FP32_WEIGHT),
 WIDTHS = [8, 64, 96, 128, 136, 1024, 2560, 4096, 4104, 5632, 6144, 8192, 8200, 16384, 18440,
           32768]
 # not multiples of 8: rows of any alignment
-ODD_WIDTHS = [5, 13, 100, 1001, 4100, 12290, 20003]
+# (32767: 4096 groups, so no lane lacks its last one, at 16 vectors per lane)
+ODD_WIDTHS = [5, 13, 100, 1001, 4100, 12290, 20003, 32767]
 
 
 def _rows_for(D):
