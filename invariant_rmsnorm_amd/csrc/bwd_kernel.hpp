@@ -140,6 +140,7 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
   constexpr bool LEAN = bwd_lean(VPL, GATED || ADD);
   constexpr bool PREFETCH = bwd_prefetch(LPR, VPL, MODE, DT);
   constexpr bool ROLL = bwd_roll(LPR, VPL, MODE, DT);
+  static_assert(!ROLL || (U == 1 && RPW == 1), "rolling loads: one row per wave step");
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
@@ -366,7 +367,6 @@ void rmsnorm_bwd_rows_kernel(BwdArgs a) {
     if constexpr (ADD) b.hq[0][v] = load_row8<DT, XP, TAIL>(n.h, voff(v, a.ld_rin), valid(v), last(v));
   };
   auto process_step = [&](auto xpol, int64_t step, StepRegs& b, int64_t nxt) __attribute__((always_inline)) {
-    constexpr int XP = decltype(xpol)::value;
     // The row's values as fp32: x, or for the fused add h = x + rin (one fp32
     // rounding, as in the forward).
     auto row_values = [&](int u, int v, float (&f)[8]) {
