@@ -116,6 +116,29 @@ def test_strided_rows(gpu, D):
     assert torch.all(ys[:, D:].float() == 0) and torch.all(dxs[:, D:].float() == 0)
 
 
+@pytest.mark.parametrize("D", [20003, 32767, 32768])
+def test_long_gated_and_add_rows_across_batches(gpu, D):
+    """Long rows of the gated and fused-add backward (rows over 4 waves that
+    load the next row during the second pass; 32767 is a row of any length
+    where no lane lacks its last group): a row's dx and dz, and its dh, are
+    the same bytes in batches of 1, 2, 3, 7 and 40 rows at every position."""
+    T = 40
+    x = dev_bf16(synth.normal_bf16(6400 + D, 1, T, D))
+    g = dev_bf16(synth.normal_bf16(6400 + D, 2, T, D))
+    z = dev_bf16(synth.normal_bf16(6400 + D, 5, T, D))
+    gamma = dev_f32(wl.gamma_for(6400 + D, D, False))
+    _, rstd = irn.rmsnorm_fwd(x, gamma)
+    fdx, fdz, _ = irn.rmsnorm_gated_bwd(g, x, z, rstd, gamma)
+    _, _, hr = irn.rmsnorm_add_fwd(x, z, gamma)
+    fdh, _ = irn.rmsnorm_add_bwd(g, x, z, hr, gamma, g_residual_out=x, want_dgamma=False)
+    for a, b in ((0, 1), (5, 6), (39, 40), (3, 5), (10, 13), (20, 27), (0, 40)):
+        pdx, pdz, _ = irn.rmsnorm_gated_bwd(g[a:b], x[a:b], z[a:b], rstd[a:b], gamma)
+        assert torch.equal(pdx, fdx[a:b]) and torch.equal(pdz, fdz[a:b]), (a, b)
+        pdh, _ = irn.rmsnorm_add_bwd(g[a:b], x[a:b], z[a:b], hr[a:b], gamma,
+                                     g_residual_out=x[a:b], want_dgamma=False)
+        assert torch.equal(pdh, fdh[a:b]), (a, b)
+
+
 def test_gated_rows_across_batches(gpu):
     """Head-size rows of the gated norm are batch-invariant too."""
     D = 128
